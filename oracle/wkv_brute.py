@@ -1,0 +1,78 @@
+"""Arbitrary-precision brute force for the WKV operator (mpmath, 50 digits).
+
+TEST INFRASTRUCTURE, like the rest of this package: it is the yardstick for the
+float64 oracle on tiny inputs, and nothing on the HIP side uses it.
+
+It evaluates the defining equation of the page "Linear attention without
+writing a CUDA kernel", section "The recurrence" (the wkv_t equation), term by
+term with mpmath's exp. mpmath's exponent range is unbounded for practical
+purposes, so no maximum is factored out: the sums are formed exactly as written.
+A non-empty initial state (n0, d0, m0) contributes n0 * exp(m0 - t w) and
+d0 * exp(m0 - t w) at 0-based position t (the reading stated in the float64
+oracle's docstring).
+"""
+
+from __future__ import annotations
+
+import mpmath
+import numpy as np
+
+
+def wkv_brute(w, u, k, v, state_in=None, dps: int = 50):
+    """Returns (out, state_out) as float64 arrays rounded from mpmath values.
+
+    out: (B, T, C). state_out: (3, B, C) as (N e^-M, D e^-M, M), M the largest
+    exponent present after the last token (the initial state's exponent counts
+    only if its den is non-zero).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    B, T, C = k.shape
+    if state_in is None:
+        n0 = np.zeros((B, C))
+        d0 = np.zeros((B, C))
+        m0 = np.full((B, C), -1e38)
+    else:
+        n0, d0, m0 = (np.asarray(p, dtype=np.float64) for p in state_in)
+    out = np.empty((B, T, C))
+    state = np.empty((3, B, C))
+    with mpmath.workdps(dps):
+        mpf, exp = mpmath.mpf, mpmath.exp
+        for b in range(B):
+            for c in range(C):
+                wc, uc = mpf(w[c]), mpf(u[c])
+                ks = [mpf(x) for x in k[b, :, c]]
+                vs = [mpf(x) for x in v[b, :, c]]
+                has_state = d0[b, c] != 0.0 or n0[b, c] != 0.0
+                for t in range(T):
+                    num = mpf(0)
+                    den = mpf(0)
+                    if has_state:
+                        f = exp(mpf(m0[b, c]) - t * wc)
+                        num += mpf(n0[b, c]) * f
+                        den += mpf(d0[b, c]) * f
+                    for i in range(t):
+                        f = exp(ks[i] - (t - 1 - i) * wc)
+                        num += f * vs[i]
+                        den += f
+                    f = exp(uc + ks[t])
+                    num += f * vs[t]
+                    den += f
+                    out[b, t, c] = float(num / den)
+                # inclusive state after the last token
+                terms = []
+                if has_state:
+                    terms.append((mpf(m0[b, c]) - T * wc, mpf(n0[b, c]), mpf(d0[b, c])))
+                for i in range(T):
+                    terms.append((ks[i] - (T - 1 - i) * wc, vs[i], mpf(1)))
+                live = [x for x in terms if x[2] != 0]
+                if not live:
+                    state[:, b, c] = (0.0, 0.0, -1e38)
+                    continue
+                top = max(x[0] for x in live)
+                N = sum((nc * exp(e - top) for e, nc, _ in terms), mpf(0))
+                D = sum((dc * exp(e - top) for e, _, dc in terms), mpf(0))
+                state[:, b, c] = (float(N), float(D), float(top))
+    return out, state
