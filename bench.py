@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the WKV operator on one MI355X.
+
+Default run (one JSON line on stdout):
+  * prefill: 8 independent layers of wkv_forward at B=8, T=1024, C=768, fp32
+    (the MicroRWKV shape: 8 layers, width 768, 1024-token block), inputs
+    resident in HBM. One "step" = the 8 forward calls on one stream.
+    value = G channel-tokens/s over the timed steps.
+  * roofline: the prefill kernel's average duration from HIP events recorded
+    around every launch inside the timed region, against its algorithmic HBM
+    bytes (read k, v; write out; write the final state; read w, u).
+  * decode: 1024 consecutive wkv_step calls at B=256, C=768 after a T=512
+    prefill; steps/s for eager launches and for one HIP graph of all 1024.
+  * cpu_baseline: the float64 oracle on the host, on the same prefill workload.
+
+--config N measures another workload (0: B=1 T=64 C=768; 2: the decode
+workload's T=512 prefill; 3: B=4 T=16384 C=2048; 4: B=64 T=4096 C=4096 bf16)
+in the same format, without the decode part.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "WKV prefill G channel-tokens/s + % HBM roofline; decode steps/s at B=256"
+PEAK_HBM_GBS = 8000.0
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(B, T, C, io_bytes, state_in=False):
+    """Bytes the operator must move: read k, v and write out (B*T*C each),
+    write the final state (3 planes of B*C fp32), read w and u (C fp32 each),
+    plus reading an initial state when one is given."""
+    b = 3 * io_bytes * B * T * C + 12 * B * C + 8 * C
+    return b + (12 * B * C if state_in else 0)
+
+
+def build_layers(wl, n_layers, dev):
+    import torch
+    from wkv_recurrence_scan_amd import inputs as I
+
+    layers = []
+    for layer in range(n_layers):
+        w, u = I.params(wl, layer)
+        k, v = I.kv(wl, layer)
+        if wl.io == "bf16":
+            kd = torch.from_numpy(I.bf16_bits(k).view(np.int16)).to(dev).view(torch.bfloat16)
+            vd = torch.from_numpy(I.bf16_bits(v).view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            kd = torch.from_numpy(k).to(dev)
+            vd = torch.from_numpy(v).to(dev)
+        layers.append(dict(
+            w=torch.from_numpy(w).to(dev), u=torch.from_numpy(u).to(dev), k=kd, v=vd,
+            out=torch.empty_like(kd),
+            st=torch.empty((3, wl.B, wl.C), dtype=torch.float32, device=dev),
+            host=(w, u, k, v)))
+        del k, v
+    return layers
+
+
+def time_prefill(layers, steps, warmup, path):
+    """Runs warmup + timed steps; returns (ms_per_step, kernel_ms_avg, wall_ms_per_step)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+
+    stream = torch.cuda.current_stream()
+
+    def one_step(evs=None):
+        for i, L in enumerate(layers):
+            if evs is not None:
+                evs[i][0].record(stream)
+            W.wkv_forward_ex(L["w"], L["u"], L["k"], L["v"], None, L["out"], L["st"], path=path)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in layers] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(steps):
+        one_step(evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3
+    total_ms = t_start.elapsed_time(t_end)
+    kms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]
+    return total_ms / steps, float(np.mean(kms)), wall / steps
+
+
+def time_decode(wl, dev, n_steps, use_graph):
+    """1024 wkv_step calls after a T-token prefill; returns steps/s (and the
+    average per-step event time in us for the eager run)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    w, u = I.params(wl)
+    k, v = I.kv(wl)
+    dk, dv = I.decode_kv(wl, steps=n_steps)
+    dw, du = torch.from_numpy(w).to(dev), torch.from_numpy(u).to(dev)
+    pk, pv = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    del k, v
+    ks = torch.from_numpy(dk).to(dev)
+    vs = torch.from_numpy(dv).to(dev)
+    del dk, dv
+    outs = torch.empty_like(ks)
+    _, st0 = W.wkv_forward(dw, du, pk, pv)
+    state = torch.empty_like(st0)
+    stream = torch.cuda.current_stream()
+
+    def run_all():
+        for s in range(n_steps):
+            W.wkv_step(dw, du, ks[s], vs[s], state, outs[s])
+
+    state.copy_(st0)
+    run_all()  # warm-up
+    torch.cuda.synchronize()
+    res = {}
+    state.copy_(st0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    res["steps_per_s"] = n_steps / (ms * 1e-3)
+    res["us_per_step"] = ms * 1e3 / n_steps
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        state.copy_(st0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            run_all()
+        torch.cuda.synchronize()
+        state.copy_(st0)
+        torch.cuda.synchronize()
+        g.replay()  # warm-up replay
+        torch.cuda.synchronize()
+        state.copy_(st0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1)
+        res["graph_steps_per_s"] = n_steps / (gms * 1e-3)
+        res["graph_us_per_step"] = gms * 1e3 / n_steps
+    bytes_step = 36 * wl.B * wl.C + 8 * wl.C
+    res["bytes_per_step"] = bytes_step
+    return res
+
+
+def cpu_baseline(layers, wl, budget_s=15.0):
+    """The float64 oracle on the host over the benchmarked workload: whole batch
+    rows of each layer in turn, stopping once about budget_s seconds of work
+    are done (every row of every layer for the small workloads)."""
+    from oracle import wkv_recurrent
+
+    t0 = time.perf_counter()
+    rows_done = 0
+    total_rows = len(layers) * wl.B
+    rows_per_call = max(1, min(wl.B, 8192 // wl.C))  # the oracle vectorises over lanes
+    for L in layers:
+        w, u, k, v = L["host"]
+        for r in range(0, wl.B, rows_per_call):
+            r1 = min(wl.B, r + rows_per_call)
+            wkv_recurrent(w, u, k[r:r1], v[r:r1])
+            rows_done += r1 - r
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    ct = rows_done * wl.T * wl.C
+    return {"value": round(ct / dt / 1e9, 6), "unit": "G channel-tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows_done} of {total_rows} (layer, batch-row) sequences of "
+                      f"T={wl.T} C={wl.C}; float64 numpy recurrence in one process, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk"])
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this operator is sharded over (batch, channel) "
+              "lanes with no communication, so more GPUs are not part of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W.load_library()
+
+    wl = I.WORKLOADS[args.config]
+    if args.config == 2:
+        wl = wl.scaled(decode_steps=0)
+    n_layers = wl.layers
+    _log(f"generating inputs for {wl.name}")
+    layers = build_layers(wl, n_layers, dev)
+    io_bytes = 2 if wl.io == "bf16" else 4
+    path_used = args.path if args.path != "auto" else W.wkv_select_path(
+        wl.B, wl.T, wl.C, W.WKV_IO_BF16 if wl.io == "bf16" else W.WKV_IO_F32)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        _log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        del a, b
+
+    _log(f"timing {args.steps} steps after {args.warmup} warm-up steps, path={path_used}")
+    ms_step, kms, wall_ms = time_prefill(layers, args.steps, args.warmup, args.path)
+    per_layer_ct = wl.B * wl.T * wl.C
+    ct_step = per_layer_ct * n_layers
+    value = ct_step / (ms_step * 1e-3) / 1e9
+    abytes = algorithmic_bytes(wl.B, wl.T, wl.C, io_bytes)
+    achieved = abytes / (kms * 1e-3) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "G channel-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "C": wl.C, "layers": n_layers,
+                   "io": wl.io, "path": path_used, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": f"wkv_{path_used}_kernel", "kernel_us": round(kms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": abytes},
+        "wall_ms_per_step": round(wall_ms, 5),
+    }
+
+    if args.config == 1 and not args.no_decode:
+        dwl = I.WORKLOADS[2]
+        _log(f"decode: {args.decode_steps} steps at B={dwl.B} C={dwl.C} after T={dwl.T}")
+        d = time_decode(dwl, dev, args.decode_steps, use_graph=True)
+        rec["decode"] = {
+            "workload": dwl.name, "B": dwl.B, "C": dwl.C, "prefill_T": dwl.T,
+            "steps": args.decode_steps,
+            "steps_per_s": round(d["steps_per_s"], 1),
+            "us_per_step": round(d["us_per_step"], 3),
+            "graph_steps_per_s": round(d.get("graph_steps_per_s", 0.0), 1),
+            "graph_us_per_step": round(d.get("graph_us_per_step", 0.0), 3),
+            "bytes_per_step": d["bytes_per_step"],
+        }
+
+    if not args.no_cpu_baseline:
+        _log("cpu baseline: float64 oracle")
+        rec["cpu_baseline"] = cpu_baseline(layers, wl)
+
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

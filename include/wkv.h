@@ -1,0 +1,150 @@
+/*
+ * wkv.h -- C interface of libwkv: the RWKV weighted-key-value (WKV) operator
+ * on AMD MI355X (gfx950), prefill and decode.
+ *
+ * The operator
+ * ------------
+ * Defined on the page "Linear attention without writing a CUDA kernel",
+ * section "The recurrence" (the wkv_t equation): for every channel c of every
+ * sequence b independently, the output at position t is a weighted mean of the
+ * values seen so far,
+ *
+ *     out_t = ( sum_{i<t} e^{k_i - (t-1-i) w} v_i + e^{u + k_t} v_t )
+ *           / ( sum_{i<t} e^{k_i - (t-1-i) w}     + e^{u + k_t}     )
+ *
+ * where w > 0 is the channel's decay rate (each step back in time costs a
+ * factor e^{-w}; the newest past token is not decayed) and u is the channel's
+ * bonus for the current token. The same section carries the sums forward as a
+ * state (num, den, max_exp): the true sums are num * e^{max_exp} and
+ * den * e^{max_exp}, kept relative to a running maximum exponent the way a
+ * stable softmax is. A step outputs from the state as it stands plus the bonus
+ * term, then decays the state by e^{-w} and adds the current token (no bonus).
+ *
+ * Memory layout and ownership
+ * ---------------------------
+ * All array arguments are HIP device pointers owned by the caller; the library
+ * allocates no device memory and keeps no state between calls apart from a
+ * once-per-device property query. Row-major, C fastest:
+ *   k, v, out : [B][T][C]  (wkv_step: [B][C])   fp32, or bf16 in the _bf16 calls
+ *   w, u      : [C] fp32
+ *   state     : [3][B][C] fp32, three planes num, den, max_exp.
+ * The empty state (before any token) is num = den = 0, max_exp = -1e38; use
+ * that, not -inf. A state passed in need not be normalised: any (n, d, m) with
+ * d > 0 describes the sums n e^m, d e^m.
+ *
+ * Calls are asynchronous: they validate arguments, enqueue kernels on `stream`
+ * (0 = the null stream) and return. Device-side faults surface at the caller's
+ * next synchronisation. Every call is thread-safe. Inputs are not modified
+ * except `state` of wkv_step, which is updated in place.
+ *
+ * Value preconditions (not checked on the device): w > 0 and finite; k, u
+ * finite; v finite. Keys of any finite size are handled (the state is
+ * rescaled against its running maximum); NaN/Inf inputs give unspecified
+ * results.
+ *
+ * Errors
+ * ------
+ * Every entry point returns WKV_OK (0) or one of the wkv_status codes below;
+ * on error nothing has been enqueued. wkv_status_string() names a code.
+ */
+#ifndef WKV_H_
+#define WKV_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wkv_status {
+  WKV_OK = 0,
+  WKV_ERR_NULL = 1,   /* a required pointer is NULL                              */
+  WKV_ERR_DIM = 2,    /* negative size, or B*T*C (in bytes) does not fit 63 bits  */
+  WKV_ERR_ALIGN = 3,  /* a pointer is not aligned to its element size             */
+  WKV_ERR_ALIAS = 4,  /* an output overlaps an input or another output            */
+  WKV_ERR_LAUNCH = 5, /* the kernel launch failed (see wkv_last_hip_error)        */
+  WKV_ERR_DEVICE = 6, /* no usable HIP device is current                          */
+  WKV_ERR_ARG = 7     /* an enumerated argument (io, path) is out of range        */
+} wkv_status;
+
+/* Element type of k, v and out (w, u and the state are always fp32). */
+enum { WKV_IO_F32 = 0, WKV_IO_BF16 = 1 };
+
+/* Prefill kernels. AUTO picks SEQ when B*C alone fills the GPU, else CHUNK.
+ * Both compute the same function; they may differ in the last bits. */
+enum { WKV_PATH_AUTO = 0, WKV_PATH_SEQ = 1, WKV_PATH_CHUNK = 2 };
+
+/* Prefill / training form over a whole sequence (page "Linear attention
+ * without writing a CUDA kernel", section "The recurrence", wkv_t equation).
+ *
+ *   B, T, C    sizes (>= 0). B == 0 or C == 0: nothing to do, WKV_OK.
+ *              T == 0: state_out receives state_in (or the empty state).
+ *   w, u       [C] fp32 decay rate (> 0) and current-token bonus.
+ *   k, v       [B][T][C] fp32 keys and values.
+ *   state_in   [3][B][C] state before token 0, or NULL for the empty state.
+ *   out        [B][T][C] fp32 outputs, written for every position.
+ *   state_out  [3][B][C] state after token T-1 (inclusive: the next step's
+ *              output uses it as it stands), or NULL to skip it. May be the
+ *              same pointer as state_in (read before written, per lane); any
+ *              other overlap with an input is WKV_ERR_ALIAS, as is any overlap
+ *              of out with another argument.
+ *   stream     HIP stream to enqueue on (0: null stream).
+ */
+int wkv_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                const float* k, const float* v, const float* state_in, float* out,
+                float* state_out, hipStream_t stream);
+
+/* As wkv_forward with k, v, out in bf16 (raw 16-bit patterns). Inputs are
+ * widened exactly to fp32; all arithmetic and the state are fp32; outputs are
+ * rounded to the nearest bf16 (ties to even). */
+int wkv_forward_bf16(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                     const uint16_t* k, const uint16_t* v, const float* state_in,
+                     uint16_t* out, float* state_out, hipStream_t stream);
+
+/* As wkv_forward / wkv_forward_bf16 with the element type (WKV_IO_*) and the
+ * prefill kernel (WKV_PATH_*) chosen by the caller; k, v, out point to
+ * elements of that type. */
+int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                   const void* k, const void* v, const float* state_in, void* out,
+                   float* state_out, int io, int path, hipStream_t stream);
+
+/* The kernel WKV_PATH_AUTO would use for these sizes on the current device
+ * (WKV_PATH_SEQ or WKV_PATH_CHUNK), or a negative wkv_status on error. */
+int wkv_select_path(int64_t B, int64_t T, int64_t C, int io);
+
+/* One decode step for B sequences at once (page "Linear attention without
+ * writing a CUDA kernel", section "The recurrence", the step function that
+ * carries num, den and max_exp).
+ *
+ *   B, C       sizes (>= 0); zero is a no-op.
+ *   w, u       [C] fp32.
+ *   k, v       [B][C] fp32, the current token.
+ *   state      [3][B][C] fp32, read and then overwritten with the state after
+ *              this token.
+ *   out        [B][C] fp32 output for this token. Must not overlap any other
+ *              argument.
+ */
+int wkv_step(int64_t B, int64_t C, const float* w, const float* u, const float* k,
+             const float* v, float* state, float* out, hipStream_t stream);
+
+/* As wkv_step with k, v, out in bf16; state stays fp32. */
+int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const uint16_t* k,
+                  const uint16_t* v, float* state, uint16_t* out, hipStream_t stream);
+
+/* Static, NUL-terminated name of a wkv_status code. */
+const char* wkv_status_string(int status);
+
+/* hipError_t of the last WKV_ERR_LAUNCH / WKV_ERR_DEVICE returned on the
+ * calling thread (0 if none). */
+int wkv_last_hip_error(void);
+
+/* Interface version; bumped on any incompatible change of this header. */
+int wkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV_H_ */

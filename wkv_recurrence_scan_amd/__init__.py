@@ -1,0 +1,32 @@
+"""RWKV weighted-key-value (WKV) operator on AMD MI355X (gfx950).
+
+The work is done by hand-written HIP kernels in libwkv.so behind the C
+interface declared in include/wkv.h; this package only marshals torch tensors
+into that interface (see _lib). Build the library with
+`python -m wkv_recurrence_scan_amd.build`.
+
+    out, state = wkv_forward(w, u, k, v)            # prefill, float32
+    out, state = wkv_forward_bf16(w, u, k, v)       # prefill, bfloat16 I/O
+    y = wkv_step(w, u, k_t, v_t, state)             # decode, state in place
+"""
+
+from ._lib import (  # noqa: F401
+    LIBRARY_PATH,
+    WKV_IO_BF16,
+    WKV_IO_F32,
+    WKV_PATH_AUTO,
+    WKV_PATH_CHUNK,
+    WKV_PATH_SEQ,
+    WKVError,
+    forward,
+    load_library,
+    step,
+    wkv_abi_version,
+    wkv_forward,
+    wkv_forward_bf16,
+    wkv_forward_ex,
+    wkv_select_path,
+    wkv_status_string,
+    wkv_step,
+    wkv_step_bf16,
+)

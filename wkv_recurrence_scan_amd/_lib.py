@@ -1,0 +1,243 @@
+"""ctypes binding of libwkv.so (include/wkv.h): argument marshalling only.
+
+Each function here has the name of the C entry point it calls and does no
+arithmetic of the operator: it checks that the torch tensors it was given have
+the device, dtype, shape and layout the C interface documents, allocates the
+outputs the caller did not supply, and passes raw device pointers plus the
+current HIP stream of the tensors' device. Everything else happens in the HIP
+kernels behind the C interface. There is no fallback: if the library cannot be
+loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libwkv.so")
+
+WKV_IO_F32, WKV_IO_BF16 = 0, 1
+WKV_PATH_AUTO, WKV_PATH_SEQ, WKV_PATH_CHUNK = 0, 1, 2
+_PATHS = {"auto": WKV_PATH_AUTO, "seq": WKV_PATH_SEQ, "chunk": WKV_PATH_CHUNK}
+
+_lib = None
+
+
+class WKVError(RuntimeError):
+    """A libwkv entry point returned a non-zero wkv_status."""
+
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{fn} failed: {wkv_status_string(status)}"
+        if hip_error:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libwkv.so (built by wkv_recurrence_scan_amd.build) once."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise RuntimeError(
+            f"{LIBRARY_PATH} is missing: build it with "
+            "`python -m wkv_recurrence_scan_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    sigs = {
+        "wkv_forward": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
+        "wkv_forward_bf16": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
+        "wkv_forward_ex": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp],
+        "wkv_select_path": [i64, i64, i64, ci],
+        "wkv_step": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
+        "wkv_step_bf16": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
+        "wkv_status_string": [ci],
+        "wkv_last_hip_error": [],
+        "wkv_abi_version": [],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "wkv_status_string" else ctypes.c_int
+    if lib.wkv_abi_version() != 1:
+        raise RuntimeError(f"{LIBRARY_PATH}: unexpected ABI version {lib.wkv_abi_version()}")
+    _lib = lib
+    return lib
+
+
+def wkv_status_string(status: int) -> str:
+    return load_library().wkv_status_string(int(status)).decode()
+
+
+def wkv_abi_version() -> int:
+    return load_library().wkv_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise WKVError(fn, status, load_library().wkv_last_hip_error())
+
+
+def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   state_in: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   state_out: Optional[torch.Tensor] = None, *, path: str = "auto",
+                   want_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill over (B, T, C). k, v: float32 or bfloat16 (same dtype; out gets
+    it too); w, u: (C,) float32; states: (3, B, C) float32. Returns
+    (out, state_out); state_out is None when want_state is False and none was
+    given. path: "auto", "seq" or "chunk"."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"k must be float32 or bfloat16, got {k.dtype}")
+    if path not in _PATHS:
+        raise ValueError(f"path must be one of {sorted(_PATHS)}")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    _need(v, "v", k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    _need(k, "k", k.dtype, (B, T, C), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=k.dtype, device=dev)
+    _need(out, "out", k.dtype, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (3, B, C), dev)
+    io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
+    with torch.cuda.device(dev):
+        st = lib.wkv_forward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                                _ptr(out), _ptr(state_out), io, _PATHS[path],
+                                _stream_handle(dev, stream))
+    _check(st, "wkv_forward_ex")
+    return out, state_out
+
+
+def wkv_forward(w, u, k, v, state_in=None, out=None, state_out=None, *, want_state=True,
+                stream=None):
+    """wkv_forward: float32 k, v, out; the kernel is chosen by the library."""
+    if k.dtype != torch.float32:
+        raise TypeError("wkv_forward takes float32 k, v (use wkv_forward_bf16 for bfloat16)")
+    return _forward_fixed("wkv_forward", w, u, k, v, state_in, out, state_out, want_state, stream)
+
+
+def wkv_forward_bf16(w, u, k, v, state_in=None, out=None, state_out=None, *, want_state=True,
+                     stream=None):
+    """wkv_forward_bf16: bfloat16 k, v, out; fp32 w, u and state."""
+    if k.dtype != torch.bfloat16:
+        raise TypeError("wkv_forward_bf16 takes bfloat16 k, v")
+    return _forward_fixed("wkv_forward_bf16", w, u, k, v, state_in, out, state_out, want_state,
+                          stream)
+
+
+def _forward_fixed(name, w, u, k, v, state_in, out, state_out, want_state, stream):
+    lib = load_library()
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    for t, nm, dt, shp in ((k, "k", k.dtype, (B, T, C)), (v, "v", k.dtype, (B, T, C)),
+                           (w, "w", torch.float32, (C,)), (u, "u", torch.float32, (C,))):
+        _need(t, nm, dt, shp, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=k.dtype, device=dev)
+    _need(out, "out", k.dtype, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (3, B, C), dev)
+    with torch.cuda.device(dev):
+        st = getattr(lib, name)(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                                _ptr(out), _ptr(state_out), _stream_handle(dev, stream))
+    _check(st, name)
+    return out, state_out
+
+
+def _step_fixed(name, dtype, w, u, k, v, state, out, stream):
+    lib = load_library()
+    if k.dim() != 2:
+        raise ValueError(f"k must be (B, C), got shape {tuple(k.shape)}")
+    B, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    for t, nm, dt, shp in ((k, "k", dtype, (B, C)), (v, "v", dtype, (B, C)),
+                           (w, "w", torch.float32, (C,)), (u, "u", torch.float32, (C,)),
+                           (state, "state", torch.float32, (3, B, C))):
+        _need(t, nm, dt, shp, dev)
+    if out is None:
+        out = torch.empty((B, C), dtype=dtype, device=dev)
+    _need(out, "out", dtype, (B, C), dev)
+    with torch.cuda.device(dev):
+        st = getattr(lib, name)(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state), _ptr(out),
+                                _stream_handle(dev, stream))
+    _check(st, name)
+    return out
+
+
+def wkv_step(w, u, k, v, state, out=None, *, stream=None) -> torch.Tensor:
+    """wkv_step: one float32 token per sequence, (B, C); state (3, B, C) is
+    updated in place. Returns out (B, C)."""
+    return _step_fixed("wkv_step", torch.float32, w, u, k, v, state, out, stream)
+
+
+def wkv_step_bf16(w, u, k, v, state, out=None, *, stream=None) -> torch.Tensor:
+    """wkv_step_bf16: bfloat16 k, v, out; fp32 state updated in place."""
+    return _step_fixed("wkv_step_bf16", torch.bfloat16, w, u, k, v, state, out, stream)
+
+
+def wkv_select_path(B: int, T: int, C: int, io: int = WKV_IO_F32) -> str:
+    """Name of the kernel the library's automatic choice uses for these sizes
+    on the current device: "seq" or "chunk"."""
+    r = load_library().wkv_select_path(B, T, C, io)
+    if r < 0:
+        raise WKVError("wkv_select_path", -r)
+    return {WKV_PATH_SEQ: "seq", WKV_PATH_CHUNK: "chunk"}[r]
+
+
+def forward(w, u, k, v, state=None, *, path="auto", out=None, state_out=None):
+    """Convenience: prefill for float32 or bfloat16 k, v. Returns (out, state_out)."""
+    return wkv_forward_ex(w, u, k, v, state, out, state_out, path=path)
+
+
+def step(w, u, k, v, state, *, out=None):
+    """Convenience: one decode step for float32 or bfloat16 k, v; state in place."""
+    if k.dtype == torch.bfloat16:
+        return wkv_step_bf16(w, u, k, v, state, out)
+    return wkv_step(w, u, k, v, state, out)

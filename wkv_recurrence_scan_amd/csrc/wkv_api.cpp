@@ -1,0 +1,208 @@
+// C interface of libwkv (declared in include/wkv.h): argument validation,
+// kernel selection and launch on the caller's stream. No device memory is
+// allocated here; the only state kept is a per-device compute-unit count,
+// queried once.
+#include "wkv.h"
+
+#include <atomic>
+#include <cstdint>
+
+#include "wkv_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0: not yet queried
+
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int fail(int status, hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return status;
+}
+
+bool mul3(int64_t a, int64_t b, int64_t c, int64_t* r) {
+  int64_t ab;
+  return !__builtin_mul_overflow(a, b, &ab) && !__builtin_mul_overflow(ab, c, r);
+}
+
+// [p, p + bytes) and [q, q + bytes2) share a byte (empty ranges never do).
+bool overlaps(const void* p, int64_t bytes, const void* q, int64_t bytes2) {
+  if (p == nullptr || q == nullptr || bytes <= 0 || bytes2 <= 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + static_cast<uintptr_t>(bytes2) && b < a + static_cast<uintptr_t>(bytes);
+}
+
+bool misaligned(const void* p, int bytes) {
+  return p != nullptr && reinterpret_cast<uintptr_t>(p) % bytes != 0;
+}
+
+// Largest byte count a single tensor may span: keeps every index computation
+// in the kernels inside int64.
+constexpr int64_t kMaxBytes = int64_t(1) << 60;
+
+int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev) {
+  // The sequential scan needs no cross-thread combine, so it wins whenever B*C
+  // lanes alone give every SIMD at least one wave (4 SIMDs per CU); below that
+  // the chunked scan splits time to create the missing parallelism.
+  const int64_t per_thread = io == wkv::kBf16 ? 2 : 1;
+  const int64_t waves = (B * C / per_thread + 63) / 64;
+  if (T < 32) return WKV_PATH_SEQ;
+  return waves >= 4LL * cu_count(dev) ? WKV_PATH_SEQ : WKV_PATH_CHUNK;
+}
+
+int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
+                 const void* v, const float* state_in, void* out, float* state_out, int io,
+                 int path, hipStream_t stream) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
+  if (path != WKV_PATH_AUTO && path != WKV_PATH_SEQ && path != WKV_PATH_CHUNK) return WKV_ERR_ARG;
+  if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+  const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
+  int64_t seq_bytes, state_bytes;
+  if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, es, &seq_bytes) ||
+      seq_bytes > kMaxBytes)
+    return WKV_ERR_DIM;
+  if (!mul3(B, C, 12, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (B == 0 || C == 0) return WKV_OK;
+
+  if (w == nullptr || u == nullptr) return WKV_ERR_NULL;
+  if (T > 0 && (k == nullptr || v == nullptr || out == nullptr)) return WKV_ERR_NULL;
+  if (misaligned(w, 4) || misaligned(u, 4) || misaligned(state_in, 4) || misaligned(state_out, 4))
+    return WKV_ERR_ALIGN;
+  if (misaligned(k, es) || misaligned(v, es) || misaligned(out, es)) return WKV_ERR_ALIGN;
+
+  const int64_t pbytes = C * 4;
+  const int64_t sbytes = T > 0 ? seq_bytes : 0;
+  // out must not touch anything else
+  if (overlaps(out, sbytes, k, sbytes) || overlaps(out, sbytes, v, sbytes) ||
+      overlaps(out, sbytes, w, pbytes) || overlaps(out, sbytes, u, pbytes) ||
+      overlaps(out, sbytes, state_in, state_bytes) || overlaps(out, sbytes, state_out, state_bytes))
+    return WKV_ERR_ALIAS;
+  // state_out may be state_in exactly, and must not touch any other input
+  if (overlaps(state_out, state_bytes, k, sbytes) || overlaps(state_out, state_bytes, v, sbytes) ||
+      overlaps(state_out, state_bytes, w, pbytes) || overlaps(state_out, state_bytes, u, pbytes))
+    return WKV_ERR_ALIAS;
+  if (state_out != state_in && overlaps(state_out, state_bytes, state_in, state_bytes))
+    return WKV_ERR_ALIAS;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+
+  if (T == 0) {
+    if (state_out == nullptr || state_out == state_in) return WKV_OK;
+    e = wkv::launch_state_copy(B, C, state_in, state_out, stream);
+    return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+  }
+
+  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out};
+  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev);
+  if (path == WKV_PATH_SEQ) {
+    e = wkv::launch_seq(a, io, wkv::seq_vec_width(io, C, a), stream);
+  } else {
+    e = wkv::launch_chunk(a, io, wkv::chunk_vec_width(io, C, a), stream);
+  }
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
+int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* k, const void* v,
+              float* state, void* out, int io, hipStream_t stream) {
+  if (B < 0 || C < 0) return WKV_ERR_DIM;
+  const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
+  int64_t io_bytes, state_bytes;
+  if (!mul3(B, C, es, &io_bytes) || io_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (!mul3(B, C, 12, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (B == 0 || C == 0) return WKV_OK;
+  if (w == nullptr || u == nullptr || k == nullptr || v == nullptr || state == nullptr ||
+      out == nullptr)
+    return WKV_ERR_NULL;
+  if (misaligned(w, 4) || misaligned(u, 4) || misaligned(state, 4)) return WKV_ERR_ALIGN;
+  if (misaligned(k, es) || misaligned(v, es) || misaligned(out, es)) return WKV_ERR_ALIGN;
+  const int64_t pbytes = C * 4;
+  if (overlaps(out, io_bytes, k, io_bytes) || overlaps(out, io_bytes, v, io_bytes) ||
+      overlaps(out, io_bytes, w, pbytes) || overlaps(out, io_bytes, u, pbytes) ||
+      overlaps(out, io_bytes, state, state_bytes))
+    return WKV_ERR_ALIAS;
+  if (overlaps(state, state_bytes, k, io_bytes) || overlaps(state, state_bytes, v, io_bytes) ||
+      overlaps(state, state_bytes, w, pbytes) || overlaps(state, state_bytes, u, pbytes))
+    return WKV_ERR_ALIAS;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  const wkv::StepArgs a{B, C, w, u, k, v, state, out};
+  e = wkv::launch_step(a, io, wkv::step_vec_width(io, C, a), stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const float* k,
+                const float* v, const float* state_in, float* out, float* state_out,
+                hipStream_t stream) {
+  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_F32, WKV_PATH_AUTO,
+                      stream);
+}
+
+int wkv_forward_bf16(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                     const uint16_t* k, const uint16_t* v, const float* state_in, uint16_t* out,
+                     float* state_out, hipStream_t stream) {
+  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_BF16, WKV_PATH_AUTO,
+                      stream);
+}
+
+int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
+                   const void* v, const float* state_in, void* out, float* state_out, int io,
+                   int path, hipStream_t stream) {
+  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, stream);
+}
+
+int wkv_select_path(int64_t B, int64_t T, int64_t C, int io) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return -WKV_ERR_ARG;
+  if (B < 0 || T < 0 || C < 0) return -WKV_ERR_DIM;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
+  return choose_path(B, T, C, io, dev);
+}
+
+int wkv_step(int64_t B, int64_t C, const float* w, const float* u, const float* k, const float* v,
+             float* state, float* out, hipStream_t stream) {
+  return step_impl(B, C, w, u, k, v, state, out, WKV_IO_F32, stream);
+}
+
+int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const uint16_t* k,
+                  const uint16_t* v, float* state, uint16_t* out, hipStream_t stream) {
+  return step_impl(B, C, w, u, k, v, state, out, WKV_IO_BF16, stream);
+}
+
+const char* wkv_status_string(int status) {
+  switch (status) {
+    case WKV_OK: return "WKV_OK";
+    case WKV_ERR_NULL: return "WKV_ERR_NULL: a required pointer is NULL";
+    case WKV_ERR_DIM: return "WKV_ERR_DIM: negative or too large size";
+    case WKV_ERR_ALIGN: return "WKV_ERR_ALIGN: pointer not aligned to its element size";
+    case WKV_ERR_ALIAS: return "WKV_ERR_ALIAS: an output overlaps another argument";
+    case WKV_ERR_LAUNCH: return "WKV_ERR_LAUNCH: kernel launch failed";
+    case WKV_ERR_DEVICE: return "WKV_ERR_DEVICE: no usable HIP device";
+    case WKV_ERR_ARG: return "WKV_ERR_ARG: io or path out of range";
+    default: return "unknown wkv_status";
+  }
+}
+
+int wkv_last_hip_error(void) { return g_last_hip_error; }
+
+int wkv_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,309 @@
+// Chunked associative scan over time, for problems whose B*C alone cannot
+// fill the GPU.
+//
+// The pages describe the time-parallel form of RWKV as an associative prefix
+// scan (page "RWKV-v6 Architecture: Attention-Free Linear Transformers",
+// section on architectural duality; page "RWKV: Merging Transformer Training
+// with RNN Speed", paragraph on the time-parallel mode). For this operator the
+// scan element is a segment summary (num, den, max_exp, length): the state a
+// run of tokens produces from the empty state. Two adjacent segments combine
+// by decaying the earlier one by the later one's length and adding.
+//
+// One workgroup owns LC*V adjacent channels of one batch row for the whole
+// sequence. Time is cut into tiles of P = W*PS sub-chunks of L tokens; thread
+// (sub-chunk s, channel group cl) holds its L tokens of k and v in registers.
+// Per tile:
+//   1. each thread summarises its sub-chunk (exact maximum first, then one
+//      exp2 per token);
+//   2. the PS sub-chunks inside a wave are scanned with lane shuffles;
+//   3. each wave's total goes through LDS; every thread folds the carry from
+//      the previous tile with the totals of the waves before its own, then
+//      with its in-wave exclusive prefix: that is the state in front of its
+//      sub-chunk;
+//   4. each thread re-runs the recurrence over its registers from that state
+//      and writes the outputs. k and v are read from HBM once.
+// The carry across tiles keeps its maximum index-tracked (exact integer age),
+// so long sequences do not accumulate rounding in the running maximum.
+//
+// Wave layout: lane = cl + LC*sl, so one load instruction reads PS rows of
+// LC*V contiguous channels. Workgroups for neighbouring channel groups are
+// placed on the same XCD (blocks are dealt round-robin over the 8 XCDs), so the
+// two halves of a 128-byte line are fetched through one L2.
+#include "wkv_device.h"
+#include "wkv_internal.h"
+
+namespace wkv {
+namespace {
+
+constexpr int kNumXcd = 8;
+
+// Block index -> work index such that consecutive work indices land on the
+// same XCD when blocks are dealt to XCDs round-robin. A bijection on [0, n).
+__device__ __forceinline__ int64_t xcd_swizzle(int64_t bid, int64_t n) {
+  const int64_t q = n / kNumXcd, r = n % kNumXcd;
+  const int64_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+__device__ __forceinline__ Seg shfl_up_seg(const Seg& x, int delta) {
+  Seg r;
+  r.n = __shfl_up(x.n, delta, 64);
+  r.d = __shfl_up(x.d, delta, 64);
+  r.m = __shfl_up(x.m, delta, 64);
+  r.len = __shfl_up(x.len, delta, 64);
+  return r;
+}
+
+// Summary of one sub-chunk: its own state from empty, maximum taken at the
+// end of the sub-chunk. MASKED: only the first nvalid tokens exist.
+template <int L, bool MASKED>
+__device__ __forceinline__ Seg summarize(const float (&kk)[L], const float (&vv)[L], float wd,
+                                         int nvalid) {
+  float z[L];
+  float top = kEmpty;
+  const float last = MASKED ? static_cast<float>(nvalid - 1) : static_cast<float>(L - 1);
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    // exponent of token i once the sub-chunk has ended: k_i - (last - i) w
+    z[i] = __builtin_fmaf(static_cast<float>(i) - last, wd, kk[i]);
+    if (!MASKED || i < nvalid) top = __builtin_fmaxf(top, z[i]);
+  }
+  float n = 0.0f, d = 0.0f;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    float e = fast_exp2((z[i] - top) * kLog2e);
+    if (MASKED && i >= nvalid) e = 0.0f;
+    d += e;
+    n = __builtin_fmaf(e, vv[i], n);
+  }
+  return Seg{n, d, top, MASKED ? static_cast<float>(nvalid) : static_cast<float>(L)};
+}
+
+template <int V, int L>
+struct ChunkRegs {
+  float k[L][V];
+  float v[L][V];
+};
+
+template <typename IoT, int V, int L, bool MASKED>
+__device__ __forceinline__ void chunk_load(ChunkRegs<V, L>& r,
+                                           const typename IoT::elem* __restrict__ kp,
+                                           const typename IoT::elem* __restrict__ vp, int64_t C,
+                                           int nvalid) {
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (!MASKED || i < nvalid) {
+      IoT::template load<V, false>(kp + i * C, r.k[i]);
+      IoT::template load<V, false>(vp + i * C, r.v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        r.k[i][j] = 0.0f;
+        r.v[i][j] = 0.0f;
+      }
+    }
+  }
+}
+
+template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED>
+__device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid, Lane (&carry)[V],
+                                           const float (&wd)[V], const float (&ub)[V],
+                                           Seg (*tot)[LC * V], typename IoT::elem* __restrict__ op,
+                                           int64_t C, bool cvalid, int wave, int sl, int cl) {
+  // 1. own summary, 2. inclusive scan over the wave's sub-chunks
+  Seg inc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    float kk[L], vv[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      kk[i] = r.k[i][j];
+      vv[i] = r.v[i][j];
+    }
+    inc[j] = summarize<L, MASKED>(kk, vv, wd[j], nvalid);
+  }
+#pragma unroll
+  for (int off = 1; off < PS; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const Seg p = shfl_up_seg(inc[j], off * LC);
+      if (sl >= off) inc[j] = seg_combine(p, inc[j], wd[j]);
+    }
+  }
+  Seg exc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const Seg p = shfl_up_seg(inc[j], LC);
+    exc[j] = sl > 0 ? p : seg_identity();
+  }
+  // 3. wave totals through LDS, fold carry -> prefix of this wave -> own prefix
+  if (sl == PS - 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) tot[wave][cl * V + j] = inc[j];
+  }
+  __syncthreads();
+  Lane pre[V];
+#pragma unroll
+  for (int jj = 0; jj < W; ++jj) {
+    if (jj == wave) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) pre[j] = carry[j];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) lane_absorb(carry[j], tot[jj][cl * V + j], wd[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) lane_absorb(pre[j], exc[j], wd[j]);
+  // 4. rescan own tokens from the prefix
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (MASKED && i >= nvalid) break;
+    float o[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) o[j] = lane_step(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j]);
+    if (cvalid) IoT::template store<V, true>(op + i * C, o);
+  }
+}
+
+template <typename IoT, int V, int LC, int PS, int W, int L>
+__global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
+    int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
+    const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
+    const float* __restrict__ state_in, typename IoT::elem* __restrict__ out,
+    float* __restrict__ state_out, int64_t groups_per_row) {
+  static_assert(LC * PS == 64, "a wave is LC channel groups by PS sub-chunks");
+  constexpr int CH = LC * V;          // channels per workgroup
+  constexpr int TL = W * PS * L;      // tokens per tile
+  __shared__ Seg tot[2][W][CH];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int cl = lane % LC;
+  const int sl = lane / LC;
+  const int sub = wave * PS + sl;
+
+  const int64_t g = xcd_swizzle(blockIdx.x, B * groups_per_row);
+  const int64_t b = g / groups_per_row;
+  const int64_t c0 = (g - b * groups_per_row) * CH + cl * V;
+  const bool cvalid = c0 < C;
+  const int64_t cc = cvalid ? c0 : C - V;  // idle tail threads mirror the last channels
+  const int64_t plane = B * C;
+  const int64_t lane0 = b * C + cc;
+
+  float wd[V], ub[V];  // decay w and bonus u of the V channels
+  IoF32::load<V, false>(w + cc, wd);
+  IoF32::load<V, false>(u + cc, ub);
+  Lane carry[V];
+  if (state_in != nullptr) {
+    float n[V], d[V], m[V];
+    IoF32::load<V, false>(state_in + lane0, n);
+    IoF32::load<V, false>(state_in + plane + lane0, d);
+    IoF32::load<V, false>(state_in + 2 * plane + lane0, m);
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = lane_from_state(n[j], d[j], m[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = lane_empty();
+  }
+
+  const int64_t base = b * T * C + cc + static_cast<int64_t>(sub) * L * C;
+  const typename IoT::elem* kp = k + base;
+  const typename IoT::elem* vp = v + base;
+  typename IoT::elem* op = out + base;
+  const int64_t step = static_cast<int64_t>(TL) * C;
+
+  const int64_t full = T / TL;  // tiles with every token present
+  ChunkRegs<V, L> A, Bf;
+  int64_t tile = 0;
+  if (full > 0) chunk_load<IoT, V, L, false>(A, kp, vp, C, L);
+  while (tile < full) {
+    const bool next_b = tile + 1 < full;
+    if (next_b) chunk_load<IoT, V, L, false>(Bf, kp + (tile + 1) * step, vp + (tile + 1) * step, C, L);
+    chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, wd, ub, tot[tile & 1], op + tile * step,
+                                            C, cvalid, wave, sl, cl);
+    ++tile;
+    if (!next_b) break;
+    const bool next_a = tile + 1 < full;
+    if (next_a) chunk_load<IoT, V, L, false>(A, kp + (tile + 1) * step, vp + (tile + 1) * step, C, L);
+    chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, wd, ub, tot[tile & 1], op + tile * step,
+                                            C, cvalid, wave, sl, cl);
+    ++tile;
+    if (!next_a) break;
+  }
+  if (full * TL < T) {  // last, partial tile
+    const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
+    const int64_t left = T - first;
+    const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
+    chunk_load<IoT, V, L, true>(A, kp + full * step, vp + full * step, C, nvalid);
+    chunk_tile<IoT, V, LC, PS, W, L, true>(A, nvalid, carry, wd, ub, tot[full & 1],
+                                           op + full * step, C, cvalid, wave, sl, cl);
+  }
+
+  if (state_out != nullptr && sub == 0 && cvalid) {
+    float n[V], d[V], m[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      n[j] = carry[j].n;
+      d[j] = carry[j].d;
+      m[j] = lane_max_exp(carry[j], wd[j]);
+    }
+    IoF32::store<V, false>(state_out + lane0, n);
+    IoF32::store<V, false>(state_out + plane + lane0, d);
+    IoF32::store<V, false>(state_out + 2 * plane + lane0, m);
+  }
+}
+
+constexpr int kLC = 16, kPS = 4, kW = 4;
+
+template <typename IoT, int V, int L>
+hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
+  constexpr int CH = kLC * V;
+  const int64_t gpr = (a.C + CH - 1) / CH;
+  const int64_t blocks = a.B * gpr;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, kW, L>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0, st, a.B, a.T, a.C,
+                     a.w, a.u, static_cast<const typename IoT::elem*>(a.k),
+                     static_cast<const typename IoT::elem*>(a.v), a.state_in,
+                     static_cast<typename IoT::elem*>(a.out), a.state_out, gpr);
+  return hipGetLastError();
+}
+
+template <typename IoT, int V>
+hipError_t launch_chunk_v(const FwdArgs& a, hipStream_t st) {
+  if (a.T <= 16 * kPS * kW) return launch_chunk_t<IoT, V, 4>(a, st);
+  return launch_chunk_t<IoT, V, 16>(a, st);
+}
+
+bool aligned(const void* p, int bytes) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+}  // namespace
+
+ChunkShape chunk_shape(int io, int vec, int64_t T) {
+  ChunkShape s;
+  s.L = T <= 16 * kPS * kW ? 4 : 16;
+  s.P = kPS * kW;
+  s.channels = kLC * vec;
+  s.threads = 64 * kW;
+  (void)io;
+  return s;
+}
+
+int chunk_vec_width(int io, int64_t C, const FwdArgs& a) {
+  if (io != kBf16) return 1;
+  const bool ok = C % 2 == 0 && aligned(a.k, 4) && aligned(a.v, 4) && aligned(a.out, 4) &&
+                  aligned(a.w, 8) && aligned(a.u, 8) && aligned(a.state_in, 8) &&
+                  aligned(a.state_out, 8);
+  return ok ? 2 : 1;
+}
+
+hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s) {
+  if (io == kF32) return launch_chunk_v<IoF32, 1>(a, s);
+  if (vec == 2) return launch_chunk_v<IoBf16, 2>(a, s);
+  return launch_chunk_v<IoBf16, 1>(a, s);
+}
+
+}  // namespace wkv

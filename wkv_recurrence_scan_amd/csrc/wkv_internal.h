@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (wkv_api.cpp) and the kernel
+// translation units. Not installed; the public interface is include/wkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv {
+
+enum Io : int { kF32 = 0, kBf16 = 1 };
+
+struct FwdArgs {
+  int64_t B, T, C;
+  const float* w;
+  const float* u;
+  const void* k;
+  const void* v;
+  const float* state_in;  // nullptr: empty state
+  void* out;
+  float* state_out;       // nullptr: not written
+};
+
+struct StepArgs {
+  int64_t B, C;
+  const float* w;
+  const float* u;
+  const void* k;
+  const void* v;
+  float* state;
+  void* out;
+};
+
+// Channels per thread each kernel can be built for; the host picks the widest
+// one that divides C and matches the pointers' alignment.
+int seq_vec_width(int io, int64_t C, const FwdArgs& a);
+int chunk_vec_width(int io, int64_t C, const FwdArgs& a);
+int step_vec_width(int io, int64_t C, const StepArgs& a);
+
+// Chunked-scan shape for a problem: tokens per sub-chunk and per tile.
+struct ChunkShape {
+  int L;          // tokens per sub-chunk per tile
+  int P;          // sub-chunks per tile (threads along T per channel group)
+  int channels;   // channels per workgroup
+  int threads;    // threads per workgroup
+};
+ChunkShape chunk_shape(int io, int vec, int64_t T);
+
+hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
+hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
+hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);
+// T == 0: state_out <- state_in, or the empty state when state_in is null.
+hipError_t launch_state_copy(int64_t B, int64_t C, const float* state_in, float* state_out,
+                             hipStream_t s);
+
+}  // namespace wkv
