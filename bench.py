@@ -4,8 +4,10 @@
 Default run (one JSON line on stdout):
   * prefill: 8 independent layers of wkv_forward at B=8, T=1024, C=768, fp32
     (the MicroRWKV shape: 8 layers, width 768, 1024-token block), inputs
-    resident in HBM. One "step" = the 8 forward calls on one stream.
-    value = G channel-tokens/s over the timed steps.
+    resident in HBM. One "step" = the 8 forward calls on one stream, captured
+    once into a HIP graph and replayed per step; value = G channel-tokens/s
+    over the timed replays. The same steps launched eagerly from Python are
+    reported beside it (eager_value).
   * roofline: the prefill kernel's average duration from HIP events recorded
     around every launch inside the timed region, against its algorithmic HBM
     bytes (read k, v; write out; write the final state; read w, u).
@@ -71,38 +73,68 @@ def build_layers(wl, n_layers, dev):
 
 
 def time_prefill(layers, steps, warmup, path):
-    """Runs warmup + timed steps; returns (ms_per_step, kernel_ms_avg, wall_ms_per_step)."""
+    """Times `steps` steps (all layers once each) after `warmup` steps, twice:
+    launched eagerly from Python with a HIP event pair around every kernel
+    (the per-kernel durations give the roofline figure), and replayed from one
+    HIP graph holding a whole step. Returns a dict of timings."""
     import torch
     import wkv_recurrence_scan_amd as W
 
     stream = torch.cuda.current_stream()
+    calls = [W.ForwardCall(L["w"], L["u"], L["k"], L["v"], None, L["out"], L["st"], path=path)
+             for L in layers]
 
     def one_step(evs=None):
-        for i, L in enumerate(layers):
+        # each call launches on the stream current at call time, which under
+        # graph capture is the capturing stream
+        for i, c in enumerate(calls):
             if evs is not None:
-                evs[i][0].record(stream)
-            W.wkv_forward_ex(L["w"], L["u"], L["k"], L["v"], None, L["out"], L["st"], path=path)
+                evs[i][0].record()
+            c()
             if evs is not None:
-                evs[i][1].record(stream)
+                evs[i][1].record()
 
     for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
             for _ in layers] for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
+    t0.record(stream)
     for s in range(steps):
         one_step(evs[s])
-    t_end.record(stream)
+    t1.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - wall0) * 1e3
-    total_ms = t_start.elapsed_time(t_end)
+    eager_ms = t0.elapsed_time(t1) / steps
     kms = [e0.elapsed_time(e1) for row in evs for (e0, e1) in row]
-    return total_ms / steps, float(np.mean(kms)), wall / steps
+
+    eager_out = [(c.out.clone(), c.state_out.clone()) for c in calls]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_step()
+    for c in calls:
+        c.out.zero_()
+        c.state_out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    for c, (o, st) in zip(calls, eager_out):  # the graph must redo exactly the eager work
+        if not (torch.equal(c.out, o) and torch.equal(c.state_out, st)):
+            raise RuntimeError("graph replay does not reproduce the eager outputs")
+    del eager_out
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / steps
+    graph_ms = t0.elapsed_time(t1) / steps
+    return {"graph_ms": graph_ms, "eager_ms": eager_ms, "kernel_ms": float(np.mean(kms)),
+            "kernel_ms_median": float(np.median(kms)), "wall_ms": wall_ms}
 
 
 def time_decode(wl, dev, n_steps, use_graph):
@@ -126,9 +158,11 @@ def time_decode(wl, dev, n_steps, use_graph):
     state = torch.empty_like(st0)
     stream = torch.cuda.current_stream()
 
+    calls = [W.StepCall(dw, du, ks[s], vs[s], state, outs[s]) for s in range(n_steps)]
+
     def run_all():
-        for s in range(n_steps):
-            W.wkv_step(dw, du, ks[s], vs[s], state, outs[s])
+        for c in calls:
+            c()  # current stream at call time (the capturing stream under capture)
 
     state.copy_(st0)
     run_all()  # warm-up
@@ -148,13 +182,18 @@ def time_decode(wl, dev, n_steps, use_graph):
         g = torch.cuda.CUDAGraph()
         state.copy_(st0)
         torch.cuda.synchronize()
+        eager_outs = outs.clone()
         with torch.cuda.graph(g):
             run_all()
         torch.cuda.synchronize()
         state.copy_(st0)
+        outs.zero_()
         torch.cuda.synchronize()
-        g.replay()  # warm-up replay
+        g.replay()  # warm-up replay, checked against the eager steps
         torch.cuda.synchronize()
+        if not torch.equal(outs, eager_outs):
+            raise RuntimeError("decode graph replay does not reproduce the eager steps")
+        del eager_outs
         state.copy_(st0)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -249,7 +288,8 @@ def main():
         del a, b
 
     _log(f"timing {args.steps} steps after {args.warmup} warm-up steps, path={path_used}")
-    ms_step, kms, wall_ms = time_prefill(layers, args.steps, args.warmup, args.path)
+    tm = time_prefill(layers, args.steps, args.warmup, args.path)
+    ms_step, kms = tm["graph_ms"], tm["kernel_ms"]
     per_layer_ct = wl.B * wl.T * wl.C
     ct_step = per_layer_ct * n_layers
     value = ct_step / (ms_step * 1e-3) / 1e9
@@ -270,12 +310,15 @@ def main():
         "dtype": "bf16" if wl.io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "C": wl.C, "layers": n_layers,
-                   "io": wl.io, "path": path_used, "parallelism": "single GPU"},
+                   "io": wl.io, "path": path_used, "launch": "hip_graph_per_step",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": f"wkv_{path_used}_kernel", "kernel_us": round(kms * 1e3, 3),
                      "algorithmic_bytes_per_launch": abytes},
-        "wall_ms_per_step": round(wall_ms, 5),
+        "eager_ms_per_step": round(tm["eager_ms"], 5),
+        "eager_value": round(ct_step / (tm["eager_ms"] * 1e-3) / 1e9, 3),
+        "wall_ms_per_step": round(tm["wall_ms"], 5),
     }
 
     if args.config == 1 and not args.no_decode:

@@ -17,12 +17,13 @@ WL0 = I.WORKLOADS[0]   # k, v ~ N(0, 1), w in [0.01, 5], u ~ N(0, 0.5)
 WL3 = I.WORKLOADS[3]   # k ~ N(0, 2), w in [1e-3, 8] (slow and fast decays), u ~ N(0, 1)
 WL4 = I.WORKLOADS[4]   # bf16, k ~ U(-20, 20) with 1% +-60 spikes
 
-# T around the chunked kernel's tiles (64 tokens for T <= 256, else 256) and
-# C around its 16-channel groups; both kernels run every shape.
+# T around the chunked kernel's tiles (64 tokens for T <= 256, else 256; its
+# workgroup shape changes at T = 256 and T = 2048) and C around its
+# 32-channel groups (64 for bf16); both kernels run every shape.
 SHAPES = [
     (1, 1, 1), (2, 2, 7), (1, 3, 16), (3, 31, 33), (2, 32, 5), (2, 63, 48), (2, 64, 64),
     (2, 65, 17), (1, 255, 16), (1, 256, 32), (1, 257, 80), (2, 511, 24), (1, 1000, 40),
-    (1, 4097, 16),
+    (1, 2048, 31), (1, 2049, 96), (2, 3000, 100), (1, 4097, 16),
 ]
 
 
@@ -40,7 +41,7 @@ def test_forward_f32(path, B, T, C, wl):
 
 @pytest.mark.parametrize("path", ["seq", "chunk"])
 @pytest.mark.parametrize("B,T,C", [(1, 1, 2), (2, 3, 6), (2, 65, 34), (1, 257, 64),
-                                   (3, 700, 32), (1, 2049, 66), (1, 130, 7)])
+                                   (3, 700, 32), (1, 2049, 66), (1, 130, 7), (1, 2500, 130)])
 def test_forward_bf16(path, B, T, C):
     say(f"forward bf16 path={path} B={B} T={T} C={C}")
     w, u, k, v = make_case(WL4, B, T, C)
@@ -220,3 +221,36 @@ def test_decode_in_hip_graph_replays_match_eager():
         assert torch.equal(outs.view(torch.int32), eager.view(torch.int32)), f"replay {rep}"
         assert torch.equal(state.view(torch.int32), eager_state.view(torch.int32)), f"replay {rep}"
         _ = W.wkv_forward(dw, du, dev_f32(k), dev_f32(v))  # unrelated eager work between replays
+
+
+def test_forward_calls_in_hip_graph_replay_exactly():
+    """Several layers of prefill captured once in a HIP graph (as the
+    benchmark runs them) give bit-identical outputs and states on every replay,
+    with unrelated eager work in between."""
+    say("forward graph capture")
+    wl = I.WORKLOADS[1].scaled(B=2, T=300, C=96)
+    layers = []
+    for layer in range(3):
+        w, u = I.params(wl, layer)
+        k, v = I.kv(wl, layer)
+        layers.append((dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v)))
+    calls = [W.ForwardCall(*L) for L in layers]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    eager = [(c.out.clone(), c.state_out.clone()) for c in calls]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for c in calls:
+            c.out.zero_()
+            c.state_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, (o, s) in zip(calls, eager):
+            assert torch.equal(c.out.view(torch.int32), o.view(torch.int32)), f"replay {rep}"
+            assert torch.equal(c.state_out.view(torch.int32), s.view(torch.int32)), f"replay {rep}"
+        _ = W.wkv_forward(*layers[0])

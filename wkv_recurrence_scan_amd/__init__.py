@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     WKV_PATH_AUTO,
     WKV_PATH_CHUNK,
     WKV_PATH_SEQ,
+    ForwardCall,
+    StepCall,
     WKVError,
     forward,
     load_library,

@@ -231,6 +231,93 @@ def wkv_select_path(B: int, T: int, C: int, io: int = WKV_IO_F32) -> str:
     return {WKV_PATH_SEQ: "seq", WKV_PATH_CHUNK: "chunk"}[r]
 
 
+class ForwardCall:
+    """A wkv_forward_ex call validated once and launched many times.
+
+    The tensors are checked (device, dtype, shape, contiguity) and their
+    pointers captured at construction; each call then only passes the saved
+    arguments and the stream to the C entry point. Keep the tensors alive and
+    unmoved while the object is used. Useful in per-layer loops and under HIP
+    graph capture, where per-call Python checks would dominate a ~10 us kernel.
+    """
+
+    def __init__(self, w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",
+                 want_state=True):
+        if k.dim() != 3:
+            raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+        if k.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"k must be float32 or bfloat16, got {k.dtype}")
+        if path not in _PATHS:
+            raise ValueError(f"path must be one of {sorted(_PATHS)}")
+        B, T, C = k.shape
+        dev = k.device
+        if dev.type != "cuda":
+            raise ValueError("tensors must live on a GPU device")
+        for t, nm, dt, shp in ((k, "k", k.dtype, (B, T, C)), (v, "v", k.dtype, (B, T, C)),
+                               (w, "w", torch.float32, (C,)), (u, "u", torch.float32, (C,))):
+            _need(t, nm, dt, shp, dev)
+        if state_in is not None:
+            _need(state_in, "state_in", torch.float32, (3, B, C), dev)
+        if out is None:
+            out = torch.empty((B, T, C), dtype=k.dtype, device=dev)
+        _need(out, "out", k.dtype, (B, T, C), dev)
+        if state_out is None and want_state:
+            state_out = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+        if state_out is not None:
+            _need(state_out, "state_out", torch.float32, (3, B, C), dev)
+        self.device = dev
+        self.out, self.state_out = out, state_out
+        self._keep = (w, u, k, v, state_in)
+        io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
+        self._fn = load_library().wkv_forward_ex
+        self._args = (B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out),
+                      _ptr(state_out), io, _PATHS[path])
+
+    def __call__(self, stream=None):
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        st = self._fn(*self._args, ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            _check(st, "wkv_forward_ex")
+        return self.out, self.state_out
+
+
+class StepCall:
+    """A wkv_step / wkv_step_bf16 call validated once and launched many times
+    (the decode loop's per-token launch, without per-call Python checks).
+    Keep the tensors alive and unmoved while the object is used."""
+
+    def __init__(self, w, u, k, v, state, out=None):
+        if k.dim() != 2:
+            raise ValueError(f"k must be (B, C), got shape {tuple(k.shape)}")
+        if k.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"k must be float32 or bfloat16, got {k.dtype}")
+        B, C = k.shape
+        dev = k.device
+        if dev.type != "cuda":
+            raise ValueError("tensors must live on a GPU device")
+        if out is None:
+            out = torch.empty((B, C), dtype=k.dtype, device=dev)
+        for t, nm, dt, shp in ((k, "k", k.dtype, (B, C)), (v, "v", k.dtype, (B, C)),
+                               (w, "w", torch.float32, (C,)), (u, "u", torch.float32, (C,)),
+                               (state, "state", torch.float32, (3, B, C)),
+                               (out, "out", k.dtype, (B, C))):
+            _need(t, nm, dt, shp, dev)
+        self.device = dev
+        self.out = out
+        self._keep = (w, u, k, v, state)
+        lib = load_library()
+        self._name = "wkv_step_bf16" if k.dtype == torch.bfloat16 else "wkv_step"
+        self._fn = getattr(lib, self._name)
+        self._args = (B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state), _ptr(out))
+
+    def __call__(self, stream=None):
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        st = self._fn(*self._args, ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            _check(st, self._name)
+        return self.out
+
+
 def forward(w, u, k, v, state=None, *, path="auto", out=None, state_out=None):
     """Convenience: prefill for float32 or bfloat16 k, v. Returns (out, state_out)."""
     return wkv_forward_ex(w, u, k, v, state, out, state_out, path=path)

@@ -27,8 +27,8 @@
 //
 // Wave layout: lane = cl + LC*sl, so one load instruction reads PS rows of
 // LC*V contiguous channels. Workgroups for neighbouring channel groups are
-// placed on the same XCD (blocks are dealt round-robin over the 8 XCDs), so the
-// two halves of a 128-byte line are fetched through one L2.
+// placed on the same XCD (blocks are dealt round-robin over the 8 XCDs), so
+// lines shared by two groups (bf16 tails, odd C) are fetched through one L2.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
@@ -157,11 +157,14 @@ __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid,
   // 4. rescan own tokens from the prefix
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    if (MASKED && i >= nvalid) break;
-    float o[V];
+    // a guard, not a break, so that the loop stays fully unrolled and the
+    // register arrays keep static indices
+    if (!MASKED || i < nvalid) {
+      float o[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) o[j] = lane_step(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j]);
-    if (cvalid) IoT::template store<V, true>(op + i * C, o);
+      for (int j = 0; j < V; ++j) o[j] = lane_step(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j]);
+      if (cvalid) IoT::template store<V, true>(op + i * C, o);
+    }
   }
 }
 
@@ -214,29 +217,31 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   const int64_t step = static_cast<int64_t>(TL) * C;
 
   const int64_t full = T / TL;  // tiles with every token present
+  // Software pipeline over two register buffers: the loads of the next tile
+  // are issued before the current one is processed. They are issued on every
+  // path (the last full tile re-reads itself, a harmless cache hit), so the
+  // compiler's counter-based waits stop at the current tile's loads instead
+  // of draining the prefetch as well.
   ChunkRegs<V, L> A, Bf;
-  int64_t tile = 0;
   if (full > 0) chunk_load<IoT, V, L, false>(A, kp, vp, C, L);
-  while (tile < full) {
-    const bool next_b = tile + 1 < full;
-    if (next_b) chunk_load<IoT, V, L, false>(Bf, kp + (tile + 1) * step, vp + (tile + 1) * step, C, L);
+  for (int64_t tile = 0; tile < full; tile += 2) {
+    const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
+    chunk_load<IoT, V, L, false>(Bf, kp + nb * step, vp + nb * step, C, L);
     chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, wd, ub, tot[tile & 1], op + tile * step,
                                             C, cvalid, wave, sl, cl);
-    ++tile;
-    if (!next_b) break;
-    const bool next_a = tile + 1 < full;
-    if (next_a) chunk_load<IoT, V, L, false>(A, kp + (tile + 1) * step, vp + (tile + 1) * step, C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, wd, ub, tot[tile & 1], op + tile * step,
-                                            C, cvalid, wave, sl, cl);
-    ++tile;
-    if (!next_a) break;
+    if (tile + 1 >= full) break;
+    const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
+    chunk_load<IoT, V, L, false>(A, kp + na * step, vp + na * step, C, L);
+    chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, wd, ub, tot[(tile + 1) & 1],
+                                            op + (tile + 1) * step, C, cvalid, wave, sl, cl);
   }
   if (full * TL < T) {  // last, partial tile
     const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
     const int64_t left = T - first;
     const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
-    chunk_load<IoT, V, L, true>(A, kp + full * step, vp + full * step, C, nvalid);
-    chunk_tile<IoT, V, LC, PS, W, L, true>(A, nvalid, carry, wd, ub, tot[full & 1],
+    ChunkRegs<V, L> last;
+    chunk_load<IoT, V, L, true>(last, kp + full * step, vp + full * step, C, nvalid);
+    chunk_tile<IoT, V, LC, PS, W, L, true>(last, nvalid, carry, wd, ub, tot[full & 1],
                                            op + full * step, C, cvalid, wave, sl, cl);
   }
 
@@ -254,26 +259,34 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   }
 }
 
-constexpr int kLC = 16, kPS = 4, kW = 4;
+// Channel threads per wave: 32 lanes x 4 bytes = one 128-byte line per row
+// (fp32), so a load instruction reads whole lines from two rows.
+constexpr int kLC = 32, kPS = 2;
 
-template <typename IoT, int V, int L>
+// Workgroup shape by sequence length (measured on MI355X): short sequences
+// want the fewest serial tiles; long ones want two waves per SIMD to overlap
+// each tile's scan with the neighbours' memory traffic.
+template <typename IoT, int V, int W, int L>
 hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
   constexpr int CH = kLC * V;
   const int64_t gpr = (a.C + CH - 1) / CH;
   const int64_t blocks = a.B * gpr;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, kW, L>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0, st, a.B, a.T, a.C,
+  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0, st, a.B, a.T, a.C,
                      a.w, a.u, static_cast<const typename IoT::elem*>(a.k),
                      static_cast<const typename IoT::elem*>(a.v), a.state_in,
                      static_cast<typename IoT::elem*>(a.out), a.state_out, gpr);
   return hipGetLastError();
 }
 
+constexpr int64_t kShortT = 256, kLongT = 2048;
+
 template <typename IoT, int V>
 hipError_t launch_chunk_v(const FwdArgs& a, hipStream_t st) {
-  if (a.T <= 16 * kPS * kW) return launch_chunk_t<IoT, V, 4>(a, st);
-  return launch_chunk_t<IoT, V, 16>(a, st);
+  if (a.T <= kShortT) return launch_chunk_t<IoT, V, 8, 4>(a, st);
+  if (a.T <= kLongT) return launch_chunk_t<IoT, V, 8, 16>(a, st);
+  return launch_chunk_t<IoT, V, 16, 8>(a, st);
 }
 
 bool aligned(const void* p, int bytes) {
@@ -283,12 +296,13 @@ bool aligned(const void* p, int bytes) {
 }  // namespace
 
 ChunkShape chunk_shape(int io, int vec, int64_t T) {
-  ChunkShape s;
-  s.L = T <= 16 * kPS * kW ? 4 : 16;
-  s.P = kPS * kW;
-  s.channels = kLC * vec;
-  s.threads = 64 * kW;
   (void)io;
+  ChunkShape s;
+  const int W = T <= kLongT ? 8 : 16;
+  s.L = T <= kShortT ? 4 : (T <= kLongT ? 16 : 8);
+  s.P = kPS * W;
+  s.channels = kLC * vec;
+  s.threads = 64 * W;
   return s;
 }
 

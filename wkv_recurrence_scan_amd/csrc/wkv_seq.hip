@@ -87,22 +87,22 @@ __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
   typename IoT::elem* op = out + row;
 
   // Two register buffers, alternating; the loads for the block after the one
-  // being computed are always issued first.
+  // being computed are issued first, on every path (the last full block
+  // re-reads itself, a cache hit), so that the compiler's counter-based waits
+  // only ever wait for the block about to be used.
   SeqBlock<IoT, V, U> A, Bf;
-  int64_t t = 0;
-  if (T >= U) seq_load<IoT, V, U>(A, kp, vp, C);
-  while (t + U <= T) {
-    const bool next_b = t + 2 * U <= T;
-    if (next_b) seq_load<IoT, V, U>(Bf, kp + (t + U) * C, vp + (t + U) * C, C);
-    seq_compute<IoT, V, U>(A, s, wd, ub, op + t * C, C);
-    t += U;
-    if (!next_b) break;
-    const bool next_a = t + 2 * U <= T;
-    if (next_a) seq_load<IoT, V, U>(A, kp + (t + U) * C, vp + (t + U) * C, C);
-    seq_compute<IoT, V, U>(Bf, s, wd, ub, op + t * C, C);
-    t += U;
-    if (!next_a) break;
+  const int64_t nblk = T / U;
+  if (nblk > 0) seq_load<IoT, V, U>(A, kp, vp, C);
+  for (int64_t blk = 0; blk < nblk; blk += 2) {
+    const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
+    seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, C);
+    seq_compute<IoT, V, U>(A, s, wd, ub, op + blk * U * C, C);
+    if (blk + 1 >= nblk) break;
+    const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
+    seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, C);
+    seq_compute<IoT, V, U>(Bf, s, wd, ub, op + (blk + 1) * U * C, C);
   }
+  int64_t t = nblk * U;
   for (; t < T; ++t) {
     float kk[V], vv[V], o[V];
     IoT::template load<V, true>(kp + t * C, kk);
