@@ -208,6 +208,32 @@ def time_decode(wl, dev, n_steps, use_graph):
     return res
 
 
+def measured_traffic(workload_key, path):
+    """HBM bytes per launch from the rocprofv3 counter summaries under
+    profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None when there is none for this workload and kernel or when the kernel's
+    sources have changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
+        kv = {}
+        for line in open(f):
+            if ":" in line and not line.startswith(("|", " ", "#")):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        if kv.get("workload_key") != workload_key or kv.get("path") != path:
+            continue
+        h = hashlib.sha256()
+        for src in kv.get("kernel_sources", "").split(","):
+            with open(os.path.join(ROOT, src), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != kv.get("source_sha256"):
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(layers, wl, budget_s=15.0):
     """The float64 oracle on the host over the benchmarked workload: whole batch
     rows of each layer in turn, stopping once about budget_s seconds of work
@@ -313,7 +339,8 @@ def main():
                    "io": wl.io, "path": path_used, "launch": "hip_graph_per_step",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(wl.name, path_used),
                      "kernel": f"wkv_{path_used}_kernel", "kernel_us": round(kms * 1e3, 3),
                      "algorithmic_bytes_per_launch": abytes},
         "eager_ms_per_step": round(tm["eager_ms"], 5),
