@@ -268,7 +268,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk"])
+    ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk", "lookback"])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -66,15 +66,22 @@ typedef enum wkv_status {
   WKV_ERR_ALIAS = 4,  /* an output overlaps an input or another output            */
   WKV_ERR_LAUNCH = 5, /* the kernel launch failed (see wkv_last_hip_error)        */
   WKV_ERR_DEVICE = 6, /* no usable HIP device is current                          */
-  WKV_ERR_ARG = 7     /* an enumerated argument (io, path) is out of range        */
+  WKV_ERR_ARG = 7,    /* an enumerated argument (io, path) is out of range        */
+  WKV_ERR_WORKSPACE = 8 /* the kernel needs a workspace: missing or too small     */
 } wkv_status;
 
 /* Element type of k, v and out (w, u and the state are always fp32). */
 enum { WKV_IO_F32 = 0, WKV_IO_BF16 = 1 };
 
-/* Prefill kernels. AUTO picks SEQ when B*C alone fills the GPU, else CHUNK.
- * Both compute the same function; they may differ in the last bits. */
-enum { WKV_PATH_AUTO = 0, WKV_PATH_SEQ = 1, WKV_PATH_CHUNK = 2 };
+/* Prefill kernels; all compute the same function and may differ in the last
+ * bits. SEQ: one lane per (b, c) walks the sequence (large B*C). CHUNK: one
+ * workgroup per channel group walks the sequence in tiles, scanning
+ * sub-chunks in parallel (small B*C, no workspace). LOOKBACK: every
+ * (sequence segment, channel group) is its own workgroup, chained by a
+ * decoupled look-back through a device workspace (small B*C, most
+ * parallelism). AUTO picks SEQ when B*C alone fills the GPU, otherwise
+ * LOOKBACK when a workspace is given and CHUNK when not. */
+enum { WKV_PATH_AUTO = 0, WKV_PATH_SEQ = 1, WKV_PATH_CHUNK = 2, WKV_PATH_LOOKBACK = 3 };
 
 /* Prefill / training form over a whole sequence (page "Linear attention
  * without writing a CUDA kernel", section "The recurrence", wkv_t equation).
@@ -110,8 +117,30 @@ int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float*
                    const void* k, const void* v, const float* state_in, void* out,
                    float* state_out, int io, int path, hipStream_t stream);
 
-/* The kernel WKV_PATH_AUTO would use for these sizes on the current device
- * (WKV_PATH_SEQ or WKV_PATH_CHUNK), or a negative wkv_status on error. */
+/* As wkv_forward_ex with a device workspace, which the LOOKBACK kernel needs
+ * (and AUTO then may choose).
+ *   workspace        device memory of at least wkv_workspace_size(...) bytes,
+ *                    256-byte aligned, owned by the caller. It must be zero-filled
+ *                    before its first use with given (B, T, C, io); every call
+ *                    leaves it ready for the next call with the same sizes (no
+ *                    clearing needed in between, HIP graph replays included).
+ *                    Before reuse with other sizes, zero-fill it again. Calls
+ *                    that may run concurrently must not share a workspace. It
+ *                    must not overlap any other argument.
+ *   workspace_bytes  its size in bytes.
+ * A call whose kernel needs no workspace ignores it (it may be NULL). */
+int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                   const void* k, const void* v, const float* state_in, void* out,
+                   float* state_out, int io, int path, void* workspace,
+                   int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace wkv_forward_ws needs for these sizes and this path
+ * (0 when the kernel uses none), or a negative wkv_status on error. */
+int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path);
+
+/* The kernel WKV_PATH_AUTO uses for these sizes on the current device when a
+ * workspace is available (WKV_PATH_SEQ or WKV_PATH_LOOKBACK; without one,
+ * LOOKBACK becomes WKV_PATH_CHUNK), or a negative wkv_status on error. */
 int wkv_select_path(int64_t B, int64_t T, int64_t C, int io);
 
 /* One decode step for B sequences at once (page "Linear attention without

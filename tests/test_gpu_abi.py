@@ -136,3 +136,27 @@ def test_binding_rejects_bad_tensors():
         W.wkv_forward(w, w, k, k.transpose(1, 2).contiguous().transpose(1, 2))
     with pytest.raises(ValueError):
         W.wkv_forward(torch.ones(7, device="cuda"), w, k, k)
+
+
+def test_forward_ws_workspace_rules(lib, case):
+    say("abi: workspace")
+    B, T, C = case["B"], case["T"], case["C"]
+    need = lib.wkv_workspace_size(B, T, C, 0, W.WKV_PATH_LOOKBACK)
+    assert need > 256
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    base = [B, T, C, ptr(case["w"]), ptr(case["u"]), ptr(case["k"]), ptr(case["v"]), None,
+            ptr(case["out"]), ptr(case["st"]), 0, W.WKV_PATH_LOOKBACK]
+    assert lib.wkv_forward_ws(*base, ptr(ws), need, stream()) == 0
+    torch.cuda.synchronize()
+    w, u, k, v = case["host"]
+    ref, _ = wkv_recurrent(w, u, k, v)
+    assert_out_close(host64(case["out"]), ref, v, F32_TOL)
+    assert lib.wkv_forward_ws(*base, ptr(ws), need - 8, stream()) == 8     # too small
+    assert lib.wkv_forward_ws(*base, None, 0, stream()) == 8               # missing
+    assert lib.wkv_forward_ex(*base, stream()) == 8                        # no workspace argument
+    assert lib.wkv_forward_ws(*base, ptr(ws, 64), need - 64, stream()) == 3  # not 256-aligned
+    assert lib.wkv_forward_ws(*base, ptr(case["out"]), need, stream()) == 4  # on top of out
+    seq = list(base)
+    seq[-1] = W.WKV_PATH_SEQ
+    assert lib.wkv_forward_ws(*seq, None, 0, stream()) == 0              # seq needs none
+    torch.cuda.synchronize()

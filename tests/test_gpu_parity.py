@@ -13,21 +13,25 @@ from wkvtest import (BF16_TOL, F32_TOL, I, W, assert_out_close, assert_state_clo
 
 pytestmark = pytest.mark.gpu
 
+PATHS = ["seq", "chunk", "lookback"]
 WL0 = I.WORKLOADS[0]   # k, v ~ N(0, 1), w in [0.01, 5], u ~ N(0, 0.5)
 WL3 = I.WORKLOADS[3]   # k ~ N(0, 2), w in [1e-3, 8] (slow and fast decays), u ~ N(0, 1)
 WL4 = I.WORKLOADS[4]   # bf16, k ~ U(-20, 20) with 1% +-60 spikes
 
 # T around the chunked kernel's tiles (64 tokens for T <= 256, else 256; its
-# workgroup shape changes at T = 256 and T = 2048) and C around its
-# 32-channel groups (64 for bf16); both kernels run every shape.
+# workgroup shape changes at T = 256 and T = 2048) and the look-back kernel's
+# segments (32 tokens for T <= 512, else 128; anchors every 8 segments), and C
+# around both kernels' 32-channel groups (64 for bf16); every kernel runs every
+# shape.
 SHAPES = [
     (1, 1, 1), (2, 2, 7), (1, 3, 16), (3, 31, 33), (2, 32, 5), (2, 63, 48), (2, 64, 64),
     (2, 65, 17), (1, 255, 16), (1, 256, 32), (1, 257, 80), (2, 511, 24), (1, 1000, 40),
-    (1, 2048, 31), (1, 2049, 96), (2, 3000, 100), (1, 4097, 16),
+    (1, 2048, 31), (1, 2049, 96), (2, 3000, 100), (1, 4097, 16), (1, 513, 40), (2, 1152, 33),
+    (1, 1153, 64),
 ]
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("B,T,C", SHAPES)
 @pytest.mark.parametrize("wl", [WL0, WL3], ids=["dist0", "dist3"])
 def test_forward_f32(path, B, T, C, wl):
@@ -39,7 +43,7 @@ def test_forward_f32(path, B, T, C, wl):
     assert_state_close(gst, rst, F32_TOL)
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("B,T,C", [(1, 1, 2), (2, 3, 6), (2, 65, 34), (1, 257, 64),
                                    (3, 700, 32), (1, 2049, 66), (1, 130, 7), (1, 2500, 130)])
 def test_forward_bf16(path, B, T, C):
@@ -51,7 +55,7 @@ def test_forward_bf16(path, B, T, C):
     assert_state_close(gst, rst, F32_TOL * 10)
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_forward_from_initial_state(path, io):
     B, T, C = 2, 300, 48
@@ -64,7 +68,7 @@ def test_forward_from_initial_state(path, io):
     assert_state_close(gst, rst, F32_TOL * (10 if io == "bf16" else 1))
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 def test_state_in_place(path):
     B, T, C = 2, 200, 32
     say(f"in-place state path={path}")
@@ -80,7 +84,7 @@ def test_state_in_place(path):
     assert_state_close(host64(ds), rst, F32_TOL)
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 def test_split_and_resume(path):
     B, T, C = 2, 777, 40
     say(f"split/resume path={path}")
@@ -133,7 +137,7 @@ def test_decode_after_prefill_scaled():
     assert_state_close(host64(st), rs, F32_TOL)
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_deterministic(path, io):
     B, T, C = 2, 600, 64
@@ -153,7 +157,7 @@ def ulp32(x: float) -> float:
     return float(np.spacing(np.float32(x)))
 
 
-@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("kmag", [60.0, 88.0, 1e4])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_extreme_keys(path, kmag, io):
@@ -179,13 +183,39 @@ def test_extreme_keys(path, kmag, io):
 
 
 def test_auto_path_choice():
-    """Large B*C goes to the sequential scan, small B*C to the chunked one."""
+    """Large B*C goes to the sequential scan, small B*C to the look-back scan
+    (the chunked scan when no workspace is given)."""
     assert W.wkv_select_path(256, 512, 768) == "seq"
     assert W.wkv_select_path(64, 4096, 4096, W.WKV_IO_BF16) == "seq"
-    assert W.wkv_select_path(8, 1024, 768) == "chunk"
-    assert W.wkv_select_path(4, 16384, 2048) == "chunk"
-    assert W.wkv_select_path(1, 64, 768) == "chunk"
+    assert W.wkv_select_path(8, 1024, 768) == "lookback"
+    assert W.wkv_select_path(4, 16384, 2048) == "lookback"
+    assert W.wkv_select_path(1, 64, 768) == "lookback"
     assert W.wkv_select_path(4, 8, 64) == "seq"
+
+
+def test_lookback_workspace_counters_and_error_word():
+    """The look-back kernel leaves its workspace ready for the next launch:
+    every channel group's ticket and finish counters back at zero, the
+    finished-groups counter at zero, the launch counter advanced once per
+    launch, and the error word (set only if a bounded wait timed out) still
+    zero."""
+    wl = WL3.scaled(B=2, T=3000, C=96)
+    w, u = I.params(wl)
+    k, v = I.kv(wl)
+    ws = W.new_workspace(W.wkv_workspace_size(2, 3000, 96, W.WKV_IO_F32, "lookback"), "cuda")
+    say("look-back workspace counters")
+    ref, _ = wkv_recurrent(w, u, k, v)
+    for n in range(3):
+        out, _ = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        assert_out_close(host64(out), ref, v, F32_TOL)
+        groups = 2 * ((96 + 31) // 32)
+        ctrl = ws[:16 + 16 * groups].view(torch.int32).cpu().numpy()
+        assert ctrl[0] == 0, "a bounded wait timed out"
+        assert ctrl[1] == n + 1 and ctrl[2] == 0, ctrl[:4]
+        per_group = ctrl[4:].reshape(groups, 4)
+        assert np.all(per_group[:, :2] == 0), per_group
 
 
 def test_decode_in_hip_graph_replays_match_eager():

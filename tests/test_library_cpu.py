@@ -55,7 +55,7 @@ def test_validation_codes_without_device():
     assert lib.wkv_forward(2, 5, 0, nul, nul, nul, nul, nul, nul, nul, nul) == 0
     assert lib.wkv_forward(1, 2, 3, nul, nul, nul, nul, nul, nul, nul, nul) == 1
     assert lib.wkv_forward_ex(1, 1, 1, nul, nul, nul, nul, nul, nul, nul, 2, 0, nul) == 7
-    assert lib.wkv_forward_ex(1, 1, 1, nul, nul, nul, nul, nul, nul, nul, 0, 3, nul) == 7
+    assert lib.wkv_forward_ex(1, 1, 1, nul, nul, nul, nul, nul, nul, nul, 0, 4, nul) == 7
     assert lib.wkv_step(-2, 4, nul, nul, nul, nul, nul, nul, nul) == 2
     assert lib.wkv_step(2, 4, nul, nul, nul, nul, nul, nul, nul) == 1
     # fake, never-dereferenced addresses: alignment and overlap are decided on the host
@@ -67,6 +67,30 @@ def test_validation_codes_without_device():
                            P(a + 128 + 32), nul, nul) == 4
     for code in range(9):
         assert lib.wkv_status_string(code)
+
+
+def test_workspace_size_and_requirement_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    seq, chunk, lookback = W.WKV_PATH_SEQ, W.WKV_PATH_CHUNK, W.WKV_PATH_LOOKBACK
+    assert lib.wkv_workspace_size(8, 1024, 768, 0, seq) == 0
+    assert lib.wkv_workspace_size(8, 1024, 768, 0, chunk) == 0
+    n = lib.wkv_workspace_size(8, 1024, 768, 0, lookback)
+    # control words (16 B + 16 B per 32-channel group, rounded up to 256 B) and
+    # 7 tagged 8-byte words per (lane, segment); T = 1024 uses 256-token segments
+    groups = 8 * 768 // 32
+    assert n == ((16 + 16 * groups + 255) // 256) * 256 + 8 * 768 * (1024 // 256) * 7 * 8
+    assert lib.wkv_workspace_size(8, 0, 768, 0, lookback) == 0
+    assert lib.wkv_workspace_size(8, 1024, 768, 5, lookback) < 0
+    assert lib.wkv_workspace_size(-1, 1024, 768, 0, lookback) < 0
+    a = 0x10000000
+    args = [P(a), P(a + 4096), P(a + 8192), P(a + 8192 + 65536), None, P(a + 8192 + 2 * 65536), None]
+    # the look-back kernel without (enough) workspace is refused before any device call
+    assert lib.wkv_forward_ex(1, 64, 256, *args, 0, lookback, None) == 8
+    assert lib.wkv_forward_ws(1, 64, 256, *args, 0, lookback, P(a + (1 << 24)), 64, None) == 8
+    assert lib.wkv_forward_ws(1, 64, 256, *args, 0, lookback, P((a + (1 << 24)) | 8), 1 << 20,
+                              None) == 3
+    assert lib.wkv_forward_ws(1, 64, 256, *args, 0, lookback, P(a + 8192), 1 << 20, None) == 4
 
 
 def test_inputs_are_seeded_and_row_independent():

@@ -16,19 +16,23 @@ from ._lib import (  # noqa: F401
     WKV_IO_F32,
     WKV_PATH_AUTO,
     WKV_PATH_CHUNK,
+    WKV_PATH_LOOKBACK,
     WKV_PATH_SEQ,
     ForwardCall,
     StepCall,
     WKVError,
     forward,
     load_library,
+    new_workspace,
     step,
     wkv_abi_version,
     wkv_forward,
     wkv_forward_bf16,
     wkv_forward_ex,
+    wkv_forward_ws,
     wkv_select_path,
     wkv_status_string,
     wkv_step,
     wkv_step_bf16,
+    wkv_workspace_size,
 )

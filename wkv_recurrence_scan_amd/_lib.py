@@ -21,8 +21,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libwkv.so")
 
 WKV_IO_F32, WKV_IO_BF16 = 0, 1
-WKV_PATH_AUTO, WKV_PATH_SEQ, WKV_PATH_CHUNK = 0, 1, 2
-_PATHS = {"auto": WKV_PATH_AUTO, "seq": WKV_PATH_SEQ, "chunk": WKV_PATH_CHUNK}
+WKV_PATH_AUTO, WKV_PATH_SEQ, WKV_PATH_CHUNK, WKV_PATH_LOOKBACK = 0, 1, 2, 3
+_PATHS = {"auto": WKV_PATH_AUTO, "seq": WKV_PATH_SEQ, "chunk": WKV_PATH_CHUNK,
+          "lookback": WKV_PATH_LOOKBACK}
+_PATH_NAMES = {v: k for k, v in _PATHS.items()}
 
 _lib = None
 
@@ -54,6 +56,8 @@ def load_library() -> ctypes.CDLL:
         "wkv_forward": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
         "wkv_forward_bf16": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
         "wkv_forward_ex": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp],
+        "wkv_forward_ws": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp, i64, vp],
+        "wkv_workspace_size": [i64, i64, i64, ci, ci],
         "wkv_select_path": [i64, i64, i64, ci],
         "wkv_step": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
         "wkv_step_bf16": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
@@ -64,7 +68,8 @@ def load_library() -> ctypes.CDLL:
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name == "wkv_status_string" else ctypes.c_int
+        fn.restype = {"wkv_status_string": ctypes.c_char_p,
+                      "wkv_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
     if lib.wkv_abi_version() != 1:
         raise RuntimeError(f"{LIBRARY_PATH}: unexpected ABI version {lib.wkv_abi_version()}")
     _lib = lib
@@ -106,14 +111,61 @@ def _check(status: int, fn: str):
         raise WKVError(fn, status, load_library().wkv_last_hip_error())
 
 
+def wkv_workspace_size(B: int, T: int, C: int, io: int = WKV_IO_F32, path: str = "auto") -> int:
+    """Bytes of workspace wkv_forward_ws needs (0 when the chosen kernel uses none)."""
+    r = load_library().wkv_workspace_size(B, T, C, io, _PATHS[path])
+    if r < 0:
+        raise WKVError("wkv_workspace_size", -r)
+    return int(r)
+
+
+def new_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled device workspace of at least nbytes (None for 0 bytes).
+    torch's allocator returns blocks aligned to at least 256 bytes."""
+    if nbytes <= 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+_ws_cache = {}
+
+
+def _cached_workspace(nbytes: int, device, stream, shape) -> Optional[torch.Tensor]:
+    """Workspace reused by one-shot calls with the same sizes on one stream
+    (calls on a stream run in order, so they may share it; its layout depends
+    on the sizes, so other sizes get another one)."""
+    if nbytes <= 0:
+        return None
+    key = (device.index, stream.cuda_stream, shape)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        if len(_ws_cache) >= 64:
+            _ws_cache.clear()
+        ws = new_workspace(nbytes, device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def wkv_forward_ws(w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",
+                   workspace=None, want_state=True, stream=None):
+    """wkv_forward_ws: wkv_forward_ex with a device workspace (a uint8 tensor from
+    new_workspace, zero-filled before its first use with these sizes). With
+    workspace=None one is taken from a per-(stream, sizes) cache."""
+    return wkv_forward_ex(w, u, k, v, state_in, out, state_out, path=path, workspace=workspace,
+                          want_state=want_state, stream=stream)
+
+
 def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    state_in: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                    state_out: Optional[torch.Tensor] = None, *, path: str = "auto",
-                   want_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                   workspace: Optional[torch.Tensor] = None, want_state: bool = True,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Prefill over (B, T, C). k, v: float32 or bfloat16 (same dtype; out gets
     it too); w, u: (C,) float32; states: (3, B, C) float32. Returns
     (out, state_out); state_out is None when want_state is False and none was
-    given. path: "auto", "seq" or "chunk"."""
+    given. path: "auto", "seq", "chunk" or "lookback". Calls go through
+    wkv_forward_ws, so "auto" may pick the look-back scan; its workspace is
+    `workspace` or one cached for the stream."""
     lib = load_library()
     if k.dim() != 3:
         raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
@@ -140,10 +192,17 @@ def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.T
         _need(state_out, "state_out", torch.float32, (3, B, C), dev)
     io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
     with torch.cuda.device(dev):
-        st = lib.wkv_forward_ex(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
-                                _ptr(out), _ptr(state_out), io, _PATHS[path],
-                                _stream_handle(dev, stream))
-    _check(st, "wkv_forward_ex")
+        strm = torch.cuda.current_stream(dev) if stream is None else stream
+        if workspace is None:
+            workspace = _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
+                                          (B, T, C, io, path))
+        elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
+        st = lib.wkv_forward_ws(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                                _ptr(out), _ptr(state_out), io, _PATHS[path], _ptr(workspace),
+                                0 if workspace is None else workspace.numel(),
+                                ctypes.c_void_p(strm.cuda_stream))
+    _check(st, "wkv_forward_ws")
     return out, state_out
 
 
@@ -224,21 +283,24 @@ def wkv_step_bf16(w, u, k, v, state, out=None, *, stream=None) -> torch.Tensor:
 
 def wkv_select_path(B: int, T: int, C: int, io: int = WKV_IO_F32) -> str:
     """Name of the kernel the library's automatic choice uses for these sizes
-    on the current device: "seq" or "chunk"."""
+    on the current device when a workspace is available: "seq" or "lookback"
+    (without a workspace, "lookback" becomes "chunk")."""
     r = load_library().wkv_select_path(B, T, C, io)
     if r < 0:
         raise WKVError("wkv_select_path", -r)
-    return {WKV_PATH_SEQ: "seq", WKV_PATH_CHUNK: "chunk"}[r]
+    return _PATH_NAMES[r]
 
 
 class ForwardCall:
-    """A wkv_forward_ex call validated once and launched many times.
+    """A wkv_forward_ws call validated once and launched many times.
 
     The tensors are checked (device, dtype, shape, contiguity) and their
     pointers captured at construction; each call then only passes the saved
     arguments and the stream to the C entry point. Keep the tensors alive and
     unmoved while the object is used. Useful in per-layer loops and under HIP
     graph capture, where per-call Python checks would dominate a ~10 us kernel.
+    The object owns the workspace of its kernel (zero-filled once here), so
+    two ForwardCall objects may run on different streams at the same time.
     """
 
     def __init__(self, w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",
@@ -267,17 +329,20 @@ class ForwardCall:
             _need(state_out, "state_out", torch.float32, (3, B, C), dev)
         self.device = dev
         self.out, self.state_out = out, state_out
-        self._keep = (w, u, k, v, state_in)
         io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
-        self._fn = load_library().wkv_forward_ex
+        with torch.cuda.device(dev):
+            self.workspace = new_workspace(wkv_workspace_size(B, T, C, io, path), dev)
+        self._keep = (w, u, k, v, state_in)
+        self._fn = load_library().wkv_forward_ws
+        ws_bytes = 0 if self.workspace is None else self.workspace.numel()
         self._args = (B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out),
-                      _ptr(state_out), io, _PATHS[path])
+                      _ptr(state_out), io, _PATHS[path], _ptr(self.workspace), ws_bytes)
 
     def __call__(self, stream=None):
         s = torch.cuda.current_stream(self.device) if stream is None else stream
         st = self._fn(*self._args, ctypes.c_void_p(s.cuda_stream))
         if st != 0:
-            _check(st, "wkv_forward_ex")
+            _check(st, "wkv_forward_ws")
         return self.out, self.state_out
 
 

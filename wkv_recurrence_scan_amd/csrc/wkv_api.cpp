@@ -51,21 +51,32 @@ bool misaligned(const void* p, int bytes) {
 // in the kernels inside int64.
 constexpr int64_t kMaxBytes = int64_t(1) << 60;
 
-int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev) {
-  // The sequential scan needs no cross-thread combine, so it wins whenever B*C
-  // lanes alone give every SIMD at least one wave (4 SIMDs per CU); below that
-  // the chunked scan splits time to create the missing parallelism.
+// Kernel for AUTO. The sequential scan needs no cross-thread combine, so it
+// wins whenever B*C lanes alone give every SIMD at least one wave (4 SIMDs per
+// CU); below that a time-parallel kernel creates the missing parallelism: the
+// look-back scan when a workspace is available, else the chunked scan.
+int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev, bool have_ws) {
   const int64_t per_thread = io == wkv::kBf16 ? 2 : 1;
   const int64_t waves = (B * C / per_thread + 63) / 64;
   if (T < 32) return WKV_PATH_SEQ;
-  return waves >= 4LL * cu_count(dev) ? WKV_PATH_SEQ : WKV_PATH_CHUNK;
+  if (waves >= 4LL * cu_count(dev)) return WKV_PATH_SEQ;
+  return have_ws ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
+}
+
+// Workspace the look-back kernel needs, whichever channel width the pointers
+// allow (the larger of the two candidates).
+int64_t lookback_bytes(int io, int64_t B, int64_t T, int64_t C) {
+  const int64_t a = wkv::lookback_workspace_bytes(1, B, T, C);
+  if (io != wkv::kBf16) return a;
+  const int64_t b = wkv::lookback_workspace_bytes(2, B, T, C);
+  return a > b ? a : b;
 }
 
 int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
                  const void* v, const float* state_in, void* out, float* state_out, int io,
-                 int path, hipStream_t stream) {
+                 int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
-  if (path != WKV_PATH_AUTO && path != WKV_PATH_SEQ && path != WKV_PATH_CHUNK) return WKV_ERR_ARG;
+  if (path < WKV_PATH_AUTO || path > WKV_PATH_LOOKBACK) return WKV_ERR_ARG;
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
   const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
   int64_t seq_bytes, state_bytes;
@@ -94,6 +105,25 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
     return WKV_ERR_ALIAS;
   if (state_out != state_in && overlaps(state_out, state_bytes, state_in, state_bytes))
     return WKV_ERR_ALIAS;
+  if (workspace != nullptr && workspace_bytes < 0) return WKV_ERR_WORKSPACE;
+  const bool have_ws = workspace != nullptr && workspace_bytes > 0;
+  if (have_ws) {
+    if (misaligned(workspace, 256)) return WKV_ERR_ALIGN;
+    if (overlaps(workspace, workspace_bytes, k, sbytes) ||
+        overlaps(workspace, workspace_bytes, v, sbytes) ||
+        overlaps(workspace, workspace_bytes, out, sbytes) ||
+        overlaps(workspace, workspace_bytes, w, pbytes) ||
+        overlaps(workspace, workspace_bytes, u, pbytes) ||
+        overlaps(workspace, workspace_bytes, state_in, state_bytes) ||
+        overlaps(workspace, workspace_bytes, state_out, state_bytes))
+      return WKV_ERR_ALIAS;
+  }
+
+  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out};
+  if (path == WKV_PATH_LOOKBACK && T > 0 &&
+      (!have_ws || workspace_bytes < wkv::lookback_workspace_bytes(
+                                         wkv::lookback_vec_width(io, C, a), B, T, C)))
+    return WKV_ERR_WORKSPACE;
 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -105,12 +135,17 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
     return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
   }
 
-  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out};
-  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev);
+  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, have_ws);
   if (path == WKV_PATH_SEQ) {
     e = wkv::launch_seq(a, io, wkv::seq_vec_width(io, C, a), stream);
-  } else {
+  } else if (path == WKV_PATH_CHUNK) {
     e = wkv::launch_chunk(a, io, wkv::chunk_vec_width(io, C, a), stream);
+  } else {
+    const int vec = wkv::lookback_vec_width(io, C, a);
+    if (!have_ws || workspace_bytes < wkv::lookback_workspace_bytes(vec, B, T, C))
+      return WKV_ERR_WORKSPACE;
+    const wkv::LbWorkspace ws{static_cast<uint32_t*>(workspace), workspace_bytes};
+    e = wkv::launch_lookback(a, io, vec, ws, stream);
   }
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
@@ -152,20 +187,44 @@ int wkv_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                 const float* v, const float* state_in, float* out, float* state_out,
                 hipStream_t stream) {
   return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_F32, WKV_PATH_AUTO,
-                      stream);
+                      nullptr, 0, stream);
 }
 
 int wkv_forward_bf16(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                      const uint16_t* k, const uint16_t* v, const float* state_in, uint16_t* out,
                      float* state_out, hipStream_t stream) {
   return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_BF16, WKV_PATH_AUTO,
-                      stream);
+                      nullptr, 0, stream);
 }
 
 int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
                    const void* v, const float* state_in, void* out, float* state_out, int io,
                    int path, hipStream_t stream) {
-  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, stream);
+  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, nullptr, 0,
+                      stream);
+}
+
+int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
+                   const void* v, const float* state_in, void* out, float* state_out, int io,
+                   int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, workspace,
+                      workspace_bytes, stream);
+}
+
+int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return -WKV_ERR_ARG;
+  if (path < WKV_PATH_AUTO || path > WKV_PATH_LOOKBACK) return -WKV_ERR_ARG;
+  if (B < 0 || T < 0 || C < 0) return -WKV_ERR_DIM;
+  int64_t cells;
+  if (!mul3(B, T, C, &cells) || cells > kMaxBytes) return -WKV_ERR_DIM;
+  if (B == 0 || C == 0 || T == 0) return 0;
+  if (path == WKV_PATH_AUTO) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
+    path = choose_path(B, T, C, io, dev, true);
+  }
+  return path == WKV_PATH_LOOKBACK ? lookback_bytes(io, B, T, C) : 0;
 }
 
 int wkv_select_path(int64_t B, int64_t T, int64_t C, int io) {
@@ -174,7 +233,7 @@ int wkv_select_path(int64_t B, int64_t T, int64_t C, int io) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
-  return choose_path(B, T, C, io, dev);
+  return choose_path(B, T, C, io, dev, true);
 }
 
 int wkv_step(int64_t B, int64_t C, const float* w, const float* u, const float* k, const float* v,
@@ -197,6 +256,7 @@ const char* wkv_status_string(int status) {
     case WKV_ERR_LAUNCH: return "WKV_ERR_LAUNCH: kernel launch failed";
     case WKV_ERR_DEVICE: return "WKV_ERR_DEVICE: no usable HIP device";
     case WKV_ERR_ARG: return "WKV_ERR_ARG: io or path out of range";
+    case WKV_ERR_WORKSPACE: return "WKV_ERR_WORKSPACE: the kernel needs a (larger) workspace";
     default: return "unknown wkv_status";
   }
 }

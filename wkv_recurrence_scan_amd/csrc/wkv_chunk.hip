@@ -31,79 +31,10 @@
 // lines shared by two groups (bf16 tails, odd C) are fetched through one L2.
 #include "wkv_device.h"
 #include "wkv_internal.h"
+#include "wkv_tile.h"
 
 namespace wkv {
 namespace {
-
-constexpr int kNumXcd = 8;
-
-// Block index -> work index such that consecutive work indices land on the
-// same XCD when blocks are dealt to XCDs round-robin. A bijection on [0, n).
-__device__ __forceinline__ int64_t xcd_swizzle(int64_t bid, int64_t n) {
-  const int64_t q = n / kNumXcd, r = n % kNumXcd;
-  const int64_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
-  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-}
-
-__device__ __forceinline__ Seg shfl_up_seg(const Seg& x, int delta) {
-  Seg r;
-  r.n = __shfl_up(x.n, delta, 64);
-  r.d = __shfl_up(x.d, delta, 64);
-  r.m = __shfl_up(x.m, delta, 64);
-  r.len = __shfl_up(x.len, delta, 64);
-  return r;
-}
-
-// Summary of one sub-chunk: its own state from empty, maximum taken at the
-// end of the sub-chunk. MASKED: only the first nvalid tokens exist.
-template <int L, bool MASKED>
-__device__ __forceinline__ Seg summarize(const float (&kk)[L], const float (&vv)[L], float wd,
-                                         int nvalid) {
-  float z[L];
-  float top = kEmpty;
-  const float last = MASKED ? static_cast<float>(nvalid - 1) : static_cast<float>(L - 1);
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    // exponent of token i once the sub-chunk has ended: k_i - (last - i) w
-    z[i] = __builtin_fmaf(static_cast<float>(i) - last, wd, kk[i]);
-    if (!MASKED || i < nvalid) top = __builtin_fmaxf(top, z[i]);
-  }
-  float n = 0.0f, d = 0.0f;
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    float e = fast_exp2((z[i] - top) * kLog2e);
-    if (MASKED && i >= nvalid) e = 0.0f;
-    d += e;
-    n = __builtin_fmaf(e, vv[i], n);
-  }
-  return Seg{n, d, top, MASKED ? static_cast<float>(nvalid) : static_cast<float>(L)};
-}
-
-template <int V, int L>
-struct ChunkRegs {
-  float k[L][V];
-  float v[L][V];
-};
-
-template <typename IoT, int V, int L, bool MASKED>
-__device__ __forceinline__ void chunk_load(ChunkRegs<V, L>& r,
-                                           const typename IoT::elem* __restrict__ kp,
-                                           const typename IoT::elem* __restrict__ vp, int64_t C,
-                                           int nvalid) {
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    if (!MASKED || i < nvalid) {
-      IoT::template load<V, false>(kp + i * C, r.k[i]);
-      IoT::template load<V, false>(vp + i * C, r.v[i]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        r.k[i][j] = 0.0f;
-        r.v[i][j] = 0.0f;
-      }
-    }
-  }
-}
 
 template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED>
 __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid, Lane (&carry)[V],

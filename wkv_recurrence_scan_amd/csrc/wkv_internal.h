@@ -45,6 +45,17 @@ struct ChunkShape {
 };
 ChunkShape chunk_shape(int io, int vec, int64_t T);
 
+// Look-back scan: device workspace = control words, then the published
+// per-(segment, channel) words. Zero-filled before first use; each launch
+// leaves it ready for the next.
+struct LbWorkspace {
+  uint32_t* ctrl;  // start of the workspace
+  int64_t bytes;   // its size
+};
+int lookback_vec_width(int io, int64_t C, const FwdArgs& a);
+int64_t lookback_workspace_bytes(int vec, int64_t B, int64_t T, int64_t C);
+hipError_t launch_lookback(const FwdArgs& a, int io, int vec, const LbWorkspace& ws, hipStream_t s);
+
 hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);
