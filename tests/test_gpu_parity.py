@@ -194,28 +194,27 @@ def test_auto_path_choice():
 
 
 def test_lookback_workspace_counters_and_error_word():
-    """The look-back kernel leaves its workspace ready for the next launch:
-    every channel group's ticket and finish counters back at zero, the
-    finished-groups counter at zero, the launch counter advanced once per
-    launch, and the error word (set only if a bounded wait timed out) still
-    zero."""
+    """The look-back kernel's workspace after n launches: every channel
+    group's ticket counter advanced by exactly S (segments per group) per
+    launch, which is what gives each launch its own epoch, and the error word
+    (set only if a bounded wait timed out) still zero. T = 3000 uses
+    256-token segments, so S = 12."""
     wl = WL3.scaled(B=2, T=3000, C=96)
     w, u = I.params(wl)
     k, v = I.kv(wl)
     ws = W.new_workspace(W.wkv_workspace_size(2, 3000, 96, W.WKV_IO_F32, "lookback"), "cuda")
     say("look-back workspace counters")
     ref, _ = wkv_recurrent(w, u, k, v)
+    groups, S = 2 * ((96 + 31) // 32), (3000 + 255) // 256
     for n in range(3):
         out, _ = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
                                   workspace=ws)
         torch.cuda.synchronize()
         assert_out_close(host64(out), ref, v, F32_TOL)
-        groups = 2 * ((96 + 31) // 32)
-        ctrl = ws[:16 + 16 * groups].view(torch.int32).cpu().numpy()
-        assert ctrl[0] == 0, "a bounded wait timed out"
-        assert ctrl[1] == n + 1 and ctrl[2] == 0, ctrl[:4]
-        per_group = ctrl[4:].reshape(groups, 4)
-        assert np.all(per_group[:, :2] == 0), per_group
+        words = ws[:16 + 16 * groups].view(torch.int64).cpu().numpy()
+        assert int(words[0]) & 0xffffffff == 0, "a bounded wait timed out"
+        tickets = words[2:].reshape(groups, 2)[:, 0]
+        assert np.all(tickets == (n + 1) * S), tickets
 
 
 def test_decode_in_hip_graph_replays_match_eager():

@@ -39,8 +39,9 @@ namespace {
 template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED>
 __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid, Lane (&carry)[V],
                                            const float (&wd)[V], const float (&ub)[V],
-                                           Seg (*tot)[LC * V], typename IoT::elem* __restrict__ op,
-                                           int64_t C, bool cvalid, int wave, int sl, int cl) {
+                                           const float (&cb)[V], bool fast, Seg (*tot)[LC * V],
+                                           typename IoT::elem* __restrict__ op, int64_t C,
+                                           bool cvalid, int wave, int sl, int cl) {
   // 1. own summary, 2. inclusive scan over the wave's sub-chunks
   Seg inc[V];
 #pragma unroll
@@ -86,17 +87,7 @@ __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid,
 #pragma unroll
   for (int j = 0; j < V; ++j) lane_absorb(pre[j], exc[j], wd[j]);
   // 4. rescan own tokens from the prefix
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    // a guard, not a break, so that the loop stays fully unrolled and the
-    // register arrays keep static indices
-    if (!MASKED || i < nvalid) {
-      float o[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) o[j] = lane_step(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j]);
-      if (cvalid) IoT::template store<V, true>(op + i * C, o);
-    }
-  }
+  rescan_sel<IoT, V, L, MASKED>(fast, pre, r, wd, ub, cb, nvalid, cvalid, op, C);
 }
 
 template <typename IoT, int V, int LC, int PS, int W, int L>
@@ -128,6 +119,9 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   float wd[V], ub[V];  // decay w and bonus u of the V channels
   IoF32::load<V, false>(w + cc, wd);
   IoF32::load<V, false>(u + cc, ub);
+  float cb[V];
+  bonus_ratios(wd, ub, cb);
+  const bool fast = wave_fast_ok(wd, ub);
   Lane carry[V];
   if (state_in != nullptr) {
     float n[V], d[V], m[V];
@@ -158,12 +152,12 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   for (int64_t tile = 0; tile < full; tile += 2) {
     const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
     chunk_load<IoT, V, L, false>(Bf, kp + nb * step, vp + nb * step, C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, wd, ub, tot[tile & 1], op + tile * step,
-                                            C, cvalid, wave, sl, cl);
+    chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, wd, ub, cb, fast, tot[tile & 1],
+                                            op + tile * step, C, cvalid, wave, sl, cl);
     if (tile + 1 >= full) break;
     const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
     chunk_load<IoT, V, L, false>(A, kp + na * step, vp + na * step, C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, wd, ub, tot[(tile + 1) & 1],
+    chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, wd, ub, cb, fast, tot[(tile + 1) & 1],
                                             op + (tile + 1) * step, C, cvalid, wave, sl, cl);
   }
   if (full * TL < T) {  // last, partial tile
@@ -172,7 +166,7 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
     const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
     ChunkRegs<V, L> last;
     chunk_load<IoT, V, L, true>(last, kp + full * step, vp + full * step, C, nvalid);
-    chunk_tile<IoT, V, LC, PS, W, L, true>(last, nvalid, carry, wd, ub, tot[full & 1],
+    chunk_tile<IoT, V, LC, PS, W, L, true>(last, nvalid, carry, wd, ub, cb, fast, tot[full & 1],
                                            op + full * step, C, cvalid, wave, sl, cl);
   }
 

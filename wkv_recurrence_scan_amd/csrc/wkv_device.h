@@ -193,6 +193,69 @@ __device__ __forceinline__ float lane_step(Lane& s, float k, float v, float w, f
   return out;
 }
 
+// The same step with one exponential instead of two. Both the update and the
+// output are taken against the state's maximum after the step,
+// m' = max(m - w, k): the decayed state then weighs F = e^(m - w - m') and the
+// token G = e^(k - m'), one of them exactly 1 and the other one exp2 of minus
+// an absolute difference. The output's weights, e^m for the state and
+// e^(u + k) for the token, are the same two scaled by e^w and e^u, so
+//   out = (F n + G c v) / (F d + G c),   c = e^(u - w) per channel.
+// Valid while c and 1/c are far inside the fp32 range (|u - w| <= kFastGap);
+// otherwise the kernels use lane_step.
+constexpr float kFastGap = 32.0f;
+
+__device__ __forceinline__ bool fast_step_ok(float w, float u) {
+  return __builtin_fabsf(u - w) <= kFastGap;  // false for NaN too
+}
+
+__device__ __forceinline__ float bonus_ratio(float w, float u) { return expf(u - w); }
+
+__device__ __forceinline__ float lane_step_fast(Lane& s, float k, float v, float w, float c) {
+  const float age1 = s.age + 1.0f;
+  const float g = __builtin_fmaf(age1, w, k - s.base);  // k - (m - w)
+  const float x = fast_exp2(__builtin_fabsf(g) * -kLog2e);
+  const bool tok_wins = g > 0.0f;
+  const float F = tok_wins ? x : 1.0f;
+  const float G = tok_wins ? 1.0f : x;
+  const float fn = F * s.n;
+  const float fd = F * s.d;
+  const float gc = G * c;
+  const float out = __builtin_fmaf(gc, v, fn) * fast_rcp(fd + gc);
+  s.n = __builtin_fmaf(G, v, fn);
+  s.d = fd + G;
+  s.base = tok_wins ? k : s.base;
+  s.age = tok_wins ? 0.0f : age1;
+  return out;
+}
+
+// c = e^(u - w) of each of V channels, for lane_step_fast.
+template <int V>
+__device__ __forceinline__ void bonus_ratios(const float (&wd)[V], const float (&ub)[V],
+                                             float (&cb)[V]) {
+#pragma unroll
+  for (int j = 0; j < V; ++j) cb[j] = bonus_ratio(wd[j], ub[j]);
+}
+
+// True when every channel of every active lane of the wave may take
+// lane_step_fast: the same answer in all lanes, so a branch on it does not
+// diverge.
+template <int V>
+__device__ __forceinline__ bool wave_fast_ok(const float (&wd)[V], const float (&ub)[V]) {
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < V; ++j) ok = ok && fast_step_ok(wd[j], ub[j]);
+  return __all(ok) != 0;
+}
+
+template <bool FAST>
+__device__ __forceinline__ float step_sel(Lane& s, float k, float v, float w, float u, float c) {
+  if constexpr (FAST) {
+    return lane_step_fast(s, k, v, w, c);
+  } else {
+    return lane_step(s, k, v, w, u);
+  }
+}
+
 // ------------------------------------------------- segment summaries (chunks)
 
 // The state produced by a run of `len` tokens from the empty state, with its

@@ -31,16 +31,22 @@
 // Publication uses 64-bit words tagged with a per-launch epoch in their high
 // half and written/read with device-scope relaxed atomics: a value is
 // accepted only when its tag is the current epoch, so the words need no
-// fences and nothing has to be cleared between launches. The epoch lives in
-// the workspace (a launch counter that the last channel group to finish
-// advances), so a launch replayed from a HIP graph still gets a fresh one;
-// tags are never 0, so a zero-filled workspace holds no valid word. The
-// workspace's layout depends on the problem's sizes: reusing it for other
-// sizes needs it zero-filled again. Inclusive prefixes
-// keep their maximum index-tracked (base, age), so chains of segments do not
-// accumulate rounding. Every wait is bounded: past the limit a workgroup
-// flags an error word in the workspace and proceeds, so the kernel always
-// finishes.
+// fences and nothing has to be cleared between launches. Each channel group's
+// ticket counter is never reset: every launch advances it by exactly S (the
+// segments per group), so ticket t means segment t mod S of launch t / S, and
+// the launch number gives the epoch (a launch replayed from a HIP graph gets
+// a fresh one too, and a workgroup needs no second counter to read or to
+// update on exit). Tags are never 0, so a zero-filled workspace holds no valid
+// word. The workspace's layout depends on the problem's sizes: reusing it for
+// other sizes needs it zero-filled again. Inclusive prefixes keep their
+// maximum index-tracked (base, age), so chains of segments do not accumulate
+// rounding. Every wait is bounded: past the limit a workgroup flags an error
+// word in the workspace and proceeds, so the kernel always finishes.
+//
+// While its ticket is in flight a workgroup already loads the tile of the
+// segment it will most likely get (blocks of a group start in index order),
+// and loads again only if the ticket says otherwise; the guess only decides
+// what is prefetched, never which segment is processed.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 #include "wkv_tile.h"
@@ -76,11 +82,11 @@ struct LbArgs {
   int64_t groups;       // G: channel groups (B * groups_per_row)
   int64_t segments;     // S: segments per lane
   int64_t gpr;          // channel groups per batch row
-  uint32_t* ctrl;       // [0] error flag, [1] launch count, [2] finished groups;
-                        // per group g at [4 + 4g]: ticket, finished workgroups
+  uint32_t* err;        // error word: bit 0 set when a wait ran out
+  uint64_t* tickets;    // ticket counter of group g at tickets[2 g]
   uint64_t* agg;        // [S][G][CH][3] tile aggregates (n, d, m)
   uint64_t* inc;        // [S][G][CH][4] inclusive prefixes (n, d, base, age)
-  uint32_t epoch;       // tag of this launch's words: launch count + 1 (never 0)
+  uint32_t epoch;       // tag of this launch's words (never 0)
 };
 
 // Wait (bounded) until the n tagged words at p carry this launch's epoch and
@@ -94,7 +100,7 @@ __device__ __forceinline__ void wait_words(const LbArgs& a, uint64_t* p, float (
     for (int i = 0; i < N; ++i) ok = get(p + i, a.epoch, x[i]) && ok;
     if (ok) return;
     if (spin >= kSpinLimit) {
-      __hip_atomic_fetch_or(a.ctrl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int i = 0; i < N; ++i) x[i] = 0.0f;
       return;
@@ -103,12 +109,26 @@ __device__ __forceinline__ void wait_words(const LbArgs& a, uint64_t* p, float (
   }
 }
 
+// Offset of thread (wave, lane)'s first token of segment s in k, v and out.
+template <int V, int W, int L>
+__device__ __forceinline__ int64_t lb_offset(int64_t s, int64_t g, int64_t gpr, int64_t T,
+                                             int64_t C) {
+  constexpr int CH = kLbLC * V, TL = W * kLbPS * L;
+  const int lane = threadIdx.x & 63;
+  const int sub = (threadIdx.x >> 6) * kLbPS + lane / kLbLC;
+  const int64_t b = g / gpr;
+  const int64_t c0 = (g - b * gpr) * CH + (lane % kLbLC) * V;
+  const int64_t cc = c0 < C ? c0 : C - V;
+  return b * T * C + cc + (s * TL + static_cast<int64_t>(sub) * L) * C;
+}
+
+// One segment of one channel group; r holds this thread's tokens of it
+// (loaded by the caller), the first nvalid of them valid.
 template <typename IoT, int V, int W, int L, bool MASKED>
 __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, int64_t B, int64_t T,
                                         int64_t C, const float* __restrict__ w,
                                         const float* __restrict__ u,
-                                        const typename IoT::elem* __restrict__ k,
-                                        const typename IoT::elem* __restrict__ v,
+                                        const ChunkRegs<V, L>& r, int nvalid,
                                         const float* __restrict__ state_in,
                                         typename IoT::elem* __restrict__ out,
                                         float* __restrict__ state_out, Seg (*tot)[kLbLC * V],
@@ -119,7 +139,6 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   const int lane = tid & 63;
   const int cl = lane % LC;
   const int sl = lane / LC;
-  const int sub = wave * PS + sl;
 
   const int64_t b = g / a.gpr;
   const int64_t c0 = (g - b * a.gpr) * CH + cl * V;
@@ -127,17 +146,11 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   const int64_t cc = cvalid ? c0 : C - V;
   const int64_t plane = B * C;
   const int64_t lane0 = b * C + cc;
+  const int64_t base = lb_offset<V, W, L>(s, g, a.gpr, T, C);
 
   float wd[V], ub[V];
   IoF32::load<V, false>(w + cc, wd);
   IoF32::load<V, false>(u + cc, ub);
-
-  const int64_t first = s * TL + static_cast<int64_t>(sub) * L;
-  const int64_t left = T - first;
-  const int nvalid = MASKED ? (left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left))) : L;
-  const int64_t base = b * T * C + cc + first * C;
-  ChunkRegs<V, L> r;
-  chunk_load<IoT, V, L, MASKED>(r, k + base, v + base, C, nvalid);
 
   // sub-chunk summaries, scan inside the wave, wave totals through LDS
   Seg inc[V], exc[V];
@@ -257,16 +270,10 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
     lane_absorb(pre[j], before[j], wd[j]);
     lane_absorb(pre[j], exc[j], wd[j]);
   }
-  typename IoT::elem* op = out + base;
-#pragma unroll
-  for (int i = 0; i < L; ++i) {
-    if (!MASKED || i < nvalid) {
-      float o[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) o[j] = lane_step(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j]);
-      if (cvalid) IoT::template store<V, true>(op + i * C, o);
-    }
-  }
+  float cb[V];
+  bonus_ratios(wd, ub, cb);
+  rescan_sel<IoT, V, L, MASKED>(wave_fast_ok(wd, ub), pre, r, wd, ub, cb, nvalid, cvalid,
+                                out + base, C);
 }
 
 template <typename IoT, int V, int W, int L>
@@ -290,44 +297,36 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   // waits for belongs to a workgroup that has already started) and the
   // counters' atomics are spread over G addresses.
   const int64_t g = blockIdx.x % a.groups;
-  uint32_t* gc = a.ctrl + 4 + 4 * g;  // ticket, finished workgroups
+  const int64_t S = a.segments;
   if (threadIdx.x == 0) {
-    seg_s = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t launches = __hip_atomic_load(a.ctrl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    epoch_s = launches % 0xffffffffu + 1u;
+    const uint64_t t =
+        __hip_atomic_fetch_add(a.tickets + 2 * g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seg_s = static_cast<uint32_t>(t % static_cast<uint64_t>(S));
+    epoch_s = static_cast<uint32_t>((t / static_cast<uint64_t>(S)) % 0xffffffffull) + 1u;
+  }
+  // prefetch the likely segment's tile while the ticket is in flight
+  const int64_t guess = blockIdx.x / a.groups;
+  const bool guess_full = (guess + 1) * TL <= T;
+  ChunkRegs<V, L> r;
+  if (guess_full) {
+    const int64_t off = lb_offset<V, W, L>(guess, g, a.gpr, T, C);
+    chunk_load<IoT, V, L, false>(r, k + off, v + off, C, L);
   }
   __syncthreads();
   a.epoch = epoch_s;
   const int64_t s = seg_s;
-  if (s >= a.segments) {
-    // only possible with a workspace that was not zero-filled: do no work
-    if (threadIdx.x == 0) {
-      __hip_atomic_fetch_or(a.ctrl, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  } else if ((s + 1) * TL <= T) {
-    lb_tile<IoT, V, W, L, false>(a, s, g, B, T, C, w, u, k, v, state_in, out, state_out, tot,
-                                 xs, fetched);
+  const int64_t off = lb_offset<V, W, L>(s, g, a.gpr, T, C);
+  if ((s + 1) * TL <= T) {
+    if (!guess_full || s != guess) chunk_load<IoT, V, L, false>(r, k + off, v + off, C, L);
+    lb_tile<IoT, V, W, L, false>(a, s, g, B, T, C, w, u, r, L, state_in, out, state_out, tot, xs,
+                                 fetched);
   } else {
-    lb_tile<IoT, V, W, L, true>(a, s, g, B, T, C, w, u, k, v, state_in, out, state_out, tot, xs,
-                                fetched);
-  }
-  // The group's last workgroup returns the group's counters to zero; the last
-  // group to finish (every workgroup of the launch has then read the launch
-  // count) advances the launch count, so the next launch, replayed from a
-  // graph or not, tags its words differently.
-  if (threadIdx.x == 0) {
-    const uint32_t done =
-        __hip_atomic_fetch_add(gc + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-    if (done == static_cast<uint32_t>(a.segments)) {
-      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gc + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t groups_done =
-          __hip_atomic_fetch_add(a.ctrl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-      if (groups_done == static_cast<uint32_t>(a.groups)) {
-        __hip_atomic_store(a.ctrl + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    const int sub = (threadIdx.x >> 6) * kLbPS + (threadIdx.x & 63) / kLbLC;
+    const int64_t left = T - (s * TL + static_cast<int64_t>(sub) * L);
+    const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
+    chunk_load<IoT, V, L, true>(r, k + off, v + off, C, nvalid);
+    lb_tile<IoT, V, W, L, true>(a, s, g, B, T, C, w, u, r, nvalid, state_in, out, state_out, tot,
+                                xs, fetched);
   }
 }
 
@@ -344,9 +343,9 @@ auto lb_dispatch(int64_t T, F&& f) {
   return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 32>{});
 }
 
-// Control words: an error word and launch counters, then four words per
-// channel group, rounded up to 256 bytes so the tagged words after them stay
-// aligned.
+// Control words: the error word, then one 64-bit ticket counter per channel
+// group (16 bytes apart), rounded up to 256 bytes so the tagged words after
+// them stay aligned.
 int64_t lookback_ctrl_bytes(int64_t groups) { return ((16 + 16 * groups + 255) / 256) * 256; }
 
 template <int V, int W, int L>
@@ -372,12 +371,13 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
   la.groups = groups;
   la.segments = segments;
   la.gpr = gpr;
-  la.ctrl = ws.ctrl;
+  la.err = ws.ctrl;
+  la.tickets = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.ctrl) + 16);
   uint64_t* slots = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.ctrl) +
                                                 lookback_ctrl_bytes(groups));
   la.agg = slots;
   la.inc = slots + items * CH * 3;
-  la.epoch = 0;  // read from the workspace by the kernel
+  la.epoch = 0;  // derived from the ticket by the kernel
   hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L>), dim3(static_cast<unsigned>(items)),
                      dim3(64 * W), 0, st, a.B, a.T, a.C, a.w, a.u,
                      static_cast<const typename IoT::elem*>(a.k),

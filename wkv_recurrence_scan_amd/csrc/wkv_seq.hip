@@ -37,16 +37,53 @@ __device__ __forceinline__ void seq_load(SeqBlock<IoT, V, U>& blk,
   }
 }
 
-template <typename IoT, int V, int U>
+template <typename IoT, int V, int U, bool FAST>
 __device__ __forceinline__ void seq_compute(const SeqBlock<IoT, V, U>& blk, Lane (&s)[V],
                                             const float (&wd)[V], const float (&ub)[V],
+                                            const float (&cb)[V],
                                             typename IoT::elem* __restrict__ op, int64_t C) {
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     float o[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) o[j] = lane_step(s[j], blk.k[i][j], blk.v[i][j], wd[j], ub[j]);
+    for (int j = 0; j < V; ++j) {
+      o[j] = step_sel<FAST>(s[j], blk.k[i][j], blk.v[i][j], wd[j], ub[j], cb[j]);
+    }
     IoT::template store<V, true>(op + i * C, o);
+  }
+}
+
+// All T tokens of one thread's channels, in order.
+template <typename IoT, int V, int U, bool FAST>
+__device__ __forceinline__ void seq_walk(Lane (&s)[V], const float (&wd)[V], const float (&ub)[V],
+                                         const float (&cb)[V],
+                                         const typename IoT::elem* __restrict__ kp,
+                                         const typename IoT::elem* __restrict__ vp,
+                                         typename IoT::elem* __restrict__ op, int64_t T,
+                                         int64_t C) {
+  // Two register buffers, alternating; the loads for the block after the one
+  // being computed are issued first, on every path (the last full block
+  // re-reads itself, a cache hit), so that the compiler's counter-based waits
+  // only ever wait for the block about to be used.
+  SeqBlock<IoT, V, U> A, Bf;
+  const int64_t nblk = T / U;
+  if (nblk > 0) seq_load<IoT, V, U>(A, kp, vp, C);
+  for (int64_t blk = 0; blk < nblk; blk += 2) {
+    const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
+    seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, C);
+    seq_compute<IoT, V, U, FAST>(A, s, wd, ub, cb, op + blk * U * C, C);
+    if (blk + 1 >= nblk) break;
+    const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
+    seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, C);
+    seq_compute<IoT, V, U, FAST>(Bf, s, wd, ub, cb, op + (blk + 1) * U * C, C);
+  }
+  for (int64_t t = nblk * U; t < T; ++t) {
+    float kk[V], vv[V], o[V];
+    IoT::template load<V, true>(kp + t * C, kk);
+    IoT::template load<V, true>(vp + t * C, vv);
+#pragma unroll
+    for (int j = 0; j < V; ++j) o[j] = step_sel<FAST>(s[j], kk[j], vv[j], wd[j], ub[j], cb[j]);
+    IoT::template store<V, true>(op + t * C, o);
   }
 }
 
@@ -86,30 +123,12 @@ __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
   const typename IoT::elem* vp = v + row;
   typename IoT::elem* op = out + row;
 
-  // Two register buffers, alternating; the loads for the block after the one
-  // being computed are issued first, on every path (the last full block
-  // re-reads itself, a cache hit), so that the compiler's counter-based waits
-  // only ever wait for the block about to be used.
-  SeqBlock<IoT, V, U> A, Bf;
-  const int64_t nblk = T / U;
-  if (nblk > 0) seq_load<IoT, V, U>(A, kp, vp, C);
-  for (int64_t blk = 0; blk < nblk; blk += 2) {
-    const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
-    seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, C);
-    seq_compute<IoT, V, U>(A, s, wd, ub, op + blk * U * C, C);
-    if (blk + 1 >= nblk) break;
-    const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
-    seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, C);
-    seq_compute<IoT, V, U>(Bf, s, wd, ub, op + (blk + 1) * U * C, C);
-  }
-  int64_t t = nblk * U;
-  for (; t < T; ++t) {
-    float kk[V], vv[V], o[V];
-    IoT::template load<V, true>(kp + t * C, kk);
-    IoT::template load<V, true>(vp + t * C, vv);
-#pragma unroll
-    for (int j = 0; j < V; ++j) o[j] = lane_step(s[j], kk[j], vv[j], wd[j], ub[j]);
-    IoT::template store<V, true>(op + t * C, o);
+  float cb[V];
+  bonus_ratios(wd, ub, cb);
+  if (wave_fast_ok(wd, ub)) {
+    seq_walk<IoT, V, U, true>(s, wd, ub, cb, kp, vp, op, T, C);
+  } else {
+    seq_walk<IoT, V, U, false>(s, wd, ub, cb, kp, vp, op, T, C);
   }
 
   if (state_out != nullptr) {

@@ -78,5 +78,39 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<V, L>& r,
   }
 }
 
+// Re-runs the recurrence over one thread's sub-chunk from the state in front
+// of it and writes the outputs. FAST selects lane_step_fast.
+template <typename IoT, int V, int L, bool MASKED, bool FAST>
+__device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L>& r,
+                                       const float (&wd)[V], const float (&ub)[V],
+                                       const float (&cb)[V], int nvalid, bool cvalid,
+                                       typename IoT::elem* __restrict__ op, int64_t C) {
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    // a guard, not a break, so that the loop stays fully unrolled and the
+    // register arrays keep static indices
+    if (!MASKED || i < nvalid) {
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        o[j] = step_sel<FAST>(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j], cb[j]);
+      }
+      if (cvalid) IoT::template store<V, true>(op + i * C, o);
+    }
+  }
+}
+
+template <typename IoT, int V, int L, bool MASKED>
+__device__ __forceinline__ void rescan_sel(bool fast, Lane (&pre)[V], const ChunkRegs<V, L>& r,
+                                           const float (&wd)[V], const float (&ub)[V],
+                                           const float (&cb)[V], int nvalid, bool cvalid,
+                                           typename IoT::elem* __restrict__ op, int64_t C) {
+  if (fast) {
+    rescan<IoT, V, L, MASKED, true>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+  } else {
+    rescan<IoT, V, L, MASKED, false>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+  }
+}
+
 }  // namespace
 }  // namespace wkv
