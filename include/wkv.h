@@ -79,8 +79,9 @@ enum { WKV_IO_F32 = 0, WKV_IO_BF16 = 1 };
  * sub-chunks in parallel (small B*C, no workspace). LOOKBACK: every
  * (sequence segment, channel group) is its own workgroup, chained by a
  * decoupled look-back through a device workspace (small B*C, most
- * parallelism). AUTO picks SEQ when B*C alone fills the GPU, otherwise
- * LOOKBACK when a workspace is given and CHUNK when not. */
+ * parallelism). AUTO picks SEQ when B*C alone fills the GPU, otherwise CHUNK
+ * up to T = 2048 and, for longer sequences, LOOKBACK when a workspace is
+ * given (CHUNK when not). */
 enum { WKV_PATH_AUTO = 0, WKV_PATH_SEQ = 1, WKV_PATH_CHUNK = 2, WKV_PATH_LOOKBACK = 3 };
 
 /* Prefill / training form over a whole sequence (page "Linear attention
@@ -139,8 +140,9 @@ int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float*
 int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path);
 
 /* The kernel WKV_PATH_AUTO uses for these sizes on the current device when a
- * workspace is available (WKV_PATH_SEQ or WKV_PATH_LOOKBACK; without one,
- * LOOKBACK becomes WKV_PATH_CHUNK), or a negative wkv_status on error. */
+ * workspace is available (WKV_PATH_SEQ, WKV_PATH_CHUNK or WKV_PATH_LOOKBACK;
+ * without one, LOOKBACK becomes WKV_PATH_CHUNK), or a negative wkv_status on
+ * error. */
 int wkv_select_path(int64_t B, int64_t T, int64_t C, int io);
 
 /* One decode step for B sequences at once (page "Linear attention without

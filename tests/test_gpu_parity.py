@@ -183,13 +183,14 @@ def test_extreme_keys(path, kmag, io):
 
 
 def test_auto_path_choice():
-    """Large B*C goes to the sequential scan, small B*C to the look-back scan
-    (the chunked scan when no workspace is given)."""
+    """Large B*C goes to the sequential scan; small B*C to the chunked scan up
+    to T = 2048 and to the look-back scan beyond (the chunked scan when no
+    workspace is given)."""
     assert W.wkv_select_path(256, 512, 768) == "seq"
     assert W.wkv_select_path(64, 4096, 4096, W.WKV_IO_BF16) == "seq"
-    assert W.wkv_select_path(8, 1024, 768) == "lookback"
+    assert W.wkv_select_path(8, 1024, 768) == "chunk"
     assert W.wkv_select_path(4, 16384, 2048) == "lookback"
-    assert W.wkv_select_path(1, 64, 768) == "lookback"
+    assert W.wkv_select_path(1, 64, 768) == "chunk"
     assert W.wkv_select_path(4, 8, 64) == "seq"
 
 

@@ -283,8 +283,8 @@ def wkv_step_bf16(w, u, k, v, state, out=None, *, stream=None) -> torch.Tensor:
 
 def wkv_select_path(B: int, T: int, C: int, io: int = WKV_IO_F32) -> str:
     """Name of the kernel the library's automatic choice uses for these sizes
-    on the current device when a workspace is available: "seq" or "lookback"
-    (without a workspace, "lookback" becomes "chunk")."""
+    on the current device when a workspace is available: "seq", "chunk" or
+    "lookback" (without a workspace, "lookback" becomes "chunk")."""
     r = load_library().wkv_select_path(B, T, C, io)
     if r < 0:
         raise WKVError("wkv_select_path", -r)

@@ -53,14 +53,18 @@ constexpr int64_t kMaxBytes = int64_t(1) << 60;
 
 // Kernel for AUTO. The sequential scan needs no cross-thread combine, so it
 // wins whenever B*C lanes alone give every SIMD at least one wave (4 SIMDs per
-// CU); below that a time-parallel kernel creates the missing parallelism: the
-// look-back scan when a workspace is available, else the chunked scan.
+// CU). Below that a time-parallel kernel creates the missing parallelism:
+// up to kChunkMaxT tokens the chunked scan (measured on MI355X: as fast as the
+// look-back scan there, and it needs no workspace), beyond it the look-back
+// scan when a workspace is available.
+constexpr int64_t kChunkMaxT = 2048;
+
 int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev, bool have_ws) {
   const int64_t per_thread = io == wkv::kBf16 ? 2 : 1;
   const int64_t waves = (B * C / per_thread + 63) / 64;
   if (T < 32) return WKV_PATH_SEQ;
   if (waves >= 4LL * cu_count(dev)) return WKV_PATH_SEQ;
-  return have_ws ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
+  return have_ws && T > kChunkMaxT ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
 }
 
 // Workspace the look-back kernel needs, whichever channel width the pointers

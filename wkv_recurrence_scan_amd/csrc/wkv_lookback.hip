@@ -153,47 +153,8 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   IoF32::load<V, false>(u + cc, ub);
 
   // sub-chunk summaries, scan inside the wave, wave totals through LDS
-  Seg inc[V], exc[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    float kk[L], vv[L];
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      kk[i] = r.k[i][j];
-      vv[i] = r.v[i][j];
-    }
-    inc[j] = summarize<L, MASKED>(kk, vv, wd[j], nvalid);
-  }
-#pragma unroll
-  for (int off = 1; off < PS; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const Seg p = shfl_up_seg(inc[j], off * LC);
-      if (sl >= off) inc[j] = seg_combine(p, inc[j], wd[j]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const Seg p = shfl_up_seg(inc[j], LC);
-    exc[j] = sl > 0 ? p : seg_identity();
-  }
-  if (sl == PS - 1) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) tot[wave][cl * V + j] = inc[j];
-  }
-  __syncthreads();
-  Seg before[V], whole[V];  // waves before this one; the whole tile
-#pragma unroll
-  for (int j = 0; j < V; ++j) whole[j] = seg_identity();
-#pragma unroll
-  for (int jj = 0; jj < W; ++jj) {
-    if (jj == wave) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) before[j] = whole[j];
-    }
-#pragma unroll
-    for (int j = 0; j < V; ++j) whole[j] = seg_combine(whole[j], tot[jj][cl * V + j], wd[j]);
-  }
+  Seg exc[V], before[V], whole[V];
+  tile_scan<V, LC, PS, W, L, MASKED>(r, wd, nvalid, tot, exc, before, whole);
 
   // Look-back. Segment s > 0 starts from the inclusive prefix of the last
   // anchor before it and folds in, oldest first, the aggregates of the

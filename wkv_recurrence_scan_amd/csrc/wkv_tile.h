@@ -78,6 +78,62 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<V, L>& r,
   }
 }
 
+// The scan of one tile held in registers, W waves of 2 x 32 lanes: lane
+// (sl, cl) of wave `wave` holds sub-chunk wave*PS + sl of channel group cl.
+// Returns per thread the segments before its sub-chunk inside its wave (exc),
+// the totals of the waves before its own (before) and the whole tile
+// (whole). tot is LDS scratch of W x CH segments; the call synchronises the
+// workgroup once.
+template <int V, int LC, int PS, int W, int L, bool MASKED>
+__device__ __forceinline__ void tile_scan(const ChunkRegs<V, L>& r, const float (&wd)[V], int nvalid,
+                                          Seg (*tot)[LC * V], Seg (&exc)[V], Seg (&before)[V],
+                                          Seg (&whole)[V]) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int cl = lane % LC;
+  const int sl = lane / LC;
+  Seg inc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    float kk[L], vv[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      kk[i] = r.k[i][j];
+      vv[i] = r.v[i][j];
+    }
+    inc[j] = summarize<L, MASKED>(kk, vv, wd[j], nvalid);
+  }
+#pragma unroll
+  for (int off = 1; off < PS; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const Seg p = shfl_up_seg(inc[j], off * LC);
+      if (sl >= off) inc[j] = seg_combine(p, inc[j], wd[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const Seg p = shfl_up_seg(inc[j], LC);
+    exc[j] = sl > 0 ? p : seg_identity();
+  }
+  if (sl == PS - 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) tot[wave][cl * V + j] = inc[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < V; ++j) whole[j] = seg_identity();
+#pragma unroll
+  for (int jj = 0; jj < W; ++jj) {
+    if (jj == wave) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) before[j] = whole[j];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) whole[j] = seg_combine(whole[j], tot[jj][cl * V + j], wd[j]);
+  }
+}
+
 // Re-runs the recurrence over one thread's sub-chunk from the state in front
 // of it and writes the outputs. FAST selects lane_step_fast.
 template <typename IoT, int V, int L, bool MASKED, bool FAST>
