@@ -4,11 +4,15 @@ TEST INFRASTRUCTURE: only the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package. It shares no code with the HIP
 library (wkv_recurrence_scan_amd) and never imports it.
 
-parity pins: every function here is pinned by tests/test_oracle.py against the
-mpmath brute force, closed forms of the defining equation, invariants and
-special cases that reduce to a softmax; none is "parity unpinned".
+parity pins: every forward function here is pinned by tests/test_oracle.py
+against the mpmath brute force, closed forms of the defining equation,
+invariants and special cases that reduce to a softmax; the gradients
+(wkv_grad) by tests/test_oracle_grad.py against central finite differences
+of the pinned forward and by invariants of the operator. None is "parity
+unpinned".
 """
 
+from .wkv_grad import wkv_backward_direct  # noqa: F401
 from .wkv_oracle import (  # noqa: F401
     EMPTY_MAX_EXP,
     canonical,
