@@ -164,6 +164,44 @@ int wkv_step(int64_t B, int64_t C, const float* w, const float* u, const float* 
 int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const uint16_t* k,
                   const uint16_t* v, float* state, uint16_t* out, hipStream_t stream);
 
+/* Backward pass of the prefill (fp32): gradients of a loss L with respect to
+ * w, u, k, v and the initial state, given dL/dout and optionally dL/dstate_out.
+ * The derivatives are those of the wkv_t ratio of the page "Linear attention
+ * without writing a CUDA kernel", section "The recurrence" (quotient rule over
+ * its terms; the page trains its model through this operator).
+ *
+ *   B, T, C     sizes (>= 0). C == 0: nothing to do. B == 0: gw, gu zeroed.
+ *   w, u        [C] the forward's decay and bonus.
+ *   k, v        [B][T][C] the forward's keys and values.
+ *   state_in    [3][B][C] the forward's initial state, or NULL (empty state).
+ *   state_out,  [3][B][C] the state the forward returned and dL/d(num, den,
+ *   gstate_out  max_exp) of it, both or neither (NULL: no gradient on the final
+ *               state). The final state's gradient is taken through num and
+ *               den at the given max_exp; the max_exp plane of gstate_out is
+ *               not read (for a loss of the state itself it equals
+ *               num * g_num + den * g_den).
+ *   gout        [B][T][C] dL/dout.
+ *   gk, gv      [B][T][C] out: dL/dk, dL/dv.
+ *   gw, gu      [C] out: dL/dw, dL/du summed over the batch.
+ *   gstate_in   [3][B][C] out: dL/d(num, den, max_exp) of state_in (zeros when
+ *               state_in is NULL), or NULL to skip it.
+ *   workspace   device memory of wkv_backward_workspace_size(B, T, C) bytes,
+ *               256-byte aligned, owned by the caller; contents need no
+ *               clearing (everything read is written first in the same
+ *               call). Must not overlap any other argument; calls that may
+ *               run concurrently must not share it.
+ * Outputs must not overlap any input or each other (WKV_ERR_ALIAS). The
+ * result is deterministic (fixed-order sums). */
+int wkv_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                 const float* k, const float* v, const float* state_in,
+                 const float* state_out, const float* gstate_out, const float* gout,
+                 float* gk, float* gv, float* gw, float* gu, float* gstate_in,
+                 void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace wkv_backward needs for these sizes, or a negative
+ * wkv_status on error. */
+int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+
 /* Static, NUL-terminated name of a wkv_status code. */
 const char* wkv_status_string(int status);
 

@@ -93,6 +93,38 @@ def test_workspace_size_and_requirement_without_device():
     assert lib.wkv_forward_ws(1, 64, 256, *args, 0, lookback, P(a + 8192), 1 << 20, None) == 4
 
 
+def test_backward_workspace_and_validation_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    # per-lane partial sums (rounded up to 256 B) + one 16-byte checkpoint per
+    # (lane, chunk of 8 tokens)
+    lanes = 256 * 768
+    assert lib.wkv_backward_workspace_size(256, 512, 768) == \
+        ((8 * lanes + 255) // 256) * 256 + (512 // 8) * lanes * 16
+    assert lib.wkv_backward_workspace_size(2, 9, 4) == 256 + 2 * 8 * 16
+    assert lib.wkv_backward_workspace_size(-1, 9, 4) < 0
+    assert lib.wkv_backward_workspace_size(3, 9, 0) == 0
+    nul = None
+    a = 0x10000000
+    args = [P(a), P(a + 4096)] + [P(a + (i + 2) * (1 << 20)) for i in range(2)]
+    # B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw, gu, gstate_in
+    base = [2, 9, 4, args[0], args[1], args[2], args[3], nul, nul, nul, P(a + 5 * (1 << 20)),
+            P(a + 6 * (1 << 20)), P(a + 7 * (1 << 20)), P(a + 8 * (1 << 20)),
+            P(a + 8 * (1 << 20) + 256), nul]
+    assert lib.wkv_backward(-1, *base[1:], nul, 0, nul) == 2
+    assert lib.wkv_backward(*base, nul, 0, nul) == 8                     # no workspace
+    bad = list(base)
+    bad[3] = nul
+    assert lib.wkv_backward(*bad, nul, 0, nul) == 1                      # w missing
+    bad = list(base)
+    bad[9] = P(a + 9 * (1 << 20))                                        # gradient without state
+    assert lib.wkv_backward(*bad, P(a + (1 << 28)), 1 << 20, nul) == 1
+    bad = list(base)
+    bad[12] = bad[5]                                                     # gv on top of k
+    assert lib.wkv_backward(*bad, P(a + (1 << 28)), 1 << 20, nul) == 4
+    assert lib.wkv_backward(*base, P(a + (1 << 28) + 8), 1 << 20, nul) == 3  # misaligned workspace
+
+
 def test_inputs_are_seeded_and_row_independent():
     wl = I.WORKLOADS[3].scaled(B=3, T=20, C=16)
     k1, v1 = I.kv(wl)

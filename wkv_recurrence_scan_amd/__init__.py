@@ -8,6 +8,7 @@ into that interface (see _lib). Build the library with
     out, state = wkv_forward(w, u, k, v)            # prefill, float32
     out, state = wkv_forward_bf16(w, u, k, v)       # prefill, bfloat16 I/O
     y = wkv_step(w, u, k_t, v_t, state)             # decode, state in place
+    gw, gu, gk, gv, gs = wkv_backward(w, u, k, v, gout)  # gradients
 """
 
 from ._lib import (  # noqa: F401
@@ -26,6 +27,8 @@ from ._lib import (  # noqa: F401
     new_workspace,
     step,
     wkv_abi_version,
+    wkv_backward,
+    wkv_backward_workspace_size,
     wkv_forward,
     wkv_forward_bf16,
     wkv_forward_ex,

@@ -64,12 +64,15 @@ def load_library() -> ctypes.CDLL:
         "wkv_status_string": [ci],
         "wkv_last_hip_error": [],
         "wkv_abi_version": [],
+        "wkv_backward": [i64, i64, i64] + [vp] * 13 + [vp, i64, vp],
+        "wkv_backward_workspace_size": [i64, i64, i64],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = {"wkv_status_string": ctypes.c_char_p,
-                      "wkv_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
+                      "wkv_workspace_size": ctypes.c_int64,
+                      "wkv_backward_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
     if lib.wkv_abi_version() != 1:
         raise RuntimeError(f"{LIBRARY_PATH}: unexpected ABI version {lib.wkv_abi_version()}")
     _lib = lib
@@ -289,6 +292,68 @@ def wkv_select_path(B: int, T: int, C: int, io: int = WKV_IO_F32) -> str:
     if r < 0:
         raise WKVError("wkv_select_path", -r)
     return _PATH_NAMES[r]
+
+
+def wkv_backward_workspace_size(B: int, T: int, C: int) -> int:
+    """Bytes of workspace wkv_backward needs."""
+    r = load_library().wkv_backward_workspace_size(B, T, C)
+    if r < 0:
+        raise WKVError("wkv_backward_workspace_size", -r)
+    return int(r)
+
+
+def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 gout: torch.Tensor, state_in: Optional[torch.Tensor] = None,
+                 state_out: Optional[torch.Tensor] = None,
+                 gstate_out: Optional[torch.Tensor] = None, *, want_gstate_in: bool = True,
+                 workspace: Optional[torch.Tensor] = None, out=None, stream=None):
+    """Gradients of the prefill (float32): returns (gw, gu, gk, gv, gstate_in)
+    for the upstream gradient gout of out (and gstate_out of state_out, which
+    must then be the state the forward returned). gstate_in is None when
+    want_gstate_in is False. `out` may hold preallocated (gk, gv, gw, gu,
+    gstate_in) tensors; `workspace` a uint8 tensor of at least
+    wkv_backward_workspace_size bytes (else one is allocated for the call)."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    f32 = torch.float32
+    for name, t in (("k", k), ("v", v), ("gout", gout)):
+        _need(t, name, f32, (B, T, C), dev)
+    _need(w, "w", f32, (C,), dev)
+    _need(u, "u", f32, (C,), dev)
+    for name, t in (("state_in", state_in), ("state_out", state_out), ("gstate_out", gstate_out)):
+        if t is not None:
+            _need(t, name, f32, (3, B, C), dev)
+    if out is None:
+        gk = torch.empty((B, T, C), dtype=f32, device=dev)
+        gv = torch.empty((B, T, C), dtype=f32, device=dev)
+        gw = torch.empty((C,), dtype=f32, device=dev)
+        gu = torch.empty((C,), dtype=f32, device=dev)
+        gs = torch.empty((3, B, C), dtype=f32, device=dev) if want_gstate_in else None
+    else:
+        gk, gv, gw, gu, gs = out
+    for name, t, shape in (("gk", gk, (B, T, C)), ("gv", gv, (B, T, C)), ("gw", gw, (C,)),
+                           ("gu", gu, (C,))):
+        _need(t, name, f32, shape, dev)
+    if gs is not None:
+        _need(gs, "gstate_in", f32, (3, B, C), dev)
+    with torch.cuda.device(dev):
+        strm = torch.cuda.current_stream(dev) if stream is None else stream
+        nbytes = wkv_backward_workspace_size(B, T, C)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
+        st = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                              _ptr(state_out), _ptr(gstate_out), _ptr(gout), _ptr(gk), _ptr(gv),
+                              _ptr(gw), _ptr(gu), _ptr(gs), _ptr(workspace), workspace.numel(),
+                              ctypes.c_void_p(strm.cuda_stream))
+    _check(st, "wkv_backward")
+    return gw, gu, gk, gv, gs
 
 
 class ForwardCall:

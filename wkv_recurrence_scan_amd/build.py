@@ -24,12 +24,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwkv.so")
 
 ARCH = "gfx950"
-SOURCES = ["wkv_api.cpp", "wkv_seq.hip", "wkv_chunk.hip", "wkv_lookback.hip", "wkv_step.hip"]
+SOURCES = ["wkv_api.cpp", "wkv_seq.hip", "wkv_chunk.hip", "wkv_lookback.hip", "wkv_step.hip",
+           "wkv_backward.hip"]
 EXPORTS = [
     "wkv_forward", "wkv_forward_bf16", "wkv_forward_ex", "wkv_forward_ws", "wkv_workspace_size",
     "wkv_select_path",
     "wkv_step", "wkv_step_bf16", "wkv_status_string", "wkv_last_hip_error",
-    "wkv_abi_version",
+    "wkv_abi_version", "wkv_backward", "wkv_backward_workspace_size",
 ]
 
 

@@ -193,6 +193,21 @@ __device__ __forceinline__ float lane_step(Lane& s, float k, float v, float w, f
   return out;
 }
 
+// The state advance alone (the second half of lane_step): decay by one step,
+// add the token at weight e^k.
+__device__ __forceinline__ void lane_advance(Lane& s, float k, float v, float w) {
+  const float age1 = s.age + 1.0f;
+  const float s2 = __builtin_fmaf(age1, w, k - s.base);  // k - (m - w)
+  const float y = fast_exp2(__builtin_fabsf(s2) * -kLog2e);
+  const bool tok_wins = s2 > 0.0f;
+  const float ga = tok_wins ? y : 1.0f;
+  const float gb = tok_wins ? 1.0f : y;
+  s.n = __builtin_fmaf(ga, s.n, gb * v);
+  s.d = __builtin_fmaf(ga, s.d, gb);
+  s.base = tok_wins ? k : s.base;
+  s.age = tok_wins ? 0.0f : age1;
+}
+
 // The same step with one exponential instead of two. Both the update and the
 // output are taken against the state's maximum after the step,
 // m' = max(m - w, k): the decayed state then weighs F = e^(m - w - m') and the

@@ -56,6 +56,28 @@ int lookback_vec_width(int io, int64_t C, const FwdArgs& a);
 int64_t lookback_workspace_bytes(int vec, int64_t B, int64_t T, int64_t C);
 hipError_t launch_lookback(const FwdArgs& a, int io, int vec, const LbWorkspace& ws, hipStream_t s);
 
+// Backward pass (fp32): gradients for w, u, k, v and the initial state.
+struct BwdArgs {
+  int64_t B, T, C;
+  const float* w;
+  const float* u;
+  const float* k;
+  const float* v;
+  const float* gout;
+  const float* state_in;    // nullptr: empty initial state
+  const float* state_out;   // with gstate_out: the forward's final state
+  const float* gstate_out;  // nullptr: no gradient on the final state
+  float* gk;
+  float* gv;
+  float* gw;                // [C], summed over the batch
+  float* gu;                // [C]
+  float* gstate_in;         // nullptr: not wanted
+};
+// Workspace: per-lane partial sums and per-chunk checkpoints, written before
+// they are read in every launch (no clearing needed).
+int64_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
+hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t s);
+
 hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);
