@@ -8,11 +8,17 @@ Default run (one JSON line on stdout):
     once into a HIP graph and replayed per step; value = G channel-tokens/s
     over the timed replays. The same steps launched eagerly from Python are
     reported beside it (eager_value).
-  * roofline: the prefill kernel's average duration from HIP events recorded
-    around every launch inside the timed region, against its algorithmic HBM
-    bytes (read k, v; write out; write the final state; read w, u).
+  * roofline: the prefill kernel's launch duration (HIP events around the
+    timed graph replays: step time over launches per step; the eager loop's
+    event pair around every launch is reported beside it) against its
+    algorithmic HBM bytes (read k, v; write out; write the final state; read
+    w, u).
   * decode: 1024 consecutive wkv_step calls at B=256, C=768 after a T=512
     prefill; steps/s for eager launches and for one HIP graph of all 1024.
+  * backward: wkv_backward (the gradients) on one layer of the prefill shape
+    and on the decode workload's B=256 T=512 prefill shape, with the
+    roofline on its algorithmic bytes (read k, v, dL/dout; write dL/dk,
+    dL/dv).
   * cpu_baseline: the float64 oracle on the host, on the same prefill workload.
 
 --config N measures another workload (0: B=1 T=64 C=768; 2: the decode
@@ -208,6 +214,51 @@ def time_decode(wl, dev, n_steps, use_graph):
     return res
 
 
+def time_backward(wl, dev, reps=10):
+    """wkv_backward (fp32) on workload wl's first layer with a seeded upstream
+    gradient: microseconds per call (event pair around `reps` back-to-back
+    calls after two warm-up calls) and the roofline on its algorithmic bytes
+    (read k, v, dL/dout; write dL/dk, dL/dv; w, u in and dL/dw, dL/du out)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    w, u = I.params(wl)
+    k, v = I.kv(wl)
+    g = I.grad_out(wl)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    dw, du, dk, dv, dg = t(w), t(u), t(k), t(v), t(g)
+    del k, v, g
+    gk, gv = torch.empty_like(dk), torch.empty_like(dk)
+    gw, gu = torch.empty_like(dw), torch.empty_like(dw)
+    ws = torch.empty(max(W.wkv_backward_workspace_size(wl.B, wl.T, wl.C), 1), dtype=torch.uint8,
+                     device=dev)
+    call = lambda: W.wkv_backward(dw, du, dk, dv, dg, want_gstate_in=False, workspace=ws,
+                                  out=(gk, gv, gw, gu, None))
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ct = wl.B * wl.T * wl.C
+    abytes = 20 * ct + 16 * wl.C
+    achieved = abytes / (us * 1e-6) / 1e9
+    return {"workload": f"{wl.name}, one layer, backward", "B": wl.B, "T": wl.T, "C": wl.C,
+            "io": "f32",
+            "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
+            "us_per_call": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "kernel": "wkv_backward_kernel", "algorithmic_bytes_per_launch": abytes},
+            "workspace_bytes": int(ws.numel())}
+
+
 def measured_traffic(workload_key, path):
     """HBM bytes per launch from the rocprofv3 counter summaries under
     profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
@@ -272,6 +323,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement (run with the default config)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -369,6 +422,13 @@ def main():
             "graph_us_per_step": round(d.get("graph_us_per_step", 0.0), 3),
             "bytes_per_step": d["bytes_per_step"],
         }
+
+    if args.config == 1 and not args.no_backward:
+        rec["backward"] = []
+        for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+            _log(f"backward: {bwl.name} (one layer)")
+            rec["backward"].append(time_backward(bwl, dev))
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         _log("cpu baseline: float64 oracle")

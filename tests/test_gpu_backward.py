@@ -83,10 +83,13 @@ def test_backward_matches_oracle(B, T, C, wl):
     say("  " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
 
 
+@pytest.mark.parametrize("T", [45, 150])
 @pytest.mark.parametrize("with_state,with_gstate", [(True, False), (False, True), (True, True)])
-def test_backward_with_states(with_state, with_gstate):
-    B, T, C = 2, 45, 24
-    say(f"backward states in={with_state} out={with_gstate}")
+def test_backward_with_states(with_state, with_gstate, T):
+    """T = 45 runs the one-thread-per-lane kernel, T = 150 (few lanes) the
+    segmented kernels, whose segments are chained both ways."""
+    B, C = 2, 24
+    say(f"backward states in={with_state} out={with_gstate} T={T}")
     w, u, k, v = make_case(WL3, B, T, C)
     gout = np.random.default_rng([42]).normal(0, 1, (B, T, C)).astype(np.float32)
     s0 = random_state(B, C, 3) if with_state else None

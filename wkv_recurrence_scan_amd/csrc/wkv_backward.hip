@@ -136,102 +136,116 @@ __device__ __forceinline__ void chunk_backward(const Chunk& c, int n, Lane st, S
   }
 }
 
-__global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(
-    int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
-    const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ gout,
-    const float* __restrict__ state_in, const float* __restrict__ state_out,
-    const float* __restrict__ gstate_out, float* __restrict__ gk, float* __restrict__ gv,
-    float* __restrict__ gstate_in, float4* __restrict__ ckpt, float* __restrict__ gw_part,
-    float* __restrict__ gu_part) {
-  const int64_t lanes = B * C;
-  const int64_t lane = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
-  if (lane >= lanes) return;
-  const int64_t b = lane / C;
-  const int64_t c = lane - b * C;
-  const float wc = w[c], uc = u[c];
-  const int64_t row = b * T * C + c;
-  const int64_t nfull = T / kLc;
-  const int rest = static_cast<int>(T - nfull * kLc);
-  const int64_t step = static_cast<int64_t>(kLc) * C;
+// Where one lane's tokens are: k, v, g and the gradients at row + t * C.
+struct LaneIo {
+  const float* k;
+  const float* v;
+  const float* g;
+  float* gk;
+  float* gv;
+  int64_t row, C, step;  // step = kLc * C
+  int64_t nfull;         // chunks of kLc tokens that are full
+  int rest;              // tokens in the last, partial chunk (0: none)
+};
 
-  // pass 1: forward state advance, a checkpoint in front of every chunk
-  const Lane s_init = state_in != nullptr
-                          ? lane_from_state(state_in[lane], state_in[lanes + lane],
-                                            state_in[2 * lanes + lane])
-                          : lane_empty();
-  {
-    Lane s = s_init;
-    // two register buffers used alternately; the next chunk's loads are
-    // issued before the current chunk is consumed (the last chunk re-reads
-    // itself, so the loads are unconditional and the compiler's counter
-    // waits stay exact)
-    float ka[kLc], va[kLc], kb[kLc], vb[kLc];
-    auto load2 = [&](float (&kk)[kLc], float (&vv)[kLc], int64_t j) {
-#pragma unroll
-      for (int i = 0; i < kLc; ++i) {
-        kk[i] = __builtin_nontemporal_load(k + row + j * step + i * C);
-        vv[i] = __builtin_nontemporal_load(v + row + j * step + i * C);
-      }
-    };
-    auto advance = [&](const float (&kk)[kLc], const float (&vv)[kLc], int64_t j) {
-      ckpt[j * lanes + lane] = make_float4(s.n, s.d, s.base, s.age);
-#pragma unroll
-      for (int i = 0; i < kLc; ++i) lane_advance(s, kk[i], vv[i], wc);
-    };
-    if (nfull > 0) load2(ka, va, 0);
-    for (int64_t j = 0; j < nfull; j += 2) {
-      load2(kb, vb, j + 1 < nfull ? j + 1 : j);
-      advance(ka, va, j);
-      if (j + 1 >= nfull) break;
-      load2(ka, va, j + 2 < nfull ? j + 2 : j + 1);
-      advance(kb, vb, j + 1);
-    }
-    if (rest > 0) ckpt[nfull * lanes + lane] = make_float4(s.n, s.d, s.base, s.age);
-  }
-
-  // pass 2: backward over the chunks, last first
-  Suffix a;
+__device__ __forceinline__ Suffix suffix_init(const float* __restrict__ state_out,
+                                              const float* __restrict__ gstate_out,
+                                              int64_t lanes, int64_t lane) {
   if (gstate_out != nullptr) {
     // dL/dN_T = g_num e^{-m_out}: p = g_num, q = -g_den relative to z = -m_out
-    a = Suffix{gstate_out[lane], -gstate_out[lanes + lane], 0.0f, 0.0f,
-               -state_out[2 * lanes + lane], 0.0f};
-  } else {
-    a = Suffix{0.0f, 0.0f, 0.0f, 0.0f, kEmpty, 0.0f};
+    return Suffix{gstate_out[lane], -gstate_out[lanes + lane], 0.0f, 0.0f,
+                  -state_out[2 * lanes + lane], 0.0f};
   }
-  float gw_acc = 0.0f, gu_acc = 0.0f;
-  if (rest > 0) {
-    const int64_t off = row + nfull * step;
-    Chunk ch;
-    load_chunk<true>(ch, k + off, v + off, gout + off, C, rest);
-    const float4 cp = ckpt[nfull * lanes + lane];
-    chunk_backward<true>(ch, rest, Lane{cp.x, cp.y, cp.z, cp.w}, a, wc, uc, gw_acc, gu_acc,
-                         gk + off, gv + off, C);
+  return Suffix{0.0f, 0.0f, 0.0f, 0.0f, kEmpty, 0.0f};
+}
+
+// Forward state advance over chunks [j0, j1) (all full), storing the state in
+// front of each chunk when CKPT. Two register buffers used alternately: the
+// next chunk's loads are issued before the current one is consumed (the last
+// chunk re-reads itself, so the loads are unconditional and the compiler's
+// counter waits stay exact).
+template <bool CKPT>
+__device__ __forceinline__ void forward_chunks(Lane& s, const LaneIo& io, int64_t j0, int64_t j1,
+                                               float w, float4* __restrict__ ckpt,
+                                               int64_t lanes, int64_t lane) {
+  float ka[kLc], va[kLc], kb[kLc], vb[kLc];
+  auto load2 = [&](float (&kk)[kLc], float (&vv)[kLc], int64_t j) {
+#pragma unroll
+    for (int i = 0; i < kLc; ++i) {
+      kk[i] = __builtin_nontemporal_load(io.k + io.row + j * io.step + i * io.C);
+      vv[i] = __builtin_nontemporal_load(io.v + io.row + j * io.step + i * io.C);
+    }
+  };
+  auto advance = [&](const float (&kk)[kLc], const float (&vv)[kLc], int64_t j) {
+    if (CKPT) ckpt[j * lanes + lane] = make_float4(s.n, s.d, s.base, s.age);
+#pragma unroll
+    for (int i = 0; i < kLc; ++i) lane_advance(s, kk[i], vv[i], w);
+  };
+  if (j0 < j1) load2(ka, va, j0);
+  for (int64_t j = j0; j < j1; j += 2) {
+    load2(kb, vb, j + 1 < j1 ? j + 1 : j);
+    advance(ka, va, j);
+    if (j + 1 >= j1) break;
+    load2(ka, va, j + 2 < j1 ? j + 2 : j + 1);
+    advance(kb, vb, j + 1);
   }
-  if (nfull > 0) {
-    Chunk A, Bf;
-    load_chunk<false>(A, k + row + (nfull - 1) * step, v + row + (nfull - 1) * step,
-                      gout + row + (nfull - 1) * step, C, kLc);
-    for (int64_t j = nfull - 1; j >= 0; j -= 2) {
-      const int64_t jb = j - 1 >= 0 ? j - 1 : 0;
-      load_chunk<false>(Bf, k + row + jb * step, v + row + jb * step, gout + row + jb * step, C,
-                        kLc);
-      float4 cp = ckpt[j * lanes + lane];
-      chunk_backward<false>(A, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, wc, uc, gw_acc, gu_acc,
-                            gk + row + j * step, gv + row + j * step, C);
-      if (j - 1 < 0) break;
-      const int64_t ja = j - 2 >= 0 ? j - 2 : 0;
-      load_chunk<false>(A, k + row + ja * step, v + row + ja * step, gout + row + ja * step, C,
-                        kLc);
-      cp = ckpt[(j - 1) * lanes + lane];
-      chunk_backward<false>(Bf, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, wc, uc, gw_acc, gu_acc,
-                            gk + row + (j - 1) * step, gv + row + (j - 1) * step, C);
+}
+
+// The partial last chunk (io.rest tokens) forward, state advance only.
+__device__ __forceinline__ void forward_rest(Lane& s, const LaneIo& io, float w) {
+  const int64_t off = io.row + io.nfull * io.step;
+#pragma unroll
+  for (int i = 0; i < kLc; ++i) {
+    if (i < io.rest) {
+      lane_advance(s, __builtin_nontemporal_load(io.k + off + i * io.C),
+                   __builtin_nontemporal_load(io.v + off + i * io.C), w);
     }
   }
+}
 
-  // the initial state: e^{m0} P_{-1}, -e^{m0} Q_{-1}, and its share of dL/dw
-  if (state_in != nullptr) {
-    const float n0 = s_init.n, d0 = s_init.d, m0 = s_init.base;
-    const float e0 = fast_exp2(__builtin_fmaf(-a.za, wc, m0 + a.zb) * kLog2e);
+// Backward walk over chunks [j0, j1) of one lane, last first, from their
+// checkpoints; chunk io.nfull (if inside the range) is the partial one.
+__device__ __forceinline__ void backward_chunks(const LaneIo& io, int64_t j0, int64_t j1,
+                                                const float4* __restrict__ ckpt, int64_t lanes,
+                                                int64_t lane, float w, float u, Suffix& a,
+                                                float& gw_acc, float& gu_acc) {
+  if (j1 > io.nfull) {  // the partial chunk comes last in time, so first here
+    const int64_t off = io.row + io.nfull * io.step;
+    Chunk ch;
+    load_chunk<true>(ch, io.k + off, io.v + off, io.g + off, io.C, io.rest);
+    const float4 cp = ckpt[io.nfull * lanes + lane];
+    chunk_backward<true>(ch, io.rest, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
+                         io.gk + off, io.gv + off, io.C);
+    j1 = io.nfull;
+  }
+  if (j0 >= j1) return;
+  auto at = [&](int64_t j) { return io.row + j * io.step; };
+  Chunk A, Bf;
+  load_chunk<false>(A, io.k + at(j1 - 1), io.v + at(j1 - 1), io.g + at(j1 - 1), io.C, kLc);
+  for (int64_t j = j1 - 1; j >= j0; j -= 2) {
+    const int64_t jb = j - 1 >= j0 ? j - 1 : j0;
+    load_chunk<false>(Bf, io.k + at(jb), io.v + at(jb), io.g + at(jb), io.C, kLc);
+    float4 cp = ckpt[j * lanes + lane];
+    chunk_backward<false>(A, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
+                          io.gk + at(j), io.gv + at(j), io.C);
+    if (j - 1 < j0) break;
+    const int64_t ja = j - 2 >= j0 ? j - 2 : j0;
+    load_chunk<false>(A, io.k + at(ja), io.v + at(ja), io.g + at(ja), io.C, kLc);
+    cp = ckpt[(j - 1) * lanes + lane];
+    chunk_backward<false>(Bf, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
+                          io.gk + at(j - 1), io.gv + at(j - 1), io.C);
+  }
+}
+
+// Gradients of the initial state from the suffix sums at position -1
+// (e^{m0} P, -e^{m0} Q) and its share of dL/dw; zeros without one.
+__device__ __forceinline__ void initial_state_grad(const Lane& s0, bool have, const Suffix& a,
+                                                   float w, float& gw_acc,
+                                                   float* __restrict__ gstate_in, int64_t lanes,
+                                                   int64_t lane) {
+  if (have) {
+    const float n0 = s0.n, d0 = s0.d, m0 = s0.base;
+    const float e0 = fast_exp2(__builtin_fmaf(-a.za, w, m0 + a.zb) * kLog2e);
     const float gn0 = a.p * e0;
     const float gd0 = -a.q * e0;
     gw_acc = __builtin_fmaf(-e0, __builtin_fmaf(n0, a.r, -d0 * a.rq), gw_acc);
@@ -245,56 +259,330 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(
     gstate_in[lanes + lane] = 0.0f;
     gstate_in[2 * lanes + lane] = 0.0f;
   }
-  gw_part[lane] = gw_acc;
-  gu_part[lane] = gu_acc;
 }
 
-// dL/dw and dL/du: the per-lane partial sums added over the batch, in order.
-__global__ __launch_bounds__(256) void wkv_grad_reduce_kernel(int64_t B, int64_t C,
-                                                              const float* __restrict__ gw_part,
-                                                              const float* __restrict__ gu_part,
-                                                              float* __restrict__ gw,
-                                                              float* __restrict__ gu) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= C) return;
-  float sw = 0.0f, su = 0.0f;
-  for (int64_t b = 0; b < B; ++b) {
-    sw += gw_part[b * C + c];
-    su += gu_part[b * C + c];
+struct BwdKernelArgs {
+  int64_t B, T, C;
+  const float* w;
+  const float* u;
+  const float* k;
+  const float* v;
+  const float* gout;
+  const float* state_in;
+  const float* state_out;
+  const float* gstate_out;
+  float* gk;
+  float* gv;
+  float* gstate_in;
+  float4* ckpt;      // [chunks][lanes] state in front of each chunk
+  float* gw_part;    // [segments][lanes]
+  float* gu_part;
+  float4* seg_fwd;   // [segments][lanes] forward summary of each segment from empty
+  float4* seg_rev;   // [segments][lanes] the segment's own suffix sums (p, q, r, rq)
+  float* seg_rev_z;  // [segments][lanes] their exponent
+  int64_t segments;  // S
+  int64_t seg_chunks;  // chunks per segment (all but the last one full)
+};
+
+__device__ __forceinline__ LaneIo lane_io(const BwdKernelArgs& a, int64_t lane) {
+  const int64_t b = lane / a.C;
+  const int64_t c = lane - b * a.C;
+  LaneIo io;
+  io.k = a.k;
+  io.v = a.v;
+  io.g = a.gout;
+  io.gk = a.gk;
+  io.gv = a.gv;
+  io.row = b * a.T * a.C + c;
+  io.C = a.C;
+  io.step = static_cast<int64_t>(kLc) * a.C;
+  io.nfull = a.T / kLc;
+  io.rest = static_cast<int>(a.T - io.nfull * kLc);
+  return io;
+}
+
+__device__ __forceinline__ Lane initial_lane(const BwdKernelArgs& a, int64_t lanes, int64_t lane) {
+  return a.state_in != nullptr ? lane_from_state(a.state_in[lane], a.state_in[lanes + lane],
+                                                 a.state_in[2 * lanes + lane])
+                               : lane_empty();
+}
+
+// Large B*C: one thread per lane, both passes over the whole sequence.
+__global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(BwdKernelArgs a) {
+  const int64_t lanes = a.B * a.C;
+  const int64_t lane = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (lane >= lanes) return;
+  const int64_t c = lane % a.C;
+  const float wc = a.w[c], uc = a.u[c];
+  const LaneIo io = lane_io(a, lane);
+  const int64_t nch = io.nfull + (io.rest > 0 ? 1 : 0);
+
+  // pass 1: forward state advance, a checkpoint in front of every chunk
+  const Lane s_init = initial_lane(a, lanes, lane);
+  {
+    Lane s = s_init;
+    forward_chunks<true>(s, io, 0, io.nfull, wc, a.ckpt, lanes, lane);
+    if (io.rest > 0) a.ckpt[io.nfull * lanes + lane] = make_float4(s.n, s.d, s.base, s.age);
   }
-  gw[c] = sw;
-  gu[c] = su;
+  // pass 2: backward over the chunks, last first
+  Suffix acc = suffix_init(a.state_out, a.gstate_out, lanes, lane);
+  float gw_acc = 0.0f, gu_acc = 0.0f;
+  backward_chunks(io, 0, nch, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
+  initial_state_grad(s_init, a.state_in != nullptr, acc, wc, gw_acc, a.gstate_in, lanes, lane);
+  a.gw_part[lane] = gw_acc;
+  a.gu_part[lane] = gu_acc;
 }
 
-int64_t part_bytes(int64_t lanes) { return ((8 * lanes + 255) / 256) * 256; }
+// Small B*C: the sequence is cut into S segments of seg_chunks chunks and
+// every (segment, lane) pair is one thread, in three launches.
+//   A: the forward summary of each segment from the empty state;
+//   B: each segment's start state (the initial state and the summaries of the
+//      segments before it, folded in order), the forward over the segment
+//      storing checkpoints, and the segment's own suffix sums (its tokens'
+//      contributions to P, Q, R, Rq at the position before it);
+//   C: each segment's suffix sums at its end (the final state's gradient and
+//      the later segments' own sums, folded from the last one down), then the
+//      backward walk over the segment's chunks.
+// Thread i is lane i % lanes of segment i / lanes.
+__device__ __forceinline__ void seg_bounds(const BwdKernelArgs& a, const LaneIo& io, int64_t s,
+                                           int64_t& j0, int64_t& j1) {
+  const int64_t nch = io.nfull + (io.rest > 0 ? 1 : 0);
+  j0 = s * a.seg_chunks;
+  j1 = j0 + a.seg_chunks < nch ? j0 + a.seg_chunks : nch;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_forward_kernel(BwdKernelArgs a) {
+  const int64_t lanes = a.B * a.C;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (id >= lanes * a.segments) return;
+  const int64_t s = id / lanes, lane = id - s * lanes;
+  const float wc = a.w[lane % a.C];
+  const LaneIo io = lane_io(a, lane);
+  int64_t j0, j1;
+  seg_bounds(a, io, s, j0, j1);
+  Lane x = lane_empty();
+  forward_chunks<false>(x, io, j0, j1 < io.nfull ? j1 : io.nfull, wc, nullptr, lanes, lane);
+  if (j1 > io.nfull) forward_rest(x, io, wc);
+  a.seg_fwd[s * lanes + lane] = make_float4(x.n, x.d, lane_max_exp(x, wc), 0.0f);
+}
+
+__global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernelArgs a) {
+  const int64_t lanes = a.B * a.C;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (id >= lanes * a.segments) return;
+  const int64_t s = id / lanes, lane = id - s * lanes;
+  const int64_t c = lane % a.C;
+  const float wc = a.w[c], uc = a.u[c];
+  const LaneIo io = lane_io(a, lane);
+  int64_t j0, j1;
+  seg_bounds(a, io, s, j0, j1);
+  // start state: the initial state, then every earlier segment (all full)
+  Lane x = initial_lane(a, lanes, lane);
+  const float seg_len = static_cast<float>(a.seg_chunks * kLc);
+  for (int64_t r = 0; r < s; ++r) {
+    const float4 f = a.seg_fwd[r * lanes + lane];
+    lane_absorb(x, Seg{f.x, f.y, f.z, seg_len}, wc);
+  }
+  // forward over the segment: checkpoints, and the segment's own suffix sums
+  // at the position before it, sum over its tokens t (j = t - first) of
+  // a_t e^{-j w} times (1, out_t, j, j out_t), a_t = g_t / Den_t, accumulated
+  // relative to the largest exponent -M_t - j w seen so far
+  float p = 0.0f, q = 0.0f, r = 0.0f, rq = 0.0f, zl = kEmpty;
+  float jj = 0.0f;
+  for (int64_t j = j0; j < j1; ++j) {
+    a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
+    const int n = j < io.nfull ? kLc : io.rest;
+    Chunk ch;
+    const int64_t off = io.row + j * io.step;
+    if (n == kLc) {
+      load_chunk<false>(ch, io.k + off, io.v + off, io.g + off, io.C, kLc);
+    } else {
+      load_chunk<true>(ch, io.k + off, io.v + off, io.g + off, io.C, n);
+    }
+#pragma unroll
+    for (int i = 0; i < kLc; ++i) {
+      if (i < n) {
+        float M, rho, om;
+        const float y = lane_step_rec(x, ch.k[i], ch.v[i], wc, uc, M, rho, om);
+        const float xe = __builtin_fmaf(-jj, wc, -M);  // exponent of a_t e^{-j w}
+        const float d = xe - zl;
+        const float e = fast_exp2(__builtin_fabsf(d) * -kLog2e);
+        const bool nw = d > 0.0f;
+        const float fo = nw ? e : 1.0f;
+        const float fn = (nw ? 1.0f : e) * ch.g[i] * rho;
+        p = __builtin_fmaf(fo, p, fn);
+        q = __builtin_fmaf(fo, q, fn * y);
+        r = __builtin_fmaf(fo, r, fn * jj);
+        rq = __builtin_fmaf(fo, rq, fn * jj * y);
+        zl = nw ? xe : zl;
+        jj += 1.0f;
+      }
+    }
+  }
+  a.seg_rev[s * lanes + lane] = make_float4(p, q, r, rq);
+  a.seg_rev_z[s * lanes + lane] = zl;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKernelArgs a) {
+  const int64_t lanes = a.B * a.C;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
+  if (id >= lanes * a.segments) return;
+  const int64_t s = id / lanes, lane = id - s * lanes;
+  const int64_t c = lane % a.C;
+  const float wc = a.w[c], uc = a.u[c];
+  const LaneIo io = lane_io(a, lane);
+  int64_t j0, j1;
+  seg_bounds(a, io, s, j0, j1);
+  // suffix sums at this segment's end: the final state's gradient, then each
+  // later segment X (last first): the sums decay across X's L tokens (their
+  // age-weighted parts gain L times the plain ones) and X's own sums are added
+  Suffix acc = suffix_init(a.state_out, a.gstate_out, lanes, lane);
+  for (int64_t x = a.segments - 1; x > s; --x) {
+    const int64_t xj0 = x * a.seg_chunks;
+    const int64_t nch = io.nfull + (io.rest > 0 ? 1 : 0);
+    const int64_t xj1 = xj0 + a.seg_chunks < nch ? xj0 + a.seg_chunks : nch;
+    const float L = static_cast<float>((xj1 - xj0) * kLc - (xj1 > io.nfull && io.rest > 0
+                                                                ? kLc - io.rest
+                                                                : 0));
+    const float4 X = a.seg_rev[x * lanes + lane];
+    const float zx = a.seg_rev_z[x * lanes + lane];
+    const float sg = __builtin_fmaf(acc.za + L, wc, zx - acc.zb);  // zx - (z - L w)
+    const float e = fast_exp2(__builtin_fabsf(sg) * -kLog2e);
+    const bool xw = sg > 0.0f;
+    const float fo = xw ? e : 1.0f;
+    const float fx = xw ? 1.0f : e;
+    acc.r = __builtin_fmaf(fo, __builtin_fmaf(L, acc.p, acc.r), fx * X.z);
+    acc.rq = __builtin_fmaf(fo, __builtin_fmaf(L, acc.q, acc.rq), fx * X.w);
+    acc.p = __builtin_fmaf(fo, acc.p, fx * X.x);
+    acc.q = __builtin_fmaf(fo, acc.q, fx * X.y);
+    acc.zb = xw ? zx : acc.zb;
+    acc.za = xw ? 0.0f : acc.za + L;
+  }
+  float gw_acc = 0.0f, gu_acc = 0.0f;
+  backward_chunks(io, j0, j1, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
+  if (s == 0) {
+    initial_state_grad(initial_lane(a, lanes, lane), a.state_in != nullptr, acc, wc, gw_acc,
+                       a.gstate_in, lanes, lane);
+  }
+  a.gw_part[s * lanes + lane] = gw_acc;
+  a.gu_part[s * lanes + lane] = gu_acc;
+}
+
+// dL/dw and dL/du: the per-lane partial sums added over the batch. A
+// workgroup owns 64 channels; its 16 row slices each add the rows
+// b = slice, slice + 16, ... in order, then slice totals are added in order
+// through LDS, so the result does not depend on timing.
+constexpr int kRedCh = 64, kRedSlices = 16;
+
+__global__ __launch_bounds__(kRedCh * kRedSlices) void wkv_grad_reduce_kernel(
+    int64_t B, int64_t C, const float* __restrict__ gw_part, const float* __restrict__ gu_part,
+    float* __restrict__ gw, float* __restrict__ gu) {
+  __shared__ float sw[kRedSlices][kRedCh], su[kRedSlices][kRedCh];
+  const int ch = threadIdx.x % kRedCh;
+  const int slice = threadIdx.x / kRedCh;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCh + ch;
+  float aw = 0.0f, au = 0.0f;
+  if (c < C) {
+    for (int64_t b = slice; b < B; b += kRedSlices) {
+      aw += gw_part[b * C + c];
+      au += gu_part[b * C + c];
+    }
+  }
+  sw[slice][ch] = aw;
+  su[slice][ch] = au;
+  __syncthreads();
+  if (slice == 0 && c < C) {
+    float tw = 0.0f, tu = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRedSlices; ++i) {
+      tw += sw[i][ch];
+      tu += su[i][ch];
+    }
+    gw[c] = tw;
+    gu[c] = tu;
+  }
+}
+
+constexpr int64_t align256(int64_t n) { return ((n + 255) / 256) * 256; }
+
+// Segments per lane: one when B*C alone gives the GPU enough threads (2^16
+// lanes: 1024 waves), otherwise enough for about 2^18 threads, each segment
+// at least 32 tokens and a whole number of checkpoint chunks.
+struct SegPlan {
+  int64_t segments, seg_chunks;
+};
+
+SegPlan seg_plan(int64_t lanes, int64_t T) {
+  const int64_t nch = (T + kLc - 1) / kLc;
+  SegPlan p{1, nch > 0 ? nch : 1};
+  if (lanes <= 0 || lanes >= (int64_t(1) << 16) || T < 64) return p;
+  int64_t want = ((int64_t(1) << 18) + lanes - 1) / lanes;
+  const int64_t most = T / 32;
+  if (want > most) want = most;
+  if (want <= 1) return p;
+  p.seg_chunks = (nch + want - 1) / want;
+  p.segments = (nch + p.seg_chunks - 1) / p.seg_chunks;
+  return p;
+}
+
+struct WsLayout {
+  int64_t part, ckpt, seg_fwd, seg_rev, seg_rev_z, total;
+};
+
+WsLayout ws_layout(int64_t B, int64_t T, int64_t C) {
+  const int64_t lanes = B * C;
+  const SegPlan sp = seg_plan(lanes, T);
+  const int64_t nch = (T + kLc - 1) / kLc;
+  WsLayout l;
+  l.part = 0;
+  l.ckpt = align256(2 * 4 * sp.segments * lanes);
+  l.seg_fwd = l.ckpt + align256(16 * nch * lanes);
+  const int64_t seg = sp.segments > 1 ? sp.segments : 0;
+  l.seg_rev = l.seg_fwd + align256(16 * seg * lanes);
+  l.seg_rev_z = l.seg_rev + align256(16 * seg * lanes);
+  l.total = l.seg_rev_z + align256(4 * seg * lanes);
+  return l;
+}
 
 }  // namespace
 
 int64_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C) {
-  const int64_t lanes = B * C;
-  const int64_t chunks = (T + kLc - 1) / kLc;
-  return part_bytes(lanes) + chunks * lanes * static_cast<int64_t>(sizeof(float4));
+  return B * C > 0 ? ws_layout(B, T, C).total : 0;
 }
 
 hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
   const int64_t lanes = a.B * a.C;
-  float* gw_part = static_cast<float*>(ws);
-  float* gu_part = gw_part + lanes;
-  float4* ckpt = reinterpret_cast<float4*>(static_cast<char*>(ws) + part_bytes(lanes));
+  const SegPlan sp = seg_plan(lanes, a.T);
+  const WsLayout l = ws_layout(a.B, a.T, a.C);
+  char* base = static_cast<char*>(ws);
+  BwdKernelArgs k{a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.gout, a.state_in, a.state_out,
+                  a.gstate_out, a.gk, a.gv, a.gstate_in,
+                  reinterpret_cast<float4*>(base + l.ckpt),
+                  reinterpret_cast<float*>(base + l.part),
+                  reinterpret_cast<float*>(base + l.part) + sp.segments * lanes,
+                  reinterpret_cast<float4*>(base + l.seg_fwd),
+                  reinterpret_cast<float4*>(base + l.seg_rev),
+                  reinterpret_cast<float*>(base + l.seg_rev_z), sp.segments, sp.seg_chunks};
   if (lanes > 0) {
-    const int64_t blocks = (lanes + kBwdThreads - 1) / kBwdThreads;
+    const int64_t threads = lanes * sp.segments;
+    const int64_t blocks = (threads + kBwdThreads - 1) / kBwdThreads;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(wkv_backward_kernel, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kBwdThreads), 0, st, a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.gout,
-                       a.state_in, a.state_out, a.gstate_out, a.gk, a.gv, a.gstate_in, ckpt,
-                       gw_part, gu_part);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kBwdThreads);
+    if (sp.segments == 1) {
+      hipLaunchKernelGGL(wkv_backward_kernel, grid, block, 0, st, k);
+    } else {
+      hipLaunchKernelGGL(wkv_bwd_seg_forward_kernel, grid, block, 0, st, k);
+      hipLaunchKernelGGL(wkv_bwd_seg_sums_kernel, grid, block, 0, st, k);
+      hipLaunchKernelGGL(wkv_bwd_seg_backward_kernel, grid, block, 0, st, k);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t rblocks = (a.C + 255) / 256;
+  const int64_t rblocks = (a.C + kRedCh - 1) / kRedCh;
   if (rblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(wkv_grad_reduce_kernel, dim3(static_cast<unsigned>(rblocks)), dim3(256), 0,
-                     st, a.B, a.C, gw_part, gu_part, a.gw, a.gu);
+  hipLaunchKernelGGL(wkv_grad_reduce_kernel, dim3(static_cast<unsigned>(rblocks)),
+                     dim3(kRedCh * kRedSlices), 0, st, a.B * sp.segments, a.C, k.gw_part,
+                     k.gu_part, a.gw, a.gu);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 # tensor ids inside a seed
-_K, _V, _W, _U, _SPIKE_MASK, _SPIKE_SIGN, _DEC_K, _DEC_V = 1, 2, 3, 4, 5, 6, 7, 8
+_K, _V, _W, _U, _SPIKE_MASK, _SPIKE_SIGN, _DEC_K, _DEC_V, _GOUT = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 @dataclasses.dataclass(frozen=True)
@@ -187,3 +187,18 @@ def decode_kv(wl: Workload, rows: Optional[Sequence[int]] = None,
 
     _map_rows(one, range(len(rows)))
     return k, v
+
+
+def grad_out(wl: Workload, layer: int = 0, rows: Optional[Sequence[int]] = None,
+             T: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient of the prefill output for the backward pass: N(0, 1)
+    float32 (B_rows, T, C), one independent stream per batch row."""
+    rows = list(range(wl.B) if rows is None else rows)
+    T = wl.T if T is None else T
+    g = np.empty((len(rows), T, wl.C), np.float32)
+
+    def one(i):
+        g[i] = _values_row(wl, layer, rows[i], T, _GOUT)
+
+    _map_rows(one, range(len(rows)))
+    return g
