@@ -12,14 +12,16 @@ of the pinned forward and by invariants of the operator. None is "parity
 unpinned".
 """
 
-from .wkv_grad import wkv_backward_direct  # noqa: F401
+from .wkv_grad import wkv_backward_direct, wkv_gated_backward_direct  # noqa: F401
 from .wkv_oracle import (  # noqa: F401
     EMPTY_MAX_EXP,
     canonical,
     empty_state,
     normalised_error,
     wkv_combine,
+    sigmoid,
     wkv_direct,
+    wkv_gated,
     wkv_recurrent,
     wkv_segment_summary,
     wkv_step_ref,

@@ -49,7 +49,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .wkv_oracle import empty_state
+from .wkv_oracle import empty_state, sigmoid, wkv_direct
 
 
 def _f64(x):
@@ -145,3 +145,21 @@ def wkv_backward_direct(w, u, k, v, gout, state_in=None, gstate_out=None, state_
 
     gstate_in = np.stack([gn0, gd0, gm0])
     return gw.sum(axis=0), gu.sum(axis=0), gk, gv, gstate_in
+
+
+# ---------------------------------------------------------------------------
+# The receptance gate on the output (see wkv_oracle.wkv_gated).
+# ---------------------------------------------------------------------------
+
+def wkv_gated_backward_direct(w, u, k, v, r, gout, state_in=None, gstate_out=None,
+                              state_out=None):
+    """Gradients of sum(gout * sigmoid(r) * wkv) (+ the final-state term of
+    wkv_backward_direct): by the product rule dL/dr = gout * wkv * s (1 - s)
+    with s = sigmoid(r), and the WKV gradients are those of the ungated
+    operator for the upstream gradient gout * s. Returns
+    (gw, gu, gk, gv, gstate_in, gr). wkv is the forward oracle's output."""
+    s = sigmoid(r)
+    y, _ = wkv_direct(w, u, k, v, state_in)
+    g = _f64(gout)
+    gw, gu, gk, gv, gs = wkv_backward_direct(w, u, k, v, g * s, state_in, gstate_out, state_out)
+    return gw, gu, gk, gv, gs, g * y * s * (1.0 - s)

@@ -192,6 +192,34 @@ def wkv_recurrent(w, u, k, v, state_in=None):
 
 
 # ---------------------------------------------------------------------------
+# The receptance gate on the output.
+# ---------------------------------------------------------------------------
+# The page "RWKV-v6 Architecture: Attention-Free Linear Transformers" gates
+# its recurrence's output elementwise with sigmoid(r_t) (the output equation
+# of its recurrence), and the page "RWKV: Merging Transformer Training with
+# RNN Speed" (Time-Mixing block) describes the receptance as the gate that
+# decides how much of the accumulated history passes on. Applied to this
+# operator's output: out_t = sigmoid(r_t) * wkv_t per channel.
+
+def sigmoid(x):
+    """The logistic function 1 / (1 + e^-x), evaluated without overflow."""
+    x = _f64(x)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def wkv_gated(w, u, k, v, r, state_in=None):
+    """(sigmoid(r) * wkv, state_out), wkv from the defining equation
+    (wkv_direct); r has k's shape. The state is the ungated one."""
+    out, st = wkv_direct(w, u, k, v, state_in)
+    return sigmoid(r) * out, st
+
+
+# ---------------------------------------------------------------------------
 # Segment summaries and their composition (the time-parallel form).
 # ---------------------------------------------------------------------------
 # The page "RWKV-v6 Architecture: Attention-Free Linear Transformers", section

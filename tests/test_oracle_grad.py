@@ -8,7 +8,9 @@ computed: the output does not change when every key and the initial state's
 max_exp move by the same amount, it is homogeneous of degree one in (v, n0),
 and it does not depend on w for T <= 2 from the empty state. Planted mistakes
 in the oracle's source (run on the CPU) must fail the finite-difference
-check."""
+check. The receptance gate's sigmoid is checked against scipy's, the gated
+output at the gate's special values (fully open, r = 0), and the gated
+gradients (including dL/dr) by finite differences of the gated forward."""
 
 import inspect
 
@@ -151,3 +153,54 @@ def test_planted_mistakes_fail_the_finite_difference_pin(old, new):
     exec(compile(code, "mutant", "exec"), ns)
     w, u, k, v, gout, s0, gs = _case(21, 1, 4, 2, 1.0, True)
     assert _fd_check(w, u, k, v, gout, s0, gs, backward=ns["wkv_backward_direct"]) > 1e-4
+
+
+# ---------------------------------------------------------------- the gate
+
+def test_sigmoid_matches_scipy():
+    import scipy.special
+
+    from oracle import sigmoid
+
+    x = np.concatenate([np.linspace(-50, 50, 1001), [-800.0, 800.0, 0.0]])
+    assert np.allclose(sigmoid(x), scipy.special.expit(x), rtol=1e-15, atol=1e-300)
+
+
+def test_gate_special_values():
+    """r -> +inf passes the WKV output through, r = 0 halves it."""
+    from oracle import wkv_gated
+
+    w, u, k, v, _, s0, _ = _case(90, 2, 7, 3, 1.0, True)
+    plain, st = wkv_direct(w, u, k, v, s0)
+    open_gate, st2 = wkv_gated(w, u, k, v, np.full(k.shape, 1e3), s0)
+    half, _ = wkv_gated(w, u, k, v, np.zeros(k.shape), s0)
+    assert np.array_equal(open_gate, plain) and np.array_equal(st2, st)
+    assert np.array_equal(half, 0.5 * plain)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_gated_gradients_match_finite_differences(with_state):
+    from oracle import wkv_gated, wkv_gated_backward_direct
+
+    w, u, k, v, gout, s0, _ = _case(91 + with_state, 2, 6, 3, 2.0, with_state)
+    r = np.random.default_rng([92]).normal(0, 2, k.shape)
+    gw, gu, gk, gv, gs0, gr = wkv_gated_backward_direct(w, u, k, v, r, gout, s0)
+    args = {"w": w, "u": u, "k": k, "v": v, "r": r}
+    if s0 is not None:
+        args["s0"] = s0
+    analytic = {"w": gw, "u": gu, "k": gk, "v": gv, "r": gr, "s0": gs0}
+
+    def loss(a):
+        out, _ = wkv_gated(a["w"], a["u"], a["k"], a["v"], a["r"], a.get("s0"))
+        return (gout * out).sum()
+
+    h, worst = 1e-6, 0.0
+    for name, arr in args.items():
+        for idx in np.ndindex(arr.shape):
+            plus = {n: x.copy() for n, x in args.items()}
+            minus = {n: x.copy() for n, x in args.items()}
+            plus[name][idx] += h
+            minus[name][idx] -= h
+            fd = (loss(plus) - loss(minus)) / (2 * h)
+            worst = max(worst, abs(fd - analytic[name][idx]))
+    assert worst / max(np.abs(gk).max(), np.abs(gr).max()) < 1e-7
