@@ -135,6 +135,17 @@ int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float*
                    float* state_out, int io, int path, void* workspace,
                    int64_t workspace_bytes, hipStream_t stream);
 
+/* As wkv_forward_ws with the output gated by the receptance:
+ * out_t = sigmoid(r_t) * wkv_t per element (page "RWKV-v6 Architecture:
+ * Attention-Free Linear Transformers", the output equation of its recurrence;
+ * page "RWKV: Merging Transformer Training with RNN Speed", Time-Mixing
+ * block). r: [B][T][C] of the element type io, required when T > 0; it must
+ * not overlap out or state_out. state_out is the ungated state. */
+int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                      const void* k, const void* v, const void* r, const float* state_in,
+                      void* out, float* state_out, int io, int path, void* workspace,
+                      int64_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace wkv_forward_ws needs for these sizes and this path
  * (0 when the kernel uses none), or a negative wkv_status on error. */
 int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path);
@@ -165,14 +176,17 @@ int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const ui
                   const uint16_t* v, float* state, uint16_t* out, hipStream_t stream);
 
 /* Backward pass of the prefill (fp32): gradients of a loss L with respect to
- * w, u, k, v and the initial state, given dL/dout and optionally dL/dstate_out.
- * The derivatives are those of the wkv_t ratio of the page "Linear attention
- * without writing a CUDA kernel", section "The recurrence" (quotient rule over
- * its terms; the page trains its model through this operator).
+ * w, u, k, v, the receptance r of a gated output and the initial state, given
+ * dL/dout and optionally dL/dstate_out. The derivatives are those of the
+ * wkv_t ratio of the page "Linear attention without writing a CUDA kernel",
+ * section "The recurrence" (quotient rule over its terms; the page trains its
+ * model through this operator), times the gate sigmoid(r) when there is one.
  *
  *   B, T, C     sizes (>= 0). C == 0: nothing to do. B == 0: gw, gu zeroed.
  *   w, u        [C] the forward's decay and bonus.
  *   k, v        [B][T][C] the forward's keys and values.
+ *   r           [B][T][C] the receptance of wkv_forward_gated, or NULL for an
+ *               ungated output.
  *   state_in    [3][B][C] the forward's initial state, or NULL (empty state).
  *   state_out,  [3][B][C] the state the forward returned and dL/d(num, den,
  *   gstate_out  max_exp) of it, both or neither (NULL: no gradient on the final
@@ -180,8 +194,9 @@ int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const ui
  *               den at the given max_exp; the max_exp plane of gstate_out is
  *               not read (for a loss of the state itself it equals
  *               num * g_num + den * g_den).
- *   gout        [B][T][C] dL/dout.
+ *   gout        [B][T][C] dL/dout (of the gated output when r is given).
  *   gk, gv      [B][T][C] out: dL/dk, dL/dv.
+ *   gr          [B][T][C] out: dL/dr; required with r, ignored without.
  *   gw, gu      [C] out: dL/dw, dL/du summed over the batch.
  *   gstate_in   [3][B][C] out: dL/d(num, den, max_exp) of state_in (zeros when
  *               state_in is NULL), or NULL to skip it.
@@ -193,14 +208,21 @@ int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const ui
  * Outputs must not overlap any input or each other (WKV_ERR_ALIAS). The
  * result is deterministic (fixed-order sums). */
 int wkv_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                 const float* k, const float* v, const float* state_in,
+                 const float* k, const float* v, const float* r, const float* state_in,
                  const float* state_out, const float* gstate_out, const float* gout,
-                 float* gk, float* gv, float* gw, float* gu, float* gstate_in,
+                 float* gk, float* gv, float* gr, float* gw, float* gu, float* gstate_in,
                  void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace wkv_backward needs for these sizes, or a negative
  * wkv_status on error. */
 int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C);
+
+/* One decode step with the gated output, out = sigmoid(r) * wkv (see
+ * wkv_forward_gated); k, v, r, out of element type io ([B][C]); the state is
+ * fp32 and ungated. */
+int wkv_step_gated(int64_t B, int64_t C, const float* w, const float* u, const void* k,
+                   const void* v, const void* r, float* state, void* out, int io,
+                   hipStream_t stream);
 
 /* Static, NUL-terminated name of a wkv_status code. */
 const char* wkv_status_string(int status);

@@ -156,15 +156,19 @@ def test_backward_abi_errors():
     need = lib.wkv_backward_workspace_size(B, T, C)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    base = [B, T, C, P(w), P(u), P(k), P(v), None, None, None, P(g), P(gk), P(gv), P(gw), P(gu),
-            None]
+    # B, T, C, w, u, k, v, r, state_in, state_out, gstate_out, gout, gk, gv, gr, gw, gu, gstate_in
+    base = [B, T, C, P(w), P(u), P(k), P(v), None, None, None, None, P(g), P(gk), P(gv), None,
+            P(gw), P(gu), None]
     assert lib.wkv_backward(*base, P(ws), need, s) == 0
     assert lib.wkv_backward(*base, P(ws), need - 16, s) == 8            # workspace too small
     bad = list(base)
-    bad[8] = P(z(3, B, C))                                              # state_out without gradient
+    bad[9] = P(z(3, B, C))                                              # state_out without gradient
     assert lib.wkv_backward(*bad, P(ws), need, s) == 1
     bad = list(base)
-    bad[11] = P(k)                                                      # gk on top of k
+    bad[7] = P(z(B, T, C))                                              # r without dL/dr
+    assert lib.wkv_backward(*bad, P(ws), need, s) == 1
+    bad = list(base)
+    bad[12] = P(k)                                                      # gk on top of k
     assert lib.wkv_backward(*bad, P(ws), need, s) == 4
     bad = list(base)
     bad[0] = 0                                                          # B = 0: gw, gu zeroed

@@ -107,22 +107,43 @@ def test_backward_workspace_and_validation_without_device():
     nul = None
     a = 0x10000000
     args = [P(a), P(a + 4096)] + [P(a + (i + 2) * (1 << 20)) for i in range(2)]
-    # B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw, gu, gstate_in
-    base = [2, 9, 4, args[0], args[1], args[2], args[3], nul, nul, nul, P(a + 5 * (1 << 20)),
-            P(a + 6 * (1 << 20)), P(a + 7 * (1 << 20)), P(a + 8 * (1 << 20)),
-            P(a + 8 * (1 << 20) + 256), nul]
+    # B, T, C, w, u, k, v, r, state_in, state_out, gstate_out, gout, gk, gv, gr, gw, gu,
+    # gstate_in
+    base = [2, 9, 4, args[0], args[1], args[2], args[3], nul, nul, nul, nul,
+            P(a + 5 * (1 << 20)), P(a + 6 * (1 << 20)), P(a + 7 * (1 << 20)), nul,
+            P(a + 8 * (1 << 20)), P(a + 8 * (1 << 20) + 256), nul]
     assert lib.wkv_backward(-1, *base[1:], nul, 0, nul) == 2
     assert lib.wkv_backward(*base, nul, 0, nul) == 8                     # no workspace
     bad = list(base)
     bad[3] = nul
     assert lib.wkv_backward(*bad, nul, 0, nul) == 1                      # w missing
     bad = list(base)
-    bad[9] = P(a + 9 * (1 << 20))                                        # gradient without state
+    bad[10] = P(a + 9 * (1 << 20))                                       # gradient without state
     assert lib.wkv_backward(*bad, P(a + (1 << 28)), 1 << 20, nul) == 1
     bad = list(base)
-    bad[12] = bad[5]                                                     # gv on top of k
+    bad[7] = P(a + 10 * (1 << 20))                                       # r without dL/dr
+    assert lib.wkv_backward(*bad, P(a + (1 << 28)), 1 << 20, nul) == 1
+    bad = list(base)
+    bad[13] = bad[5]                                                     # gv on top of k
     assert lib.wkv_backward(*bad, P(a + (1 << 28)), 1 << 20, nul) == 4
     assert lib.wkv_backward(*base, P(a + (1 << 28) + 8), 1 << 20, nul) == 3  # misaligned workspace
+
+
+def test_gated_entry_points_validate_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    a = 0x10000000
+    w, u, k, v, r = P(a), P(a + 4096), P(a + 8192), P(a + 8192 + 4096), P(a + 8192 + 8192)
+    out = P(a + 8192 + 3 * 4096)
+    # B, T, C, w, u, k, v, r, state_in, out, state_out, io, path, workspace, bytes, stream
+    assert lib.wkv_forward_gated(1, 4, 4, w, u, k, v, nul, nul, out, nul, 0, 1, nul, 0, nul) == 1
+    assert lib.wkv_forward_gated(1, 4, 4, w, u, k, v, r, nul, r, nul, 0, 1, nul, 0, nul) == 4
+    assert lib.wkv_forward_gated(1, 4, 4, w, u, k, v, P(a + 8192 + 8194), nul, out, nul, 0, 1,
+                                 nul, 0, nul) == 3
+    # B, C, w, u, k, v, r, state, out, io, stream
+    assert lib.wkv_step_gated(2, 4, w, u, k, v, nul, P(a + 65536), out, 0, nul) == 1
+    assert lib.wkv_step_gated(2, 4, w, u, k, v, r, P(a + 65536), out, 3, nul) == 7
 
 
 def test_inputs_are_seeded_and_row_independent():

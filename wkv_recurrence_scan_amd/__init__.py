@@ -32,10 +32,12 @@ from ._lib import (  # noqa: F401
     wkv_forward,
     wkv_forward_bf16,
     wkv_forward_ex,
+    wkv_forward_gated,
     wkv_forward_ws,
     wkv_select_path,
     wkv_status_string,
     wkv_step,
     wkv_step_bf16,
+    wkv_step_gated,
     wkv_workspace_size,
 )

@@ -64,7 +64,9 @@ def load_library() -> ctypes.CDLL:
         "wkv_status_string": [ci],
         "wkv_last_hip_error": [],
         "wkv_abi_version": [],
-        "wkv_backward": [i64, i64, i64] + [vp] * 13 + [vp, i64, vp],
+        "wkv_backward": [i64, i64, i64] + [vp] * 15 + [vp, i64, vp],
+        "wkv_forward_gated": [i64, i64, i64] + [vp] * 8 + [ci, ci, vp, i64, vp],
+        "wkv_step_gated": [i64, i64] + [vp] * 7 + [ci, vp],
         "wkv_backward_workspace_size": [i64, i64, i64],
     }
     for name, args in sigs.items():
@@ -305,14 +307,17 @@ def wkv_backward_workspace_size(B: int, T: int, C: int) -> int:
 def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  gout: torch.Tensor, state_in: Optional[torch.Tensor] = None,
                  state_out: Optional[torch.Tensor] = None,
-                 gstate_out: Optional[torch.Tensor] = None, *, want_gstate_in: bool = True,
-                 workspace: Optional[torch.Tensor] = None, out=None, stream=None):
-    """Gradients of the prefill (float32): returns (gw, gu, gk, gv, gstate_in)
+                 gstate_out: Optional[torch.Tensor] = None, *, r: Optional[torch.Tensor] = None,
+                 want_gstate_in: bool = True, workspace: Optional[torch.Tensor] = None, out=None,
+                 stream=None):
+    """Gradients of the prefill (float32). Returns (gw, gu, gk, gv, gstate_in)
     for the upstream gradient gout of out (and gstate_out of state_out, which
-    must then be the state the forward returned). gstate_in is None when
-    want_gstate_in is False. `out` may hold preallocated (gk, gv, gw, gu,
-    gstate_in) tensors; `workspace` a uint8 tensor of at least
-    wkv_backward_workspace_size bytes (else one is allocated for the call)."""
+    must then be the state the forward returned), or (gw, gu, gk, gv,
+    gstate_in, gr) when r, the receptance of a gated output, is given.
+    gstate_in is None when want_gstate_in is False. `out` may hold
+    preallocated (gk, gv, gw, gu, gstate_in[, gr]) tensors; `workspace` a uint8
+    tensor of at least wkv_backward_workspace_size bytes (else one is
+    allocated for the call)."""
     lib = load_library()
     if k.dim() != 3:
         raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
@@ -323,6 +328,8 @@ def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Ten
     f32 = torch.float32
     for name, t in (("k", k), ("v", v), ("gout", gout)):
         _need(t, name, f32, (B, T, C), dev)
+    if r is not None:
+        _need(r, "r", f32, (B, T, C), dev)
     _need(w, "w", f32, (C,), dev)
     _need(u, "u", f32, (C,), dev)
     for name, t in (("state_in", state_in), ("state_out", state_out), ("gstate_out", gstate_out)):
@@ -334,13 +341,19 @@ def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Ten
         gw = torch.empty((C,), dtype=f32, device=dev)
         gu = torch.empty((C,), dtype=f32, device=dev)
         gs = torch.empty((3, B, C), dtype=f32, device=dev) if want_gstate_in else None
+        gr = torch.empty((B, T, C), dtype=f32, device=dev) if r is not None else None
     else:
-        gk, gv, gw, gu, gs = out
+        gk, gv, gw, gu, gs = out[:5]
+        gr = out[5] if len(out) > 5 else None
     for name, t, shape in (("gk", gk, (B, T, C)), ("gv", gv, (B, T, C)), ("gw", gw, (C,)),
                            ("gu", gu, (C,))):
         _need(t, name, f32, shape, dev)
     if gs is not None:
         _need(gs, "gstate_in", f32, (3, B, C), dev)
+    if r is not None:
+        if gr is None:
+            raise ValueError("a gated backward needs a tensor for dL/dr")
+        _need(gr, "gr", f32, (B, T, C), dev)
     with torch.cuda.device(dev):
         strm = torch.cuda.current_stream(dev) if stream is None else stream
         nbytes = wkv_backward_workspace_size(B, T, C)
@@ -348,12 +361,76 @@ def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Ten
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
-        st = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
-                              _ptr(state_out), _ptr(gstate_out), _ptr(gout), _ptr(gk), _ptr(gv),
-                              _ptr(gw), _ptr(gu), _ptr(gs), _ptr(workspace), workspace.numel(),
-                              ctypes.c_void_p(strm.cuda_stream))
+        st = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                              _ptr(state_in), _ptr(state_out), _ptr(gstate_out), _ptr(gout),
+                              _ptr(gk), _ptr(gv), _ptr(gr), _ptr(gw), _ptr(gu), _ptr(gs),
+                              _ptr(workspace), workspace.numel(), ctypes.c_void_p(strm.cuda_stream))
     _check(st, "wkv_backward")
-    return gw, gu, gk, gv, gs
+    return (gw, gu, gk, gv, gs) if r is None else (gw, gu, gk, gv, gs, gr)
+
+
+def wkv_forward_gated(w, u, k, v, r, state_in=None, out=None, state_out=None, *, path="auto",
+                      workspace=None, want_state=True, stream=None):
+    """wkv_forward_gated: out = sigmoid(r) * wkv, r shaped and typed like k
+    (float32 or bfloat16). Returns (out, state_out) like wkv_forward_ex; the
+    state is the ungated one."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    if path not in _PATHS:
+        raise ValueError(f"path must be one of {sorted(_PATHS)}")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"k must be float32 or bfloat16, got {k.dtype}")
+    for name, t in (("v", v), ("r", r)):
+        _need(t, name, k.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=k.dtype, device=dev)
+    _need(out, "out", k.dtype, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (3, B, C), dev)
+    io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
+    with torch.cuda.device(dev):
+        strm = torch.cuda.current_stream(dev) if stream is None else stream
+        if workspace is None:
+            workspace = _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
+                                          (B, T, C, io, path))
+        st = lib.wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                   _ptr(state_in), _ptr(out), _ptr(state_out), io, _PATHS[path],
+                                   _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   ctypes.c_void_p(strm.cuda_stream))
+    _check(st, "wkv_forward_gated")
+    return out, state_out
+
+
+def wkv_step_gated(w, u, k, v, r, state, out=None, stream=None):
+    """wkv_step_gated: one decode step with out = sigmoid(r) * wkv; k, v, r,
+    out (B, C) float32 or bfloat16; the fp32 state is updated in place."""
+    lib = load_library()
+    B, C = k.shape
+    dev = k.device
+    for name, t in (("v", v), ("r", r)):
+        _need(t, name, k.dtype, (B, C), dev)
+    _need(w, "w", torch.float32, (C,), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    _need(state, "state", torch.float32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, C), dtype=k.dtype, device=dev)
+    io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
+    with torch.cuda.device(dev):
+        st = lib.wkv_step_gated(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state),
+                                _ptr(out), io, _stream_handle(dev, stream))
+    _check(st, "wkv_step_gated")
+    return out
 
 
 class ForwardCall:

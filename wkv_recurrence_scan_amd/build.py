@@ -30,7 +30,8 @@ EXPORTS = [
     "wkv_forward", "wkv_forward_bf16", "wkv_forward_ex", "wkv_forward_ws", "wkv_workspace_size",
     "wkv_select_path",
     "wkv_step", "wkv_step_bf16", "wkv_status_string", "wkv_last_hip_error",
-    "wkv_abi_version", "wkv_backward", "wkv_backward_workspace_size",
+    "wkv_abi_version", "wkv_backward", "wkv_backward_workspace_size", "wkv_forward_gated",
+    "wkv_step_gated",
 ]
 
 

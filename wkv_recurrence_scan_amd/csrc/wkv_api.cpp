@@ -77,8 +77,9 @@ int64_t lookback_bytes(int io, int64_t B, int64_t T, int64_t C) {
 }
 
 int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
-                 const void* v, const float* state_in, void* out, float* state_out, int io,
-                 int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                 const void* v, const void* r, bool gated, const float* state_in, void* out,
+                 float* state_out, int io, int path, void* workspace, int64_t workspace_bytes,
+                 hipStream_t stream) {
   if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
   if (path < WKV_PATH_AUTO || path > WKV_PATH_LOOKBACK) return WKV_ERR_ARG;
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
@@ -92,12 +93,17 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
 
   if (w == nullptr || u == nullptr) return WKV_ERR_NULL;
   if (T > 0 && (k == nullptr || v == nullptr || out == nullptr)) return WKV_ERR_NULL;
+  if (gated && T > 0 && r == nullptr) return WKV_ERR_NULL;
+  if (!gated || T == 0) r = nullptr;
   if (misaligned(w, 4) || misaligned(u, 4) || misaligned(state_in, 4) || misaligned(state_out, 4))
     return WKV_ERR_ALIGN;
-  if (misaligned(k, es) || misaligned(v, es) || misaligned(out, es)) return WKV_ERR_ALIGN;
+  if (misaligned(k, es) || misaligned(v, es) || misaligned(out, es) || misaligned(r, es))
+    return WKV_ERR_ALIGN;
 
   const int64_t pbytes = C * 4;
   const int64_t sbytes = T > 0 ? seq_bytes : 0;
+  if (overlaps(out, sbytes, r, sbytes) || overlaps(state_out, state_bytes, r, sbytes))
+    return WKV_ERR_ALIAS;
   // out must not touch anything else
   if (overlaps(out, sbytes, k, sbytes) || overlaps(out, sbytes, v, sbytes) ||
       overlaps(out, sbytes, w, pbytes) || overlaps(out, sbytes, u, pbytes) ||
@@ -116,6 +122,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
     if (overlaps(workspace, workspace_bytes, k, sbytes) ||
         overlaps(workspace, workspace_bytes, v, sbytes) ||
         overlaps(workspace, workspace_bytes, out, sbytes) ||
+        overlaps(workspace, workspace_bytes, r, sbytes) ||
         overlaps(workspace, workspace_bytes, w, pbytes) ||
         overlaps(workspace, workspace_bytes, u, pbytes) ||
         overlaps(workspace, workspace_bytes, state_in, state_bytes) ||
@@ -123,7 +130,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
       return WKV_ERR_ALIAS;
   }
 
-  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out};
+  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out, r};
   if (path == WKV_PATH_LOOKBACK && T > 0 &&
       (!have_ws || workspace_bytes < wkv::lookback_workspace_bytes(
                                          wkv::lookback_vec_width(io, C, a), B, T, C)))
@@ -155,7 +162,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
 }
 
 int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* k, const void* v,
-              float* state, void* out, int io, hipStream_t stream) {
+              const void* r, bool gated, float* state, void* out, int io, hipStream_t stream) {
   if (B < 0 || C < 0) return WKV_ERR_DIM;
   const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
   int64_t io_bytes, state_bytes;
@@ -163,31 +170,34 @@ int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* 
   if (!mul3(B, C, 12, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
   if (B == 0 || C == 0) return WKV_OK;
   if (w == nullptr || u == nullptr || k == nullptr || v == nullptr || state == nullptr ||
-      out == nullptr)
+      out == nullptr || (gated && r == nullptr))
     return WKV_ERR_NULL;
+  if (!gated) r = nullptr;
   if (misaligned(w, 4) || misaligned(u, 4) || misaligned(state, 4)) return WKV_ERR_ALIGN;
-  if (misaligned(k, es) || misaligned(v, es) || misaligned(out, es)) return WKV_ERR_ALIGN;
+  if (misaligned(k, es) || misaligned(v, es) || misaligned(out, es) || misaligned(r, es))
+    return WKV_ERR_ALIGN;
   const int64_t pbytes = C * 4;
   if (overlaps(out, io_bytes, k, io_bytes) || overlaps(out, io_bytes, v, io_bytes) ||
       overlaps(out, io_bytes, w, pbytes) || overlaps(out, io_bytes, u, pbytes) ||
-      overlaps(out, io_bytes, state, state_bytes))
+      overlaps(out, io_bytes, state, state_bytes) || overlaps(out, io_bytes, r, io_bytes))
     return WKV_ERR_ALIAS;
   if (overlaps(state, state_bytes, k, io_bytes) || overlaps(state, state_bytes, v, io_bytes) ||
-      overlaps(state, state_bytes, w, pbytes) || overlaps(state, state_bytes, u, pbytes))
+      overlaps(state, state_bytes, w, pbytes) || overlaps(state, state_bytes, u, pbytes) ||
+      overlaps(state, state_bytes, r, io_bytes))
     return WKV_ERR_ALIAS;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
-  const wkv::StepArgs a{B, C, w, u, k, v, state, out};
+  const wkv::StepArgs a{B, C, w, u, k, v, state, out, r};
   e = wkv::launch_step(a, io, wkv::step_vec_width(io, C, a), stream);
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
 
 int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                  const float* k, const float* v, const float* state_in, const float* state_out,
-                  const float* gstate_out, const float* gout, float* gk, float* gv, float* gw,
-                  float* gu, float* gstate_in, void* workspace, int64_t workspace_bytes,
-                  hipStream_t stream) {
+                  const float* k, const float* v, const float* r, const float* state_in,
+                  const float* state_out, const float* gstate_out, const float* gout, float* gk,
+                  float* gv, float* gr, float* gw, float* gu, float* gstate_in, void* workspace,
+                  int64_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
   int64_t seq_bytes, state_bytes;
   if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, 4, &seq_bytes) ||
@@ -203,7 +213,11 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
   if (tokens && (k == nullptr || v == nullptr || gout == nullptr || gk == nullptr || gv == nullptr))
     return WKV_ERR_NULL;
   if ((gstate_out == nullptr) != (state_out == nullptr)) return WKV_ERR_NULL;
-  const void* all[] = {w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw, gu, gstate_in};
+  if (tokens && r != nullptr && gr == nullptr) return WKV_ERR_NULL;
+  if (!tokens) r = nullptr, gr = nullptr;
+  if (r == nullptr) gr = nullptr;
+  const void* all[] = {w,    u,  k,  v,  r,  state_in, state_out, gstate_out,
+                       gout, gk, gv, gr, gw, gu,       gstate_in};
   for (const void* p : all)
     if (misaligned(p, 4)) return WKV_ERR_ALIGN;
 
@@ -214,11 +228,12 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
     int64_t n;
   };
   const Range inputs[] = {{w, pbytes},        {u, pbytes},          {k, sbytes},
-                          {v, sbytes},        {gout, sbytes},       {state_in, state_bytes},
-                          {state_out, state_bytes}, {gstate_out, state_bytes}};
-  const Range outputs[] = {{gk, sbytes}, {gv, sbytes}, {gw, pbytes}, {gu, pbytes},
+                          {v, sbytes},        {r, sbytes},          {gout, sbytes},
+                          {state_in, state_bytes}, {state_out, state_bytes},
+                          {gstate_out, state_bytes}};
+  const Range outputs[] = {{gk, sbytes}, {gv, sbytes}, {gr, sbytes}, {gw, pbytes}, {gu, pbytes},
                            {gstate_in, state_bytes}};
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < 6; ++i) {
     for (const Range& r : inputs)
       if (overlaps(outputs[i].p, outputs[i].n, r.p, r.n)) return WKV_ERR_ALIAS;
     for (int j = 0; j < i; ++j)
@@ -236,8 +251,8 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
-  const wkv::BwdArgs a{B,         T,          C,  w,  u,  k,  v,        gout,
-                       state_in,  state_out,  gstate_out, gk, gv, gw, gu, gstate_in};
+  const wkv::BwdArgs a{B,        T,         C,          w,  u,  k,  v,  gout,     state_in,
+                       state_out, gstate_out, gk,        gv, gw, gu, gstate_in, r,  gr};
   e = wkv::launch_backward(a, workspace, stream);
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
@@ -247,12 +262,12 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
 extern "C" {
 
 int wkv_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const float* k,
-                 const float* v, const float* state_in, const float* state_out,
-                 const float* gstate_out, const float* gout, float* gk, float* gv, float* gw,
-                 float* gu, float* gstate_in, void* workspace, int64_t workspace_bytes,
-                 hipStream_t stream) {
-  return backward_impl(B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw, gu,
-                       gstate_in, workspace, workspace_bytes, stream);
+                 const float* v, const float* r, const float* state_in, const float* state_out,
+                 const float* gstate_out, const float* gout, float* gk, float* gv, float* gr,
+                 float* gw, float* gu, float* gstate_in, void* workspace,
+                 int64_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(B, T, C, w, u, k, v, r, state_in, state_out, gstate_out, gout, gk, gv, gr,
+                       gw, gu, gstate_in, workspace, workspace_bytes, stream);
 }
 
 int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
@@ -268,29 +283,37 @@ int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
 int wkv_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const float* k,
                 const float* v, const float* state_in, float* out, float* state_out,
                 hipStream_t stream) {
-  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_F32, WKV_PATH_AUTO,
-                      nullptr, 0, stream);
+  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, WKV_IO_F32,
+                      WKV_PATH_AUTO, nullptr, 0, stream);
 }
 
 int wkv_forward_bf16(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                      const uint16_t* k, const uint16_t* v, const float* state_in, uint16_t* out,
                      float* state_out, hipStream_t stream) {
-  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_BF16, WKV_PATH_AUTO,
-                      nullptr, 0, stream);
+  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, WKV_IO_BF16,
+                      WKV_PATH_AUTO, nullptr, 0, stream);
 }
 
 int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
                    const void* v, const float* state_in, void* out, float* state_out, int io,
                    int path, hipStream_t stream) {
-  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, nullptr, 0,
-                      stream);
+  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
+                      nullptr, 0, stream);
 }
 
 int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
                    const void* v, const float* state_in, void* out, float* state_out, int io,
                    int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  return forward_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, workspace,
-                      workspace_bytes, stream);
+  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
+                      workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                      const void* k, const void* v, const void* r, const float* state_in,
+                      void* out, float* state_out, int io, int path, void* workspace,
+                      int64_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(B, T, C, w, u, k, v, r, true, state_in, out, state_out, io, path,
+                      workspace, workspace_bytes, stream);
 }
 
 int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path) {
@@ -320,12 +343,19 @@ int wkv_select_path(int64_t B, int64_t T, int64_t C, int io) {
 
 int wkv_step(int64_t B, int64_t C, const float* w, const float* u, const float* k, const float* v,
              float* state, float* out, hipStream_t stream) {
-  return step_impl(B, C, w, u, k, v, state, out, WKV_IO_F32, stream);
+  return step_impl(B, C, w, u, k, v, nullptr, false, state, out, WKV_IO_F32, stream);
 }
 
 int wkv_step_bf16(int64_t B, int64_t C, const float* w, const float* u, const uint16_t* k,
                   const uint16_t* v, float* state, uint16_t* out, hipStream_t stream) {
-  return step_impl(B, C, w, u, k, v, state, out, WKV_IO_BF16, stream);
+  return step_impl(B, C, w, u, k, v, nullptr, false, state, out, WKV_IO_BF16, stream);
+}
+
+int wkv_step_gated(int64_t B, int64_t C, const float* w, const float* u, const void* k,
+                   const void* v, const void* r, float* state, void* out, int io,
+                   hipStream_t stream) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
+  return step_impl(B, C, w, u, k, v, r, true, state, out, io, stream);
 }
 
 const char* wkv_status_string(int status) {

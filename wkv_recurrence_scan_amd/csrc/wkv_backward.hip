@@ -72,35 +72,49 @@ __device__ __forceinline__ float lane_step_rec(Lane& s, float k, float v, float 
   return out;
 }
 
+// One chunk's k, v, dL/dout and, for a gated output (G), the receptance.
+template <bool G>
 struct Chunk {
-  float k[kLc], v[kLc], g[kLc];
+  float k[kLc], v[kLc], g[kLc], r[G ? kLc : 1];
 };
 
-template <bool MASKED>
-__device__ __forceinline__ void load_chunk(Chunk& c, const float* __restrict__ kp,
+template <bool MASKED, bool G>
+__device__ __forceinline__ void load_chunk(Chunk<G>& c, const float* __restrict__ kp,
                                            const float* __restrict__ vp,
-                                           const float* __restrict__ gp, int64_t C, int n) {
+                                           const float* __restrict__ gp,
+                                           const float* __restrict__ rp, int64_t C, int n) {
 #pragma unroll
   for (int i = 0; i < kLc; ++i) {
     if (!MASKED || i < n) {
       c.k[i] = __builtin_nontemporal_load(kp + i * C);
       c.v[i] = __builtin_nontemporal_load(vp + i * C);
       c.g[i] = __builtin_nontemporal_load(gp + i * C);
+      if constexpr (G) c.r[i] = __builtin_nontemporal_load(rp + i * C);
     } else {
       c.k[i] = 0.0f;
       c.v[i] = 0.0f;
       c.g[i] = 0.0f;
+      if constexpr (G) c.r[i] = 0.0f;
     }
   }
 }
 
+// dL/d(wkv_t) from dL/dout_t: the gate's share when the output is gated.
+template <bool G>
+__device__ __forceinline__ float wkv_grad(const Chunk<G>& c, int i) {
+  if constexpr (G) return c.g[i] * gate(c.r[i]);
+  return c.g[i];
+}
+
 // Backward walk over one chunk of n tokens (all kLc unless MASKED) starting
-// from checkpoint state st; gk, gv point at the chunk's first token.
-template <bool MASKED>
-__device__ __forceinline__ void chunk_backward(const Chunk& c, int n, Lane st, Suffix& a,
+// from checkpoint state st; gk, gv (and gr when G) point at the chunk's first
+// token. With a gate, dL/dr_t = dL/dout_t wkv_t s (1 - s), s = sigmoid(r_t),
+// and the WKV sees dL/dout_t s.
+template <bool MASKED, bool G>
+__device__ __forceinline__ void chunk_backward(const Chunk<G>& c, int n, Lane st, Suffix& a,
                                                float w, float u, float& gw_acc, float& gu_acc,
                                                float* __restrict__ gkp, float* __restrict__ gvp,
-                                               int64_t C) {
+                                               float* __restrict__ grp, int64_t C) {
   float y[kLc], M[kLc], rho[kLc], om[kLc];
 #pragma unroll
   for (int i = 0; i < kLc; ++i) {
@@ -110,7 +124,13 @@ __device__ __forceinline__ void chunk_backward(const Chunk& c, int n, Lane st, S
   for (int i = kLc - 1; i >= 0; --i) {
     if (!MASKED || i < n) {
       // gradients of token i from the suffix sums over t > i
-      const float e_cur = c.g[i] * om[i];
+      float gi = c.g[i];
+      if constexpr (G) {
+        const float sg = gate(c.r[i]);
+        __builtin_nontemporal_store(gi * y[i] * sg * (1.0f - sg), grp + i * C);
+        gi *= sg;
+      }
+      const float e_cur = gi * om[i];
       const float ex = fast_exp2(__builtin_fmaf(-a.za, w, c.k[i] + a.zb) * kLog2e);  // e^(k_i+z)
       const float gv = __builtin_fmaf(a.p, ex, e_cur);
       const float gk = __builtin_fmaf(c.v[i], gv, -__builtin_fmaf(a.q, ex, e_cur * y[i]));
@@ -125,7 +145,7 @@ __device__ __forceinline__ void chunk_backward(const Chunk& c, int n, Lane st, S
       const bool new_wins = sg > 0.0f;
       const float fo = new_wins ? x : 1.0f;
       const float fn = new_wins ? 1.0f : x;
-      const float ai = c.g[i] * rho[i] * fn;
+      const float ai = gi * rho[i] * fn;
       a.r = fo * (a.r + a.p);
       a.rq = fo * (a.rq + a.q);
       a.p = __builtin_fmaf(fo, a.p, ai);
@@ -141,8 +161,10 @@ struct LaneIo {
   const float* k;
   const float* v;
   const float* g;
+  const float* r;  // receptance (gated output) or nullptr
   float* gk;
   float* gv;
+  float* gr;       // dL/dr or nullptr
   int64_t row, C, step;  // step = kLc * C
   int64_t nfull;         // chunks of kLc tokens that are full
   int rest;              // tokens in the last, partial chunk (0: none)
@@ -205,35 +227,41 @@ __device__ __forceinline__ void forward_rest(Lane& s, const LaneIo& io, float w)
 
 // Backward walk over chunks [j0, j1) of one lane, last first, from their
 // checkpoints; chunk io.nfull (if inside the range) is the partial one.
+template <bool G>
 __device__ __forceinline__ void backward_chunks(const LaneIo& io, int64_t j0, int64_t j1,
                                                 const float4* __restrict__ ckpt, int64_t lanes,
                                                 int64_t lane, float w, float u, Suffix& a,
                                                 float& gw_acc, float& gu_acc) {
+  // r and gr only exist for a gated output
+  auto rp = [&](int64_t off) { return G ? io.r + off : io.r; };
+  auto grp = [&](int64_t off) { return G ? io.gr + off : io.gr; };
   if (j1 > io.nfull) {  // the partial chunk comes last in time, so first here
     const int64_t off = io.row + io.nfull * io.step;
-    Chunk ch;
-    load_chunk<true>(ch, io.k + off, io.v + off, io.g + off, io.C, io.rest);
+    Chunk<G> ch;
+    load_chunk<true, G>(ch, io.k + off, io.v + off, io.g + off, rp(off), io.C, io.rest);
     const float4 cp = ckpt[io.nfull * lanes + lane];
-    chunk_backward<true>(ch, io.rest, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
-                         io.gk + off, io.gv + off, io.C);
+    chunk_backward<true, G>(ch, io.rest, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
+                            io.gk + off, io.gv + off, grp(off), io.C);
     j1 = io.nfull;
   }
   if (j0 >= j1) return;
   auto at = [&](int64_t j) { return io.row + j * io.step; };
-  Chunk A, Bf;
-  load_chunk<false>(A, io.k + at(j1 - 1), io.v + at(j1 - 1), io.g + at(j1 - 1), io.C, kLc);
+  Chunk<G> A, Bf;
+  load_chunk<false, G>(A, io.k + at(j1 - 1), io.v + at(j1 - 1), io.g + at(j1 - 1), rp(at(j1 - 1)),
+                       io.C, kLc);
   for (int64_t j = j1 - 1; j >= j0; j -= 2) {
     const int64_t jb = j - 1 >= j0 ? j - 1 : j0;
-    load_chunk<false>(Bf, io.k + at(jb), io.v + at(jb), io.g + at(jb), io.C, kLc);
+    load_chunk<false, G>(Bf, io.k + at(jb), io.v + at(jb), io.g + at(jb), rp(at(jb)), io.C,
+                         kLc);
     float4 cp = ckpt[j * lanes + lane];
-    chunk_backward<false>(A, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
-                          io.gk + at(j), io.gv + at(j), io.C);
+    chunk_backward<false, G>(A, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
+                             io.gk + at(j), io.gv + at(j), grp(at(j)), io.C);
     if (j - 1 < j0) break;
     const int64_t ja = j - 2 >= j0 ? j - 2 : j0;
-    load_chunk<false>(A, io.k + at(ja), io.v + at(ja), io.g + at(ja), io.C, kLc);
+    load_chunk<false, G>(A, io.k + at(ja), io.v + at(ja), io.g + at(ja), rp(at(ja)), io.C, kLc);
     cp = ckpt[(j - 1) * lanes + lane];
-    chunk_backward<false>(Bf, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
-                          io.gk + at(j - 1), io.gv + at(j - 1), io.C);
+    chunk_backward<false, G>(Bf, kLc, Lane{cp.x, cp.y, cp.z, cp.w}, a, w, u, gw_acc, gu_acc,
+                             io.gk + at(j - 1), io.gv + at(j - 1), grp(at(j - 1)), io.C);
   }
 }
 
@@ -271,8 +299,10 @@ struct BwdKernelArgs {
   const float* state_in;
   const float* state_out;
   const float* gstate_out;
+  const float* r;    // receptance of a gated output, or nullptr
   float* gk;
   float* gv;
+  float* gr;         // dL/dr (gated output only)
   float* gstate_in;
   float4* ckpt;      // [chunks][lanes] state in front of each chunk
   float* gw_part;    // [segments][lanes]
@@ -291,8 +321,10 @@ __device__ __forceinline__ LaneIo lane_io(const BwdKernelArgs& a, int64_t lane) 
   io.k = a.k;
   io.v = a.v;
   io.g = a.gout;
+  io.r = a.r;
   io.gk = a.gk;
   io.gv = a.gv;
+  io.gr = a.gr;
   io.row = b * a.T * a.C + c;
   io.C = a.C;
   io.step = static_cast<int64_t>(kLc) * a.C;
@@ -308,6 +340,7 @@ __device__ __forceinline__ Lane initial_lane(const BwdKernelArgs& a, int64_t lan
 }
 
 // Large B*C: one thread per lane, both passes over the whole sequence.
+template <bool G>
 __global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(BwdKernelArgs a) {
   const int64_t lanes = a.B * a.C;
   const int64_t lane = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
@@ -327,7 +360,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(BwdKernelArgs
   // pass 2: backward over the chunks, last first
   Suffix acc = suffix_init(a.state_out, a.gstate_out, lanes, lane);
   float gw_acc = 0.0f, gu_acc = 0.0f;
-  backward_chunks(io, 0, nch, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
+  backward_chunks<G>(io, 0, nch, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
   initial_state_grad(s_init, a.state_in != nullptr, acc, wc, gw_acc, a.gstate_in, lanes, lane);
   a.gw_part[lane] = gw_acc;
   a.gu_part[lane] = gu_acc;
@@ -366,6 +399,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_forward_kernel(BwdKer
   a.seg_fwd[s * lanes + lane] = make_float4(x.n, x.d, lane_max_exp(x, wc), 0.0f);
 }
 
+template <bool G>
 __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernelArgs a) {
   const int64_t lanes = a.B * a.C;
   const int64_t id = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
@@ -392,12 +426,13 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   for (int64_t j = j0; j < j1; ++j) {
     a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
     const int n = j < io.nfull ? kLc : io.rest;
-    Chunk ch;
+    Chunk<G> ch;
     const int64_t off = io.row + j * io.step;
+    const float* rp = G ? io.r + off : io.r;
     if (n == kLc) {
-      load_chunk<false>(ch, io.k + off, io.v + off, io.g + off, io.C, kLc);
+      load_chunk<false, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, kLc);
     } else {
-      load_chunk<true>(ch, io.k + off, io.v + off, io.g + off, io.C, n);
+      load_chunk<true, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, n);
     }
 #pragma unroll
     for (int i = 0; i < kLc; ++i) {
@@ -409,7 +444,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
         const float e = fast_exp2(__builtin_fabsf(d) * -kLog2e);
         const bool nw = d > 0.0f;
         const float fo = nw ? e : 1.0f;
-        const float fn = (nw ? 1.0f : e) * ch.g[i] * rho;
+        const float fn = (nw ? 1.0f : e) * wkv_grad<G>(ch, i) * rho;
         p = __builtin_fmaf(fo, p, fn);
         q = __builtin_fmaf(fo, q, fn * y);
         r = __builtin_fmaf(fo, r, fn * jj);
@@ -423,6 +458,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   a.seg_rev_z[s * lanes + lane] = zl;
 }
 
+template <bool G>
 __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKernelArgs a) {
   const int64_t lanes = a.B * a.C;
   const int64_t id = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
@@ -459,7 +495,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKe
     acc.za = xw ? 0.0f : acc.za + L;
   }
   float gw_acc = 0.0f, gu_acc = 0.0f;
-  backward_chunks(io, j0, j1, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
+  backward_chunks<G>(io, j0, j1, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
   if (s == 0) {
     initial_state_grad(initial_lane(a, lanes, lane), a.state_in != nullptr, acc, wc, gw_acc,
                        a.gstate_in, lanes, lane);
@@ -556,7 +592,7 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
   const WsLayout l = ws_layout(a.B, a.T, a.C);
   char* base = static_cast<char*>(ws);
   BwdKernelArgs k{a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.gout, a.state_in, a.state_out,
-                  a.gstate_out, a.gk, a.gv, a.gstate_in,
+                  a.gstate_out, a.r, a.gk, a.gv, a.gr, a.gstate_in,
                   reinterpret_cast<float4*>(base + l.ckpt),
                   reinterpret_cast<float*>(base + l.part),
                   reinterpret_cast<float*>(base + l.part) + sp.segments * lanes,
@@ -568,12 +604,22 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     const int64_t blocks = (threads + kBwdThreads - 1) / kBwdThreads;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kBwdThreads);
+    const bool gated = a.r != nullptr;
     if (sp.segments == 1) {
-      hipLaunchKernelGGL(wkv_backward_kernel, grid, block, 0, st, k);
+      if (gated) {
+        hipLaunchKernelGGL(wkv_backward_kernel<true>, grid, block, 0, st, k);
+      } else {
+        hipLaunchKernelGGL(wkv_backward_kernel<false>, grid, block, 0, st, k);
+      }
     } else {
       hipLaunchKernelGGL(wkv_bwd_seg_forward_kernel, grid, block, 0, st, k);
-      hipLaunchKernelGGL(wkv_bwd_seg_sums_kernel, grid, block, 0, st, k);
-      hipLaunchKernelGGL(wkv_bwd_seg_backward_kernel, grid, block, 0, st, k);
+      if (gated) {
+        hipLaunchKernelGGL(wkv_bwd_seg_sums_kernel<true>, grid, block, 0, st, k);
+        hipLaunchKernelGGL(wkv_bwd_seg_backward_kernel<true>, grid, block, 0, st, k);
+      } else {
+        hipLaunchKernelGGL(wkv_bwd_seg_sums_kernel<false>, grid, block, 0, st, k);
+        hipLaunchKernelGGL(wkv_bwd_seg_backward_kernel<false>, grid, block, 0, st, k);
+      }
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -36,8 +36,8 @@
 namespace wkv {
 namespace {
 
-template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED>
-__device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid, Lane (&carry)[V],
+template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED, bool G>
+__device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L, G>& r, int nvalid, Lane (&carry)[V],
                                            const float (&wd)[V], const float (&ub)[V],
                                            const float (&cb)[V], bool fast, Seg (*tot)[LC * V],
                                            typename IoT::elem* __restrict__ op, int64_t C,
@@ -87,15 +87,16 @@ __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L>& r, int nvalid,
 #pragma unroll
   for (int j = 0; j < V; ++j) lane_absorb(pre[j], exc[j], wd[j]);
   // 4. rescan own tokens from the prefix
-  rescan_sel<IoT, V, L, MASKED>(fast, pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+  rescan_sel<IoT, V, L, MASKED, G>(fast, pre, r, wd, ub, cb, nvalid, cvalid, op, C);
 }
 
-template <typename IoT, int V, int LC, int PS, int W, int L>
+template <typename IoT, int V, int LC, int PS, int W, int L, bool G>
 __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
-    const float* __restrict__ state_in, typename IoT::elem* __restrict__ out,
-    float* __restrict__ state_out, int64_t groups_per_row) {
+    const typename IoT::elem* __restrict__ rg, const float* __restrict__ state_in,
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out,
+    int64_t groups_per_row) {
   static_assert(LC * PS == 64, "a wave is LC channel groups by PS sub-chunks");
   constexpr int CH = LC * V;          // channels per workgroup
   constexpr int TL = W * PS * L;      // tokens per tile
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   const int64_t base = b * T * C + cc + static_cast<int64_t>(sub) * L * C;
   const typename IoT::elem* kp = k + base;
   const typename IoT::elem* vp = v + base;
+  const typename IoT::elem* rp = G ? rg + base : nullptr;
   typename IoT::elem* op = out + base;
   const int64_t step = static_cast<int64_t>(TL) * C;
 
@@ -147,27 +149,31 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   // path (the last full tile re-reads itself, a harmless cache hit), so the
   // compiler's counter-based waits stop at the current tile's loads instead
   // of draining the prefetch as well.
-  ChunkRegs<V, L> A, Bf;
-  if (full > 0) chunk_load<IoT, V, L, false>(A, kp, vp, C, L);
+  ChunkRegs<V, L, G> A, Bf;
+  auto at = [&](const typename IoT::elem* p, int64_t t) { return G ? p + t * step : p; };
+  if (full > 0) chunk_load<IoT, V, L, false, G>(A, kp, vp, rp, C, L);
   for (int64_t tile = 0; tile < full; tile += 2) {
     const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
-    chunk_load<IoT, V, L, false>(Bf, kp + nb * step, vp + nb * step, C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, wd, ub, cb, fast, tot[tile & 1],
-                                            op + tile * step, C, cvalid, wave, sl, cl);
+    chunk_load<IoT, V, L, false, G>(Bf, kp + nb * step, vp + nb * step, at(rp, nb), C, L);
+    chunk_tile<IoT, V, LC, PS, W, L, false, G>(A, L, carry, wd, ub, cb, fast, tot[tile & 1],
+                                               op + tile * step, C, cvalid, wave, sl, cl);
     if (tile + 1 >= full) break;
     const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
-    chunk_load<IoT, V, L, false>(A, kp + na * step, vp + na * step, C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, wd, ub, cb, fast, tot[(tile + 1) & 1],
-                                            op + (tile + 1) * step, C, cvalid, wave, sl, cl);
+    chunk_load<IoT, V, L, false, G>(A, kp + na * step, vp + na * step, at(rp, na), C, L);
+    chunk_tile<IoT, V, LC, PS, W, L, false, G>(Bf, L, carry, wd, ub, cb, fast,
+                                               tot[(tile + 1) & 1], op + (tile + 1) * step, C,
+                                               cvalid, wave, sl, cl);
   }
   if (full * TL < T) {  // last, partial tile
     const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
     const int64_t left = T - first;
     const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
-    ChunkRegs<V, L> last;
-    chunk_load<IoT, V, L, true>(last, kp + full * step, vp + full * step, C, nvalid);
-    chunk_tile<IoT, V, LC, PS, W, L, true>(last, nvalid, carry, wd, ub, cb, fast, tot[full & 1],
-                                           op + full * step, C, cvalid, wave, sl, cl);
+    ChunkRegs<V, L, G> last;
+    chunk_load<IoT, V, L, true, G>(last, kp + full * step, vp + full * step, at(rp, full), C,
+                                   nvalid);
+    chunk_tile<IoT, V, LC, PS, W, L, true, G>(last, nvalid, carry, wd, ub, cb, fast,
+                                              tot[full & 1], op + full * step, C, cvalid, wave,
+                                              sl, cl);
   }
 
   if (state_out != nullptr && sub == 0 && cvalid) {
@@ -191,18 +197,25 @@ constexpr int kLC = 32, kPS = 2;
 // Workgroup shape by sequence length (measured on MI355X): short sequences
 // want the fewest serial tiles; long ones want two waves per SIMD to overlap
 // each tile's scan with the neighbours' memory traffic.
-template <typename IoT, int V, int W, int L>
-hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
+template <typename IoT, int V, int W, int L, bool G>
+hipError_t launch_chunk_g(const FwdArgs& a, hipStream_t st) {
   constexpr int CH = kLC * V;
   const int64_t gpr = (a.C + CH - 1) / CH;
   const int64_t blocks = a.B * gpr;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L>),
+  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L, G>),
                      dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0, st, a.B, a.T, a.C,
                      a.w, a.u, static_cast<const typename IoT::elem*>(a.k),
-                     static_cast<const typename IoT::elem*>(a.v), a.state_in,
+                     static_cast<const typename IoT::elem*>(a.v),
+                     static_cast<const typename IoT::elem*>(a.r), a.state_in,
                      static_cast<typename IoT::elem*>(a.out), a.state_out, gpr);
   return hipGetLastError();
+}
+
+template <typename IoT, int V, int W, int L>
+hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
+  return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true>(a, st)
+                        : launch_chunk_g<IoT, V, W, L, false>(a, st);
 }
 
 constexpr int64_t kShortT = 256, kLongT = 2048;
@@ -234,8 +247,8 @@ ChunkShape chunk_shape(int io, int vec, int64_t T) {
 int chunk_vec_width(int io, int64_t C, const FwdArgs& a) {
   if (io != kBf16) return 1;
   const bool ok = C % 2 == 0 && aligned(a.k, 4) && aligned(a.v, 4) && aligned(a.out, 4) &&
-                  aligned(a.w, 8) && aligned(a.u, 8) && aligned(a.state_in, 8) &&
-                  aligned(a.state_out, 8);
+                  aligned(a.r, 4) && aligned(a.w, 8) && aligned(a.u, 8) &&
+                  aligned(a.state_in, 8) && aligned(a.state_out, 8);
   return ok ? 2 : 1;
 }
 

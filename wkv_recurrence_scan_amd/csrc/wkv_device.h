@@ -271,6 +271,13 @@ __device__ __forceinline__ float step_sel(Lane& s, float k, float v, float w, fl
   }
 }
 
+// The receptance gate sigmoid(r) = 1 / (1 + e^-r) on an output; e^-r
+// overflows to +inf for r < -88, giving exactly 0, and underflows to 0 for
+// r > 104, giving exactly 1.
+__device__ __forceinline__ float gate(float r) {
+  return fast_rcp(1.0f + fast_exp2(r * -kLog2e));
+}
+
 // ------------------------------------------------- segment summaries (chunks)
 
 // The state produced by a run of `len` tokens from the empty state, with its

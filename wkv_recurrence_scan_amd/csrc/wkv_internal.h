@@ -18,6 +18,7 @@ struct FwdArgs {
   const float* state_in;  // nullptr: empty state
   void* out;
   float* state_out;       // nullptr: not written
+  const void* r = nullptr;  // receptance, like k; non-null: out = sigmoid(r) * wkv
 };
 
 struct StepArgs {
@@ -28,6 +29,7 @@ struct StepArgs {
   const void* v;
   float* state;
   void* out;
+  const void* r = nullptr;  // receptance, like k; non-null: out = sigmoid(r) * wkv
 };
 
 // Channels per thread each kernel can be built for; the host picks the widest
@@ -72,6 +74,8 @@ struct BwdArgs {
   float* gw;                // [C], summed over the batch
   float* gu;                // [C]
   float* gstate_in;         // nullptr: not wanted
+  const float* r = nullptr; // receptance of a gated output (out = sigmoid(r) * wkv)
+  float* gr = nullptr;      // dL/dr, with r
 };
 // Workspace: per-lane partial sums and per-chunk checkpoints, written before
 // they are read in every launch (no clearing needed).

@@ -124,11 +124,11 @@ __device__ __forceinline__ int64_t lb_offset(int64_t s, int64_t g, int64_t gpr, 
 
 // One segment of one channel group; r holds this thread's tokens of it
 // (loaded by the caller), the first nvalid of them valid.
-template <typename IoT, int V, int W, int L, bool MASKED>
+template <typename IoT, int V, int W, int L, bool MASKED, bool G>
 __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, int64_t B, int64_t T,
                                         int64_t C, const float* __restrict__ w,
                                         const float* __restrict__ u,
-                                        const ChunkRegs<V, L>& r, int nvalid,
+                                        const ChunkRegs<V, L, G>& r, int nvalid,
                                         const float* __restrict__ state_in,
                                         typename IoT::elem* __restrict__ out,
                                         float* __restrict__ state_out, Seg (*tot)[kLbLC * V],
@@ -233,16 +233,16 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   }
   float cb[V];
   bonus_ratios(wd, ub, cb);
-  rescan_sel<IoT, V, L, MASKED>(wave_fast_ok(wd, ub), pre, r, wd, ub, cb, nvalid, cvalid,
-                                out + base, C);
+  rescan_sel<IoT, V, L, MASKED, G>(wave_fast_ok(wd, ub), pre, r, wd, ub, cb, nvalid, cvalid,
+                                   out + base, C);
 }
 
-template <typename IoT, int V, int W, int L>
+template <typename IoT, int V, int W, int L, bool G>
 __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
-    const float* __restrict__ state_in, typename IoT::elem* __restrict__ out,
-    float* __restrict__ state_out, LbArgs a) {
+    const typename IoT::elem* __restrict__ rg, const float* __restrict__ state_in,
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out, LbArgs a) {
   // (state_in is read by segment 0's workgroups before state_out is written
   // by the last segment's, which waited on segment 0 through the published
   // prefixes, so the two may be the same buffer)
@@ -268,26 +268,29 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   // prefetch the likely segment's tile while the ticket is in flight
   const int64_t guess = blockIdx.x / a.groups;
   const bool guess_full = (guess + 1) * TL <= T;
-  ChunkRegs<V, L> r;
+  ChunkRegs<V, L, G> r;
+  auto rat = [&](int64_t off) { return G ? rg + off : rg; };
   if (guess_full) {
     const int64_t off = lb_offset<V, W, L>(guess, g, a.gpr, T, C);
-    chunk_load<IoT, V, L, false>(r, k + off, v + off, C, L);
+    chunk_load<IoT, V, L, false, G>(r, k + off, v + off, rat(off), C, L);
   }
   __syncthreads();
   a.epoch = epoch_s;
   const int64_t s = seg_s;
   const int64_t off = lb_offset<V, W, L>(s, g, a.gpr, T, C);
   if ((s + 1) * TL <= T) {
-    if (!guess_full || s != guess) chunk_load<IoT, V, L, false>(r, k + off, v + off, C, L);
-    lb_tile<IoT, V, W, L, false>(a, s, g, B, T, C, w, u, r, L, state_in, out, state_out, tot, xs,
-                                 fetched);
+    if (!guess_full || s != guess) {
+      chunk_load<IoT, V, L, false, G>(r, k + off, v + off, rat(off), C, L);
+    }
+    lb_tile<IoT, V, W, L, false, G>(a, s, g, B, T, C, w, u, r, L, state_in, out, state_out, tot,
+                                    xs, fetched);
   } else {
     const int sub = (threadIdx.x >> 6) * kLbPS + (threadIdx.x & 63) / kLbLC;
     const int64_t left = T - (s * TL + static_cast<int64_t>(sub) * L);
     const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
-    chunk_load<IoT, V, L, true>(r, k + off, v + off, C, nvalid);
-    lb_tile<IoT, V, W, L, true>(a, s, g, B, T, C, w, u, r, nvalid, state_in, out, state_out, tot,
-                                xs, fetched);
+    chunk_load<IoT, V, L, true, G>(r, k + off, v + off, rat(off), C, nvalid);
+    lb_tile<IoT, V, W, L, true, G>(a, s, g, B, T, C, w, u, r, nvalid, state_in, out, state_out,
+                                   tot, xs, fetched);
   }
 }
 
@@ -339,11 +342,19 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
   la.agg = slots;
   la.inc = slots + items * CH * 3;
   la.epoch = 0;  // derived from the ticket by the kernel
-  hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L>), dim3(static_cast<unsigned>(items)),
-                     dim3(64 * W), 0, st, a.B, a.T, a.C, a.w, a.u,
-                     static_cast<const typename IoT::elem*>(a.k),
-                     static_cast<const typename IoT::elem*>(a.v), a.state_in,
-                     static_cast<typename IoT::elem*>(a.out), a.state_out, la);
+  const auto* kk = static_cast<const typename IoT::elem*>(a.k);
+  const auto* vv = static_cast<const typename IoT::elem*>(a.v);
+  const auto* rr = static_cast<const typename IoT::elem*>(a.r);
+  auto* oo = static_cast<typename IoT::elem*>(a.out);
+  if (rr != nullptr) {
+    hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L, true>),
+                       dim3(static_cast<unsigned>(items)), dim3(64 * W), 0, st, a.B, a.T, a.C,
+                       a.w, a.u, kk, vv, rr, a.state_in, oo, a.state_out, la);
+  } else {
+    hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L, false>),
+                       dim3(static_cast<unsigned>(items)), dim3(64 * W), 0, st, a.B, a.T, a.C,
+                       a.w, a.u, kk, vv, rr, a.state_in, oo, a.state_out, la);
+  }
   return hipGetLastError();
 }
 

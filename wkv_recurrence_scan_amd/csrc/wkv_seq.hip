@@ -20,25 +20,29 @@ namespace {
 
 constexpr int kSeqThreads = 256;
 
-template <typename IoT, int V, int U>
+// U tokens of k, v and, for gated calls (G), the receptance r.
+template <typename IoT, int V, int U, bool G>
 struct SeqBlock {
   float k[U][V];
   float v[U][V];
+  float r[G ? U : 1][V];
 };
 
-template <typename IoT, int V, int U>
-__device__ __forceinline__ void seq_load(SeqBlock<IoT, V, U>& blk,
+template <typename IoT, int V, int U, bool G>
+__device__ __forceinline__ void seq_load(SeqBlock<IoT, V, U, G>& blk,
                                          const typename IoT::elem* __restrict__ kp,
-                                         const typename IoT::elem* __restrict__ vp, int64_t C) {
+                                         const typename IoT::elem* __restrict__ vp,
+                                         const typename IoT::elem* __restrict__ rp, int64_t C) {
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     IoT::template load<V, true>(kp + i * C, blk.k[i]);
     IoT::template load<V, true>(vp + i * C, blk.v[i]);
+    if constexpr (G) IoT::template load<V, true>(rp + i * C, blk.r[i]);
   }
 }
 
-template <typename IoT, int V, int U, bool FAST>
-__device__ __forceinline__ void seq_compute(const SeqBlock<IoT, V, U>& blk, Lane (&s)[V],
+template <typename IoT, int V, int U, bool FAST, bool G>
+__device__ __forceinline__ void seq_compute(const SeqBlock<IoT, V, U, G>& blk, Lane (&s)[V],
                                             const float (&wd)[V], const float (&ub)[V],
                                             const float (&cb)[V],
                                             typename IoT::elem* __restrict__ op, int64_t C) {
@@ -48,51 +52,58 @@ __device__ __forceinline__ void seq_compute(const SeqBlock<IoT, V, U>& blk, Lane
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       o[j] = step_sel<FAST>(s[j], blk.k[i][j], blk.v[i][j], wd[j], ub[j], cb[j]);
+      if constexpr (G) o[j] *= gate(blk.r[i][j]);
     }
     IoT::template store<V, true>(op + i * C, o);
   }
 }
 
 // All T tokens of one thread's channels, in order.
-template <typename IoT, int V, int U, bool FAST>
+template <typename IoT, int V, int U, bool FAST, bool G>
 __device__ __forceinline__ void seq_walk(Lane (&s)[V], const float (&wd)[V], const float (&ub)[V],
                                          const float (&cb)[V],
                                          const typename IoT::elem* __restrict__ kp,
                                          const typename IoT::elem* __restrict__ vp,
+                                         const typename IoT::elem* __restrict__ rp,
                                          typename IoT::elem* __restrict__ op, int64_t T,
                                          int64_t C) {
   // Two register buffers, alternating; the loads for the block after the one
   // being computed are issued first, on every path (the last full block
   // re-reads itself, a cache hit), so that the compiler's counter-based waits
   // only ever wait for the block about to be used.
-  SeqBlock<IoT, V, U> A, Bf;
+  SeqBlock<IoT, V, U, G> A, Bf;
+  auto at = [&](int64_t t) { return G ? rp + t * C : rp; };
   const int64_t nblk = T / U;
-  if (nblk > 0) seq_load<IoT, V, U>(A, kp, vp, C);
+  if (nblk > 0) seq_load<IoT, V, U, G>(A, kp, vp, rp, C);
   for (int64_t blk = 0; blk < nblk; blk += 2) {
     const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
-    seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, C);
-    seq_compute<IoT, V, U, FAST>(A, s, wd, ub, cb, op + blk * U * C, C);
+    seq_load<IoT, V, U, G>(Bf, kp + nb * C, vp + nb * C, at(nb), C);
+    seq_compute<IoT, V, U, FAST, G>(A, s, wd, ub, cb, op + blk * U * C, C);
     if (blk + 1 >= nblk) break;
     const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
-    seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, C);
-    seq_compute<IoT, V, U, FAST>(Bf, s, wd, ub, cb, op + (blk + 1) * U * C, C);
+    seq_load<IoT, V, U, G>(A, kp + na * C, vp + na * C, at(na), C);
+    seq_compute<IoT, V, U, FAST, G>(Bf, s, wd, ub, cb, op + (blk + 1) * U * C, C);
   }
   for (int64_t t = nblk * U; t < T; ++t) {
-    float kk[V], vv[V], o[V];
+    float kk[V], vv[V], rr[V], o[V];
     IoT::template load<V, true>(kp + t * C, kk);
     IoT::template load<V, true>(vp + t * C, vv);
+    if constexpr (G) IoT::template load<V, true>(rp + t * C, rr);
 #pragma unroll
-    for (int j = 0; j < V; ++j) o[j] = step_sel<FAST>(s[j], kk[j], vv[j], wd[j], ub[j], cb[j]);
+    for (int j = 0; j < V; ++j) {
+      o[j] = step_sel<FAST>(s[j], kk[j], vv[j], wd[j], ub[j], cb[j]);
+      if constexpr (G) o[j] *= gate(rr[j]);
+    }
     IoT::template store<V, true>(op + t * C, o);
   }
 }
 
-template <typename IoT, int V, int U>
+template <typename IoT, int V, int U, bool G>
 __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
-    const float* __restrict__ state_in, typename IoT::elem* __restrict__ out,
-    float* __restrict__ state_out) {
+    const typename IoT::elem* __restrict__ rg, const float* __restrict__ state_in,
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out) {
   const int64_t groups_per_row = C / V;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kSeqThreads + threadIdx.x;
   if (gid >= B * groups_per_row) return;
@@ -121,14 +132,15 @@ __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
   const int64_t row = b * T * C + c0;
   const typename IoT::elem* kp = k + row;
   const typename IoT::elem* vp = v + row;
+  const typename IoT::elem* rp = G ? rg + row : nullptr;
   typename IoT::elem* op = out + row;
 
   float cb[V];
   bonus_ratios(wd, ub, cb);
   if (wave_fast_ok(wd, ub)) {
-    seq_walk<IoT, V, U, true>(s, wd, ub, cb, kp, vp, op, T, C);
+    seq_walk<IoT, V, U, true, G>(s, wd, ub, cb, kp, vp, rp, op, T, C);
   } else {
-    seq_walk<IoT, V, U, false>(s, wd, ub, cb, kp, vp, op, T, C);
+    seq_walk<IoT, V, U, false, G>(s, wd, ub, cb, kp, vp, rp, op, T, C);
   }
 
   if (state_out != nullptr) {
@@ -145,18 +157,24 @@ __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
   }
 }
 
-template <typename IoT, int V>
-hipError_t launch_seq_t(const FwdArgs& a, hipStream_t st) {
+template <typename IoT, int V, bool G>
+hipError_t launch_seq_g(const FwdArgs& a, hipStream_t st) {
   constexpr int U = 8;
   const int64_t threads = a.B * (a.C / V);
   const int64_t blocks = (threads + kSeqThreads - 1) / kSeqThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_seq_kernel<IoT, V, U>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((wkv_seq_kernel<IoT, V, U, G>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kSeqThreads), 0, st, a.B, a.T, a.C, a.w, a.u,
                      static_cast<const typename IoT::elem*>(a.k),
-                     static_cast<const typename IoT::elem*>(a.v), a.state_in,
+                     static_cast<const typename IoT::elem*>(a.v),
+                     static_cast<const typename IoT::elem*>(a.r), a.state_in,
                      static_cast<typename IoT::elem*>(a.out), a.state_out);
   return hipGetLastError();
+}
+
+template <typename IoT, int V>
+hipError_t launch_seq_t(const FwdArgs& a, hipStream_t st) {
+  return a.r != nullptr ? launch_seq_g<IoT, V, true>(a, st) : launch_seq_g<IoT, V, false>(a, st);
 }
 
 bool aligned(const void* p, int bytes) {
@@ -176,6 +194,7 @@ int seq_vec_width(int io, int64_t C, const FwdArgs& a) {
     const int V = c[i];
     if (C % V) continue;
     if (!aligned(a.k, V * elem) || !aligned(a.v, V * elem) || !aligned(a.out, V * elem)) continue;
+    if (!aligned(a.r, V * elem)) continue;
     if (!aligned(a.w, V * 4) || !aligned(a.u, V * 4)) continue;
     if (!aligned(a.state_in, V * 4) || !aligned(a.state_out, V * 4)) continue;
     return V;

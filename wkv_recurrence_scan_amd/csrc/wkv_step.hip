@@ -17,11 +17,12 @@ namespace {
 
 constexpr int kStepThreads = 256;
 
-template <typename IoT, int V>
+template <typename IoT, int V, bool G>
 __global__ __launch_bounds__(kStepThreads) void wkv_step_kernel(
     int64_t B, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
-    float* __restrict__ state, typename IoT::elem* __restrict__ out) {
+    const typename IoT::elem* __restrict__ rg, float* __restrict__ state,
+    typename IoT::elem* __restrict__ out) {
   const int64_t groups_per_row = C / V;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kStepThreads + threadIdx.x;
   if (gid >= B * groups_per_row) return;
@@ -30,11 +31,12 @@ __global__ __launch_bounds__(kStepThreads) void wkv_step_kernel(
   const int64_t lane0 = b * C + c0;
   const int64_t plane = B * C;
 
-  float ww[V], uu[V], kk[V], vv[V], n[V], d[V], m[V], o[V];
+  float ww[V], uu[V], kk[V], vv[V], rr[V], n[V], d[V], m[V], o[V];
   IoF32::load<V, false>(w + c0, ww);
   IoF32::load<V, false>(u + c0, uu);
   IoT::template load<V, true>(k + lane0, kk);
   IoT::template load<V, true>(v + lane0, vv);
+  if constexpr (G) IoT::template load<V, true>(rg + lane0, rr);
   IoF32::load<V, false>(state + lane0, n);
   IoF32::load<V, false>(state + plane + lane0, d);
   IoF32::load<V, false>(state + 2 * plane + lane0, m);
@@ -47,6 +49,7 @@ __global__ __launch_bounds__(kStepThreads) void wkv_step_kernel(
     const float fa = cur_wins ? x : 1.0f;
     const float fb = cur_wins ? 1.0f : x;
     o[j] = __builtin_fmaf(fa, n[j], fb * vv[j]) * fast_rcp(__builtin_fmaf(fa, d[j], fb));
+    if constexpr (G) o[j] *= gate(rr[j]);
     // advance: decayed state against the current token without the bonus
     const float md = m[j] - ww[j];
     const float t2 = kk[j] - md;
@@ -69,11 +72,17 @@ hipError_t launch_step_t(const StepArgs& a, hipStream_t st) {
   const int64_t threads = a.B * (a.C / V);
   const int64_t blocks = (threads + kStepThreads - 1) / kStepThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_step_kernel<IoT, V>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kStepThreads), 0, st, a.B, a.C, a.w, a.u,
-                     static_cast<const typename IoT::elem*>(a.k),
-                     static_cast<const typename IoT::elem*>(a.v), a.state,
-                     static_cast<typename IoT::elem*>(a.out));
+  const auto* k = static_cast<const typename IoT::elem*>(a.k);
+  const auto* v = static_cast<const typename IoT::elem*>(a.v);
+  const auto* r = static_cast<const typename IoT::elem*>(a.r);
+  auto* out = static_cast<typename IoT::elem*>(a.out);
+  if (r != nullptr) {
+    hipLaunchKernelGGL((wkv_step_kernel<IoT, V, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kStepThreads), 0, st, a.B, a.C, a.w, a.u, k, v, r, a.state, out);
+  } else {
+    hipLaunchKernelGGL((wkv_step_kernel<IoT, V, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kStepThreads), 0, st, a.B, a.C, a.w, a.u, k, v, r, a.state, out);
+  }
   return hipGetLastError();
 }
 
@@ -100,6 +109,7 @@ int step_vec_width(int io, int64_t C, const StepArgs& a) {
   for (int V : {4, 2, 1}) {
     if (C % V) continue;
     if (!aligned(a.k, V * elem) || !aligned(a.v, V * elem) || !aligned(a.out, V * elem)) continue;
+    if (!aligned(a.r, V * elem)) continue;
     if (!aligned(a.w, V * 4) || !aligned(a.u, V * 4) || !aligned(a.state, V * 4)) continue;
     return V;
   }

@@ -52,27 +52,34 @@ __device__ __forceinline__ Seg summarize(const float (&kk)[L], const float (&vv)
   return Seg{n, d, top, MASKED ? static_cast<float>(nvalid) : static_cast<float>(L)};
 }
 
-template <int V, int L>
+// One thread's tokens of a tile: k, v and, for gated calls (G), the
+// receptance r.
+template <int V, int L, bool G = false>
 struct ChunkRegs {
   float k[L][V];
   float v[L][V];
+  float r[G ? L : 1][V];
 };
 
-template <typename IoT, int V, int L, bool MASKED>
-__device__ __forceinline__ void chunk_load(ChunkRegs<V, L>& r,
+// rp is read only when G.
+template <typename IoT, int V, int L, bool MASKED, bool G>
+__device__ __forceinline__ void chunk_load(ChunkRegs<V, L, G>& r,
                                            const typename IoT::elem* __restrict__ kp,
-                                           const typename IoT::elem* __restrict__ vp, int64_t C,
+                                           const typename IoT::elem* __restrict__ vp,
+                                           const typename IoT::elem* __restrict__ rp, int64_t C,
                                            int nvalid) {
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     if (!MASKED || i < nvalid) {
       IoT::template load<V, false>(kp + i * C, r.k[i]);
       IoT::template load<V, false>(vp + i * C, r.v[i]);
+      if constexpr (G) IoT::template load<V, false>(rp + i * C, r.r[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         r.k[i][j] = 0.0f;
         r.v[i][j] = 0.0f;
+        if constexpr (G) r.r[i][j] = 0.0f;
       }
     }
   }
@@ -84,8 +91,8 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<V, L>& r,
 // the totals of the waves before its own (before) and the whole tile
 // (whole). tot is LDS scratch of W x CH segments; the call synchronises the
 // workgroup once.
-template <int V, int LC, int PS, int W, int L, bool MASKED>
-__device__ __forceinline__ void tile_scan(const ChunkRegs<V, L>& r, const float (&wd)[V], int nvalid,
+template <int V, int LC, int PS, int W, int L, bool MASKED, bool G>
+__device__ __forceinline__ void tile_scan(const ChunkRegs<V, L, G>& r, const float (&wd)[V], int nvalid,
                                           Seg (*tot)[LC * V], Seg (&exc)[V], Seg (&before)[V],
                                           Seg (&whole)[V]) {
   const int wave = threadIdx.x >> 6;
@@ -135,9 +142,10 @@ __device__ __forceinline__ void tile_scan(const ChunkRegs<V, L>& r, const float 
 }
 
 // Re-runs the recurrence over one thread's sub-chunk from the state in front
-// of it and writes the outputs. FAST selects lane_step_fast.
-template <typename IoT, int V, int L, bool MASKED, bool FAST>
-__device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L>& r,
+// of it and writes the outputs (gated by sigmoid(r) when G). FAST selects
+// lane_step_fast.
+template <typename IoT, int V, int L, bool MASKED, bool FAST, bool G>
+__device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L, G>& r,
                                        const float (&wd)[V], const float (&ub)[V],
                                        const float (&cb)[V], int nvalid, bool cvalid,
                                        typename IoT::elem* __restrict__ op, int64_t C) {
@@ -150,21 +158,22 @@ __device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L>& r,
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         o[j] = step_sel<FAST>(pre[j], r.k[i][j], r.v[i][j], wd[j], ub[j], cb[j]);
+        if constexpr (G) o[j] *= gate(r.r[i][j]);
       }
       if (cvalid) IoT::template store<V, true>(op + i * C, o);
     }
   }
 }
 
-template <typename IoT, int V, int L, bool MASKED>
-__device__ __forceinline__ void rescan_sel(bool fast, Lane (&pre)[V], const ChunkRegs<V, L>& r,
+template <typename IoT, int V, int L, bool MASKED, bool G>
+__device__ __forceinline__ void rescan_sel(bool fast, Lane (&pre)[V], const ChunkRegs<V, L, G>& r,
                                            const float (&wd)[V], const float (&ub)[V],
                                            const float (&cb)[V], int nvalid, bool cvalid,
                                            typename IoT::elem* __restrict__ op, int64_t C) {
   if (fast) {
-    rescan<IoT, V, L, MASKED, true>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+    rescan<IoT, V, L, MASKED, true, G>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
   } else {
-    rescan<IoT, V, L, MASKED, false>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+    rescan<IoT, V, L, MASKED, false, G>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
   }
 }
 

@@ -30,7 +30,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 # tensor ids inside a seed
-_K, _V, _W, _U, _SPIKE_MASK, _SPIKE_SIGN, _DEC_K, _DEC_V, _GOUT = 1, 2, 3, 4, 5, 6, 7, 8, 9
+_K, _V, _W, _U, _SPIKE_MASK, _SPIKE_SIGN, _DEC_K, _DEC_V, _GOUT, _R = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -202,3 +202,19 @@ def grad_out(wl: Workload, layer: int = 0, rows: Optional[Sequence[int]] = None,
 
     _map_rows(one, range(len(rows)))
     return g
+
+
+def receptance(wl: Workload, layer: int = 0, rows: Optional[Sequence[int]] = None,
+               T: Optional[int] = None) -> np.ndarray:
+    """Receptance for the gated output: N(0, 1) float32 (B_rows, T, C), rounded
+    to bf16 for bf16 workloads, one independent stream per batch row."""
+    rows = list(range(wl.B) if rows is None else rows)
+    T = wl.T if T is None else T
+    r = np.empty((len(rows), T, wl.C), np.float32)
+
+    def one(i):
+        rr = _values_row(wl, layer, rows[i], T, _R)
+        r[i] = round_to_bf16(rr) if wl.io == "bf16" else rr
+
+    _map_rows(one, range(len(rows)))
+    return r
