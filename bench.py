@@ -15,6 +15,8 @@ Default run (one JSON line on stdout):
     w, u).
   * decode: 1024 consecutive wkv_step calls at B=256, C=768 after a T=512
     prefill; steps/s for eager launches and for one HIP graph of all 1024.
+  * gated_forward: wkv_forward_gated (out = sigmoid(r) * wkv) on one layer of
+    the prefill shape.
   * backward: wkv_backward (the gradients) on one layer of the prefill shape
     and on the decode workload's B=256 T=512 prefill shape, with the
     roofline on its algorithmic bytes (read k, v, dL/dout; write dL/dk,
@@ -259,6 +261,46 @@ def time_backward(wl, dev, reps=10):
             "workspace_bytes": int(ws.numel())}
 
 
+def time_gated(wl, dev, path, reps=50):
+    """wkv_forward_gated (out = sigmoid(r) * wkv) on workload wl's first
+    layer: microseconds per call from an event pair around `reps`
+    back-to-back calls, and the roofline on its algorithmic bytes (read k,
+    v, r; write out and the final state; read w, u)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    w, u = I.params(wl)
+    k, v = I.kv(wl)
+    r = I.receptance(wl)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    dw, du, dk, dv, dr = t(w), t(u), t(k), t(v), t(r)
+    del k, v, r
+    out = torch.empty_like(dk)
+    st = torch.empty((3, wl.B, wl.C), dtype=torch.float32, device=dev)
+    call = lambda: W.wkv_forward_gated(dw, du, dk, dv, dr, out=out, state_out=st, path=path)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ct = wl.B * wl.T * wl.C
+    abytes = 16 * ct + 12 * wl.B * wl.C + 8 * wl.C
+    achieved = abytes / (us * 1e-6) / 1e9
+    return {"workload": f"{wl.name}, one layer, gated output", "path": path,
+            "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
+            "us_per_call": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": abytes}}
+
+
 def measured_traffic(workload_key, path):
     """HBM bytes per launch from the rocprofv3 counter summaries under
     profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
@@ -424,6 +466,8 @@ def main():
         }
 
     if args.config == 1 and not args.no_backward:
+        _log("gated forward: one layer")
+        rec["gated_forward"] = time_gated(wl.scaled(layers=1), dev, path_used)
         rec["backward"] = []
         for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
             _log(f"backward: {bwl.name} (one layer)")
