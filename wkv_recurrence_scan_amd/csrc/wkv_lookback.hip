@@ -9,7 +9,9 @@
 // are read from HBM once.
 //
 // A workgroup:
-//   1. serves channel group blockIdx % G and takes that group's next segment
+//   1. serves a channel group (one block per group in every row of G blocks,
+//      the group shifting from row to row so that every XCD sees every
+//      group) and takes that group's next segment
 //      from the group's own ticket counter, so every segment it will wait for
 //      was taken by a workgroup that has already started: no co-residency or
 //      dispatch order is assumed and no wait can deadlock (per-group counters
@@ -252,12 +254,18 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   __shared__ Seg fetched[anchor_spacing<V, W>()][CH];
   __shared__ uint32_t seg_s, epoch_s;
 
-  // Work assignment per channel group: block i serves group i % G and takes
-  // the group's next segment from the group's own ticket counter, so within a
-  // group segments are handed out in start order (every segment a workgroup
-  // waits for belongs to a workgroup that has already started) and the
-  // counters' atomics are spread over G addresses.
-  const int64_t g = blockIdx.x % a.groups;
+  // Work assignment per channel group: block i of row q = i / G serves group
+  // (i + q) mod G and takes the group's next segment from the group's own
+  // ticket counter, so within a group segments are handed out in start order
+  // (every segment a workgroup waits for belongs to a workgroup that has
+  // already started) and the counters' atomics are spread over G addresses.
+  // Blocks are dealt to the 8 XCDs round-robin; the shift by the row moves
+  // each group to another XCD from one row to the next, so every XCD sees
+  // every channel group. (Without it a group, and so one fixed column of the
+  // tensors, stays on one XCD: measured on MI355X, columns that stream more
+  // slowly than the rest then put a whole XCD's queue behind.)
+  const int64_t row = blockIdx.x / a.groups;
+  const int64_t g = (blockIdx.x + row) % a.groups;
   const int64_t S = a.segments;
   if (threadIdx.x == 0) {
     const uint64_t t =
@@ -265,8 +273,9 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
     seg_s = static_cast<uint32_t>(t % static_cast<uint64_t>(S));
     epoch_s = static_cast<uint32_t>((t / static_cast<uint64_t>(S)) % 0xffffffffull) + 1u;
   }
-  // prefetch the likely segment's tile while the ticket is in flight
-  const int64_t guess = blockIdx.x / a.groups;
+  // prefetch the likely segment's tile while the ticket is in flight: the
+  // group's blocks are one per row, so this block is most likely its row-th
+  const int64_t guess = row;
   const bool guess_full = (guess + 1) * TL <= T;
   ChunkRegs<V, L, G> r;
   auto rat = [&](int64_t off) { return G ? rg + off : rg; };
