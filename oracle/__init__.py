@@ -8,10 +8,13 @@ parity pins: every forward function here is pinned by tests/test_oracle.py
 against the mpmath brute force, closed forms of the defining equation,
 invariants and special cases that reduce to a softmax; the gradients
 (wkv_grad) by tests/test_oracle_grad.py against central finite differences
-of the pinned forward and by invariants of the operator. None is "parity
-unpinned".
+of the pinned forward and by invariants of the operator; the per-token-decay
+operator (wkv_decay) by tests/test_oracle_decay.py against its own mpmath
+recurrence, the constant-decay operator, a hand-worked case and invariants.
+None is "parity unpinned".
 """
 
+from .wkv_decay import wkv_dd_direct, wkv_dd_recurrent, wkv_dd_step_ref  # noqa: F401
 from .wkv_grad import wkv_backward_direct, wkv_gated_backward_direct  # noqa: F401
 from .wkv_oracle import (  # noqa: F401
     EMPTY_MAX_EXP,

@@ -76,3 +76,54 @@ def wkv_brute(w, u, k, v, state_in=None, dps: int = 50):
                 D = sum((dc * exp(e - top) for e, _, dc in terms), mpf(0))
                 state[:, b, c] = (float(N), float(D), float(top))
     return out, state
+
+
+def wkv_dd_brute(w, u, k, v, state_in=None, dps: int = 50):
+    """The per-token-decay operator (oracle/wkv_decay.py) in 50-digit mpmath,
+    written as a linear recurrence on the raw sums rather than as a sum over
+    tokens: before step t the numerator and denominator sums are multiplied by
+    the factor exp(-w_t) and the token is added with weight exp(k_t); the
+    output of step t is formed from the sums before that multiplication plus
+    the current token at exp(u + k_t). No maximum is factored out (mpmath's
+    exponent range makes that unnecessary).
+
+    Returns (out, state_out) rounded to float64, state_out as
+    (N e^-M, D e^-M, M) with M the largest exponent among the terms present,
+    tracked alongside the sums."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    B, T, C = k.shape
+    if state_in is None:
+        n0, d0, m0 = np.zeros((B, C)), np.zeros((B, C)), np.full((B, C), -1e38)
+    else:
+        n0, d0, m0 = (np.asarray(p, dtype=np.float64) for p in state_in)
+    out = np.empty((B, T, C))
+    state = np.empty((3, B, C))
+    with mpmath.workdps(dps):
+        mpf, exp = mpmath.mpf, mpmath.exp
+        for b in range(B):
+            for c in range(C):
+                has_state = d0[b, c] != 0.0 or n0[b, c] != 0.0
+                if has_state:
+                    N = mpf(n0[b, c]) * exp(mpf(m0[b, c]))
+                    D = mpf(d0[b, c]) * exp(mpf(m0[b, c]))
+                    top = mpf(m0[b, c])
+                else:
+                    N, D, top = mpf(0), mpf(0), None
+                uc = mpf(u[c])
+                for t in range(T):
+                    kt, vt = mpf(k[b, t, c]), mpf(v[b, t, c])
+                    f = exp(uc + kt)
+                    out[b, t, c] = float((N + f * vt) / (D + f))
+                    decay = exp(-mpf(w[b, t, c]))
+                    g = exp(kt)
+                    N = N * decay + g * vt
+                    D = D * decay + g
+                    top = kt if top is None else max(top - mpf(w[b, t, c]), kt)
+                if top is None:
+                    state[:, b, c] = (0.0, 0.0, -1e38)
+                else:
+                    state[:, b, c] = (float(N / exp(top)), float(D / exp(top)), float(top))
+    return out, state
