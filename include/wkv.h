@@ -224,6 +224,34 @@ int wkv_step_gated(int64_t B, int64_t C, const float* w, const float* u, const v
                    const void* v, const void* r, float* state, void* out, int io,
                    hipStream_t stream);
 
+/* Prefill with a per-token (data-dependent) decay (page "RWKV-v6
+ * Architecture: Attention-Free Linear Transformers", section "The Core
+ * Components of the RWKV-v6 Time-Mixing Block", items on the dynamic
+ * data-dependent decay and the matrix-valued state: step t decays the state
+ * carried in from step t-1 before its own term is added). Step t multiplies
+ * the state by e^(-w[b][t][c]); the output uses the state before that decay
+ * plus the current token at e^(u + k), as in wkv_forward. With w[b][t][c] = w[c]
+ * for every t this is wkv_forward.
+ *
+ *   w          [B][T][C] positive rates, element type io (like k), required
+ *              when T > 0. It must not overlap out or state_out.
+ *   u, k, v, state_in, out, state_out, io, stream: as wkv_forward_ex.
+ *   path       WKV_PATH_AUTO, WKV_PATH_SEQ or WKV_PATH_CHUNK (no look-back
+ *              kernel for this operator: WKV_PATH_LOOKBACK gives WKV_ERR_ARG).
+ * Running maxima and accumulated rates are carried in fp64 inside the
+ * kernels (the per-token rate rules out the constant-decay kernels' exact
+ * integer ages); everything else is fp32. */
+int wkv_forward_dd(int64_t B, int64_t T, int64_t C, const void* w, const float* u,
+                   const void* k, const void* v, const float* state_in, void* out,
+                   float* state_out, int io, int path, hipStream_t stream);
+
+/* One decode step with this step's own rates w ([B][C], element type io, like
+ * k): out = the state mixed with the token at e^(u + k); then the state decays
+ * by e^(-w) and the token is added at e^k. k, v, out of element type io; the
+ * state is fp32, updated in place. Overlaps as wkv_step. */
+int wkv_step_dd(int64_t B, int64_t C, const void* w, const float* u, const void* k,
+                const void* v, float* state, void* out, int io, hipStream_t stream);
+
 /* Static, NUL-terminated name of a wkv_status code. */
 const char* wkv_status_string(int status);
 

@@ -146,6 +146,40 @@ def test_gated_entry_points_validate_without_device():
     assert lib.wkv_step_gated(2, 4, w, u, k, v, r, P(a + 65536), out, 3, nul) == 7
 
 
+def test_per_token_decay_entry_points_validate_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    a = 0x10000000
+    w, u, k, v = P(a), P(a + 4096), P(a + 8192), P(a + 12288)
+    out = P(a + 16384)
+    # B, T, C, w, u, k, v, state_in, out, state_out, io, path, stream
+    assert lib.wkv_forward_dd(1, 4, 4, w, u, k, v, nul, out, nul, 0, 3, nul) == 7  # no look-back
+    assert lib.wkv_forward_dd(1, 4, 4, w, u, k, v, nul, out, nul, 2, 0, nul) == 7
+    assert lib.wkv_forward_dd(-1, 4, 4, w, u, k, v, nul, out, nul, 0, 0, nul) == 2
+    assert lib.wkv_forward_dd(0, 4, 4, nul, nul, nul, nul, nul, nul, nul, 0, 0, nul) == 0
+    assert lib.wkv_forward_dd(1, 4, 4, nul, u, k, v, nul, out, nul, 0, 0, nul) == 1
+    assert lib.wkv_forward_dd(1, 4, 4, w, u, k, v, nul, w, nul, 0, 0, nul) == 4
+    assert lib.wkv_forward_dd(1, 4, 4, P(a + 2), u, k, v, nul, out, nul, 0, 0, nul) == 3
+    # B, C, w, u, k, v, state, out, io, stream
+    assert lib.wkv_step_dd(2, 4, nul, u, k, v, P(a + 65536), out, 0, nul) == 1
+    assert lib.wkv_step_dd(2, 4, w, u, k, v, P(a + 65536), w, 0, nul) == 4
+    assert lib.wkv_step_dd(2, 4, w, u, k, v, P(a + 65536), out, 5, nul) == 7
+
+
+def test_per_token_decay_rates_are_seeded_and_positive():
+    wl = I.WORKLOADS[1].scaled(B=3, T=50, C=32)
+    r1 = I.decay_rates(wl)
+    r2 = I.decay_rates(wl, rows=[1])
+    assert np.array_equal(r1[1], r2[0]) and (r1 > 0).all()
+    wc, _ = I.params(wl)
+    ratio = np.log(r1 / wc[None, None, :])
+    assert abs(ratio.std() - I.DD_LOG_STD) < 0.02 and abs(ratio.mean()) < 0.02
+    rb = I.decay_rates(I.WORKLOADS[4].scaled(B=1, T=8, C=16))
+    assert np.array_equal(I.round_to_bf16(rb), rb)
+    assert I.decode_decay_rates(I.WORKLOADS[2].scaled(B=2, C=8), steps=5).shape == (5, 2, 8)
+
+
 def test_inputs_are_seeded_and_row_independent():
     wl = I.WORKLOADS[3].scaled(B=3, T=20, C=16)
     k1, v1 = I.kv(wl)

@@ -9,6 +9,7 @@ into that interface (see _lib). Build the library with
     out, state = wkv_forward_bf16(w, u, k, v)       # prefill, bfloat16 I/O
     y = wkv_step(w, u, k_t, v_t, state)             # decode, state in place
     gw, gu, gk, gv, gs = wkv_backward(w, u, k, v, gout)  # gradients
+    out, state = wkv_forward_dd(w_t, u, k, v)     # per-token decay w_t (B, T, C)
 """
 
 from ._lib import (  # noqa: F401
@@ -31,6 +32,7 @@ from ._lib import (  # noqa: F401
     wkv_backward_workspace_size,
     wkv_forward,
     wkv_forward_bf16,
+    wkv_forward_dd,
     wkv_forward_ex,
     wkv_forward_gated,
     wkv_forward_ws,
@@ -38,6 +40,7 @@ from ._lib import (  # noqa: F401
     wkv_status_string,
     wkv_step,
     wkv_step_bf16,
+    wkv_step_dd,
     wkv_step_gated,
     wkv_workspace_size,
 )

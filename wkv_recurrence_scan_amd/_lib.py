@@ -68,6 +68,8 @@ def load_library() -> ctypes.CDLL:
         "wkv_forward_gated": [i64, i64, i64] + [vp] * 8 + [ci, ci, vp, i64, vp],
         "wkv_step_gated": [i64, i64] + [vp] * 7 + [ci, vp],
         "wkv_backward_workspace_size": [i64, i64, i64],
+        "wkv_forward_dd": [i64, i64, i64] + [vp] * 7 + [ci, ci, vp],
+        "wkv_step_dd": [i64, i64] + [vp] * 6 + [ci, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -430,6 +432,70 @@ def wkv_step_gated(w, u, k, v, r, state, out=None, stream=None):
         st = lib.wkv_step_gated(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r), _ptr(state),
                                 _ptr(out), io, _stream_handle(dev, stream))
     _check(st, "wkv_step_gated")
+    return out
+
+
+def wkv_forward_dd(w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",
+                   want_state=True, stream=None):
+    """wkv_forward_dd: prefill with a per-token decay. w, k, v: (B, T, C) of one
+    dtype (float32 or bfloat16; out gets it too), w > 0 the rate of each step;
+    u: (C,) float32; states (3, B, C) float32. path: "auto", "seq" or "chunk".
+    Returns (out, state_out)."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"k must be float32 or bfloat16, got {k.dtype}")
+    if path not in ("auto", "seq", "chunk"):
+        raise ValueError("path must be one of auto, seq, chunk")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    for name, t in (("v", v), ("w", w)):
+        _need(t, name, k.dtype, (B, T, C), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=k.dtype, device=dev)
+    _need(out, "out", k.dtype, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (3, B, C), dev)
+    io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
+    with torch.cuda.device(dev):
+        st = lib.wkv_forward_dd(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                                _ptr(out), _ptr(state_out), io, _PATHS[path],
+                                _stream_handle(dev, stream))
+    _check(st, "wkv_forward_dd")
+    return out, state_out
+
+
+def wkv_step_dd(w, u, k, v, state, out=None, *, stream=None):
+    """wkv_step_dd: one decode step with this step's rates w; w, k, v, out (B, C)
+    of one dtype (float32 or bfloat16); u (C,) float32; the fp32 state (3, B, C)
+    is updated in place. Returns out."""
+    lib = load_library()
+    if k.dim() != 2:
+        raise ValueError(f"k must be (B, C), got shape {tuple(k.shape)}")
+    B, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    for name, t in (("v", v), ("w", w)):
+        _need(t, name, k.dtype, (B, C), dev)
+    _need(u, "u", torch.float32, (C,), dev)
+    _need(state, "state", torch.float32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, C), dtype=k.dtype, device=dev)
+    _need(out, "out", k.dtype, (B, C), dev)
+    io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
+    with torch.cuda.device(dev):
+        st = lib.wkv_step_dd(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state), _ptr(out), io,
+                             _stream_handle(dev, stream))
+    _check(st, "wkv_step_dd")
     return out
 
 

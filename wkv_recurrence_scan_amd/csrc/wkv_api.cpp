@@ -193,6 +193,86 @@ int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* 
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
 
+// Per-token decay: w is a sequence like k (same element type), u per channel.
+int forward_dd_impl(int64_t B, int64_t T, int64_t C, const void* w, const float* u, const void* k,
+                    const void* v, const float* state_in, void* out, float* state_out, int io,
+                    int path, hipStream_t stream) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
+  if (path != WKV_PATH_AUTO && path != WKV_PATH_SEQ && path != WKV_PATH_CHUNK) return WKV_ERR_ARG;
+  if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+  const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
+  int64_t seq_bytes, state_bytes;
+  if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, es, &seq_bytes) ||
+      seq_bytes > kMaxBytes)
+    return WKV_ERR_DIM;
+  if (!mul3(B, C, 12, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (B == 0 || C == 0) return WKV_OK;
+  if (u == nullptr) return WKV_ERR_NULL;
+  if (T > 0 && (w == nullptr || k == nullptr || v == nullptr || out == nullptr))
+    return WKV_ERR_NULL;
+  if (misaligned(u, 4) || misaligned(state_in, 4) || misaligned(state_out, 4))
+    return WKV_ERR_ALIGN;
+  if (misaligned(w, es) || misaligned(k, es) || misaligned(v, es) || misaligned(out, es))
+    return WKV_ERR_ALIGN;
+  const int64_t pbytes = C * 4;
+  const int64_t sbytes = T > 0 ? seq_bytes : 0;
+  if (overlaps(out, sbytes, w, sbytes) || overlaps(out, sbytes, k, sbytes) ||
+      overlaps(out, sbytes, v, sbytes) || overlaps(out, sbytes, u, pbytes) ||
+      overlaps(out, sbytes, state_in, state_bytes) || overlaps(out, sbytes, state_out, state_bytes))
+    return WKV_ERR_ALIAS;
+  if (overlaps(state_out, state_bytes, w, sbytes) || overlaps(state_out, state_bytes, k, sbytes) ||
+      overlaps(state_out, state_bytes, v, sbytes) || overlaps(state_out, state_bytes, u, pbytes))
+    return WKV_ERR_ALIAS;
+  if (state_out != state_in && overlaps(state_out, state_bytes, state_in, state_bytes))
+    return WKV_ERR_ALIAS;
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  if (T == 0) {
+    if (state_out == nullptr || state_out == state_in) return WKV_OK;
+    e = wkv::launch_state_copy(B, C, state_in, state_out, stream);
+    return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+  }
+  const wkv::DdArgs a{B, T, C, w, u, k, v, state_in, out, state_out};
+  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, false);
+  const int vec = wkv::dd_vec_width(io, C, a);
+  e = path == WKV_PATH_SEQ ? wkv::launch_dd_seq(a, io, vec, stream)
+                           : wkv::launch_dd_chunk(a, io, vec, stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
+int step_dd_impl(int64_t B, int64_t C, const void* w, const float* u, const void* k,
+                 const void* v, float* state, void* out, int io, hipStream_t stream) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
+  if (B < 0 || C < 0) return WKV_ERR_DIM;
+  const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
+  int64_t io_bytes, state_bytes;
+  if (!mul3(B, C, es, &io_bytes) || io_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (!mul3(B, C, 12, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (B == 0 || C == 0) return WKV_OK;
+  if (w == nullptr || u == nullptr || k == nullptr || v == nullptr || state == nullptr ||
+      out == nullptr)
+    return WKV_ERR_NULL;
+  if (misaligned(u, 4) || misaligned(state, 4)) return WKV_ERR_ALIGN;
+  if (misaligned(w, es) || misaligned(k, es) || misaligned(v, es) || misaligned(out, es))
+    return WKV_ERR_ALIGN;
+  const int64_t pbytes = C * 4;
+  if (overlaps(out, io_bytes, w, io_bytes) || overlaps(out, io_bytes, k, io_bytes) ||
+      overlaps(out, io_bytes, v, io_bytes) || overlaps(out, io_bytes, u, pbytes) ||
+      overlaps(out, io_bytes, state, state_bytes))
+    return WKV_ERR_ALIAS;
+  if (overlaps(state, state_bytes, w, io_bytes) || overlaps(state, state_bytes, k, io_bytes) ||
+      overlaps(state, state_bytes, v, io_bytes) || overlaps(state, state_bytes, u, pbytes))
+    return WKV_ERR_ALIAS;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  const wkv::DdStepArgs a{B, C, w, u, k, v, state, out};
+  e = wkv::launch_dd_step(a, io, wkv::dd_step_vec_width(io, C, a), stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
 int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                   const float* k, const float* v, const float* r, const float* state_in,
                   const float* state_out, const float* gstate_out, const float* gout, float* gk,
@@ -314,6 +394,17 @@ int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float* w, const flo
                       int64_t workspace_bytes, hipStream_t stream) {
   return forward_impl(B, T, C, w, u, k, v, r, true, state_in, out, state_out, io, path,
                       workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_dd(int64_t B, int64_t T, int64_t C, const void* w, const float* u, const void* k,
+                   const void* v, const float* state_in, void* out, float* state_out, int io,
+                   int path, hipStream_t stream) {
+  return forward_dd_impl(B, T, C, w, u, k, v, state_in, out, state_out, io, path, stream);
+}
+
+int wkv_step_dd(int64_t B, int64_t C, const void* w, const float* u, const void* k, const void* v,
+                float* state, void* out, int io, hipStream_t stream) {
+  return step_dd_impl(B, C, w, u, k, v, state, out, io, stream);
 }
 
 int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path) {

@@ -1,0 +1,567 @@
+// WKV with a per-token (data-dependent) decay rate.
+//
+// The page "RWKV-v6 Architecture: Attention-Free Linear Transformers"
+// (section "The Core Components of the RWKV-v6 Time-Mixing Block", the items
+// on the dynamic data-dependent decay and on the matrix-valued state) computes
+// the decay from every token and applies step t's decay to the state carried
+// in from step t-1 before step t's own term is added. Here the vector-state
+// operator of the page "Linear attention without writing a CUDA kernel"
+// (section "The recurrence") takes a positive rate w[b][t][c] per token and
+// channel: step t multiplies the state by e^(-w_t). A constant rate gives the
+// constant-decay operator.
+//
+// Precision. With a rate per token the running maximum can no longer be kept
+// as (key, whole number of steps); instead every exponent that accumulates
+// rates -- the running maximum, a segment's total rate and the decay behind
+// each token of a sub-chunk -- is fp64, and differences are rounded to fp32
+// only right before v_exp_f32. Values, numerators and denominators stay fp32.
+// The fp64 work is a handful of adds and conversions per token, small next to
+// the 16 bytes per channel-token these kernels move.
+//
+// Kernels: a channel-parallel sequential scan (large B*C), a chunked scan
+// over time (small B*C) with the layout of the constant-decay chunked scan --
+// a segment summary carries its total rate where that one carries a length --
+// and the batched decode step.
+#include "wkv_device.h"
+#include "wkv_internal.h"
+#include "wkv_tile.h"
+
+namespace wkv {
+namespace {
+
+constexpr double kEmptyD = static_cast<double>(kEmpty);  // the fp32 empty max_exp, exactly
+
+// e^(-|x|) of an fp64 exponent difference.
+__device__ __forceinline__ float exp_neg_abs(double x) {
+  return fast_exp2(__builtin_fabsf(static_cast<float>(x)) * -kLog2e);
+}
+
+// Running state of one channel: true sums n e^m and d e^m.
+struct LaneD {
+  float n, d;
+  double m;
+};
+
+__device__ __forceinline__ LaneD laned_empty() { return LaneD{0.0f, 0.0f, kEmptyD}; }
+
+// One token. Output: the state as it stands mixed with the token at weight
+// e^(u + k); then the state decays by e^(-w) and the token is added at e^k.
+// Of each pair of weights, taken against the larger exponent, one is 1.
+__device__ __forceinline__ float laned_step(LaneD& s, float k, float v, float w, double ud) {
+  const double kd = static_cast<double>(k);
+  const double dk = kd - s.m;   // k - m
+  const double s1 = dk + ud;    // (u + k) - m
+  const float x = exp_neg_abs(s1);
+  const bool cur_wins = s1 > 0.0;
+  const float fa = cur_wins ? x : 1.0f;
+  const float fb = cur_wins ? 1.0f : x;
+  const float out = __builtin_fmaf(fa, s.n, fb * v) * fast_rcp(__builtin_fmaf(fa, s.d, fb));
+  const double wd = static_cast<double>(w);
+  const double s2 = dk + wd;    // k - (m - w)
+  const float y = exp_neg_abs(s2);
+  const bool tok_wins = s2 > 0.0;
+  const float ga = tok_wins ? y : 1.0f;
+  const float gb = tok_wins ? 1.0f : y;
+  s.n = __builtin_fmaf(ga, s.n, gb * v);
+  s.d = __builtin_fmaf(ga, s.d, gb);
+  s.m = tok_wins ? kd : s.m - wd;
+  return out;
+}
+
+// A run of tokens from the empty state: (n, d) against the largest exponent
+// m at the end of the run, and the run's total rate ws (what a state that
+// enters the run decays by while it passes).
+struct SegD {
+  float n, d;
+  double m, ws;
+};
+
+__device__ __forceinline__ SegD segd_identity() { return SegD{0.0f, 0.0f, kEmptyD, 0.0}; }
+
+// a then b: a decays by b's total rate, then the two add against the larger
+// exponent.
+__device__ __forceinline__ SegD segd_combine(const SegD& a, const SegD& b) {
+  const double am = a.m - b.ws;
+  const double t = am - b.m;
+  const float e = exp_neg_abs(t);
+  const bool a_wins = t >= 0.0;
+  const float fa = a_wins ? 1.0f : e;
+  const float fb = a_wins ? e : 1.0f;
+  return SegD{__builtin_fmaf(fa, a.n, fb * b.n), __builtin_fmaf(fa, a.d, fb * b.d),
+              a_wins ? am : b.m, a.ws + b.ws};
+}
+
+// A running state followed by a run.
+__device__ __forceinline__ void laned_absorb(LaneD& s, const SegD& b) {
+  const double am = s.m - b.ws;
+  const double t = am - b.m;
+  const float e = exp_neg_abs(t);
+  const bool a_wins = t >= 0.0;
+  const float fa = a_wins ? 1.0f : e;
+  const float fb = a_wins ? e : 1.0f;
+  s.n = __builtin_fmaf(fa, s.n, fb * b.n);
+  s.d = __builtin_fmaf(fa, s.d, fb * b.d);
+  s.m = a_wins ? am : b.m;
+}
+
+__device__ __forceinline__ SegD shfl_up_segd(const SegD& x, int delta) {
+  SegD r;
+  r.n = __shfl_up(x.n, delta, 64);
+  r.d = __shfl_up(x.d, delta, 64);
+  r.m = __shfl_up(x.m, delta, 64);
+  r.ws = __shfl_up(x.ws, delta, 64);
+  return r;
+}
+
+// Summary of one thread's sub-chunk. Token i has decayed by the rates of the
+// sub-chunk's later steps (accumulated in fp64, newest first); its exponent
+// k_i minus that is rounded once to fp32, as the constant-decay kernels round
+// theirs. MASKED: only the first nvalid tokens exist.
+template <int L, bool MASKED>
+__device__ __forceinline__ SegD summarize_d(const float (&kk)[L], const float (&vv)[L],
+                                            const float (&ww)[L], int nvalid) {
+  float z[L];
+  double suf = 0.0;
+  float top = kEmpty;
+#pragma unroll
+  for (int i = L - 1; i >= 0; --i) {
+    z[i] = kEmpty;
+    if (!MASKED || i < nvalid) {
+      z[i] = static_cast<float>(static_cast<double>(kk[i]) - suf);
+      suf += static_cast<double>(ww[i]);
+      top = __builtin_fmaxf(top, z[i]);
+    }
+  }
+  float n = 0.0f, d = 0.0f;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    float e = fast_exp2((z[i] - top) * kLog2e);
+    if (MASKED && i >= nvalid) e = 0.0f;
+    d += e;
+    n = __builtin_fmaf(e, vv[i], n);
+  }
+  return SegD{n, d, static_cast<double>(top), suf};
+}
+
+template <int V>
+__device__ __forceinline__ void load_state_d(const float* __restrict__ state_in, int64_t lane0,
+                                             int64_t plane, LaneD (&s)[V]) {
+  if (state_in != nullptr) {
+    float n[V], d[V], m[V];
+    IoF32::load<V, false>(state_in + lane0, n);
+    IoF32::load<V, false>(state_in + plane + lane0, d);
+    IoF32::load<V, false>(state_in + 2 * plane + lane0, m);
+#pragma unroll
+    for (int j = 0; j < V; ++j) s[j] = LaneD{n[j], d[j], static_cast<double>(m[j])};
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) s[j] = laned_empty();
+  }
+}
+
+template <int V>
+__device__ __forceinline__ void store_state_d(float* __restrict__ state_out, int64_t lane0,
+                                              int64_t plane, const LaneD (&s)[V]) {
+  float n[V], d[V], m[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    n[j] = s[j].n;
+    d[j] = s[j].d;
+    m[j] = static_cast<float>(s[j].m);
+  }
+  IoF32::store<V, false>(state_out + lane0, n);
+  IoF32::store<V, false>(state_out + plane + lane0, d);
+  IoF32::store<V, false>(state_out + 2 * plane + lane0, m);
+}
+
+// ------------------------------------------------------ sequential scan
+
+constexpr int kDdSeqThreads = 256;
+
+template <int V, int U>
+struct DdBlock {
+  float k[U][V];
+  float v[U][V];
+  float w[U][V];
+};
+
+template <typename IoT, int V, int U>
+__device__ __forceinline__ void dd_seq_load(DdBlock<V, U>& blk,
+                                            const typename IoT::elem* __restrict__ kp,
+                                            const typename IoT::elem* __restrict__ vp,
+                                            const typename IoT::elem* __restrict__ wp, int64_t C) {
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    IoT::template load<V, true>(kp + i * C, blk.k[i]);
+    IoT::template load<V, true>(vp + i * C, blk.v[i]);
+    IoT::template load<V, true>(wp + i * C, blk.w[i]);
+  }
+}
+
+template <typename IoT, int V, int U>
+__device__ __forceinline__ void dd_seq_compute(const DdBlock<V, U>& blk, LaneD (&s)[V],
+                                               const double (&ud)[V],
+                                               typename IoT::elem* __restrict__ op, int64_t C) {
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    float o[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) o[j] = laned_step(s[j], blk.k[i][j], blk.v[i][j], blk.w[i][j], ud[j]);
+    IoT::template store<V, true>(op + i * C, o);
+  }
+}
+
+template <typename IoT, int V, int U>
+__global__ __launch_bounds__(kDdSeqThreads) void wkv_dd_seq_kernel(
+    int64_t B, int64_t T, int64_t C, const typename IoT::elem* __restrict__ w,
+    const float* __restrict__ u, const typename IoT::elem* __restrict__ k,
+    const typename IoT::elem* __restrict__ v, const float* __restrict__ state_in,
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out) {
+  const int64_t groups_per_row = C / V;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kDdSeqThreads + threadIdx.x;
+  if (gid >= B * groups_per_row) return;
+  const int64_t b = gid / groups_per_row;
+  const int64_t c0 = (gid - b * groups_per_row) * V;
+  const int64_t plane = B * C;
+  const int64_t lane0 = b * C + c0;
+
+  float uu[V];
+  IoF32::load<V, false>(u + c0, uu);
+  double ud[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) ud[j] = static_cast<double>(uu[j]);
+  LaneD s[V];
+  load_state_d<V>(state_in, lane0, plane, s);
+
+  const int64_t row = b * T * C + c0;
+  const typename IoT::elem* kp = k + row;
+  const typename IoT::elem* vp = v + row;
+  const typename IoT::elem* wp = w + row;
+  typename IoT::elem* op = out + row;
+
+  // two register buffers; the next block's loads are issued before the
+  // current block is computed (on every path: the last full block re-reads
+  // itself), so the counter-based waits stop at the block about to be used
+  DdBlock<V, U> A, Bf;
+  const int64_t nblk = T / U;
+  if (nblk > 0) dd_seq_load<IoT, V, U>(A, kp, vp, wp, C);
+  for (int64_t blk = 0; blk < nblk; blk += 2) {
+    const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
+    dd_seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, wp + nb * C, C);
+    dd_seq_compute<IoT, V, U>(A, s, ud, op + blk * U * C, C);
+    if (blk + 1 >= nblk) break;
+    const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
+    dd_seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, wp + na * C, C);
+    dd_seq_compute<IoT, V, U>(Bf, s, ud, op + (blk + 1) * U * C, C);
+  }
+  for (int64_t t = nblk * U; t < T; ++t) {
+    float kk[V], vv[V], ww[V], o[V];
+    IoT::template load<V, true>(kp + t * C, kk);
+    IoT::template load<V, true>(vp + t * C, vv);
+    IoT::template load<V, true>(wp + t * C, ww);
+#pragma unroll
+    for (int j = 0; j < V; ++j) o[j] = laned_step(s[j], kk[j], vv[j], ww[j], ud[j]);
+    IoT::template store<V, true>(op + t * C, o);
+  }
+  if (state_out != nullptr) store_state_d<V>(state_out, lane0, plane, s);
+}
+
+// ------------------------------------------------------ chunked scan
+
+constexpr int kDdLC = 32, kDdPS = 2;
+
+template <int V, int L>
+struct DdRegs {
+  float k[L][V];
+  float v[L][V];
+  float w[L][V];
+};
+
+template <typename IoT, int V, int L, bool MASKED>
+__device__ __forceinline__ void dd_chunk_load(DdRegs<V, L>& r,
+                                              const typename IoT::elem* __restrict__ kp,
+                                              const typename IoT::elem* __restrict__ vp,
+                                              const typename IoT::elem* __restrict__ wp, int64_t C,
+                                              int nvalid) {
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (!MASKED || i < nvalid) {
+      IoT::template load<V, false>(kp + i * C, r.k[i]);
+      IoT::template load<V, false>(vp + i * C, r.v[i]);
+      IoT::template load<V, false>(wp + i * C, r.w[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j) r.k[i][j] = r.v[i][j] = r.w[i][j] = 0.0f;
+    }
+  }
+}
+
+// One tile: summaries, scan inside the wave, wave totals through LDS, the
+// state in front of every sub-chunk, then the rescan of each thread's tokens.
+template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED>
+__device__ __forceinline__ void dd_chunk_tile(const DdRegs<V, L>& r, int nvalid, LaneD (&carry)[V],
+                                              const double (&ud)[V], SegD (*tot)[LC * V],
+                                              typename IoT::elem* __restrict__ op, int64_t C,
+                                              bool cvalid, int wave, int sl, int cl) {
+  SegD inc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    float kk[L], vv[L], ww[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      kk[i] = r.k[i][j];
+      vv[i] = r.v[i][j];
+      ww[i] = r.w[i][j];
+    }
+    inc[j] = summarize_d<L, MASKED>(kk, vv, ww, nvalid);
+  }
+#pragma unroll
+  for (int off = 1; off < PS; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const SegD p = shfl_up_segd(inc[j], off * LC);
+      if (sl >= off) inc[j] = segd_combine(p, inc[j]);
+    }
+  }
+  SegD exc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const SegD p = shfl_up_segd(inc[j], LC);
+    exc[j] = sl > 0 ? p : segd_identity();
+  }
+  if (sl == PS - 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) tot[wave][cl * V + j] = inc[j];
+  }
+  __syncthreads();
+  LaneD pre[V];
+#pragma unroll
+  for (int jj = 0; jj < W; ++jj) {
+    if (jj == wave) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) pre[j] = carry[j];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) laned_absorb(carry[j], tot[jj][cl * V + j]);
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) laned_absorb(pre[j], exc[j]);
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (!MASKED || i < nvalid) {
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) o[j] = laned_step(pre[j], r.k[i][j], r.v[i][j], r.w[i][j], ud[j]);
+      if (cvalid) IoT::template store<V, true>(op + i * C, o);
+    }
+  }
+}
+
+template <typename IoT, int V, int LC, int PS, int W, int L>
+__global__ __launch_bounds__(64 * W) void wkv_dd_chunk_kernel(
+    int64_t B, int64_t T, int64_t C, const typename IoT::elem* __restrict__ w,
+    const float* __restrict__ u, const typename IoT::elem* __restrict__ k,
+    const typename IoT::elem* __restrict__ v, const float* __restrict__ state_in,
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out, int64_t groups_per_row) {
+  static_assert(LC * PS == 64, "a wave is LC channel groups by PS sub-chunks");
+  constexpr int CH = LC * V;
+  constexpr int TL = W * PS * L;
+  __shared__ SegD tot[2][W][CH];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int cl = lane % LC;
+  const int sl = lane / LC;
+  const int sub = wave * PS + sl;
+
+  const int64_t g = xcd_swizzle(blockIdx.x, B * groups_per_row);
+  const int64_t b = g / groups_per_row;
+  const int64_t c0 = (g - b * groups_per_row) * CH + cl * V;
+  const bool cvalid = c0 < C;
+  const int64_t cc = cvalid ? c0 : C - V;  // idle tail threads mirror the last channels
+  const int64_t plane = B * C;
+  const int64_t lane0 = b * C + cc;
+
+  float uu[V];
+  IoF32::load<V, false>(u + cc, uu);
+  double ud[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) ud[j] = static_cast<double>(uu[j]);
+  LaneD carry[V];
+  load_state_d<V>(state_in, lane0, plane, carry);
+
+  const int64_t base = b * T * C + cc + static_cast<int64_t>(sub) * L * C;
+  const typename IoT::elem* kp = k + base;
+  const typename IoT::elem* vp = v + base;
+  const typename IoT::elem* wp = w + base;
+  typename IoT::elem* op = out + base;
+  const int64_t step = static_cast<int64_t>(TL) * C;
+
+  const int64_t full = T / TL;
+  DdRegs<V, L> A, Bf;
+  if (full > 0) dd_chunk_load<IoT, V, L, false>(A, kp, vp, wp, C, L);
+  for (int64_t tile = 0; tile < full; tile += 2) {
+    const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
+    dd_chunk_load<IoT, V, L, false>(Bf, kp + nb * step, vp + nb * step, wp + nb * step, C, L);
+    dd_chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, ud, tot[tile & 1], op + tile * step,
+                                               C, cvalid, wave, sl, cl);
+    if (tile + 1 >= full) break;
+    const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
+    dd_chunk_load<IoT, V, L, false>(A, kp + na * step, vp + na * step, wp + na * step, C, L);
+    dd_chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, ud, tot[(tile + 1) & 1],
+                                               op + (tile + 1) * step, C, cvalid, wave, sl, cl);
+  }
+  if (full * TL < T) {  // last, partial tile
+    const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
+    const int64_t left = T - first;
+    const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
+    DdRegs<V, L> last;
+    dd_chunk_load<IoT, V, L, true>(last, kp + full * step, vp + full * step, wp + full * step, C,
+                                   nvalid);
+    dd_chunk_tile<IoT, V, LC, PS, W, L, true>(last, nvalid, carry, ud, tot[full & 1],
+                                              op + full * step, C, cvalid, wave, sl, cl);
+  }
+  if (state_out != nullptr && sub == 0 && cvalid) store_state_d<V>(state_out, lane0, plane, carry);
+}
+
+// ------------------------------------------------------ decode step
+
+constexpr int kDdStepThreads = 256;
+
+template <typename IoT, int V>
+__global__ __launch_bounds__(kDdStepThreads) void wkv_dd_step_kernel(
+    int64_t B, int64_t C, const typename IoT::elem* __restrict__ w, const float* __restrict__ u,
+    const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
+    float* __restrict__ state, typename IoT::elem* __restrict__ out) {
+  const int64_t groups_per_row = C / V;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kDdStepThreads + threadIdx.x;
+  if (gid >= B * groups_per_row) return;
+  const int64_t b = gid / groups_per_row;
+  const int64_t c0 = (gid - b * groups_per_row) * V;
+  const int64_t lane0 = b * C + c0;
+  const int64_t plane = B * C;
+
+  float ww[V], uu[V], kk[V], vv[V], o[V];
+  IoT::template load<V, true>(w + lane0, ww);
+  IoF32::load<V, false>(u + c0, uu);
+  IoT::template load<V, true>(k + lane0, kk);
+  IoT::template load<V, true>(v + lane0, vv);
+  LaneD s[V];
+  load_state_d<V>(state, lane0, plane, s);
+#pragma unroll
+  for (int j = 0; j < V; ++j) o[j] = laned_step(s[j], kk[j], vv[j], ww[j], static_cast<double>(uu[j]));
+  IoT::template store<V, true>(out + lane0, o);
+  store_state_d<V>(state, lane0, plane, s);
+}
+
+// ------------------------------------------------------ launchers
+
+template <typename T>
+const T* cp(const void* p) {
+  return static_cast<const T*>(p);
+}
+
+template <typename IoT, int V>
+hipError_t launch_dd_seq_t(const DdArgs& a, hipStream_t st) {
+  constexpr int U = 8;
+  const int64_t threads = a.B * (a.C / V);
+  const int64_t blocks = (threads + kDdSeqThreads - 1) / kDdSeqThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  using E = typename IoT::elem;
+  hipLaunchKernelGGL((wkv_dd_seq_kernel<IoT, V, U>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kDdSeqThreads), 0, st, a.B, a.T, a.C, cp<E>(a.w), a.u, cp<E>(a.k),
+                     cp<E>(a.v), a.state_in, static_cast<E*>(a.out), a.state_out);
+  return hipGetLastError();
+}
+
+template <typename IoT, int V, int W, int L>
+hipError_t launch_dd_chunk_t(const DdArgs& a, hipStream_t st) {
+  constexpr int CH = kDdLC * V;
+  const int64_t gpr = (a.C + CH - 1) / CH;
+  const int64_t blocks = a.B * gpr;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  using E = typename IoT::elem;
+  hipLaunchKernelGGL((wkv_dd_chunk_kernel<IoT, V, kDdLC, kDdPS, W, L>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0, st, a.B, a.T, a.C,
+                     cp<E>(a.w), a.u, cp<E>(a.k), cp<E>(a.v), a.state_in, static_cast<E*>(a.out),
+                     a.state_out, gpr);
+  return hipGetLastError();
+}
+
+// Tile shapes: short sequences want few serial tiles; longer ones two waves
+// per SIMD. The rate array makes the register tile half as large again as the
+// constant-decay scan's, so tiles hold fewer tokens per thread (no spills at
+// these shapes).
+constexpr int64_t kDdShortT = 256;
+
+template <typename IoT, int V>
+hipError_t launch_dd_chunk_v(const DdArgs& a, hipStream_t st) {
+  constexpr int LL = V == 1 ? 8 : 4;
+  if (a.T <= kDdShortT) return launch_dd_chunk_t<IoT, V, 8, 4>(a, st);
+  return launch_dd_chunk_t<IoT, V, 16, LL>(a, st);
+}
+
+template <typename IoT, int V>
+hipError_t launch_dd_step_t(const DdStepArgs& a, hipStream_t st) {
+  const int64_t threads = a.B * (a.C / V);
+  const int64_t blocks = (threads + kDdStepThreads - 1) / kDdStepThreads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  using E = typename IoT::elem;
+  hipLaunchKernelGGL((wkv_dd_step_kernel<IoT, V>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kDdStepThreads), 0, st, a.B, a.C, cp<E>(a.w), a.u, cp<E>(a.k),
+                     cp<E>(a.v), a.state, static_cast<E*>(a.out));
+  return hipGetLastError();
+}
+
+bool aligned(const void* p, int bytes) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+}  // namespace
+
+int dd_vec_width(int io, int64_t C, const DdArgs& a) {
+  if (io != kBf16) return 1;
+  const bool ok = C % 2 == 0 && aligned(a.k, 4) && aligned(a.v, 4) && aligned(a.w, 4) &&
+                  aligned(a.out, 4) && aligned(a.u, 8) && aligned(a.state_in, 8) &&
+                  aligned(a.state_out, 8);
+  return ok ? 2 : 1;
+}
+
+int dd_step_vec_width(int io, int64_t C, const DdStepArgs& a) {
+  const int elem = io == kBf16 ? 2 : 4;
+  for (int V : {4, 2, 1}) {
+    if (C % V) continue;
+    if (!aligned(a.k, V * elem) || !aligned(a.v, V * elem) || !aligned(a.w, V * elem) ||
+        !aligned(a.out, V * elem))
+      continue;
+    if (!aligned(a.u, V * 4) || !aligned(a.state, V * 4)) continue;
+    return V;
+  }
+  return 1;
+}
+
+hipError_t launch_dd_seq(const DdArgs& a, int io, int vec, hipStream_t s) {
+  if (io == kF32) return launch_dd_seq_t<IoF32, 1>(a, s);
+  if (vec == 2) return launch_dd_seq_t<IoBf16, 2>(a, s);
+  return launch_dd_seq_t<IoBf16, 1>(a, s);
+}
+
+hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, hipStream_t s) {
+  if (io == kF32) return launch_dd_chunk_v<IoF32, 1>(a, s);
+  if (vec == 2) return launch_dd_chunk_v<IoBf16, 2>(a, s);
+  return launch_dd_chunk_v<IoBf16, 1>(a, s);
+}
+
+hipError_t launch_dd_step(const DdStepArgs& a, int io, int vec, hipStream_t s) {
+  if (io == kF32) {
+    if (vec == 4) return launch_dd_step_t<IoF32, 4>(a, s);
+    if (vec == 2) return launch_dd_step_t<IoF32, 2>(a, s);
+    return launch_dd_step_t<IoF32, 1>(a, s);
+  }
+  if (vec == 4) return launch_dd_step_t<IoBf16, 4>(a, s);
+  if (vec == 2) return launch_dd_step_t<IoBf16, 2>(a, s);
+  return launch_dd_step_t<IoBf16, 1>(a, s);
+}
+
+}  // namespace wkv

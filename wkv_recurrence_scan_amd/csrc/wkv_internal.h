@@ -82,6 +82,32 @@ struct BwdArgs {
 int64_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
 hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t s);
 
+// Per-token (data-dependent) decay: w has k's layout and element type.
+struct DdArgs {
+  int64_t B, T, C;
+  const void* w;
+  const float* u;
+  const void* k;
+  const void* v;
+  const float* state_in;  // nullptr: empty state
+  void* out;
+  float* state_out;       // nullptr: not written
+};
+struct DdStepArgs {
+  int64_t B, C;
+  const void* w;          // this step's rates, [B][C]
+  const float* u;
+  const void* k;
+  const void* v;
+  float* state;
+  void* out;
+};
+int dd_vec_width(int io, int64_t C, const DdArgs& a);
+int dd_step_vec_width(int io, int64_t C, const DdStepArgs& a);
+hipError_t launch_dd_seq(const DdArgs& a, int io, int vec, hipStream_t s);
+hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, hipStream_t s);
+hipError_t launch_dd_step(const DdStepArgs& a, int io, int vec, hipStream_t s);
+
 hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);

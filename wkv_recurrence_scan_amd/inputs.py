@@ -31,6 +31,7 @@ import numpy as np
 
 # tensor ids inside a seed
 _K, _V, _W, _U, _SPIKE_MASK, _SPIKE_SIGN, _DEC_K, _DEC_V, _GOUT, _R = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
+_WT, _DEC_WT = 11, 12
 
 
 @dataclasses.dataclass(frozen=True)
@@ -218,3 +219,53 @@ def receptance(wl: Workload, layer: int = 0, rows: Optional[Sequence[int]] = Non
 
     _map_rows(one, range(len(rows)))
     return r
+
+
+# Per-token decay. The page "RWKV-v6 Architecture: Attention-Free Linear
+# Transformers" (section "The Core Components of the RWKV-v6 Time-Mixing
+# Block", dynamic data-dependent decay) computes the decay of each token as
+# exp(-exp(.)) of a projection of that token; the rate (the inner exp) is then
+# a per-channel base times the exponential of a token-dependent term. Here the
+# base is the workload's per-channel w and the token term is N(0, 0.5): a
+# log-normal modulation, so rates stay positive and spread about 1.6x either
+# way around each channel's base.
+DD_LOG_STD = 0.5
+
+
+def decay_rates(wl: Workload, layer: int = 0, rows: Optional[Sequence[int]] = None,
+                T: Optional[int] = None) -> np.ndarray:
+    """Per-token decay rates (B_rows, T, C) float32: params()' w per channel
+    times exp(N(0, DD_LOG_STD)) per entry, rounded to bf16 for bf16 workloads;
+    one independent stream per batch row."""
+    rows = list(range(wl.B) if rows is None else rows)
+    T = wl.T if T is None else T
+    wc, _ = params(wl, layer)
+    out = np.empty((len(rows), T, wl.C), np.float32)
+
+    def one(i):
+        g = _rng(wl, layer, _WT, rows[i])
+        z = g.standard_normal(T * wl.C, dtype=np.float32).reshape(T, wl.C)
+        r = wc[None, :] * np.exp(np.float32(DD_LOG_STD) * z)
+        out[i] = round_to_bf16(r) if wl.io == "bf16" else r
+
+    _map_rows(one, range(len(rows)))
+    return out
+
+
+def decode_decay_rates(wl: Workload, rows: Optional[Sequence[int]] = None,
+                       steps: Optional[int] = None) -> np.ndarray:
+    """Per-step decay rates for the decode steps (steps, B_rows, C), drawn
+    like decay_rates."""
+    rows = list(range(wl.B) if rows is None else rows)
+    steps = wl.decode_steps if steps is None else steps
+    wc, _ = params(wl, 0)
+    out = np.empty((steps, len(rows), wl.C), np.float32)
+
+    def one(i):
+        g = _rng(wl, 0, _DEC_WT, rows[i])
+        z = g.standard_normal(steps * wl.C, dtype=np.float32).reshape(steps, wl.C)
+        r = wc[None, :] * np.exp(np.float32(DD_LOG_STD) * z)
+        out[:, i] = round_to_bf16(r) if wl.io == "bf16" else r
+
+    _map_rows(one, range(len(rows)))
+    return out
