@@ -17,6 +17,9 @@ Default run (one JSON line on stdout):
     prefill; steps/s for eager launches and for one HIP graph of all 1024.
   * gated_forward: wkv_forward_gated (out = sigmoid(r) * wkv) on one layer of
     the prefill shape.
+  * per_token_decay: wkv_forward_dd (a decay rate per token and channel) on
+    one layer of the prefill shape and on the decode workload's B=256 T=512
+    prefill shape.
   * backward: wkv_backward (the gradients) on one layer of the prefill shape
     and on the decode workload's B=256 T=512 prefill shape, with the
     roofline on its algorithmic bytes (read k, v, dL/dout; write dL/dk,
@@ -301,6 +304,48 @@ def time_gated(wl, dev, path, reps=50):
                          "algorithmic_bytes_per_launch": abytes}}
 
 
+def time_decay(wl, dev, reps=50):
+    """wkv_forward_dd (per-token decay) on workload wl's first layer with the
+    seeded per-token rates: microseconds per call from an event pair around
+    `reps` back-to-back calls, and the roofline on its algorithmic bytes (read
+    w, k, v; write out and the final state; read u)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    _, u = I.params(wl)
+    k, v = I.kv(wl)
+    wt = I.decay_rates(wl)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    dw, du, dk, dv = t(wt), t(u), t(k), t(v)
+    del k, v, wt
+    out = torch.empty_like(dk)
+    st = torch.empty((3, wl.B, wl.C), dtype=torch.float32, device=dev)
+    call = lambda: W.wkv_forward_dd(dw, du, dk, dv, out=out, state_out=st)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ct = wl.B * wl.T * wl.C
+    abytes = 16 * ct + 12 * wl.B * wl.C + 4 * wl.C
+    achieved = abytes / (us * 1e-6) / 1e9
+    path = W.wkv_select_path(wl.B, wl.T, wl.C, W.WKV_IO_F32)
+    return {"workload": f"{wl.name}, one layer, per-token decay", "B": wl.B, "T": wl.T,
+            "C": wl.C, "path": "chunk" if path == "lookback" else path,
+            "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
+            "us_per_call": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": abytes}}
+
+
 def measured_traffic(workload_key, path):
     """HBM bytes per launch from the rocprofv3 counter summaries under
     profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
@@ -366,7 +411,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward-pass measurement (run with the default config)")
+                    help="skip the gated, per-token-decay and backward measurements (default config)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -472,6 +517,13 @@ def main():
         for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
             _log(f"backward: {bwl.name} (one layer)")
             rec["backward"].append(time_backward(bwl, dev))
+            torch.cuda.empty_cache()
+
+    if args.config == 1 and not args.no_backward:
+        rec["per_token_decay"] = []
+        for dwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+            _log(f"per-token decay forward: {dwl.name} (one layer)")
+            rec["per_token_decay"].append(time_decay(dwl, dev))
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -9,9 +9,9 @@
 // are read from HBM once.
 //
 // A workgroup:
-//   1. serves a channel group (one block per group in every row of G blocks,
-//      the group shifting from row to row so that every XCD sees every
-//      group) and takes that group's next segment
+//   1. serves a channel group (one block per group in every row of G blocks;
+//      a group keeps its XCD, and every XCD serves a mix of column offsets)
+//      and takes that group's next segment
 //      from the group's own ticket counter, so every segment it will wait for
 //      was taken by a workgroup that has already started: no co-residency or
 //      dispatch order is assumed and no wait can deadlock (per-group counters
@@ -254,18 +254,27 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   __shared__ Seg fetched[anchor_spacing<V, W>()][CH];
   __shared__ uint32_t seg_s, epoch_s;
 
-  // Work assignment per channel group: block i of row q = i / G serves group
-  // (i + q) mod G and takes the group's next segment from the group's own
-  // ticket counter, so within a group segments are handed out in start order
-  // (every segment a workgroup waits for belongs to a workgroup that has
-  // already started) and the counters' atomics are spread over G addresses.
-  // Blocks are dealt to the 8 XCDs round-robin; the shift by the row moves
-  // each group to another XCD from one row to the next, so every XCD sees
-  // every channel group. (Without it a group, and so one fixed column of the
-  // tensors, stays on one XCD: measured on MI355X, columns that stream more
-  // slowly than the rest then put a whole XCD's queue behind.)
+  // Work assignment per channel group: block i = q G + o (row q, offset o)
+  // serves group g(o), the same group in every row, and takes the group's
+  // next segment from the group's own ticket counter, so within a group
+  // segments are handed out in start order (every segment a workgroup waits
+  // for belongs to a workgroup that has already started) and the counters'
+  // atomics are spread over G addresses.
+  // Blocks are dealt to the 8 XCDs round-robin. When G is a multiple of 8 a
+  // group's blocks therefore all run on one XCD and start in row order, which
+  // keeps the prefetch guess below right (a group whose blocks hop between
+  // XCDs gets its tickets out of row order whenever one XCD runs ahead, and
+  // every wrong guess fetches a tile twice). g(o) then permutes each run of
+  // 8 offsets by its run index, so that every XCD serves every residue of g
+  // mod 8, i.e. every 128-byte column offset within 1 KiB: measured on
+  // MI355X, some column offsets stream more slowly than others, and an XCD
+  // holding only those falls behind the rest.
   const int64_t row = blockIdx.x / a.groups;
-  const int64_t g = (blockIdx.x + row) % a.groups;
+  const int64_t o = blockIdx.x - row * a.groups;
+  const int64_t g = (a.groups % kNumXcd) != 0
+                        ? o
+                        : (o & ~int64_t{kNumXcd - 1}) | (((o & (kNumXcd - 1)) + (o / kNumXcd)) &
+                                                         (kNumXcd - 1));
   const int64_t S = a.segments;
   if (threadIdx.x == 0) {
     const uint64_t t =
