@@ -10,12 +10,15 @@ invariants and special cases that reduce to a softmax; the gradients
 (wkv_grad) by tests/test_oracle_grad.py against central finite differences
 of the pinned forward and by invariants of the operator; the per-token-decay
 operator (wkv_decay) by tests/test_oracle_decay.py against its own mpmath
-recurrence, the constant-decay operator, a hand-worked case and invariants.
-None is "parity unpinned".
+recurrence, the constant-decay operator, a hand-worked case and invariants;
+the matrix-valued-state recurrence (wkv_matrix) by tests/test_oracle_matrix.py
+against its own mpmath attention form, causal linear attention by matmul,
+closed forms and invariants. None is "parity unpinned".
 """
 
 from .wkv_decay import wkv_dd_direct, wkv_dd_recurrent, wkv_dd_step_ref  # noqa: F401
 from .wkv_grad import wkv_backward_direct, wkv_gated_backward_direct  # noqa: F401
+from .wkv_matrix import wkv6_direct, wkv6_recurrent, wkv6_step_ref  # noqa: F401
 from .wkv_oracle import (  # noqa: F401
     EMPTY_MAX_EXP,
     canonical,

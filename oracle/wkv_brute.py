@@ -127,3 +127,36 @@ def wkv_dd_brute(w, u, k, v, state_in=None, dps: int = 50):
                 else:
                     state[:, b, c] = (float(N / exp(top)), float(D / exp(top)), float(top))
     return out, state
+
+
+def wkv6_brute(lam, k, v, r, H, state_in=None, dps: int = 50):
+    """The matrix-valued-state recurrence (oracle/wkv_matrix.py) in 50-digit
+    mpmath, written in its attention form: y_t[i] = sigmoid(r_t[i]) times the
+    sum over s <= t of exp(-sum_{s<tau<=t} lam_tau[i]) k_s[i] (v_s . k_t), plus
+    the initial state's row i applied to k_t and decayed by every step so far.
+    No state matrix is formed. Returns y (B, T, C) rounded to float64."""
+    lam, k, v, r = (np.asarray(x, dtype=np.float64) for x in (lam, k, v, r))
+    B, T, C = k.shape
+    D = C // H
+    y = np.empty((B, T, C))
+    with mpmath.workdps(dps):
+        mpf, exp = mpmath.mpf, mpmath.exp
+        for b in range(B):
+            for h in range(H):
+                cs = range(h * D, (h + 1) * D)
+                K = [[mpf(k[b, t, c]) for c in cs] for t in range(T)]
+                Vv = [[mpf(v[b, t, c]) for c in cs] for t in range(T)]
+                Lm = [[mpf(lam[b, t, c]) for c in cs] for t in range(T)]
+                for t in range(T):
+                    dots = [sum((Vv[s][j] * K[t][j] for j in range(D)), mpf(0)) for s in range(t + 1)]
+                    for i in range(D):
+                        acc = mpf(0)
+                        if state_in is not None:
+                            row = sum((mpf(state_in[b, h, i, j]) * K[t][j] for j in range(D)), mpf(0))
+                            acc += row * exp(-sum((Lm[tau][i] for tau in range(t + 1)), mpf(0)))
+                        for s in range(t + 1):
+                            decay = exp(-sum((Lm[tau][i] for tau in range(s + 1, t + 1)), mpf(0)))
+                            acc += decay * K[s][i] * dots[s]
+                        gate = 1 / (1 + exp(-mpf(r[b, t, h * D + i])))
+                        y[b, t, h * D + i] = float(gate * acc)
+    return y
