@@ -20,6 +20,8 @@ Default run (one JSON line on stdout):
   * per_token_decay: wkv_forward_dd (a decay rate per token and channel) on
     one layer of the prefill shape and on the decode workload's B=256 T=512
     prefill shape.
+  * matrix_state: wkv_matrix_forward (a 64 x 64 state per head of 64
+    channels) on the same two shapes.
   * backward: wkv_backward (the gradients) on one layer of the prefill shape
     and on the decode workload's B=256 T=512 prefill shape, with the
     roofline on its algorithmic bytes (read k, v, dL/dout; write dL/dk,
@@ -346,6 +348,58 @@ def time_decay(wl, dev, reps=50):
                          "algorithmic_bytes_per_launch": abytes}}
 
 
+def time_matrix(wl, dev, reps=20):
+    """wkv_matrix_forward (matrix-valued state, heads of 64) on workload wl's
+    first layer: k, v, the receptance and the per-token rates of the
+    workload, C / 64 heads. Microseconds per call (event pair around `reps`
+    back-to-back calls) against both rooflines: HBM on the algorithmic bytes
+    (read w, k, v, r; write out and the final state) and the fp32 vector ALU on
+    the algorithmic flops (per state entry and token: a multiply and an FMA
+    for the update, an FMA for the readout: 5 flops, i.e. 320 per
+    channel-token)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    H = wl.C // W.MATRIX_HEAD
+    k, v = I.kv(wl)
+    r = I.receptance(wl)
+    lam = I.decay_rates(wl)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    dl, dk, dv, dr = t(lam), t(k), t(v), t(r)
+    del k, v, r, lam
+    out = torch.empty_like(dk)
+    st = torch.empty((wl.B, H, W.MATRIX_HEAD, W.MATRIX_HEAD), dtype=torch.float32, device=dev)
+    nws = W.wkv_matrix_workspace_size(wl.B, wl.T, H)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    call = lambda: W.wkv_matrix_forward(dl, dk, dv, dr, H, out=out, state_out=st, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ct = wl.B * wl.T * wl.C
+    abytes = 20 * ct + 4 * wl.B * H * W.MATRIX_HEAD ** 2
+    aflops = 5 * W.MATRIX_HEAD * ct
+    gbs = abytes / (us * 1e-6) / 1e9
+    tfs = aflops / (us * 1e-6) / 1e12
+    return {"workload": f"{wl.name}, one layer, matrix-valued state ({H} heads of 64)",
+            "B": wl.B, "T": wl.T, "C": wl.C, "heads": H,
+            "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
+            "us_per_call": round(us, 2), "workspace_bytes": nws,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": abytes},
+            "alu_roofline": {"achieved": round(tfs, 2), "peak": 157.3, "unit": "TFLOP/s",
+                             "frac": round(tfs / 157.3, 4), "algorithmic_flops_per_call": aflops}}
+
+
 def measured_traffic(workload_key, path):
     """HBM bytes per launch from the rocprofv3 counter summaries under
     profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
@@ -411,7 +465,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the gated, per-token-decay and backward measurements (default config)")
+                    help="skip the gated, per-token-decay, matrix-state and backward measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -524,6 +578,13 @@ def main():
         for dwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
             _log(f"per-token decay forward: {dwl.name} (one layer)")
             rec["per_token_decay"].append(time_decay(dwl, dev))
+            torch.cuda.empty_cache()
+
+    if args.config == 1 and not args.no_backward:
+        rec["matrix_state"] = []
+        for mwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+            _log(f"matrix-valued state forward: {mwl.name} (one layer)")
+            rec["matrix_state"].append(time_matrix(mwl, dev))
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -252,6 +252,48 @@ int wkv_forward_dd(int64_t B, int64_t T, int64_t C, const void* w, const float* 
 int wkv_step_dd(int64_t B, int64_t C, const void* w, const float* u, const void* k,
                 const void* v, float* state, void* out, int io, hipStream_t stream);
 
+/* Matrix-valued-state recurrence (page "RWKV-v6 Architecture: Attention-Free
+ * Linear Transformers", section "The Core Components of the RWKV-v6
+ * Time-Mixing Block", item "Matrix-Valued Hidden State", and the step
+ * function of its PyTorch listing). Per head of D channels a D x D state:
+ *   S_t[i][j] = e^(-w_t[i]) S_{t-1}[i][j] + k_t[i] v_t[j]
+ *   out_t[i]  = sigmoid(r_t[i]) * sum_j S_t[i][j] k_t[j]
+ * with channel c = h * D + i. fp32 throughout.
+ *
+ *   B, T, H     sizes (>= 0); B == 0 or H == 0: nothing to do.
+ *   D           head size; only 64 is built (other values: WKV_ERR_DIM).
+ *   w           [B][T][H*D] positive decay rates (the factor is e^(-w)).
+ *   k, v, r     [B][T][H*D] key, value, receptance.
+ *   state_in    [B][H][D][D] (row i, column j), or NULL for the zero state.
+ *   out         [B][T][H*D].
+ *   state_out   [B][H][D][D] state after the last token, or NULL; may equal
+ *               state_in exactly.
+ *   workspace   optional device memory, 256-byte aligned, of up to
+ *               wkv_matrix_workspace_size(...) bytes; contents need no
+ *               clearing. With less (or NULL) the kernel cuts the sequence
+ *               into fewer segments (none without one): same result up to
+ *               rounding, less parallelism. Must not overlap any other
+ *               argument; concurrent calls must not share it.
+ * Pointers to 8-byte-aligned sequences, 16-byte-aligned states. out and
+ * state_out must not overlap an input (WKV_ERR_ALIAS). T == 0 copies the
+ * state through (or zero-fills state_out). */
+int wkv_matrix_forward(int64_t B, int64_t T, int64_t H, int64_t D, const float* w,
+                       const float* k, const float* v, const float* r, const float* state_in,
+                       float* out, float* state_out, void* workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Bytes of workspace that lets wkv_matrix_forward use all the segments it
+ * wants for these sizes on the current device (0: it needs none), or a
+ * negative wkv_status. */
+int64_t wkv_matrix_workspace_size(int64_t B, int64_t T, int64_t H, int64_t D);
+
+/* One decode step of the matrix-valued-state recurrence for all (batch,
+ * head) pairs: w, k, v, r, out [B][H*D] fp32 (one token), state [B][H][D][D]
+ * fp32 updated in place; D == 64. */
+int wkv_matrix_step(int64_t B, int64_t H, int64_t D, const float* w, const float* k,
+                    const float* v, const float* r, float* state, float* out,
+                    hipStream_t stream);
+
 /* Static, NUL-terminated name of a wkv_status code. */
 const char* wkv_status_string(int status);
 

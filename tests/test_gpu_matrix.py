@@ -1,0 +1,220 @@
+"""GPU parity of the matrix-valued-state recurrence (wkv_matrix_forward,
+wkv_matrix_step) with its float64 oracle (oracle/wkv_matrix.py, pinned in
+test_oracle_matrix.py), through the C interface: ragged T around the staged
+8-token blocks and the segment split, several heads and batch rows, initial
+and in-place states, split/resume, with and without segments, decode steps,
+a state-wiping rate, the error paths and a sampled check at the 8-layer
+model's layer shape (B=8, T=1024, 12 heads of 64).
+
+Tolerance: elementwise |got - ref| / (|ref| + s) <= MATRIX_TOL = 1e-5 with s
+the RMS of the reference output (states: of the reference state). The fp32
+kernel rounds each state entry once per step and that error decays with the
+state: for a row with rate lam it settles near eps_32 * sqrt(1 / (1 - e^-2lam))
+relative to the state (rounding errors of random sign; a coherent worst case
+would be eps_32 / (1 - e^-lam)), and the readout sums 64 such entries of
+random sign. With the slowest rates here (~2e-3, a memory of ~500 steps) that
+is ~1e-6; measured maxima are 0.8-2.1e-6."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import wkv6_recurrent, wkv6_step_ref
+from wkvtest import I, W, dev_f32, host64, say
+
+pytestmark = pytest.mark.gpu
+
+MATRIX_TOL = 1e-5
+D = 64
+
+
+def rms(a):
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a))) if a.size else 1.0
+
+
+def assert_close(got, ref, what, tol=MATRIX_TOL):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - ref) / (np.abs(ref) + max(rms(ref), 1e-30))
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max normalised error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+def mcase(B, T, H, layer=0, wl=I.WORKLOADS[1]):
+    sw = wl.scaled(B=B, T=T, C=H * D)
+    k, v = I.kv(sw, layer)
+    r = I.receptance(sw, layer)
+    lam = I.decay_rates(sw, layer)
+    return lam, k, v, r
+
+
+def random_mstate(B, H, seed):
+    return np.random.default_rng([71, seed]).normal(0, 1, (B, H, D, D)).astype(np.float32)
+
+
+def gpu_matrix(lam, k, v, r, H, state_in=None, workspace="auto"):
+    ds = None if state_in is None else dev_f32(state_in)
+    y, s = W.wkv_matrix_forward(dev_f32(lam), dev_f32(k), dev_f32(v), dev_f32(r), H, ds,
+                                workspace=workspace)
+    torch.cuda.synchronize()
+    return host64(y), host64(s)
+
+
+SHAPES = [(1, 1, 1), (2, 7, 1), (1, 8, 2), (2, 9, 1), (1, 63, 2), (2, 64, 1), (1, 65, 3),
+          (2, 200, 2), (1, 1000, 1), (3, 513, 2), (1, 1500, 1)]
+
+
+@pytest.mark.parametrize("segments", ["auto", "none"])
+@pytest.mark.parametrize("B,T,H", SHAPES)
+def test_matrix_forward(B, T, H, segments):
+    say(f"matrix forward B={B} T={T} H={H} segments={segments}")
+    lam, k, v, r = mcase(B, T, H)
+    got, gst = gpu_matrix(lam, k, v, r, H, workspace="auto" if segments == "auto" else None)
+    ref, rst = wkv6_recurrent(lam, k, v, r, H)
+    e = assert_close(got, ref, "out")
+    assert_close(gst, rst, "state")
+    say(f"  max normalised error {e:.2e}")
+
+
+@pytest.mark.parametrize("segments", ["auto", "none"])
+def test_matrix_from_initial_state_and_in_place(segments):
+    B, T, H = 2, 700, 2
+    say(f"matrix initial state, in place, segments={segments}")
+    lam, k, v, r = mcase(B, T, H, layer=1)
+    s0 = random_mstate(B, H, 1)
+    ds = dev_f32(s0)
+    y, _ = W.wkv_matrix_forward(dev_f32(lam), dev_f32(k), dev_f32(v), dev_f32(r), H, ds,
+                                state_out=ds, workspace="auto" if segments == "auto" else None)
+    torch.cuda.synchronize()
+    ref, rst = wkv6_recurrent(lam, k, v, r, H, s0.astype(np.float64))
+    assert_close(host64(y), ref, "out")
+    assert_close(host64(ds), rst, "state")
+
+
+def test_matrix_split_resume_and_segments_agree():
+    B, T, H = 1, 900, 3
+    say("matrix split/resume")
+    lam, k, v, r = mcase(B, T, H, layer=2)
+    ref, rst = wkv6_recurrent(lam, k, v, r, H)
+    a, sa = gpu_matrix(lam, k, v, r, H)
+    b, sb = gpu_matrix(lam, k, v, r, H, workspace=None)
+    assert_close(a, b, "segmented vs one segment", 2 * MATRIX_TOL)
+    cut = 333
+    y1, s1 = gpu_matrix(lam[:, :cut], k[:, :cut], v[:, :cut], r[:, :cut], H)
+    y2, s2 = gpu_matrix(lam[:, cut:], k[:, cut:], v[:, cut:], r[:, cut:], H,
+                        s1.astype(np.float32))
+    assert_close(np.concatenate([y1, y2], axis=1), ref, "split")
+    assert_close(s2, rst, "split state")
+
+
+def test_matrix_steps_match_oracle_and_forward():
+    B, T, H, S = 3, 40, 2, 10
+    say("matrix decode steps")
+    lam, k, v, r = mcase(B, T + S, H, layer=3)
+    ref, rst = wkv6_recurrent(lam, k, v, r, H)
+    _, st = W.wkv_matrix_forward(dev_f32(lam[:, :T]), dev_f32(k[:, :T]), dev_f32(v[:, :T]),
+                                 dev_f32(r[:, :T]), H)
+    outs = [W.wkv_matrix_step(dev_f32(lam[:, t]), dev_f32(k[:, t]), dev_f32(v[:, t]),
+                              dev_f32(r[:, t]), H, st) for t in range(T, T + S)]
+    torch.cuda.synchronize()
+    got = np.stack([host64(o) for o in outs], axis=1)
+    assert_close(got, ref[:, T:], "steps")
+    assert_close(host64(st), rst, "state after steps")
+    s0 = random_mstate(B, H, 2)
+    ds = dev_f32(s0)
+    o = W.wkv_matrix_step(dev_f32(lam[:, 0]), dev_f32(k[:, 0]), dev_f32(v[:, 0]),
+                          dev_f32(r[:, 0]), H, ds)
+    torch.cuda.synchronize()
+    ro, rs = wkv6_step_ref(lam[:, 0], k[:, 0], v[:, 0], r[:, 0], H, s0.astype(np.float64))
+    assert_close(host64(o), ro, "one step")
+    assert_close(host64(ds), rs, "one step state")
+
+
+def test_matrix_huge_rate_wipes_the_state():
+    B, T, H, t0 = 2, 300, 2, 151
+    say("matrix state-wiping rate")
+    lam, k, v, r = mcase(B, T, H, layer=4)
+    lam[:, t0] = 1e4
+    s0 = random_mstate(B, H, 3)
+    got, gst = gpu_matrix(lam, k, v, r, H, s0)
+    fresh, fst = gpu_matrix(lam[:, t0:], k[:, t0:], v[:, t0:], r[:, t0:], H)
+    assert_close(got[:, t0:], fresh, "after the wipe", 2 * MATRIX_TOL)
+    ref, _ = wkv6_recurrent(lam, k, v, r, H, s0.astype(np.float64))
+    assert_close(got, ref, "out")
+
+
+def test_matrix_deterministic():
+    B, T, H = 2, 1100, 2
+    say("matrix determinism")
+    lam, k, v, r = mcase(B, T, H, layer=5)
+    a, sa = gpu_matrix(lam, k, v, r, H)
+    b, sb = gpu_matrix(lam, k, v, r, H)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
+def test_matrix_empty_and_degenerate_sizes():
+    say("matrix T=0, B=0")
+    B, H = 2, 2
+    s0 = random_mstate(B, H, 4)
+    ds, dso = dev_f32(s0), dev_f32(np.full((B, H, D, D), 7.0))
+    e = torch.empty((B, 0, H * D), device="cuda")
+    W.wkv_matrix_forward(e, e, e, e, H, ds, state_out=dso)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(dso), s0.astype(np.float64))
+    W.wkv_matrix_forward(e, e, e, e, H, None, state_out=dso)
+    torch.cuda.synchronize()
+    assert np.all(host64(dso) == 0)
+    z = torch.zeros((0, 5, H * D), device="cuda")
+    y, _ = W.wkv_matrix_forward(z, z, z, z, H)
+    assert y.shape == (0, 5, H * D)
+
+
+def test_matrix_abi_errors():
+    say("matrix abi errors")
+    lib = W.load_library()
+    B, T, H = 1, 16, 1
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    z = lambda *s: torch.zeros(s, device="cuda")
+    w, k, v, r, o = (z(B, T, H * D) for _ in range(5))
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    base = [B, T, H, D, P(w), P(k), P(v), P(r), None, P(o), None]
+    assert lib.wkv_matrix_forward(*base, None, 0, s) == 0
+    bad = list(base)
+    bad[3] = 32
+    assert lib.wkv_matrix_forward(*bad, None, 0, s) == 2      # only head size 64
+    bad = list(base)
+    bad[7] = None
+    assert lib.wkv_matrix_forward(*bad, None, 0, s) == 1      # receptance missing
+    bad = list(base)
+    bad[9] = P(k)
+    assert lib.wkv_matrix_forward(*bad, None, 0, s) == 4      # out on top of k
+    st = z(B, H, D, D)
+    x = z(B, H * D)
+    assert lib.wkv_matrix_step(B, H, D, P(x), P(x), P(x), P(x), P(st), P(z(B, H * D)), s) == 0
+    assert lib.wkv_matrix_step(B, H, 16, P(x), P(x), P(x), P(x), P(st), P(z(B, H * D)), s) == 2
+    assert lib.wkv_matrix_step(B, H, D, P(x), P(x), P(x), P(x), P(st), P(x), s) == 4
+    torch.cuda.synchronize()
+
+
+def test_matrix_layer_shape_sampled():
+    """B=8, T=1024, C=768 (12 heads of 64), the 8-layer model's layer shape,
+    with the segments the library picks; heads 0 and 7 of every batch row
+    against the oracle (heads are independent, so a head slice is exact)."""
+    wl = I.WORKLOADS[1]
+    H = wl.C // D
+    say(f"matrix layer shape B={wl.B} T={wl.T} H={H}")
+    k, v = I.kv(wl, 0)
+    r = I.receptance(wl, 0)
+    lam = I.decay_rates(wl, 0)
+    got, gst = gpu_matrix(lam, k, v, r, H)
+    for h in (0, 7):
+        sl = slice(h * D, (h + 1) * D)
+        ref, rst = wkv6_recurrent(lam[..., sl], k[..., sl], v[..., sl], r[..., sl], 1)
+        e = assert_close(got[..., sl], ref, f"head {h}")
+        assert_close(gst[:, h:h + 1], rst, f"head {h} state")
+        say(f"  head {h}: max normalised error {e:.2e}")

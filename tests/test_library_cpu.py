@@ -167,6 +167,26 @@ def test_per_token_decay_entry_points_validate_without_device():
     assert lib.wkv_step_dd(2, 4, w, u, k, v, P(a + 65536), out, 5, nul) == 7
 
 
+def test_matrix_entry_points_validate_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    a = 0x10000000
+    w, k, v, r, out = P(a), P(a + 8192), P(a + 16384), P(a + 24576), P(a + 32768)
+    # B, T, H, D, w, k, v, r, state_in, out, state_out, workspace, bytes, stream
+    assert lib.wkv_matrix_forward(1, 2, 1, 32, w, k, v, r, nul, out, nul, nul, 0, nul) == 2
+    assert lib.wkv_matrix_forward(-1, 2, 1, 64, w, k, v, r, nul, out, nul, nul, 0, nul) == 2
+    assert lib.wkv_matrix_forward(0, 2, 1, 64, nul, nul, nul, nul, nul, nul, nul, nul, 0, nul) == 0
+    assert lib.wkv_matrix_forward(1, 2, 1, 64, w, k, v, nul, nul, out, nul, nul, 0, nul) == 1
+    assert lib.wkv_matrix_forward(1, 2, 1, 64, w, k, v, r, nul, k, nul, nul, 0, nul) == 4
+    assert lib.wkv_matrix_forward(1, 2, 1, 64, P(a + 4), k, v, r, nul, out, nul, nul, 0, nul) == 3
+    assert lib.wkv_matrix_workspace_size(1, 2, 1, 16) == -2
+    # B, H, D, w, k, v, r, state, out, stream
+    assert lib.wkv_matrix_step(1, 1, 16, w, k, v, r, P(a + 65536), out, nul) == 2
+    assert lib.wkv_matrix_step(1, 1, 64, w, k, v, r, nul, out, nul) == 1
+    assert lib.wkv_matrix_step(1, 1, 64, w, k, v, r, P(a + 65536), w, nul) == 4
+
+
 def test_per_token_decay_rates_are_seeded_and_positive():
     wl = I.WORKLOADS[1].scaled(B=3, T=50, C=32)
     r1 = I.decay_rates(wl)

@@ -10,10 +10,12 @@ into that interface (see _lib). Build the library with
     y = wkv_step(w, u, k_t, v_t, state)             # decode, state in place
     gw, gu, gk, gv, gs = wkv_backward(w, u, k, v, gout)  # gradients
     out, state = wkv_forward_dd(w_t, u, k, v)     # per-token decay w_t (B, T, C)
+    y, S = wkv_matrix_forward(w_t, k, v, r, H)     # matrix-valued state per head
 """
 
 from ._lib import (  # noqa: F401
     LIBRARY_PATH,
+    MATRIX_HEAD,
     WKV_IO_BF16,
     WKV_IO_F32,
     WKV_PATH_AUTO,
@@ -36,6 +38,9 @@ from ._lib import (  # noqa: F401
     wkv_forward_ex,
     wkv_forward_gated,
     wkv_forward_ws,
+    wkv_matrix_forward,
+    wkv_matrix_step,
+    wkv_matrix_workspace_size,
     wkv_select_path,
     wkv_status_string,
     wkv_step,

@@ -70,13 +70,17 @@ def load_library() -> ctypes.CDLL:
         "wkv_backward_workspace_size": [i64, i64, i64],
         "wkv_forward_dd": [i64, i64, i64] + [vp] * 7 + [ci, ci, vp],
         "wkv_step_dd": [i64, i64] + [vp] * 6 + [ci, vp],
+        "wkv_matrix_forward": [i64, i64, i64, i64] + [vp] * 8 + [i64, vp],
+        "wkv_matrix_workspace_size": [i64, i64, i64, i64],
+        "wkv_matrix_step": [i64, i64, i64] + [vp] * 6 + [vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = {"wkv_status_string": ctypes.c_char_p,
                       "wkv_workspace_size": ctypes.c_int64,
-                      "wkv_backward_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
+                      "wkv_backward_workspace_size": ctypes.c_int64,
+                      "wkv_matrix_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
     if lib.wkv_abi_version() != 1:
         raise RuntimeError(f"{LIBRARY_PATH}: unexpected ABI version {lib.wkv_abi_version()}")
     _lib = lib
@@ -496,6 +500,85 @@ def wkv_step_dd(w, u, k, v, state, out=None, *, stream=None):
         st = lib.wkv_step_dd(B, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state), _ptr(out), io,
                              _stream_handle(dev, stream))
     _check(st, "wkv_step_dd")
+    return out
+
+
+MATRIX_HEAD = 64
+
+
+def wkv_matrix_workspace_size(B: int, T: int, H: int, D: int = MATRIX_HEAD) -> int:
+    """Bytes of workspace that lets wkv_matrix_forward use all its segments."""
+    r = load_library().wkv_matrix_workspace_size(B, T, H, D)
+    if r < 0:
+        raise WKVError("wkv_matrix_workspace_size", -r)
+    return int(r)
+
+
+def wkv_matrix_forward(w, k, v, r, H: int, state_in=None, out=None, state_out=None, *,
+                       workspace="auto", want_state=True, stream=None):
+    """wkv_matrix_forward: the matrix-valued-state recurrence over (B, T, C),
+    C = H * 64, float32. w: positive decay rates; k, v, r: key, value,
+    receptance, all (B, T, C); states (B, H, 64, 64). workspace: a uint8
+    tensor, None (no segments) or "auto" (one of wkv_matrix_workspace_size
+    bytes, allocated for the call). Returns (out, state_out)."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    B, T, C = k.shape
+    if H <= 0 or C != H * MATRIX_HEAD:
+        raise ValueError(f"C = {C} must be H * {MATRIX_HEAD} with H = {H}")
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    f32 = torch.float32
+    for name, t in (("w", w), ("k", k), ("v", v), ("r", r)):
+        _need(t, name, f32, (B, T, C), dev)
+    sshape = (B, H, MATRIX_HEAD, MATRIX_HEAD)
+    if state_in is not None:
+        _need(state_in, "state_in", f32, sshape, dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=f32, device=dev)
+    _need(out, "out", f32, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty(sshape, dtype=f32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", f32, sshape, dev)
+    with torch.cuda.device(dev):
+        if isinstance(workspace, str):
+            n = wkv_matrix_workspace_size(B, T, H)
+            workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
+        elif workspace is not None and (workspace.device != dev or workspace.dtype != torch.uint8
+                                        or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
+        st = lib.wkv_matrix_forward(B, T, H, MATRIX_HEAD, _ptr(w), _ptr(k), _ptr(v), _ptr(r),
+                                    _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(),
+                                    _stream_handle(dev, stream))
+    _check(st, "wkv_matrix_forward")
+    return out, state_out
+
+
+def wkv_matrix_step(w, k, v, r, H: int, state, out=None, *, stream=None):
+    """wkv_matrix_step: one token (B, C) of the matrix-valued-state recurrence;
+    the state (B, H, 64, 64) is updated in place. Returns out (B, C)."""
+    lib = load_library()
+    if k.dim() != 2:
+        raise ValueError(f"k must be (B, C), got shape {tuple(k.shape)}")
+    B, C = k.shape
+    if H <= 0 or C != H * MATRIX_HEAD:
+        raise ValueError(f"C = {C} must be H * {MATRIX_HEAD} with H = {H}")
+    dev = k.device
+    f32 = torch.float32
+    for name, t in (("w", w), ("k", k), ("v", v), ("r", r)):
+        _need(t, name, f32, (B, C), dev)
+    _need(state, "state", f32, (B, H, MATRIX_HEAD, MATRIX_HEAD), dev)
+    if out is None:
+        out = torch.empty((B, C), dtype=f32, device=dev)
+    _need(out, "out", f32, (B, C), dev)
+    with torch.cuda.device(dev):
+        st = lib.wkv_matrix_step(B, H, MATRIX_HEAD, _ptr(w), _ptr(k), _ptr(v), _ptr(r),
+                                 _ptr(state), _ptr(out), _stream_handle(dev, stream))
+    _check(st, "wkv_matrix_step")
     return out
 
 

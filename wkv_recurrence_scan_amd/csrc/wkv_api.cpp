@@ -273,6 +273,97 @@ int step_dd_impl(int64_t B, int64_t C, const void* w, const float* u, const void
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
 
+// Matrix-valued state: segments for these sizes on this device, limited to
+// what the workspace holds (one segment, i.e. none, without a workspace).
+int64_t matrix_plan(int64_t B, int64_t T, int64_t H, int dev, int64_t ws_bytes) {
+  int64_t P = wkv::matrix_segments(B, T, H, cu_count(dev));
+  while (P > 1 && wkv::matrix_workspace_bytes(B, T, H, P) > ws_bytes) --P;
+  return P;
+}
+
+int matrix_forward_impl(int64_t B, int64_t T, int64_t H, int64_t D, const float* w,
+                        const float* k, const float* v, const float* r, const float* state_in,
+                        float* out, float* state_out, void* workspace, int64_t workspace_bytes,
+                        hipStream_t stream) {
+  if (B < 0 || T < 0 || H < 0 || D < 0) return WKV_ERR_DIM;
+  if (D != wkv::kMatrixHead) return WKV_ERR_DIM;
+  int64_t seq_bytes, state_bytes;
+  if (!mul3(B, T, H * D, &seq_bytes) || __builtin_mul_overflow(seq_bytes, 4, &seq_bytes) ||
+      seq_bytes > kMaxBytes)
+    return WKV_ERR_DIM;
+  if (!mul3(B, H, D * D * 4, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (B == 0 || H == 0) return WKV_OK;
+  if (T > 0 && (w == nullptr || k == nullptr || v == nullptr || r == nullptr || out == nullptr))
+    return WKV_ERR_NULL;
+  const void* all[] = {w, k, v, r, out};
+  for (const void* p : all)
+    if (misaligned(p, 8)) return WKV_ERR_ALIGN;
+  if (misaligned(state_in, 16) || misaligned(state_out, 16)) return WKV_ERR_ALIGN;
+  const int64_t sbytes = T > 0 ? seq_bytes : 0;
+  const void* ins[] = {w, k, v, r};
+  for (const void* p : ins) {
+    if (overlaps(out, sbytes, p, sbytes) || overlaps(state_out, state_bytes, p, sbytes))
+      return WKV_ERR_ALIAS;
+  }
+  if (overlaps(out, sbytes, state_in, state_bytes) || overlaps(out, sbytes, state_out, state_bytes))
+    return WKV_ERR_ALIAS;
+  if (state_out != state_in && overlaps(state_out, state_bytes, state_in, state_bytes))
+    return WKV_ERR_ALIAS;
+  if (workspace_bytes < 0) return WKV_ERR_WORKSPACE;
+  const int64_t wsb = workspace == nullptr ? 0 : workspace_bytes;
+  if (wsb > 0) {
+    if (misaligned(workspace, 256)) return WKV_ERR_ALIGN;
+    const void* every[] = {w, k, v, r, out};
+    for (const void* p : every)
+      if (overlaps(workspace, wsb, p, sbytes)) return WKV_ERR_ALIAS;
+    if (overlaps(workspace, wsb, state_in, state_bytes) ||
+        overlaps(workspace, wsb, state_out, state_bytes))
+      return WKV_ERR_ALIAS;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  if (T == 0) {
+    if (state_out == nullptr || state_out == state_in) return WKV_OK;
+    e = wkv::launch_matrix_state_copy(B, H, state_in, state_out, stream);
+    return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+  }
+  const int64_t P = matrix_plan(B, T, H, dev, wsb);
+  const wkv::MatrixArgs a{B, T, H, w, k, v, r, state_in, out, state_out};
+  e = wkv::launch_matrix(a, P, workspace, stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
+int matrix_step_impl(int64_t B, int64_t H, int64_t D, const float* w, const float* k,
+                     const float* v, const float* r, float* state, float* out,
+                     hipStream_t stream) {
+  if (B < 0 || H < 0 || D < 0) return WKV_ERR_DIM;
+  if (D != wkv::kMatrixHead) return WKV_ERR_DIM;
+  int64_t io_bytes, state_bytes;
+  if (!mul3(B, H, D * 4, &io_bytes) || io_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (!mul3(B, H, D * D * 4, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (B == 0 || H == 0) return WKV_OK;
+  if (w == nullptr || k == nullptr || v == nullptr || r == nullptr || state == nullptr ||
+      out == nullptr)
+    return WKV_ERR_NULL;
+  const void* all[] = {w, k, v, r, out};
+  for (const void* p : all)
+    if (misaligned(p, 4)) return WKV_ERR_ALIGN;
+  if (misaligned(state, 16)) return WKV_ERR_ALIGN;
+  const void* ins[] = {w, k, v, r};
+  for (const void* p : ins) {
+    if (overlaps(out, io_bytes, p, io_bytes) || overlaps(state, state_bytes, p, io_bytes))
+      return WKV_ERR_ALIAS;
+  }
+  if (overlaps(out, io_bytes, state, state_bytes)) return WKV_ERR_ALIAS;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  const wkv::MatrixStepArgs a{B, H, w, k, v, r, state, out};
+  e = wkv::launch_matrix_step(a, stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
 int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                   const float* k, const float* v, const float* r, const float* state_in,
                   const float* state_out, const float* gstate_out, const float* gout, float* gk,
@@ -405,6 +496,33 @@ int wkv_forward_dd(int64_t B, int64_t T, int64_t C, const void* w, const float* 
 int wkv_step_dd(int64_t B, int64_t C, const void* w, const float* u, const void* k, const void* v,
                 float* state, void* out, int io, hipStream_t stream) {
   return step_dd_impl(B, C, w, u, k, v, state, out, io, stream);
+}
+
+int wkv_matrix_forward(int64_t B, int64_t T, int64_t H, int64_t D, const float* w,
+                       const float* k, const float* v, const float* r, const float* state_in,
+                       float* out, float* state_out, void* workspace, int64_t workspace_bytes,
+                       hipStream_t stream) {
+  return matrix_forward_impl(B, T, H, D, w, k, v, r, state_in, out, state_out, workspace,
+                             workspace_bytes, stream);
+}
+
+int64_t wkv_matrix_workspace_size(int64_t B, int64_t T, int64_t H, int64_t D) {
+  if (B < 0 || T < 0 || H < 0 || D < 0) return -WKV_ERR_DIM;
+  if (D != wkv::kMatrixHead) return -WKV_ERR_DIM;
+  int64_t cells;
+  if (!mul3(B, T, H * D, &cells) || cells > kMaxBytes) return -WKV_ERR_DIM;
+  if (B == 0 || H == 0 || T == 0) return 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
+  const int64_t P = wkv::matrix_segments(B, T, H, cu_count(dev));
+  return wkv::matrix_workspace_bytes(B, T, H, P);
+}
+
+int wkv_matrix_step(int64_t B, int64_t H, int64_t D, const float* w, const float* k,
+                    const float* v, const float* r, float* state, float* out,
+                    hipStream_t stream) {
+  return matrix_step_impl(B, H, D, w, k, v, r, state, out, stream);
 }
 
 int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path) {

@@ -108,6 +108,36 @@ hipError_t launch_dd_seq(const DdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_dd_step(const DdStepArgs& a, int io, int vec, hipStream_t s);
 
+// Matrix-valued state (head size 64, fp32): r, k, v, lam, out [B][T][H*64];
+// states [B][H][64][64].
+struct MatrixArgs {
+  int64_t B, T, H;
+  const float* lam;
+  const float* k;
+  const float* v;
+  const float* r;
+  const float* state_in;  // nullptr: zero state
+  float* out;
+  float* state_out;       // nullptr: not written
+};
+struct MatrixStepArgs {
+  int64_t B, H;
+  const float* lam;
+  const float* k;
+  const float* v;
+  const float* r;
+  float* state;
+  float* out;
+};
+constexpr int64_t kMatrixHead = 64;
+int64_t matrix_segments(int64_t B, int64_t T, int64_t H, int cus);
+int64_t matrix_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t P);
+hipError_t launch_matrix(const MatrixArgs& m, int64_t P, void* ws, hipStream_t s);
+hipError_t launch_matrix_step(const MatrixStepArgs& m, hipStream_t s);
+// T == 0: state_out <- state_in, or zeros when state_in is null.
+hipError_t launch_matrix_state_copy(int64_t B, int64_t H, const float* src, float* dst,
+                                    hipStream_t s);
+
 hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);
