@@ -65,37 +65,72 @@ struct MsStage {
   float r[R ? kMsU : 1][kMsD];
 };
 
-// Thread t's share of a block: token t / 32, channels 2 (t % 32) and the next.
+// Thread t's share of a block: token t / TPR, channels FV (t % TPR) and the
+// FV - 1 after them (TPR threads per 64-channel row).
+constexpr int kMsFV = kMsU * kMsD / kMsThreads;
+constexpr int kMsTPR = kMsD / kMsFV;
+typedef float msvec __attribute__((ext_vector_type(kMsFV)));
+
 template <bool R>
 struct MsPrefetch {
-  float2 k, v, lam, r;
+  msvec k, v, lam, r;
 };
 
 template <bool R>
 __device__ __forceinline__ void ms_fetch(MsPrefetch<R>& f, const MsKernelArgs& a, int64_t row0,
                                          int64_t t0, int64_t tend) {
-  const int u = threadIdx.x >> 5;
-  const int c = 2 * (threadIdx.x & 31);
+  const int u = threadIdx.x / kMsTPR;
+  const int c = kMsFV * (threadIdx.x % kMsTPR);
   const int64_t t = t0 + u;
   if (t < tend) {
     const int64_t off = row0 + t * a.H * kMsD + c;
-    f.k = *reinterpret_cast<const float2*>(a.k + off);
-    f.v = *reinterpret_cast<const float2*>(a.v + off);
-    f.lam = *reinterpret_cast<const float2*>(a.lam + off);
-    if constexpr (R) f.r = *reinterpret_cast<const float2*>(a.r + off);
+    f.k = *reinterpret_cast<const msvec*>(a.k + off);
+    f.v = *reinterpret_cast<const msvec*>(a.v + off);
+    f.lam = *reinterpret_cast<const msvec*>(a.lam + off);
+    if constexpr (R) f.r = *reinterpret_cast<const msvec*>(a.r + off);
   } else {
-    f.k = f.v = f.lam = f.r = float2{0.0f, 0.0f};
+    f.k = f.v = f.lam = f.r = msvec{};
   }
 }
 
 template <bool R>
 __device__ __forceinline__ void ms_put(MsStage<R>& s, const MsPrefetch<R>& f) {
-  const int u = threadIdx.x >> 5;
-  const int c = 2 * (threadIdx.x & 31);
-  *reinterpret_cast<float2*>(&s.k[u][c]) = f.k;
-  *reinterpret_cast<float2*>(&s.v[u][c]) = f.v;
-  *reinterpret_cast<float2*>(&s.lam[u][c]) = f.lam;
-  if constexpr (R) *reinterpret_cast<float2*>(&s.r[u][c]) = f.r;
+  const int u = threadIdx.x / kMsTPR;
+  const int c = kMsFV * (threadIdx.x % kMsTPR);
+  *reinterpret_cast<msvec*>(&s.k[u][c]) = f.k;
+  *reinterpret_cast<msvec*>(&s.v[u][c]) = f.v;
+  *reinterpret_cast<msvec*>(&s.lam[u][c]) = f.lam;
+  if constexpr (R) *reinterpret_cast<msvec*>(&s.r[u][c]) = f.r;
+}
+
+// The first nt tokens of a staged block (FULL: all kMsU of them, without
+// guards, so the state stays in place across tokens).
+template <bool READ, bool FULL>
+__device__ __forceinline__ void ms_tokens(const MsStage<READ>& st, float (*part)[kMsU][kMsD],
+                                          int nt, float (&S)[kMsJW], float& prod) {
+  const int lane = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < kMsU; ++u) {
+    if (FULL || u < nt) {
+      const float ki = st.k[u][lane];
+      const float wf = fast_exp2(st.lam[u][lane] * -kLog2e);
+      prod *= wf;
+      float vj[kMsJW], kj[kMsJW];
+#pragma unroll
+      for (int c = 0; c < kMsJW; ++c) {
+        vj[c] = st.v[u][q * kMsJW + c];
+        kj[c] = st.k[u][q * kMsJW + c];
+      }
+      float p = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kMsJW; ++c) {
+        S[c] = __builtin_fmaf(wf, S[c], ki * vj[c]);
+        if constexpr (READ) p = __builtin_fmaf(S[c], kj[c], p);
+      }
+      if constexpr (READ) part[q][u][lane] = p;
+    }
+  }
 }
 
 // Walks tokens [t0, tend) of one (batch, head) from the state in S (this
@@ -121,26 +156,10 @@ __device__ __forceinline__ float ms_walk(const MsKernelArgs& a, int64_t row0, in
     const MsStage<READ>& st = stage[n & 1];
     const int64_t tb = t0 + n * kMsU;
     const int nt = tend - tb < kMsU ? static_cast<int>(tend - tb) : kMsU;
-#pragma unroll
-    for (int u = 0; u < kMsU; ++u) {
-      if (u < nt) {
-        const float ki = st.k[u][lane];
-        const float wf = fast_exp2(st.lam[u][lane] * -kLog2e);
-        prod *= wf;
-        float vj[kMsJW], kj[kMsJW];
-#pragma unroll
-        for (int c = 0; c < kMsJW; ++c) {
-          vj[c] = st.v[u][q * kMsJW + c];
-          kj[c] = st.k[u][q * kMsJW + c];
-        }
-        float p = 0.0f;
-#pragma unroll
-        for (int c = 0; c < kMsJW; ++c) {
-          S[c] = __builtin_fmaf(wf, S[c], ki * vj[c]);
-          if constexpr (READ) p = __builtin_fmaf(S[c], kj[c], p);
-        }
-        if constexpr (READ) part[n & 1][q][u][lane] = p;
-      }
+    if (nt == kMsU) {
+      ms_tokens<READ, true>(st, part[n & 1], nt, S, prod);
+    } else {
+      ms_tokens<READ, false>(st, part[n & 1], nt, S, prod);
     }
     // wave q finishes tokens q and q + 4 of the block after the barrier; it
     // takes their receptance now, since the next block's data may overwrite
