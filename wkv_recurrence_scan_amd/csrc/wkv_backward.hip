@@ -377,6 +377,8 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(BwdKernelArgs
 //      the later segments' own sums, folded from the last one down), then the
 //      backward walk over the segment's chunks.
 // Thread i is lane i % lanes of segment i / lanes.
+constexpr int kFoldBatch = 8;  // earlier/later segment sums fetched together
+
 __device__ __forceinline__ void seg_bounds(const BwdKernelArgs& a, const LaneIo& io, int64_t s,
                                            int64_t& j0, int64_t& j1) {
   const int64_t nch = io.nfull + (io.rest > 0 ? 1 : 0);
@@ -413,8 +415,18 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   // start state: the initial state, then every earlier segment (all full)
   Lane x = initial_lane(a, lanes, lane);
   const float seg_len = static_cast<float>(a.seg_chunks * kLc);
-  for (int64_t r = 0; r < s; ++r) {
-    const float4 f = a.seg_fwd[r * lanes + lane];
+  // (summaries fetched kFoldBatch at a time so that their loads overlap; the
+  // fold order is unchanged)
+  int64_t sr = 0;
+  for (; sr + kFoldBatch <= s; sr += kFoldBatch) {
+    float4 f[kFoldBatch];
+#pragma unroll
+    for (int m = 0; m < kFoldBatch; ++m) f[m] = a.seg_fwd[(sr + m) * lanes + lane];
+#pragma unroll
+    for (int m = 0; m < kFoldBatch; ++m) lane_absorb(x, Seg{f[m].x, f[m].y, f[m].z, seg_len}, wc);
+  }
+  for (; sr < s; ++sr) {
+    const float4 f = a.seg_fwd[sr * lanes + lane];
     lane_absorb(x, Seg{f.x, f.y, f.z, seg_len}, wc);
   }
   // forward over the segment: checkpoints, and the segment's own suffix sums
@@ -473,15 +485,13 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKe
   // later segment X (last first): the sums decay across X's L tokens (their
   // age-weighted parts gain L times the plain ones) and X's own sums are added
   Suffix acc = suffix_init(a.state_out, a.gstate_out, lanes, lane);
-  for (int64_t x = a.segments - 1; x > s; --x) {
+  const int64_t nch = io.nfull + (io.rest > 0 ? 1 : 0);
+  auto absorb_later = [&](int64_t x, const float4& X, float zx) {
     const int64_t xj0 = x * a.seg_chunks;
-    const int64_t nch = io.nfull + (io.rest > 0 ? 1 : 0);
     const int64_t xj1 = xj0 + a.seg_chunks < nch ? xj0 + a.seg_chunks : nch;
     const float L = static_cast<float>((xj1 - xj0) * kLc - (xj1 > io.nfull && io.rest > 0
                                                                 ? kLc - io.rest
                                                                 : 0));
-    const float4 X = a.seg_rev[x * lanes + lane];
-    const float zx = a.seg_rev_z[x * lanes + lane];
     const float sg = __builtin_fmaf(acc.za + L, wc, zx - acc.zb);  // zx - (z - L w)
     const float e = fast_exp2(__builtin_fabsf(sg) * -kLog2e);
     const bool xw = sg > 0.0f;
@@ -493,7 +503,21 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKe
     acc.q = __builtin_fmaf(fo, acc.q, fx * X.y);
     acc.zb = xw ? zx : acc.zb;
     acc.za = xw ? 0.0f : acc.za + L;
+  };
+  // later segments, last first, their sums fetched kFoldBatch at a time
+  int64_t x = a.segments - 1;
+  for (; x - kFoldBatch >= s; x -= kFoldBatch) {
+    float4 X[kFoldBatch];
+    float zx[kFoldBatch];
+#pragma unroll
+    for (int m = 0; m < kFoldBatch; ++m) {
+      X[m] = a.seg_rev[(x - m) * lanes + lane];
+      zx[m] = a.seg_rev_z[(x - m) * lanes + lane];
+    }
+#pragma unroll
+    for (int m = 0; m < kFoldBatch; ++m) absorb_later(x - m, X[m], zx[m]);
   }
+  for (; x > s; --x) absorb_later(x, a.seg_rev[x * lanes + lane], a.seg_rev_z[x * lanes + lane]);
   float gw_acc = 0.0f, gu_acc = 0.0f;
   backward_chunks<G>(io, j0, j1, a.ckpt, lanes, lane, wc, uc, acc, gw_acc, gu_acc);
   if (s == 0) {
@@ -519,7 +543,22 @@ __global__ __launch_bounds__(kRedCh * kRedSlices) void wkv_grad_reduce_kernel(
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCh + ch;
   float aw = 0.0f, au = 0.0f;
   if (c < C) {
-    for (int64_t b = slice; b < B; b += kRedSlices) {
+    // rows b = slice, slice + 16, ... in order, fetched four at a time
+    int64_t b = slice;
+    for (; b + 3 * kRedSlices < B; b += 4 * kRedSlices) {
+      float xw[4], xu[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        xw[m] = gw_part[(b + m * kRedSlices) * C + c];
+        xu[m] = gu_part[(b + m * kRedSlices) * C + c];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        aw += xw[m];
+        au += xu[m];
+      }
+    }
+    for (; b < B; b += kRedSlices) {
       aw += gw_part[b * C + c];
       au += gu_part[b * C + c];
     }
