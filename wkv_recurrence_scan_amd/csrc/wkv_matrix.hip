@@ -13,38 +13,70 @@
 // Layout: r, k, v, lam, y are [B][T][C] with C = H * 64 (channel h*64 + i);
 // a state is [B][H][64][64], row i then column j.
 //
-// Work split. A workgroup of 4 waves owns one (batch, head) over one segment
-// of the sequence: lane i of every wave holds row i of the state, and wave q
-// holds its columns 16q .. 16q+15, so every wave updates 64 x 16 entries and
-// forms a partial readout over its 16 columns; the four partials of each
-// token meet in LDS. Token rows (k, v, lam and r: 256 bytes each) are staged
-// through LDS a block of 8 tokens at a time, double-buffered, with the next
-// block's global loads in flight while the current one is computed; a wave
-// reads its 16 key and value entries of a token as broadcast LDS reads.
+// Chunked form. The recurrence is linear in the state, so over a chunk of
+// L = 16 tokens with decay factors w_t = e^-lam_t the state moves as
+//   S_end = diag(E_15) S_start + sum_s diag(P_(s,15)) k_s v_s^T
+// and the outputs are
+//   y_t = sigmoid(r_t) (E_t (S_start k_t) + sum_(s<=t) P_(s,t) k_s (v_s . k_t)),
+// where E_t is the product of the chunk's factors up to and including token
+// t and P_(s,t) the product over the tokens after s up to t (elementwise per
+// row i). Three 64-deep contractions per chunk run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32): the readout S_start k_t for the 16 tokens, the
+// key-value products G[s][t] = v_s . k_t, and the state update V^T K^ with
+// K^[s][i] = P_(s,15)[i] k_s[i]. The remaining causal sum over s <= t is
+// elementwise per row and runs on the vector units.
+//
+// The factors are only ever multiplied, never divided, so a huge rate sends
+// the affected terms to zero and nothing overflows: the chunk is cut into
+// four blocks of four tokens, P_(s,t) for s and t in different blocks is
+// (product over the rest of s's block) x (whole blocks in between) x
+// (product over t's block up to t), and inside a block the products are taken
+// directly.
+//
+// Work split. A workgroup of four waves owns one (batch, head) over one
+// segment of the sequence; wave w owns state rows i = 16w .. 16w+15. Lane
+// (n = lane % 16, q = lane / 16) holds, in the accumulator layout of the
+// matrix instruction, S[16w + n][16m + 4q + e] for m, e = 0..3, so the state
+// stays in registers across chunks and feeds the readout as its B operand
+// with no data movement. The readout's token rows are permuted so that lane
+// q's four tokens are q, 7 - q, 8 + q and 15 - q -- one in each block, with
+// the same amount of causal-sum work on every lane. Each chunk's rows of k,
+// v, lam and r (256 bytes per row) are staged once through LDS by the whole
+// workgroup, double-buffered, with the next chunk's global loads in flight
+// while the current one is computed; the staging threads turn lam into the
+// factor e^-lam and r into its gate, and also store k, v and the factors
+// transposed (channel-major) for the column reads of the causal sum.
 //
 // Segments. With few (batch, head) pairs the sequence is cut into P segments
-// so that there are enough workgroups: a first kernel runs every segment but
-// the last from the zero state and stores its final state and, per row, the
-// product of its decay factors; the second kernel starts each segment from
-// the state in front of it -- the initial state carried through the earlier
-// segments in order, S <- diag(A_p) S + S_p (the recurrence itself, one step
-// per segment) -- and re-runs it with the readout. No atomics, no waits; the
-// result does not depend on P beyond rounding.
+// (of a whole number of chunks) so that there are enough workgroups: a first
+// kernel runs every segment but the last from the zero state (state update
+// only) and stores its final state and, per row, the product of its decay
+// factors; the second kernel starts each segment from the state in front of
+// it -- the initial state carried through the earlier segments in order,
+// S <- diag(A_p) S + S_p (the recurrence itself, one step per segment) -- and
+// runs it with the readout. No atomics, no waits; the result does not depend
+// on P beyond rounding.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
 namespace wkv {
 namespace {
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 constexpr int kMsD = 64;                    // head size
-constexpr int kMsJW = 16;                   // state columns per wave
-constexpr int kMsWaves = kMsD / kMsJW;      // 4 waves per workgroup
+constexpr int kMsL = 16;                    // tokens per chunk
+constexpr int kMsWaves = 4;                 // wave w owns state rows 16w ..
 constexpr int kMsThreads = 64 * kMsWaves;
-constexpr int kMsU = 8;                     // tokens per staged block
+constexpr int kMsRow = kMsD + 4;            // padded row of a token-major tile
+constexpr int kMsCol = kMsL + 4;            // padded row of a channel-major tile
+
+// decode step kernel: lane i holds row i, wave q columns 16q ..
+constexpr int kMsJW = 16;
 
 struct MsKernelArgs {
   int64_t B, T, H;
-  int64_t P, SL;          // P segments of SL tokens (the last may be shorter)
+  int64_t P, SL;          // P segments of SL tokens (a multiple of kMsL; the last may be shorter)
   const float* lam;
   const float* k;
   const float* v;
@@ -56,147 +88,296 @@ struct MsKernelArgs {
   float* seg_decay;       // [P-1][B*H][64]: product of segment p's decay factors per row
 };
 
-// One staged block of token rows.
-template <bool R>
-struct MsStage {
-  float k[kMsU][kMsD];
-  float v[kMsU][kMsD];
-  float lam[kMsU][kMsD];
-  float r[R ? kMsU : 1][kMsD];
+// One staged chunk, per channel i and block b of four tokens: the decay
+// factors, the keys raw and decayed to the end of their block, the values and
+// the gates (channel-major), and the product of the block's factors. READ:
+// also the token-major keys and values for the matrix operands.
+template <bool READ>
+struct alignas(16) MsStage {
+  float wt[kMsD][kMsCol];               // decay factors e^-lam
+  float kd[kMsD][kMsCol];               // k_s * factors after s up to the end of its block
+  float vt[kMsD][kMsCol];               // values
+  float kt[READ ? kMsD : 1][kMsCol];    // keys
+  float gt[READ ? kMsD : 1][kMsCol];    // gates sigmoid(r)
+  float bp[kMsD][4];                    // product of the factors of block b
+  float kr[READ ? kMsL : 1][kMsRow];    // keys, token-major
+  float vr[READ ? kMsL : 1][kMsRow];    // values, token-major
 };
 
-// Thread t's share of a block: token t / TPR, channels FV (t % TPR) and the
-// FV - 1 after them (TPR threads per 64-channel row).
-constexpr int kMsFV = kMsU * kMsD / kMsThreads;
-constexpr int kMsTPR = kMsD / kMsFV;
-typedef float msvec __attribute__((ext_vector_type(kMsFV)));
-
-template <bool R>
+// Thread x's share of a chunk: channel x % 64, tokens 4 (x / 64) .. + 3
+// (every load instruction of a wave reads one 256-byte token row).
+template <bool READ>
 struct MsPrefetch {
-  msvec k, v, lam, r;
+  float k[4], v[4], lam[4], r[READ ? 4 : 1];
 };
 
-template <bool R>
-__device__ __forceinline__ void ms_fetch(MsPrefetch<R>& f, const MsKernelArgs& a, int64_t row0,
+template <bool READ>
+__device__ __forceinline__ void ms_fetch(MsPrefetch<READ>& f, const MsKernelArgs& a, int64_t row0,
                                          int64_t t0, int64_t tend) {
-  const int u = threadIdx.x / kMsTPR;
-  const int c = kMsFV * (threadIdx.x % kMsTPR);
-  const int64_t t = t0 + u;
-  if (t < tend) {
-    const int64_t off = row0 + t * a.H * kMsD + c;
-    f.k = *reinterpret_cast<const msvec*>(a.k + off);
-    f.v = *reinterpret_cast<const msvec*>(a.v + off);
-    f.lam = *reinterpret_cast<const msvec*>(a.lam + off);
-    if constexpr (R) f.r = *reinterpret_cast<const msvec*>(a.r + off);
-  } else {
-    f.k = f.v = f.lam = f.r = msvec{};
-  }
-}
-
-template <bool R>
-__device__ __forceinline__ void ms_put(MsStage<R>& s, const MsPrefetch<R>& f) {
-  const int u = threadIdx.x / kMsTPR;
-  const int c = kMsFV * (threadIdx.x % kMsTPR);
-  *reinterpret_cast<msvec*>(&s.k[u][c]) = f.k;
-  *reinterpret_cast<msvec*>(&s.v[u][c]) = f.v;
-  *reinterpret_cast<msvec*>(&s.lam[u][c]) = f.lam;
-  if constexpr (R) *reinterpret_cast<msvec*>(&s.r[u][c]) = f.r;
-}
-
-// The first nt tokens of a staged block (FULL: all kMsU of them, without
-// guards, so the state stays in place across tokens).
-template <bool READ, bool FULL>
-__device__ __forceinline__ void ms_tokens(const MsStage<READ>& st, float (*part)[kMsU][kMsD],
-                                          int nt, float (&S)[kMsJW], float& prod) {
-  const int lane = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;
+  const int c = threadIdx.x & 63;
+  const int64_t tb = t0 + 4 * (threadIdx.x >> 6);
+  const int64_t C = a.H * kMsD;
 #pragma unroll
-  for (int u = 0; u < kMsU; ++u) {
-    if (FULL || u < nt) {
-      const float ki = st.k[u][lane];
-      const float wf = fast_exp2(st.lam[u][lane] * -kLog2e);
-      prod *= wf;
-      float vj[kMsJW], kj[kMsJW];
-#pragma unroll
-      for (int c = 0; c < kMsJW; ++c) {
-        vj[c] = st.v[u][q * kMsJW + c];
-        kj[c] = st.k[u][q * kMsJW + c];
-      }
-      float p = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kMsJW; ++c) {
-        S[c] = __builtin_fmaf(wf, S[c], ki * vj[c]);
-        if constexpr (READ) p = __builtin_fmaf(S[c], kj[c], p);
-      }
-      if constexpr (READ) part[q][u][lane] = p;
+  for (int e = 0; e < 4; ++e) {
+    if (tb + e < tend) {
+      const int64_t off = row0 + (tb + e) * C + c;
+      f.k[e] = a.k[off];
+      f.v[e] = a.v[off];
+      f.lam[e] = a.lam[off];
+      if constexpr (READ) f.r[e] = a.r[off];
+    } else {
+      // a token past the end leaves the state as it is: no key, no value, factor 1
+      f.k[e] = f.v[e] = f.lam[e] = 0.0f;
+      if constexpr (READ) f.r[e] = 0.0f;
     }
   }
 }
 
-// Walks tokens [t0, tend) of one (batch, head) from the state in S (this
-// thread's row i = lane, columns 16q ..). READ: also form the gated outputs.
-// Returns the product of the decay factors of row i over the walk.
+template <bool READ>
+__device__ __forceinline__ void ms_put(MsStage<READ>& s, const MsPrefetch<READ>& f) {
+  const int c = threadIdx.x & 63;
+  const int b = threadIdx.x >> 6;
+  float w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = fast_exp2(f.lam[e] * -kLog2e);
+  const float s3 = w[3], s2 = w[2] * s3, s1 = w[1] * s2;
+  *reinterpret_cast<f4*>(&s.wt[c][4 * b]) = f4{w[0], w[1], w[2], w[3]};
+  *reinterpret_cast<f4*>(&s.kd[c][4 * b]) = f4{f.k[0] * s1, f.k[1] * s2, f.k[2] * s3, f.k[3]};
+  *reinterpret_cast<f4*>(&s.vt[c][4 * b]) = f4{f.v[0], f.v[1], f.v[2], f.v[3]};
+  s.bp[c][b] = w[0] * s1;
+  if constexpr (READ) {
+    *reinterpret_cast<f4*>(&s.kt[c][4 * b]) = f4{f.k[0], f.k[1], f.k[2], f.k[3]};
+    *reinterpret_cast<f4*>(&s.gt[c][4 * b]) =
+        f4{gate(f.r[0]), gate(f.r[1]), gate(f.r[2]), gate(f.r[3])};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s.kr[4 * b + e][c] = f.k[e];
+      s.vr[4 * b + e][c] = f.v[e];
+    }
+  }
+}
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Token of row m of the readout's A operand: lane q's accumulator rows
+// 4q .. 4q+3 then hold tokens q, 7 - q, 8 + q, 15 - q.
+__device__ __forceinline__ int ms_token(int m) {
+  const int b = m & 3, o = m >> 2;
+  return 4 * b + ((b & 1) ? 3 - o : o);
+}
+
+// 4-way select by q (q = 0..3).
+__device__ __forceinline__ float sel4(int q, float x0, float x1, float x2, float x3) {
+  const float lo = (q & 1) ? x1 : x0;
+  const float hi = (q & 1) ? x3 : x2;
+  return (q & 2) ? hi : lo;
+}
+
+// One chunk of one (batch, head) from the state S (this lane's 16 entries of
+// row 16w + n): READ also forms the gated outputs of tokens [tb, tend) into
+// out (FULL: all 16 of them, without guards). Returns the product of the
+// chunk's decay factors of row 16w + n.
+template <bool READ, bool FULL>
+__device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[kMsCol],
+                                          const MsKernelArgs& a, int64_t orow, int64_t tb,
+                                          int64_t tend, f4 (&S)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, q = lane >> 4;
+  const int w = threadIdx.x >> 6;
+  const int i = 16 * w + n;  // this lane's state row (channel of the head)
+
+  const f4 bp = *reinterpret_cast<const f4*>(&st.bp[i][0]);
+  const float pre1 = bp[0], pre2 = pre1 * bp[1], pre3 = pre2 * bp[2];
+  const float total = pre3 * bp[3];
+
+  // the state-update operands: values transposed (A) and the keys of tokens
+  // s = 4q .. 4q+3 decayed to the end of the chunk (B)
+  f4 vA[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vA[m] = *reinterpret_cast<const f4*>(&st.vt[16 * m + n][4 * q]);
+  const float tail = sel4(q, bp[1] * bp[2] * bp[3], bp[2] * bp[3], bp[3], 1.0f);
+  const f4 kh = tail * *reinterpret_cast<const f4*>(&st.kd[i][4 * q]);
+
+  if constexpr (READ) {
+    // token-major operands: row ms_token(n) of the keys, row n of the values,
+    // columns 16m + 4q .. + 3
+    f4 kA[4], vG[4];
+    const int tn = ms_token(n);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      kA[m] = *reinterpret_cast<const f4*>(&st.kr[tn][16 * m + 4 * q]);
+      vG[m] = *reinterpret_cast<const f4*>(&st.vr[n][16 * m + 4 * q]);
+    }
+    // G[s][ms_token(n)] for s = 4q + e, and the readout X[ms_token(4q + e)][i]
+    f4 g = {0.0f, 0.0f, 0.0f, 0.0f}, x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g = mfma4(vG[m][e], kA[m][e], g);
+        x = mfma4(kA[m][e], S[m][e], x);
+      }
+    }
+    // G to this wave's LDS tile, token-major: gt[t][s]
+    *reinterpret_cast<f4*>(&gt[tn][4 * q]) = g;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // lane q's token in block j is t = 4j + o: o = q for even j, 3 - q for odd j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = (j & 1) ? 3 - q : q;
+      const int t = 4 * j + o;
+      // earlier blocks: sum_b (whole blocks between) * sum_(s in b) kd[s] G[s][t]
+      float cross = 0.0f;
+#pragma unroll
+      for (int b = 0; b < j; ++b) {
+        const f4 gs = *reinterpret_cast<const f4*>(&gt[t][4 * b]);
+        const f4 kb = *reinterpret_cast<const f4*>(&st.kd[i][4 * b]);
+        float yb = kb[0] * gs[0];
+        yb = __builtin_fmaf(kb[1], gs[1], yb);
+        yb = __builtin_fmaf(kb[2], gs[2], yb);
+        yb = __builtin_fmaf(kb[3], gs[3], yb);
+        cross = __builtin_fmaf(bp[b], cross, yb);
+      }
+      // t's own block, tokens 4j .. t: direct products
+      const f4 gs = *reinterpret_cast<const f4*>(&gt[t][4 * j]);
+      const f4 wj = *reinterpret_cast<const f4*>(&st.wt[i][4 * j]);
+      const f4 kj = *reinterpret_cast<const f4*>(&st.kt[i][4 * j]);
+      float inb = 0.0f, pb = 1.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e <= o) {
+          inb = __builtin_fmaf(wj[e], inb, kj[e] * gs[e]);
+          pb *= wj[e];
+        }
+      }
+      const float prej = j == 0 ? 1.0f : (j == 1 ? pre1 : (j == 2 ? pre2 : pre3));
+      const float acc = __builtin_fmaf(prej, x[j], cross);
+      const float y = st.gt[i][t] * __builtin_fmaf(pb, acc, inb);
+      if (FULL || tb + t < tend)
+        __builtin_nontemporal_store(y, a.out + orow + (tb + t) * a.H * kMsD + i);
+    }
+  }
+
+  // state update: S <- diag(total) S + V^T K^
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    S[m] *= total;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[m] = mfma4(vA[m][e], kh[e], S[m]);
+  }
+  return total;
+}
+
+// Walks chunks [t0, tend) of one (batch, head) from the state in S.
+// Returns the product of the decay factors of row 16w + n over the walk.
 template <bool READ>
 __device__ __forceinline__ float ms_walk(const MsKernelArgs& a, int64_t row0, int64_t t0,
-                                         int64_t tend, float (&S)[kMsJW]) {
+                                         int64_t tend, f4 (&S)[4]) {
   __shared__ MsStage<READ> stage[2];
-  __shared__ float part[2][kMsWaves][kMsU][kMsD];
-  const int lane = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;
-  const int64_t C = a.H * kMsD;
+  __shared__ float gtile[READ ? kMsWaves : 1][kMsL][kMsCol];
   float prod = 1.0f;
-  const int64_t nblk = (tend - t0 + kMsU - 1) / kMsU;
-  if (nblk <= 0) return prod;
+  const int64_t nch = (tend - t0 + kMsL - 1) / kMsL;
+  if (nch <= 0) return prod;
+  float (*gt)[kMsCol] = gtile[READ ? (threadIdx.x >> 6) : 0];
   MsPrefetch<READ> f;
   ms_fetch<READ>(f, a, row0, t0, tend);
   ms_put<READ>(stage[0], f);
-  ms_fetch<READ>(f, a, row0, t0 + kMsU, tend);
+  ms_fetch<READ>(f, a, row0, t0 + kMsL, tend);
   __syncthreads();
-  for (int64_t n = 0; n < nblk; ++n) {
-    const MsStage<READ>& st = stage[n & 1];
-    const int64_t tb = t0 + n * kMsU;
-    const int nt = tend - tb < kMsU ? static_cast<int>(tend - tb) : kMsU;
-    if (nt == kMsU) {
-      ms_tokens<READ, true>(st, part[n & 1], nt, S, prod);
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t tb = t0 + c * kMsL;
+    if (tb + kMsL <= tend) {
+      prod *= ms_chunk<READ, true>(stage[c & 1], gt, a, row0, tb, tend, S);
     } else {
-      ms_tokens<READ, false>(st, part[n & 1], nt, S, prod);
+      prod *= ms_chunk<READ, false>(stage[c & 1], gt, a, row0, tb, tend, S);
     }
-    // wave q finishes tokens q and q + 4 of the block after the barrier; it
-    // takes their receptance now, since the next block's data may overwrite
-    // this stage buffer before a slower wave reaches that point
-    float rg[kMsU / kMsWaves];
-    if constexpr (READ) {
-#pragma unroll
-      for (int m = 0; m < kMsU / kMsWaves; ++m) {
-        const int u = q + m * kMsWaves;
-        rg[m] = u < nt ? st.r[u][lane] : 0.0f;
-      }
-    }
-    // the next block goes into the other stage buffer, whose readers (block
-    // n - 1) all passed the previous barrier
-    if (n + 1 < nblk) {
-      ms_put<READ>(stage[(n + 1) & 1], f);
-      ms_fetch<READ>(f, a, row0, tb + 2 * kMsU, tend);
+    // the next chunk goes into the other stage buffer, whose readers (chunk
+    // c - 1) all passed the previous barrier
+    if (c + 1 < nch) {
+      ms_put<READ>(stage[(c + 1) & 1], f);
+      ms_fetch<READ>(f, a, row0, tb + 2 * kMsL, tend);
     }
     __syncthreads();
-    if constexpr (READ) {
-#pragma unroll
-      for (int m = 0; m < kMsU / kMsWaves; ++m) {
-        const int u = q + m * kMsWaves;
-        if (u < nt) {
-          float y = 0.0f;
-#pragma unroll
-          for (int qq = 0; qq < kMsWaves; ++qq) y += part[n & 1][qq][u][lane];
-          y *= gate(rg[m]);
-          __builtin_nontemporal_store(y, a.out + row0 + (tb + u) * C + lane);
-        }
-      }
-    }
   }
   return prod;
 }
 
-// This thread's 16 state entries of (batch, head) bh: row = lane, columns 16q ..
+// This lane's state entries of (batch, head) bh: row 16w + n, columns
+// 16m + 4q .. + 3 for m = 0..3 (float4 m at offset + 16m).
+__device__ __forceinline__ int64_t ms_row_off(int64_t bh) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  return bh * kMsD * kMsD + static_cast<int64_t>(16 * w + (lane & 15)) * kMsD + 4 * (lane >> 4);
+}
+
+__device__ __forceinline__ void ms_load_state(const float* __restrict__ p, f4 (&S)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) S[m] = *reinterpret_cast<const f4*>(p + 16 * m);
+}
+
+__device__ __forceinline__ void ms_store_state(float* __restrict__ p, const f4 (&S)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) *reinterpret_cast<f4*>(p + 16 * m) = S[m];
+}
+
+// Segment p < P - 1 of (batch, head) bh from the zero state: its final state
+// and the product of its decay factors per row.
+__global__ __launch_bounds__(kMsThreads) void wkv6_seg_state_kernel(MsKernelArgs a) {
+  const int64_t nbh = a.B * a.H;
+  const int64_t bh = blockIdx.x % nbh;
+  const int64_t p = blockIdx.x / nbh;
+  const int64_t b = bh / a.H, h = bh - b * a.H;
+  const int64_t row0 = b * a.T * a.H * kMsD + h * kMsD;
+  const int64_t t0 = p * a.SL;
+  const int64_t tend = t0 + a.SL < a.T ? t0 + a.SL : a.T;
+  f4 S[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) S[m] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float prod = ms_walk<false>(a, row0, t0, tend, S);
+  ms_store_state(a.seg_state + p * nbh * kMsD * kMsD + ms_row_off(bh), S);
+  if ((threadIdx.x & 63) < 16)
+    a.seg_decay[(p * nbh + bh) * kMsD + 16 * (threadIdx.x >> 6) + (threadIdx.x & 15)] = prod;
+}
+
+// Segment p of (batch, head) bh: the state in front of it, then the walk with
+// the gated readout; the last segment writes the final state.
+__global__ __launch_bounds__(kMsThreads) void wkv6_scan_kernel(MsKernelArgs a) {
+  const int64_t nbh = a.B * a.H;
+  const int64_t bh = blockIdx.x % nbh;
+  const int64_t p = blockIdx.x / nbh;
+  const int64_t b = bh / a.H, h = bh - b * a.H;
+  const int64_t row0 = b * a.T * a.H * kMsD + h * kMsD;
+  const int64_t t0 = p * a.SL;
+  const int64_t tend = t0 + a.SL < a.T ? t0 + a.SL : a.T;
+  const int i = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15);
+  f4 S[4];
+  if (a.state_in != nullptr) {
+    ms_load_state(a.state_in + ms_row_off(bh), S);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) S[m] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // carry the state through the earlier segments, oldest first
+  for (int64_t pp = 0; pp < p; ++pp) {
+    f4 L[4];
+    ms_load_state(a.seg_state + pp * nbh * kMsD * kMsD + ms_row_off(bh), L);
+    const float A = a.seg_decay[(pp * nbh + bh) * kMsD + i];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[m][e] = __builtin_fmaf(A, S[m][e], L[m][e]);
+    }
+  }
+  ms_walk<true>(a, row0, t0, tend, S);
+  if (p == a.P - 1 && a.state_out != nullptr) ms_store_state(a.state_out + ms_row_off(bh), S);
+}
+
+// Decode step: this thread's 16 state entries of (batch, head) bh: row =
+// lane, columns 16q ..
 __device__ __forceinline__ int64_t ms_state_off(int64_t bh) {
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
@@ -218,54 +399,6 @@ __device__ __forceinline__ void ms_store16(float* __restrict__ p, const float (&
 #pragma unroll
   for (int c = 0; c < kMsJW; c += 4)
     *reinterpret_cast<float4*>(p + c) = float4{S[c], S[c + 1], S[c + 2], S[c + 3]};
-}
-
-// Segment p < P - 1 of (batch, head) bh from the zero state: its final state
-// and the product of its decay factors per row.
-__global__ __launch_bounds__(kMsThreads) void wkv6_seg_state_kernel(MsKernelArgs a) {
-  const int64_t nbh = a.B * a.H;
-  const int64_t bh = blockIdx.x % nbh;
-  const int64_t p = blockIdx.x / nbh;
-  const int64_t b = bh / a.H, h = bh - b * a.H;
-  const int64_t row0 = b * a.T * a.H * kMsD + h * kMsD;
-  const int64_t t0 = p * a.SL;
-  const int64_t tend = t0 + a.SL < a.T ? t0 + a.SL : a.T;
-  float S[kMsJW];
-#pragma unroll
-  for (int c = 0; c < kMsJW; ++c) S[c] = 0.0f;
-  const float prod = ms_walk<false>(a, row0, t0, tend, S);
-  ms_store16(a.seg_state + p * nbh * kMsD * kMsD + ms_state_off(bh), S);
-  if ((threadIdx.x >> 6) == 0) a.seg_decay[(p * nbh + bh) * kMsD + threadIdx.x] = prod;
-}
-
-// Segment p of (batch, head) bh: the state in front of it, then the walk with
-// the gated readout; the last segment writes the final state.
-__global__ __launch_bounds__(kMsThreads) void wkv6_scan_kernel(MsKernelArgs a) {
-  const int64_t nbh = a.B * a.H;
-  const int64_t bh = blockIdx.x % nbh;
-  const int64_t p = blockIdx.x / nbh;
-  const int64_t b = bh / a.H, h = bh - b * a.H;
-  const int64_t row0 = b * a.T * a.H * kMsD + h * kMsD;
-  const int64_t t0 = p * a.SL;
-  const int64_t tend = t0 + a.SL < a.T ? t0 + a.SL : a.T;
-  const int lane = threadIdx.x & 63;
-  float S[kMsJW];
-  if (a.state_in != nullptr) {
-    ms_load16(a.state_in + ms_state_off(bh), S);
-  } else {
-#pragma unroll
-    for (int c = 0; c < kMsJW; ++c) S[c] = 0.0f;
-  }
-  // carry the state through the earlier segments, oldest first
-  for (int64_t pp = 0; pp < p; ++pp) {
-    float L[kMsJW];
-    ms_load16(a.seg_state + pp * nbh * kMsD * kMsD + ms_state_off(bh), L);
-    const float A = a.seg_decay[(pp * nbh + bh) * kMsD + lane];
-#pragma unroll
-    for (int c = 0; c < kMsJW; ++c) S[c] = __builtin_fmaf(A, S[c], L[c]);
-  }
-  ms_walk<true>(a, row0, t0, tend, S);
-  if (p == a.P - 1 && a.state_out != nullptr) ms_store16(a.state_out + ms_state_off(bh), S);
 }
 
 // One decode step for every (batch, head): state read and written in place.
@@ -326,13 +459,20 @@ hipError_t launch_matrix_state_copy(int64_t B, int64_t H, const float* src, floa
   return hipGetLastError();
 }
 
-// Segments for a problem: enough workgroups to give every CU about four, but
-// no segment shorter than 64 tokens.
+#ifndef WKV_MS_WG_PER_CU
+#define WKV_MS_WG_PER_CU 4
+#endif
+#ifndef WKV_MS_MIN_SEG
+#define WKV_MS_MIN_SEG 64
+#endif
+
+// Segments for a problem: enough workgroups to give every CU about
+// WKV_MS_WG_PER_CU, but no segment shorter than WKV_MS_MIN_SEG tokens.
 int64_t matrix_segments(int64_t B, int64_t T, int64_t H, int cus) {
   const int64_t nbh = B * H;
   if (nbh <= 0 || T <= 0) return 1;
-  const int64_t want = (4LL * cus + nbh - 1) / nbh;
-  const int64_t cap = T / 64 > 1 ? T / 64 : 1;
+  const int64_t want = (static_cast<int64_t>(WKV_MS_WG_PER_CU) * cus + nbh - 1) / nbh;
+  const int64_t cap = T / WKV_MS_MIN_SEG > 1 ? T / WKV_MS_MIN_SEG : 1;
   const int64_t P = want < cap ? want : cap;
   return P > 1 ? P : 1;
 }
@@ -350,8 +490,13 @@ hipError_t launch_matrix(const MatrixArgs& m, int64_t P, void* ws, hipStream_t s
   a.B = m.B;
   a.T = m.T;
   a.H = m.H;
+  // whole chunks per segment; rounding up may leave fewer segments than the
+  // workspace was sized for
+  a.SL = ((m.T + P - 1) / P + kMsL - 1) / kMsL * kMsL;
+  if (a.SL <= 0) a.SL = kMsL;
+  P = (m.T + a.SL - 1) / a.SL;
+  if (P < 1) P = 1;
   a.P = P;
-  a.SL = (m.T + P - 1) / P;
   a.lam = m.lam;
   a.k = m.k;
   a.v = m.v;
