@@ -260,7 +260,8 @@ int wkv_step_dd(int64_t B, int64_t C, const void* w, const float* u, const void*
  *   out_t[i]  = sigmoid(r_t[i]) * sum_j S_t[i][j] k_t[j]
  * with channel c = h * D + i. fp32 throughout.
  *
- *   B, T, H     sizes (>= 0); B == 0 or H == 0: nothing to do.
+ *   B, T, H     sizes (>= 0); B == 0 or H == 0: nothing to do; H above
+ *               2^22 heads: WKV_ERR_DIM.
  *   D           head size; only 64 is built (other values: WKV_ERR_DIM).
  *   w           [B][T][H*D] positive decay rates (the factor is e^(-w)).
  *   k, v, r     [B][T][H*D] key, value, receptance.

@@ -181,6 +181,9 @@ def test_matrix_entry_points_validate_without_device():
     assert lib.wkv_matrix_forward(1, 2, 1, 64, w, k, v, r, nul, k, nul, nul, 0, nul) == 4
     assert lib.wkv_matrix_forward(1, 2, 1, 64, P(a + 4), k, v, r, nul, out, nul, nul, 0, nul) == 3
     assert lib.wkv_matrix_workspace_size(1, 2, 1, 16) == -2
+    # more heads than the 32-bit chunk offsets of the prefill kernels cover
+    assert lib.wkv_matrix_forward(1, 1, (1 << 22) + 1, 64, w, k, v, r, nul, out, nul, nul, 0, nul) == 2
+    assert lib.wkv_matrix_workspace_size(1, 1, (1 << 22) + 1, 64) == -2
     # B, H, D, w, k, v, r, state, out, stream
     assert lib.wkv_matrix_step(1, 1, 16, w, k, v, r, P(a + 65536), out, nul) == 2
     assert lib.wkv_matrix_step(1, 1, 64, w, k, v, r, nul, out, nul) == 1

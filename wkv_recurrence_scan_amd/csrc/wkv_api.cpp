@@ -286,7 +286,7 @@ int matrix_forward_impl(int64_t B, int64_t T, int64_t H, int64_t D, const float*
                         float* out, float* state_out, void* workspace, int64_t workspace_bytes,
                         hipStream_t stream) {
   if (B < 0 || T < 0 || H < 0 || D < 0) return WKV_ERR_DIM;
-  if (D != wkv::kMatrixHead) return WKV_ERR_DIM;
+  if (D != wkv::kMatrixHead || H > wkv::kMatrixMaxHeads) return WKV_ERR_DIM;
   int64_t seq_bytes, state_bytes;
   if (!mul3(B, T, H * D, &seq_bytes) || __builtin_mul_overflow(seq_bytes, 4, &seq_bytes) ||
       seq_bytes > kMaxBytes)
@@ -508,7 +508,7 @@ int wkv_matrix_forward(int64_t B, int64_t T, int64_t H, int64_t D, const float* 
 
 int64_t wkv_matrix_workspace_size(int64_t B, int64_t T, int64_t H, int64_t D) {
   if (B < 0 || T < 0 || H < 0 || D < 0) return -WKV_ERR_DIM;
-  if (D != wkv::kMatrixHead) return -WKV_ERR_DIM;
+  if (D != wkv::kMatrixHead || H > wkv::kMatrixMaxHeads) return -WKV_ERR_DIM;
   int64_t cells;
   if (!mul3(B, T, H * D, &cells) || cells > kMaxBytes) return -WKV_ERR_DIM;
   if (B == 0 || H == 0 || T == 0) return 0;

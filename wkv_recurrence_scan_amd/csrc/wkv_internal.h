@@ -130,6 +130,8 @@ struct MatrixStepArgs {
   float* out;
 };
 constexpr int64_t kMatrixHead = 64;
+// the prefill kernels address 16 token rows of H * 64 channels with 32-bit offsets
+constexpr int64_t kMatrixMaxHeads = int64_t{1} << 22;
 int64_t matrix_segments(int64_t B, int64_t T, int64_t H, int cus);
 int64_t matrix_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t P);
 hipError_t launch_matrix(const MatrixArgs& m, int64_t P, void* ws, hipStream_t s);

@@ -68,8 +68,8 @@ constexpr int kMsD = 64;                    // head size
 constexpr int kMsL = 16;                    // tokens per chunk
 constexpr int kMsWaves = 4;                 // wave w owns state rows 16w ..
 constexpr int kMsThreads = 64 * kMsWaves;
-constexpr int kMsRow = kMsD + 4;            // padded row of a token-major tile
 constexpr int kMsCol = kMsL + 4;            // padded row of a channel-major tile
+constexpr int kMsFold = 4;                  // earlier segments folded per batch of loads
 
 // decode step kernel: lane i holds row i, wave q columns 16q ..
 constexpr int kMsJW = 16;
@@ -88,20 +88,24 @@ struct MsKernelArgs {
   float* seg_decay;       // [P-1][B*H][64]: product of segment p's decay factors per row
 };
 
-// One staged chunk, per channel i and block b of four tokens: the decay
-// factors, the keys raw and decayed to the end of their block, the values and
-// the gates (channel-major), and the product of the block's factors. READ:
-// also the token-major keys and values for the matrix operands.
+// One staged chunk: one row per channel i holding, for the chunk's 16
+// tokens, the decay factors e^-lam, the keys decayed to the end of their
+// block of four, the values and the four block products of the factors;
+// READ adds the keys and the gates sigmoid(r). A row is 52 (84) floats: 52
+// and 84 are 20 and 52 modulo the 64 banks, so the rows of 16 neighbouring
+// channels start on distinct 4-bank groups and every access pattern below is
+// conflict-free.
 template <bool READ>
-struct alignas(16) MsStage {
-  float wt[kMsD][kMsCol];               // decay factors e^-lam
-  float kd[kMsD][kMsCol];               // k_s * factors after s up to the end of its block
-  float vt[kMsD][kMsCol];               // values
-  float kt[READ ? kMsD : 1][kMsCol];    // keys
-  float gt[READ ? kMsD : 1][kMsCol];    // gates sigmoid(r)
-  float bp[kMsD][4];                    // product of the factors of block b
-  float kr[READ ? kMsL : 1][kMsRow];    // keys, token-major
-  float vr[READ ? kMsL : 1][kMsRow];    // values, token-major
+struct MsStage {
+  static constexpr int kW = 0, kKD = 16, kV = 32, kBP = 48, kK = 52, kG = 68;
+  static constexpr int kLen = READ ? 84 : 52;
+  alignas(16) float row[kMsD][kLen];
+  __device__ __forceinline__ f4 ld4(int i, int field, int t) const {
+    return *reinterpret_cast<const f4*>(&row[i][field + t]);
+  }
+  __device__ __forceinline__ void st4(int i, int field, int t, f4 x) {
+    *reinterpret_cast<f4*>(&row[i][field + t]) = x;
+  }
 };
 
 // Thread x's share of a chunk: channel x % 64, tokens 4 (x / 64) .. + 3
@@ -114,17 +118,25 @@ struct MsPrefetch {
 template <bool READ>
 __device__ __forceinline__ void ms_fetch(MsPrefetch<READ>& f, const MsKernelArgs& a, int64_t row0,
                                          int64_t t0, int64_t tend) {
-  const int c = threadIdx.x & 63;
-  const int64_t tb = t0 + 4 * (threadIdx.x >> 6);
+  // a uniform base at the chunk's first token and 32-bit per-thread offsets
+  // (16 token rows of one sequence always fit)
   const int64_t C = a.H * kMsD;
+  const int64_t base = row0 + t0 * C;
+  const float* __restrict__ k = a.k + base;
+  const float* __restrict__ v = a.v + base;
+  const float* __restrict__ lam = a.lam + base;
+  const float* __restrict__ r = a.r + base;
+  const uint32_t u0 = 4 * (threadIdx.x >> 6);
+  const uint32_t off0 = u0 * static_cast<uint32_t>(C) + (threadIdx.x & 63);
+  const int64_t left = tend - t0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if (tb + e < tend) {
-      const int64_t off = row0 + (tb + e) * C + c;
-      f.k[e] = a.k[off];
-      f.v[e] = a.v[off];
-      f.lam[e] = a.lam[off];
-      if constexpr (READ) f.r[e] = a.r[off];
+    const uint32_t off = off0 + e * static_cast<uint32_t>(C);
+    if (left >= kMsL || static_cast<int64_t>(u0 + e) < left) {
+      f.k[e] = k[off];
+      f.v[e] = v[off];
+      f.lam[e] = lam[off];
+      if constexpr (READ) f.r[e] = r[off];
     } else {
       // a token past the end leaves the state as it is: no key, no value, factor 1
       f.k[e] = f.v[e] = f.lam[e] = 0.0f;
@@ -135,25 +147,20 @@ __device__ __forceinline__ void ms_fetch(MsPrefetch<READ>& f, const MsKernelArgs
 
 template <bool READ>
 __device__ __forceinline__ void ms_put(MsStage<READ>& s, const MsPrefetch<READ>& f) {
+  using St = MsStage<READ>;
   const int c = threadIdx.x & 63;
   const int b = threadIdx.x >> 6;
   float w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) w[e] = fast_exp2(f.lam[e] * -kLog2e);
   const float s3 = w[3], s2 = w[2] * s3, s1 = w[1] * s2;
-  *reinterpret_cast<f4*>(&s.wt[c][4 * b]) = f4{w[0], w[1], w[2], w[3]};
-  *reinterpret_cast<f4*>(&s.kd[c][4 * b]) = f4{f.k[0] * s1, f.k[1] * s2, f.k[2] * s3, f.k[3]};
-  *reinterpret_cast<f4*>(&s.vt[c][4 * b]) = f4{f.v[0], f.v[1], f.v[2], f.v[3]};
-  s.bp[c][b] = w[0] * s1;
+  s.st4(c, St::kW, 4 * b, f4{w[0], w[1], w[2], w[3]});
+  s.st4(c, St::kKD, 4 * b, f4{f.k[0] * s1, f.k[1] * s2, f.k[2] * s3, f.k[3]});
+  s.st4(c, St::kV, 4 * b, f4{f.v[0], f.v[1], f.v[2], f.v[3]});
+  s.row[c][St::kBP + b] = w[0] * s1;
   if constexpr (READ) {
-    *reinterpret_cast<f4*>(&s.kt[c][4 * b]) = f4{f.k[0], f.k[1], f.k[2], f.k[3]};
-    *reinterpret_cast<f4*>(&s.gt[c][4 * b]) =
-        f4{gate(f.r[0]), gate(f.r[1]), gate(f.r[2]), gate(f.r[3])};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s.kr[4 * b + e][c] = f.k[e];
-      s.vr[4 * b + e][c] = f.v[e];
-    }
+    s.st4(c, St::kK, 4 * b, f4{f.k[0], f.k[1], f.k[2], f.k[3]});
+    s.st4(c, St::kG, 4 * b, f4{gate(f.r[0]), gate(f.r[1]), gate(f.r[2]), gate(f.r[3])});
   }
 }
 
@@ -188,7 +195,8 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
   const int w = threadIdx.x >> 6;
   const int i = 16 * w + n;  // this lane's state row (channel of the head)
 
-  const f4 bp = *reinterpret_cast<const f4*>(&st.bp[i][0]);
+  using St = MsStage<READ>;
+  const f4 bp = st.ld4(i, St::kBP, 0);
   const float pre1 = bp[0], pre2 = pre1 * bp[1], pre3 = pre2 * bp[2];
   const float total = pre3 * bp[3];
 
@@ -196,19 +204,22 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
   // s = 4q .. 4q+3 decayed to the end of the chunk (B)
   f4 vA[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) vA[m] = *reinterpret_cast<const f4*>(&st.vt[16 * m + n][4 * q]);
+  for (int m = 0; m < 4; ++m) vA[m] = st.ld4(16 * m + n, St::kV, 4 * q);
   const float tail = sel4(q, bp[1] * bp[2] * bp[3], bp[2] * bp[3], bp[3], 1.0f);
-  const f4 kh = tail * *reinterpret_cast<const f4*>(&st.kd[i][4 * q]);
+  const f4 kh = tail * st.ld4(i, St::kKD, 4 * q);
 
   if constexpr (READ) {
-    // token-major operands: row ms_token(n) of the keys, row n of the values,
-    // columns 16m + 4q .. + 3
+    // token-major operands: token ms_token(n) of the keys and token n of the
+    // values at channels 16m + 4q + e
     f4 kA[4], vG[4];
     const int tn = ms_token(n);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      kA[m] = *reinterpret_cast<const f4*>(&st.kr[tn][16 * m + 4 * q]);
-      vG[m] = *reinterpret_cast<const f4*>(&st.vr[n][16 * m + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kA[m][e] = st.row[16 * m + 4 * q + e][St::kK + tn];
+        vG[m][e] = st.row[16 * m + 4 * q + e][St::kV + n];
+      }
     }
     // G[s][ms_token(n)] for s = 4q + e, and the readout X[ms_token(4q + e)][i]
     f4 g = {0.0f, 0.0f, 0.0f, 0.0f}, x = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -225,6 +236,9 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
+    float* __restrict__ out = a.out + orow + tb * a.H * kMsD;  // the chunk's first token row
+    const uint32_t C32 = static_cast<uint32_t>(a.H * kMsD);
+    const int rem = tend - tb < kMsL ? static_cast<int>(tend - tb) : kMsL;  // tokens of this chunk
     // lane q's token in block j is t = 4j + o: o = q for even j, 3 - q for odd j
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -235,7 +249,7 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
 #pragma unroll
       for (int b = 0; b < j; ++b) {
         const f4 gs = *reinterpret_cast<const f4*>(&gt[t][4 * b]);
-        const f4 kb = *reinterpret_cast<const f4*>(&st.kd[i][4 * b]);
+        const f4 kb = st.ld4(i, St::kKD, 4 * b);
         float yb = kb[0] * gs[0];
         yb = __builtin_fmaf(kb[1], gs[1], yb);
         yb = __builtin_fmaf(kb[2], gs[2], yb);
@@ -244,8 +258,8 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
       }
       // t's own block, tokens 4j .. t: direct products
       const f4 gs = *reinterpret_cast<const f4*>(&gt[t][4 * j]);
-      const f4 wj = *reinterpret_cast<const f4*>(&st.wt[i][4 * j]);
-      const f4 kj = *reinterpret_cast<const f4*>(&st.kt[i][4 * j]);
+      const f4 wj = st.ld4(i, St::kW, 4 * j);
+      const f4 kj = st.ld4(i, St::kK, 4 * j);
       float inb = 0.0f, pb = 1.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -256,9 +270,8 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
       }
       const float prej = j == 0 ? 1.0f : (j == 1 ? pre1 : (j == 2 ? pre2 : pre3));
       const float acc = __builtin_fmaf(prej, x[j], cross);
-      const float y = st.gt[i][t] * __builtin_fmaf(pb, acc, inb);
-      if (FULL || tb + t < tend)
-        __builtin_nontemporal_store(y, a.out + orow + (tb + t) * a.H * kMsD + i);
+      const float y = st.row[i][St::kG + t] * __builtin_fmaf(pb, acc, inb);
+      if (FULL || t < rem) __builtin_nontemporal_store(y, out + (t * C32 + i));
     }
   }
 
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(kMsThreads) void wkv6_seg_state_kernel(MsKernelArgs
 
 // Segment p of (batch, head) bh: the state in front of it, then the walk with
 // the gated readout; the last segment writes the final state.
-__global__ __launch_bounds__(kMsThreads) void wkv6_scan_kernel(MsKernelArgs a) {
+__global__ __launch_bounds__(kMsThreads, 3) void wkv6_scan_kernel(MsKernelArgs a) {
   const int64_t nbh = a.B * a.H;
   const int64_t bh = blockIdx.x % nbh;
   const int64_t p = blockIdx.x / nbh;
@@ -361,15 +374,27 @@ __global__ __launch_bounds__(kMsThreads) void wkv6_scan_kernel(MsKernelArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) S[m] = f4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // carry the state through the earlier segments, oldest first
-  for (int64_t pp = 0; pp < p; ++pp) {
-    f4 L[4];
-    ms_load_state(a.seg_state + pp * nbh * kMsD * kMsD + ms_row_off(bh), L);
-    const float A = a.seg_decay[(pp * nbh + bh) * kMsD + i];
+  // carry the state through the earlier segments, oldest first; the loads of
+  // kMsFold segments are issued together so that their latencies overlap
+  for (int64_t p0 = 0; p0 < p; p0 += kMsFold) {
+    f4 L[kMsFold][4];
+    float A[kMsFold];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int u = 0; u < kMsFold; ++u) {
+      if (p0 + u < p) {
+        ms_load_state(a.seg_state + (p0 + u) * nbh * kMsD * kMsD + ms_row_off(bh), L[u]);
+        A[u] = a.seg_decay[((p0 + u) * nbh + bh) * kMsD + i];
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][e] = __builtin_fmaf(A, S[m][e], L[m][e]);
+    for (int u = 0; u < kMsFold; ++u) {
+      if (p0 + u < p) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[m][e] = __builtin_fmaf(A[u], S[m][e], L[u][m][e]);
+        }
+      }
     }
   }
   ms_walk<true>(a, row0, t0, tend, S);
@@ -460,7 +485,7 @@ hipError_t launch_matrix_state_copy(int64_t B, int64_t H, const float* src, floa
 }
 
 #ifndef WKV_MS_WG_PER_CU
-#define WKV_MS_WG_PER_CU 4
+#define WKV_MS_WG_PER_CU 3
 #endif
 #ifndef WKV_MS_MIN_SEG
 #define WKV_MS_MIN_SEG 64
