@@ -48,6 +48,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "WKV prefill G channel-tokens/s + % HBM roofline; decode steps/s at B=256"
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F32_TFS = 157.3   # dense fp32 matrix-core peak of MI355X
 
 
 def _log(*a):
@@ -352,11 +353,13 @@ def time_matrix(wl, dev, reps=20):
     """wkv_matrix_forward (matrix-valued state, heads of 64) on workload wl's
     first layer: k, v, the receptance and the per-token rates of the
     workload, C / 64 heads. Microseconds per call (event pair around `reps`
-    back-to-back calls) against both rooflines: HBM on the algorithmic bytes
-    (read w, k, v, r; write out and the final state) and the fp32 vector ALU on
-    the algorithmic flops (per state entry and token: a multiply and an FMA
-    for the update, an FMA for the readout: 5 flops, i.e. 320 per
-    channel-token)."""
+    back-to-back calls) against two rooflines: HBM on the algorithmic bytes
+    (read w, k, v, r; write out and the final state), and the fp32 matrix
+    cores on the flops of the chunked form's three contractions per 16-token
+    chunk and head of 64 -- the readout S k_t (64 x 64 per token), the state
+    update V^T K (64 x 64 per token) and the key-value products v_s . k_t (16
+    x 64 per token): 2 (64 + 64 + 16) = 288 flops per channel-token. The
+    causal sum inside a chunk runs on the vector units and is not counted."""
     import torch
     import wkv_recurrence_scan_amd as W
     from wkv_recurrence_scan_amd import inputs as I
@@ -386,7 +389,7 @@ def time_matrix(wl, dev, reps=20):
     us = e0.elapsed_time(e1) * 1e3 / reps
     ct = wl.B * wl.T * wl.C
     abytes = 20 * ct + 4 * wl.B * H * W.MATRIX_HEAD ** 2
-    aflops = 5 * W.MATRIX_HEAD * ct
+    aflops = 2 * (W.MATRIX_HEAD + W.MATRIX_HEAD + 16) * ct
     gbs = abytes / (us * 1e-6) / 1e9
     tfs = aflops / (us * 1e-6) / 1e12
     return {"workload": f"{wl.name}, one layer, matrix-valued state ({H} heads of 64)",
@@ -396,8 +399,9 @@ def time_matrix(wl, dev, reps=20):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes_per_launch": abytes},
-            "alu_roofline": {"achieved": round(tfs, 2), "peak": 157.3, "unit": "TFLOP/s",
-                             "frac": round(tfs / 157.3, 4), "algorithmic_flops_per_call": aflops}}
+            "mfma_roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_MFMA_F32_TFS,
+                              "unit": "TFLOP/s", "frac": round(tfs / PEAK_MFMA_F32_TFS, 4),
+                              "algorithmic_flops_per_call": aflops}}
 
 
 def measured_traffic(workload_key, path):
