@@ -148,6 +148,35 @@ def test_matrix_huge_rate_wipes_the_state():
     assert_close(got, ref, "out")
 
 
+@pytest.mark.parametrize("t0", [0, 1, 3, 4, 15, 16, 17, 63, 64, 250])
+def test_matrix_huge_rate_at_block_and_chunk_edges(t0):
+    """A state-wiping rate at the first, last and inner tokens of the 4-token
+    blocks and 16-token chunks the kernel forms its decay products over."""
+    B, T, H = 1, 260, 1
+    say(f"matrix huge rate at t={t0}")
+    lam, k, v, r = mcase(B, T, H, layer=6)
+    lam[:, t0, ::3] = 1e4
+    s0 = random_mstate(B, H, 5)
+    ref, rst = wkv6_recurrent(lam, k, v, r, H, s0.astype(np.float64))
+    for ws in ("auto", None):
+        got, gst = gpu_matrix(lam, k, v, r, H, s0, workspace=ws)
+        assert_close(got, ref, f"out (workspace {ws})")
+        assert_close(gst, rst, f"state (workspace {ws})")
+
+
+def test_matrix_fast_decay_underflows_cleanly():
+    """Rates of e^N(2, 1) (median 7.4 per token, tails past 100): products of a
+    few factors underflow inside a block; nothing may turn into inf or NaN."""
+    B, T, H = 2, 300, 2
+    say("matrix fast decay")
+    lam, k, v, r = mcase(B, T, H, layer=7)
+    lam = np.exp(np.random.default_rng([72, 1]).normal(2.0, 1.0, lam.shape)).astype(np.float32)
+    got, gst = gpu_matrix(lam, k, v, r, H)
+    ref, rst = wkv6_recurrent(lam, k, v, r, H)
+    assert_close(got, ref, "out")
+    assert_close(gst, rst, "state")
+
+
 def test_matrix_deterministic():
     B, T, H = 2, 1100, 2
     say("matrix determinism")
