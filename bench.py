@@ -349,6 +349,88 @@ def time_decay(wl, dev, reps=50):
                          "algorithmic_bytes_per_launch": abytes}}
 
 
+def time_decode_steps(kind, wl, dev, n_steps=256):
+    """Decode steps of the per-token-decay operator (kind "dd": wkv_step_dd)
+    or of the matrix-valued state (kind "matrix": wkv_matrix_step) at workload
+    wl's batch and width, from the empty state, with the seeded decode
+    inputs: the n_steps launches are captured in one HIP graph whose replay
+    must reproduce the eager steps; microseconds per step from an event pair
+    around one replay, against HBM on the algorithmic bytes per step (dd: read
+    w, k, v and the three state planes, write the state and out, read u;
+    matrix: read w, k, v, r and the 64 x 64 state per head, write the state
+    and out)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    ks, vs = I.decode_kv(wl, steps=n_steps)
+    ws = I.decode_decay_rates(wl, steps=n_steps)
+    dk, dv, dw = t(ks), t(vs), t(ws)
+    del ks, vs, ws
+    B, C = wl.B, wl.C
+    outs = torch.empty_like(dk)
+    if kind == "dd":
+        _, u = I.params(wl)
+        du = t(u)
+        state = torch.empty((3, B, C), dtype=torch.float32, device=dev)
+
+        def reset():
+            state[0].zero_()
+            state[1].zero_()
+            state[2].fill_(-1e38)
+
+        step = lambda s: W.wkv_step_dd(dw[s], du, dk[s], dv[s], state, out=outs[s])
+        bytes_step = 40 * B * C + 4 * C
+        name = "per-token decay decode step (wkv_step_dd)"
+    else:
+        H = C // W.MATRIX_HEAD
+        rs = I.receptance(wl, layer=1, T=n_steps).transpose(1, 0, 2)
+        dr = t(rs)
+        del rs
+        state = torch.empty((B, H, W.MATRIX_HEAD, W.MATRIX_HEAD), dtype=torch.float32, device=dev)
+        reset = state.zero_
+        step = lambda s: W.wkv_matrix_step(dw[s], dk[s], dv[s], dr[s], H, state, out=outs[s])
+        bytes_step = 20 * B * C + 2 * 4 * B * H * W.MATRIX_HEAD ** 2
+        name = f"matrix-valued state decode step (wkv_matrix_step, {H} heads of 64)"
+
+    def run_all():
+        for s in range(n_steps):
+            step(s)
+
+    reset()
+    run_all()
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    g = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run_all()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(3):
+        reset()
+        outs.zero_()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if not torch.equal(outs, eager):
+            raise RuntimeError(f"{kind} decode graph replay does not reproduce the eager steps")
+        times.append(e0.elapsed_time(e1) * 1e3 / n_steps)
+    us = float(np.median(times))
+    achieved = bytes_step / (us * 1e-6) / 1e9
+    return {"workload": f"{wl.name}, {name}, from the empty state", "B": B, "C": C,
+            "steps": n_steps, "graph_us_per_step": round(us, 3),
+            "graph_steps_per_s": round(1e6 / us, 1), "bytes_per_step": bytes_step,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}}
+
+
 def time_matrix(wl, dev, reps=20):
     """wkv_matrix_forward (matrix-valued state, heads of 64) on workload wl's
     first layer: k, v, the receptance and the per-token rates of the
@@ -589,6 +671,13 @@ def main():
         for mwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
             _log(f"matrix-valued state forward: {mwl.name} (one layer)")
             rec["matrix_state"].append(time_matrix(mwl, dev))
+            torch.cuda.empty_cache()
+
+    if args.config == 1 and not args.no_decode and not args.no_backward:
+        rec["decode_next"] = []
+        for kind in ("dd", "matrix"):
+            _log(f"decode steps: {kind} at B={I.WORKLOADS[2].B} C={I.WORKLOADS[2].C}")
+            rec["decode_next"].append(time_decode_steps(kind, I.WORKLOADS[2], dev))
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -71,9 +71,6 @@ constexpr int kMsThreads = 64 * kMsWaves;
 constexpr int kMsCol = kMsL + 4;            // padded row of a channel-major tile
 constexpr int kMsFold = 4;                  // earlier segments folded per batch of loads
 
-// decode step kernel: lane i holds row i, wave q columns 16q ..
-constexpr int kMsJW = 16;
-
 struct MsKernelArgs {
   int64_t B, T, H;
   int64_t P, SL;          // P segments of SL tokens (a multiple of kMsL; the last may be shorter)
@@ -401,66 +398,54 @@ __global__ __launch_bounds__(kMsThreads, 3) void wkv6_scan_kernel(MsKernelArgs a
   if (p == a.P - 1 && a.state_out != nullptr) ms_store_state(a.state_out + ms_row_off(bh), S);
 }
 
-// Decode step: this thread's 16 state entries of (batch, head) bh: row =
-// lane, columns 16q ..
-__device__ __forceinline__ int64_t ms_state_off(int64_t bh) {
-  const int lane = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;
-  return bh * kMsD * kMsD + static_cast<int64_t>(lane) * kMsD + q * kMsJW;
-}
-
-__device__ __forceinline__ void ms_load16(const float* __restrict__ p, float (&S)[kMsJW]) {
-#pragma unroll
-  for (int c = 0; c < kMsJW; c += 4) {
-    const float4 x = *reinterpret_cast<const float4*>(p + c);
-    S[c] = x.x;
-    S[c + 1] = x.y;
-    S[c + 2] = x.z;
-    S[c + 3] = x.w;
-  }
-}
-
-__device__ __forceinline__ void ms_store16(float* __restrict__ p, const float (&S)[kMsJW]) {
-#pragma unroll
-  for (int c = 0; c < kMsJW; c += 4)
-    *reinterpret_cast<float4*>(p + c) = float4{S[c], S[c + 1], S[c + 2], S[c + 3]};
-}
-
-// One decode step for every (batch, head): state read and written in place.
-__global__ __launch_bounds__(kMsThreads) void wkv6_step_kernel(
+// One decode step for every (batch, head), the state read and written in
+// place: a workgroup of 256 threads per (batch, head). Thread x owns the
+// state's 16-byte pieces 256c + x (c = 0..3) in flat row-major order -- row
+// i = 16c + x / 16, columns j = 4 (x % 16) .. + 3 -- so every load and store
+// instruction of a wave covers 1 KiB of contiguous state; a row's readout
+// sum_j S[i][j] k_j is reduced over the 16 lanes that hold it.
+__global__ __launch_bounds__(256) void wkv6_step_kernel(
     int64_t H, const float* __restrict__ lam, const float* __restrict__ k,
     const float* __restrict__ v, const float* __restrict__ r, float* __restrict__ state,
     float* __restrict__ out) {
-  __shared__ float kv[2][kMsD];
-  __shared__ float part[kMsWaves][kMsD];
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / H, h = bh - b * H;
   const int64_t row = b * H * kMsD + h * kMsD;  // this head's channels of batch row b
-  const int lane = threadIdx.x & 63;
-  const int q = threadIdx.x >> 6;
-  if (q == 0) {
-    kv[0][lane] = k[row + lane];
-    kv[1][lane] = v[row + lane];
-  }
-  float S[kMsJW];
-  ms_load16(state + ms_state_off(bh), S);
-  const float ki = k[row + lane];
-  const float wf = fast_exp2(lam[row + lane] * -kLog2e);
-  __syncthreads();
-  float p = 0.0f;
+  const int x = threadIdx.x;
+  const int j0 = 4 * (x & 15);
+  float* __restrict__ S = state + bh * kMsD * kMsD;
+  f4 st[4];
 #pragma unroll
-  for (int c = 0; c < kMsJW; ++c) {
-    S[c] = __builtin_fmaf(wf, S[c], ki * kv[1][q * kMsJW + c]);
-    p = __builtin_fmaf(S[c], kv[0][q * kMsJW + c], p);
-  }
-  part[q][lane] = p;
-  ms_store16(state + ms_state_off(bh), S);
-  __syncthreads();
-  if (q == 0) {
-    float y = 0.0f;
+  for (int c = 0; c < 4; ++c) st[c] = *reinterpret_cast<const f4*>(S + 4 * (256 * c + x));
+  // every load is issued before the first use: columns' k, v, rows' k, rate, r
+  float kj[4], vj[4], ki[4], li[4], ri[4];
 #pragma unroll
-    for (int qq = 0; qq < kMsWaves; ++qq) y += part[qq][lane];
-    out[row + lane] = y * gate(r[row + lane]);
+  for (int e = 0; e < 4; ++e) {
+    kj[e] = k[row + j0 + e];
+    vj[e] = v[row + j0 + e];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = 16 * c + (x >> 4);
+    ki[c] = k[row + i];
+    li[c] = lam[row + i];
+    ri[c] = r[row + i];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float wf = fast_exp2(li[c] * -kLog2e);
+    float p = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      st[c][e] = __builtin_fmaf(wf, st[c][e], ki[c] * vj[e]);
+      p = __builtin_fmaf(st[c][e], kj[e], p);
+    }
+    *reinterpret_cast<f4*>(S + 4 * (256 * c + x)) = st[c];
+    // butterfly: all 16 lanes of the row end with the full sum and store the
+    // same value (no branch, so nothing is deferred behind one)
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) p += __shfl_xor(p, m, 16);
+    out[row + 16 * c + (x >> 4)] = p * gate(ri[c]);
   }
 }
 
@@ -551,7 +536,7 @@ hipError_t launch_matrix(const MatrixArgs& m, int64_t P, void* ws, hipStream_t s
 hipError_t launch_matrix_step(const MatrixStepArgs& m, hipStream_t s) {
   const int64_t blocks = m.B * m.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(wkv6_step_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kMsThreads), 0, s,
+  hipLaunchKernelGGL(wkv6_step_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                      m.H, m.lam, m.k, m.v, m.r, m.state, m.out);
   return hipGetLastError();
 }
