@@ -88,8 +88,8 @@ struct MsKernelArgs {
 // One staged chunk: one row per channel i holding, for the chunk's 16
 // tokens, the decay factors e^-lam, the keys decayed to the end of their
 // block of four, the values and the four block products of the factors;
-// READ adds the keys and the gates sigmoid(r). A row is 52 (84) floats: 52
-// and 84 are 20 and 52 modulo the 64 banks, so the rows of 16 neighbouring
+// READ adds the keys and the gates sigmoid(r). A row is 52 floats (84 with
+// READ), i.e. 52 (20) modulo the 64 banks, so the rows of 16 neighbouring
 // channels start on distinct 4-bank groups and every access pattern below is
 // conflict-free.
 template <bool READ>
