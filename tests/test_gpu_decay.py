@@ -24,12 +24,13 @@ pytestmark = pytest.mark.gpu
 PATHS = ["seq", "chunk"]
 WL0, WL3, WL4 = I.WORKLOADS[0], I.WORKLOADS[3], I.WORKLOADS[4]
 
-# T around the chunked kernel's tiles (64 tokens up to T = 256, then 256 for
-# fp32 and 128 for paired bf16) and C around its 32-channel groups.
+# T around the chunked kernel's tiles (64 tokens up to T = 256, then 128 for
+# fp32 and 64 for paired bf16, with a change of workgroup shape at T = 2048)
+# and C around its 32-channel groups.
 SHAPES = [
     (1, 1, 1), (2, 2, 7), (3, 31, 33), (2, 63, 48), (2, 64, 64), (2, 65, 17), (1, 255, 16),
-    (1, 256, 32), (1, 257, 80), (2, 511, 24), (1, 1000, 40), (1, 2049, 96), (2, 3000, 100),
-    (1, 4097, 16),
+    (1, 256, 32), (1, 257, 80), (1, 384, 40), (2, 511, 24), (2, 640, 24), (1, 1000, 40),
+    (1, 2048, 8), (1, 2049, 96), (2, 3000, 100), (1, 4097, 16),
 ]
 
 
