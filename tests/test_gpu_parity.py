@@ -18,8 +18,8 @@ WL0 = I.WORKLOADS[0]   # k, v ~ N(0, 1), w in [0.01, 5], u ~ N(0, 0.5)
 WL3 = I.WORKLOADS[3]   # k ~ N(0, 2), w in [1e-3, 8] (slow and fast decays), u ~ N(0, 1)
 WL4 = I.WORKLOADS[4]   # bf16, k ~ U(-20, 20) with 1% +-60 spikes
 
-# T around the chunked kernel's tiles (64 tokens for T <= 256, else 256; its
-# workgroup shape changes at T = 256 and T = 2048) and the look-back kernel's
+# T around the chunked kernel's tiles (64 tokens for T <= 256, 256 up to
+# T = 2048, 128 beyond; its workgroup shape changes at T = 256 and T = 2048) and the look-back kernel's
 # segments (32 tokens for T <= 512, else 128; anchors every 8 segments), and C
 # around both kernels' 32-channel groups (64 for bf16); every kernel runs every
 # shape.

@@ -195,8 +195,10 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
 constexpr int kLC = 32, kPS = 2;
 
 // Workgroup shape by sequence length (measured on MI355X): short sequences
-// want the fewest serial tiles; long ones want two waves per SIMD to overlap
-// each tile's scan with the neighbours' memory traffic.
+// want the fewest serial tiles (B=8 T=1024 C=768: 8 waves of 16 tokens, 24.6
+// us, against 25.7-27.2 for 8 x 8, 4 x 16, 16 x 8 and 4 x 32); long ones
+// smaller tiles (B=4 T=16384 C=2048: 8 x 8, 346 us, against 370-402 for
+// 16 x 8, 8 x 16, 4 x 16 and 4 x 32).
 template <typename IoT, int V, int W, int L, bool G>
 hipError_t launch_chunk_g(const FwdArgs& a, hipStream_t st) {
   constexpr int CH = kLC * V;
@@ -224,7 +226,7 @@ template <typename IoT, int V>
 hipError_t launch_chunk_v(const FwdArgs& a, hipStream_t st) {
   if (a.T <= kShortT) return launch_chunk_t<IoT, V, 8, 4>(a, st);
   if (a.T <= kLongT) return launch_chunk_t<IoT, V, 8, 16>(a, st);
-  return launch_chunk_t<IoT, V, 16, 8>(a, st);
+  return launch_chunk_t<IoT, V, 8, 8>(a, st);
 }
 
 bool aligned(const void* p, int bytes) {
@@ -232,17 +234,6 @@ bool aligned(const void* p, int bytes) {
 }
 
 }  // namespace
-
-ChunkShape chunk_shape(int io, int vec, int64_t T) {
-  (void)io;
-  ChunkShape s;
-  const int W = T <= kLongT ? 8 : 16;
-  s.L = T <= kShortT ? 4 : (T <= kLongT ? 16 : 8);
-  s.P = kPS * W;
-  s.channels = kLC * vec;
-  s.threads = 64 * W;
-  return s;
-}
 
 int chunk_vec_width(int io, int64_t C, const FwdArgs& a) {
   if (io != kBf16) return 1;

@@ -38,15 +38,6 @@ int seq_vec_width(int io, int64_t C, const FwdArgs& a);
 int chunk_vec_width(int io, int64_t C, const FwdArgs& a);
 int step_vec_width(int io, int64_t C, const StepArgs& a);
 
-// Chunked-scan shape for a problem: tokens per sub-chunk and per tile.
-struct ChunkShape {
-  int L;          // tokens per sub-chunk per tile
-  int P;          // sub-chunks per tile (threads along T per channel group)
-  int channels;   // channels per workgroup
-  int threads;    // threads per workgroup
-};
-ChunkShape chunk_shape(int io, int vec, int64_t T);
-
 // Look-back scan: device workspace = control words, then the published
 // per-(segment, channel) words. Zero-filled before first use; each launch
 // leaves it ready for the next.
