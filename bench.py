@@ -26,6 +26,10 @@ Default run (one JSON line on stdout):
     and on the decode workload's B=256 T=512 prefill shape, with the
     roofline on its algorithmic bytes (read k, v, dL/dout; write dL/dk,
     dL/dv).
+  * checkpointed_training: on the same two shapes, the plain prefill then
+    wkv_backward against wkv_forward_ckpt (the prefill that saves the
+    backward's checkpoints) then wkv_backward_ckpt (the backward that reads
+    them instead of re-running the recurrence).
   * cpu_baseline: the float64 oracle on the host, on the same prefill workload.
 
 --config N measures another workload (0: B=1 T=64 C=768; 2: the decode
@@ -265,6 +269,77 @@ def time_backward(wl, dev, reps=10):
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                          "kernel": "wkv_backward_kernel", "algorithmic_bytes_per_launch": abytes},
             "workspace_bytes": int(ws.numel())}
+
+
+def time_ckpt_pair(wl, dev, reps=10):
+    """A training layer's two calls both ways on workload wl's first layer
+    (fp32, seeded inputs and upstream gradient): the plain prefill then
+    wkv_backward, which re-runs the recurrence for its own checkpoints, against
+    wkv_forward_ckpt, which saves them while it runs, then wkv_backward_ckpt,
+    which reads them. Microseconds per call from event pairs around `reps`
+    back-to-back calls after two warm-up calls; the roofline of each
+    checkpoint call on its algorithmic bytes (the plain call's, plus 16 bytes
+    per channel per 8 tokens written by the forward and read by the
+    backward)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    w, u = I.params(wl)
+    k, v = I.kv(wl)
+    g = I.grad_out(wl)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    dw, du, dk, dv, dg = t(w), t(u), t(k), t(v), t(g)
+    del k, v, g
+    out, st = torch.empty_like(dk), torch.empty((3, wl.B, wl.C), device=dev)
+    ck = torch.empty(W.ckpt_shape(wl.B, wl.T, wl.C), device=dev)
+    gk, gv = torch.empty_like(dk), torch.empty_like(dk)
+    gw, gu = torch.empty_like(dw), torch.empty_like(dw)
+    ws = torch.empty(max(W.wkv_backward_workspace_size(wl.B, wl.T, wl.C), 1), dtype=torch.uint8,
+                     device=dev)
+    grads = (gk, gv, gw, gu, None)
+    calls = {
+        "forward": lambda: W.wkv_forward_ex(dw, du, dk, dv, out=out, state_out=st),
+        "backward": lambda: W.wkv_backward(dw, du, dk, dv, dg, want_gstate_in=False,
+                                           workspace=ws, out=grads),
+        "forward_ckpt": lambda: W.wkv_forward_ckpt(dw, du, dk, dv, out=out, state_out=st,
+                                                   ckpt=ck),
+        "backward_ckpt": lambda: W.wkv_backward(dw, du, dk, dv, dg, want_gstate_in=False,
+                                                workspace=ws, out=grads, ckpt=ck),
+    }
+    stream = torch.cuda.current_stream()
+    us = {}
+    for name, call in calls.items():
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / reps
+    ct = wl.B * wl.T * wl.C
+    ck_bytes = W.wkv_ckpt_bytes(wl.B, wl.T, wl.C)
+    fbytes = 12 * ct + 12 * wl.B * wl.C + 8 * wl.C + ck_bytes
+    bbytes = 20 * ct + 16 * wl.C + ck_bytes
+
+    def roof(nbytes, t_us):
+        a = nbytes / (t_us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(a / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": nbytes}
+
+    plain = us["forward"] + us["backward"]
+    saved = us["forward_ckpt"] + us["backward_ckpt"]
+    return {"workload": f"{wl.name}, one layer, forward then backward", "B": wl.B, "T": wl.T,
+            "C": wl.C, "io": "f32", "ckpt_bytes": ck_bytes,
+            "us_per_call": {k_: round(x, 2) for k_, x in us.items()},
+            "value": round(ct / (saved * 1e-6) / 1e9, 3),
+            "plain_value": round(ct / (plain * 1e-6) / 1e9, 3),
+            "unit": "G channel-tokens/s (forward + backward)",
+            "roofline_forward_ckpt": roof(fbytes, us["forward_ckpt"]),
+            "roofline_backward_ckpt": roof(bbytes, us["backward_ckpt"])}
 
 
 def time_gated(wl, dev, path, reps=50):
@@ -668,6 +743,11 @@ def main():
         for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
             _log(f"backward: {bwl.name} (one layer)")
             rec["backward"].append(time_backward(bwl, dev))
+            torch.cuda.empty_cache()
+        rec["checkpointed_training"] = []
+        for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+            _log(f"checkpointed forward + backward: {bwl.name} (one layer)")
+            rec["checkpointed_training"].append(time_ckpt_pair(bwl, dev))
             torch.cuda.empty_cache()
 
     if args.config == 1 and not args.no_backward:

@@ -217,6 +217,44 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u
  * wkv_status on error. */
 int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C);
 
+/* Training pair for the prefill (fp32): a forward that saves, and a backward
+ * that takes, the state in front of every chunk of 8 tokens of every lane.
+ * The backward then skips its own re-run of the forward to rebuild those
+ * states (for large B*C one of its two passes over k and v; for small B*C its
+ * segment summaries and their folds). Same operator, derivatives and
+ * conventions as wkv_forward_gated / wkv_backward.
+ *
+ * wkv_ckpt_bytes: size of ckpt for these sizes, ceil(T / 8) * B * C * 16
+ * bytes, or a negative wkv_status.
+ *
+ * wkv_forward_ckpt: as wkv_forward_gated (r NULL: ungated output) with
+ *   ckpt   out: [ceil(T / 8)][B][C] float4 (num, den, base, age), the lane
+ *          state in front of token 8j at [j][b][c], the maximum exponent kept
+ *          as base - age * w; 16-byte aligned, wkv_ckpt_bytes bytes, owned by
+ *          the caller; must not overlap any other argument. Required when
+ *          B, T, C > 0 (WKV_ERR_NULL).
+ *   path   WKV_PATH_AUTO, WKV_PATH_SEQ or WKV_PATH_CHUNK (the look-back scan
+ *          saves no checkpoints: WKV_PATH_LOOKBACK gives WKV_ERR_ARG). The
+ *          outputs equal those of the same kernel without checkpoints bit
+ *          for bit.
+ *
+ * wkv_backward_ckpt: as wkv_backward with
+ *   ckpt   [ceil(T / 8)][B][C] float4, what wkv_forward_ckpt wrote for the
+ *          same w, u, k, v and state_in (checkpoints of other inputs give
+ *          wrong gradients; this is not detected); 16-byte aligned, read
+ *          only; required when B, T, C > 0. The workspace is as for
+ *          wkv_backward (wkv_backward_workspace_size). */
+int64_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C);
+int wkv_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                     const float* k, const float* v, const float* r, const float* state_in,
+                     float* out, float* state_out, float* ckpt, int path, hipStream_t stream);
+int wkv_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                      const float* k, const float* v, const float* r, const float* state_in,
+                      const float* state_out, const float* gstate_out, const float* gout,
+                      const float* ckpt, float* gk, float* gv, float* gr, float* gw, float* gu,
+                      float* gstate_in, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream);
+
 /* One decode step with the gated output, out = sigmoid(r) * wkv (see
  * wkv_forward_gated); k, v, r, out of element type io ([B][C]); the state is
  * fp32 and ungated. */

@@ -190,6 +190,31 @@ def test_matrix_entry_points_validate_without_device():
     assert lib.wkv_matrix_step(1, 1, 64, w, k, v, r, P(a + 65536), w, nul) == 4
 
 
+def test_checkpoint_entry_points_validate_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    assert lib.wkv_ckpt_bytes(8, 1024, 768) == (1024 // 8) * 8 * 768 * 16
+    assert lib.wkv_ckpt_bytes(2, 9, 3) == 2 * 2 * 3 * 16      # ceil(9 / 8) chunks
+    assert lib.wkv_ckpt_bytes(-1, 8, 8) < 0
+    a = 0x10000000
+    w, u, k, v, out, ck = P(a), P(a + 4096), P(a + 8192), P(a + 16384), P(a + 24576), P(a + 65536)
+    # B, T, C, w, u, k, v, r, state_in, out, state_out, ckpt, path, stream
+    base = [1, 16, 64, w, u, k, v, nul, nul, out, nul]
+    assert lib.wkv_forward_ckpt(*base, ck, W.WKV_PATH_LOOKBACK, nul) == 7
+    assert lib.wkv_forward_ckpt(*base, nul, W.WKV_PATH_AUTO, nul) == 1
+    assert lib.wkv_forward_ckpt(*base, P(a + 65536 + 8), W.WKV_PATH_AUTO, nul) == 3
+    assert lib.wkv_forward_ckpt(*base, out, W.WKV_PATH_AUTO, nul) == 4
+    # B, T, C, w, u, k, v, r, state_in, state_out, gstate_out, gout, ckpt, gk, gv, gr, gw, gu,
+    # gstate_in, workspace, bytes, stream
+    g, gk, gv, gw, gu = P(a + 32768), P(a + 40960), P(a + 49152), P(a + 57344), P(a + 61440)
+    bwd = [1, 16, 64, w, u, k, v, nul, nul, nul, nul, g]
+    rest = [gk, gv, nul, gw, gu, nul, P(a + (1 << 24)), 1 << 20, nul]
+    assert lib.wkv_backward_ckpt(*bwd, nul, *rest) == 1
+    assert lib.wkv_backward_ckpt(*bwd, P(a + 65536 + 4), *rest) == 3
+    assert lib.wkv_backward_ckpt(*bwd, gk, *rest) == 4
+
+
 def test_per_token_decay_rates_are_seeded_and_positive():
     wl = I.WORKLOADS[1].scaled(B=3, T=50, C=32)
     r1 = I.decay_rates(wl)

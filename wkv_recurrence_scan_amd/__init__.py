@@ -31,6 +31,10 @@ from ._lib import (  # noqa: F401
     step,
     wkv_abi_version,
     wkv_backward,
+    wkv_forward_ckpt,
+    wkv_ckpt_bytes,
+    ckpt_shape,
+    CKPT_TOKENS,
     wkv_backward_workspace_size,
     wkv_forward,
     wkv_forward_bf16,

@@ -73,6 +73,9 @@ def load_library() -> ctypes.CDLL:
         "wkv_matrix_forward": [i64, i64, i64, i64] + [vp] * 8 + [i64, vp],
         "wkv_matrix_workspace_size": [i64, i64, i64, i64],
         "wkv_matrix_step": [i64, i64, i64] + [vp] * 6 + [vp],
+        "wkv_ckpt_bytes": [i64, i64, i64],
+        "wkv_forward_ckpt": [i64, i64, i64] + [vp] * 9 + [ci, vp],
+        "wkv_backward_ckpt": [i64, i64, i64] + [vp] * 16 + [vp, i64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -80,6 +83,7 @@ def load_library() -> ctypes.CDLL:
         fn.restype = {"wkv_status_string": ctypes.c_char_p,
                       "wkv_workspace_size": ctypes.c_int64,
                       "wkv_backward_workspace_size": ctypes.c_int64,
+                      "wkv_ckpt_bytes": ctypes.c_int64,
                       "wkv_matrix_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
     if lib.wkv_abi_version() != 1:
         raise RuntimeError(f"{LIBRARY_PATH}: unexpected ABI version {lib.wkv_abi_version()}")
@@ -315,7 +319,7 @@ def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Ten
                  state_out: Optional[torch.Tensor] = None,
                  gstate_out: Optional[torch.Tensor] = None, *, r: Optional[torch.Tensor] = None,
                  want_gstate_in: bool = True, workspace: Optional[torch.Tensor] = None, out=None,
-                 stream=None):
+                 ckpt: Optional[torch.Tensor] = None, stream=None):
     """Gradients of the prefill (float32). Returns (gw, gu, gk, gv, gstate_in)
     for the upstream gradient gout of out (and gstate_out of state_out, which
     must then be the state the forward returned), or (gw, gu, gk, gv,
@@ -323,7 +327,8 @@ def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Ten
     gstate_in is None when want_gstate_in is False. `out` may hold
     preallocated (gk, gv, gw, gu, gstate_in[, gr]) tensors; `workspace` a uint8
     tensor of at least wkv_backward_workspace_size bytes (else one is
-    allocated for the call)."""
+    allocated for the call). `ckpt`: the checkpoints wkv_forward_ckpt saved
+    for the same inputs (wkv_backward_ckpt), or None."""
     lib = load_library()
     if k.dim() != 3:
         raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
@@ -367,12 +372,79 @@ def wkv_backward(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.Ten
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
-        st = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
-                              _ptr(state_in), _ptr(state_out), _ptr(gstate_out), _ptr(gout),
-                              _ptr(gk), _ptr(gv), _ptr(gr), _ptr(gw), _ptr(gu), _ptr(gs),
-                              _ptr(workspace), workspace.numel(), ctypes.c_void_p(strm.cuda_stream))
-    _check(st, "wkv_backward")
+        if ckpt is None:
+            st = lib.wkv_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                  _ptr(state_in), _ptr(state_out), _ptr(gstate_out), _ptr(gout),
+                                  _ptr(gk), _ptr(gv), _ptr(gr), _ptr(gw), _ptr(gu), _ptr(gs),
+                                  _ptr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(strm.cuda_stream))
+            _check(st, "wkv_backward")
+        else:
+            _need(ckpt, "ckpt", f32, ckpt_shape(B, T, C), dev)
+            st = lib.wkv_backward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                       _ptr(state_in), _ptr(state_out), _ptr(gstate_out),
+                                       _ptr(gout), _ptr(ckpt), _ptr(gk), _ptr(gv), _ptr(gr),
+                                       _ptr(gw), _ptr(gu), _ptr(gs), _ptr(workspace),
+                                       workspace.numel(), ctypes.c_void_p(strm.cuda_stream))
+            _check(st, "wkv_backward_ckpt")
     return (gw, gu, gk, gv, gs) if r is None else (gw, gu, gk, gv, gs, gr)
+
+
+CKPT_TOKENS = 8
+
+
+def ckpt_shape(B: int, T: int, C: int):
+    """Shape of the checkpoint tensor (float32): (ceil(T / 8), B, C, 4), the
+    lane state (num, den, base, age) in front of every chunk of 8 tokens."""
+    return ((T + CKPT_TOKENS - 1) // CKPT_TOKENS, B, C, 4)
+
+
+def wkv_ckpt_bytes(B: int, T: int, C: int) -> int:
+    """Bytes of the checkpoints wkv_forward_ckpt saves for these sizes."""
+    n = load_library().wkv_ckpt_bytes(B, T, C)
+    if n < 0:
+        raise WKVError("wkv_ckpt_bytes", -n)
+    return int(n)
+
+
+def wkv_forward_ckpt(w, u, k, v, r=None, state_in=None, out=None, state_out=None, ckpt=None, *,
+                     path="auto", want_state=True, stream=None):
+    """wkv_forward_ckpt: the float32 prefill (gated when r is given) that also
+    saves the backward pass's checkpoints. Returns (out, state_out, ckpt);
+    pass ckpt to wkv_backward(..., ckpt=ckpt) with the same inputs."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    if path not in ("auto", "seq", "chunk"):
+        raise ValueError("path must be 'auto', 'seq' or 'chunk'")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    f32 = torch.float32
+    for name, t, shape in (("k", k, (B, T, C)), ("v", v, (B, T, C)), ("w", w, (C,)),
+                           ("u", u, (C,))):
+        _need(t, name, f32, shape, dev)
+    if r is not None:
+        _need(r, "r", f32, (B, T, C), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", f32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=f32, device=dev)
+    _need(out, "out", f32, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((3, B, C), dtype=f32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", f32, (3, B, C), dev)
+    if ckpt is None:
+        ckpt = torch.empty(ckpt_shape(B, T, C), dtype=f32, device=dev)
+    _need(ckpt, "ckpt", f32, ckpt_shape(B, T, C), dev)
+    with torch.cuda.device(dev):
+        st = lib.wkv_forward_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
+                                  _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ckpt),
+                                  _PATHS[path], _stream_handle(dev, stream))
+    _check(st, "wkv_forward_ckpt")
+    return out, state_out, ckpt
 
 
 def wkv_forward_gated(w, u, k, v, r, state_in=None, out=None, state_out=None, *, path="auto",

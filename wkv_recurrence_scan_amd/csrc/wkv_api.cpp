@@ -76,10 +76,19 @@ int64_t lookback_bytes(int io, int64_t B, int64_t T, int64_t C) {
   return a > b ? a : b;
 }
 
+// Bytes of the backward pass's checkpoints for these sizes: one float4 per
+// lane and chunk of kCkptTokens tokens, or -1 past the size limit.
+int64_t ckpt_bytes(int64_t B, int64_t T, int64_t C) {
+  const int64_t nch = (T + wkv::kCkptTokens - 1) / wkv::kCkptTokens;
+  int64_t n;
+  if (!mul3(nch, B, C, &n) || __builtin_mul_overflow(n, 16, &n) || n > kMaxBytes) return -1;
+  return n;
+}
+
 int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
                  const void* v, const void* r, bool gated, const float* state_in, void* out,
                  float* state_out, int io, int path, void* workspace, int64_t workspace_bytes,
-                 hipStream_t stream) {
+                 hipStream_t stream, float* ckpt = nullptr) {
   if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
   if (path < WKV_PATH_AUTO || path > WKV_PATH_LOOKBACK) return WKV_ERR_ARG;
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
@@ -115,8 +124,23 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
     return WKV_ERR_ALIAS;
   if (state_out != state_in && overlaps(state_out, state_bytes, state_in, state_bytes))
     return WKV_ERR_ALIAS;
+  if (ckpt != nullptr && T > 0) {
+    // checkpoints for the backward pass: fp32, the sequential or chunked scan
+    const int64_t cb = ckpt_bytes(B, T, C);
+    if (io != WKV_IO_F32) return WKV_ERR_ARG;
+    if (cb < 0) return WKV_ERR_DIM;
+    if (misaligned(ckpt, 16)) return WKV_ERR_ALIGN;
+    if (overlaps(ckpt, cb, k, sbytes) || overlaps(ckpt, cb, v, sbytes) ||
+        overlaps(ckpt, cb, r, sbytes) || overlaps(ckpt, cb, out, sbytes) ||
+        overlaps(ckpt, cb, w, pbytes) || overlaps(ckpt, cb, u, pbytes) ||
+        overlaps(ckpt, cb, state_in, state_bytes) || overlaps(ckpt, cb, state_out, state_bytes))
+      return WKV_ERR_ALIAS;
+    if (path == WKV_PATH_LOOKBACK) return WKV_ERR_ARG;
+  } else {
+    ckpt = nullptr;
+  }
   if (workspace != nullptr && workspace_bytes < 0) return WKV_ERR_WORKSPACE;
-  const bool have_ws = workspace != nullptr && workspace_bytes > 0;
+  const bool have_ws = ckpt == nullptr && workspace != nullptr && workspace_bytes > 0;
   if (have_ws) {
     if (misaligned(workspace, 256)) return WKV_ERR_ALIGN;
     if (overlaps(workspace, workspace_bytes, k, sbytes) ||
@@ -130,7 +154,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
       return WKV_ERR_ALIAS;
   }
 
-  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out, r};
+  const wkv::FwdArgs a{B, T, C, w, u, k, v, state_in, out, state_out, r, ckpt};
   if (path == WKV_PATH_LOOKBACK && T > 0 &&
       (!have_ws || workspace_bytes < wkv::lookback_workspace_bytes(
                                          wkv::lookback_vec_width(io, C, a), B, T, C)))
@@ -368,7 +392,7 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
                   const float* k, const float* v, const float* r, const float* state_in,
                   const float* state_out, const float* gstate_out, const float* gout, float* gk,
                   float* gv, float* gr, float* gw, float* gu, float* gstate_in, void* workspace,
-                  int64_t workspace_bytes, hipStream_t stream) {
+                  int64_t workspace_bytes, hipStream_t stream, const float* ckpt = nullptr) {
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
   int64_t seq_bytes, state_bytes;
   if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, 4, &seq_bytes) ||
@@ -391,6 +415,10 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
                        gout, gk, gv, gr, gw, gu,       gstate_in};
   for (const void* p : all)
     if (misaligned(p, 4)) return WKV_ERR_ALIGN;
+  if (!tokens) ckpt = nullptr;
+  const int64_t cbytes = ckpt != nullptr ? ckpt_bytes(B, T, C) : 0;
+  if (cbytes < 0) return WKV_ERR_DIM;
+  if (misaligned(ckpt, 16)) return WKV_ERR_ALIGN;
 
   const int64_t pbytes = C * 4;
   const int64_t sbytes = tokens ? seq_bytes : 0;
@@ -401,7 +429,7 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
   const Range inputs[] = {{w, pbytes},        {u, pbytes},          {k, sbytes},
                           {v, sbytes},        {r, sbytes},          {gout, sbytes},
                           {state_in, state_bytes}, {state_out, state_bytes},
-                          {gstate_out, state_bytes}};
+                          {gstate_out, state_bytes}, {ckpt, cbytes}};
   const Range outputs[] = {{gk, sbytes}, {gv, sbytes}, {gr, sbytes}, {gw, pbytes}, {gu, pbytes},
                            {gstate_in, state_bytes}};
   for (int i = 0; i < 6; ++i) {
@@ -422,8 +450,8 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
-  const wkv::BwdArgs a{B,        T,         C,          w,  u,  k,  v,  gout,     state_in,
-                       state_out, gstate_out, gk,        gv, gw, gu, gstate_in, r,  gr};
+  const wkv::BwdArgs a{B,  T,  C,  w,  u,         k, v,  gout, state_in, state_out, gstate_out,
+                       gk, gv, gw, gu, gstate_in, r, gr, ckpt};
   e = wkv::launch_backward(a, workspace, stream);
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
@@ -439,6 +467,32 @@ int wkv_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u
                  int64_t workspace_bytes, hipStream_t stream) {
   return backward_impl(B, T, C, w, u, k, v, r, state_in, state_out, gstate_out, gout, gk, gv, gr,
                        gw, gu, gstate_in, workspace, workspace_bytes, stream);
+}
+
+int wkv_backward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                      const float* k, const float* v, const float* r, const float* state_in,
+                      const float* state_out, const float* gstate_out, const float* gout,
+                      const float* ckpt, float* gk, float* gv, float* gr, float* gw, float* gu,
+                      float* gstate_in, void* workspace, int64_t workspace_bytes,
+                      hipStream_t stream) {
+  if (ckpt == nullptr && B > 0 && T > 0 && C > 0) return WKV_ERR_NULL;
+  return backward_impl(B, T, C, w, u, k, v, r, state_in, state_out, gstate_out, gout, gk, gv, gr,
+                       gw, gu, gstate_in, workspace, workspace_bytes, stream, ckpt);
+}
+
+int64_t wkv_ckpt_bytes(int64_t B, int64_t T, int64_t C) {
+  if (B < 0 || T < 0 || C < 0) return -WKV_ERR_DIM;
+  const int64_t n = ckpt_bytes(B, T, C);
+  return n < 0 ? -WKV_ERR_DIM : n;
+}
+
+int wkv_forward_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                     const float* k, const float* v, const float* r, const float* state_in,
+                     float* out, float* state_out, float* ckpt, int path, hipStream_t stream) {
+  if (path != WKV_PATH_AUTO && path != WKV_PATH_SEQ && path != WKV_PATH_CHUNK) return WKV_ERR_ARG;
+  if (ckpt == nullptr && B > 0 && T > 0 && C > 0) return WKV_ERR_NULL;
+  return forward_impl(B, T, C, w, u, k, v, r, r != nullptr, state_in, out, state_out, WKV_IO_F32,
+                      path, nullptr, 0, stream, ckpt);
 }
 
 int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {

@@ -46,7 +46,7 @@ namespace wkv {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kLc = 8;  // tokens per checkpoint chunk
+constexpr int kLc = kCkptTokens;  // tokens per checkpoint chunk
 
 // Suffix sums of one lane, relative to e^z with z = zb - za * w.
 struct Suffix {
@@ -339,8 +339,9 @@ __device__ __forceinline__ Lane initial_lane(const BwdKernelArgs& a, int64_t lan
                                : lane_empty();
 }
 
-// Large B*C: one thread per lane, both passes over the whole sequence.
-template <bool G>
+// Large B*C: one thread per lane, both passes over the whole sequence
+// (GIVEN: the forward saved the checkpoints, pass 1 is skipped).
+template <bool G, bool GIVEN>
 __global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(BwdKernelArgs a) {
   const int64_t lanes = a.B * a.C;
   const int64_t lane = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_backward_kernel(BwdKernelArgs
 
   // pass 1: forward state advance, a checkpoint in front of every chunk
   const Lane s_init = initial_lane(a, lanes, lane);
-  {
+  if constexpr (!GIVEN) {
     Lane s = s_init;
     forward_chunks<true>(s, io, 0, io.nfull, wc, a.ckpt, lanes, lane);
     if (io.rest > 0) a.ckpt[io.nfull * lanes + lane] = make_float4(s.n, s.d, s.base, s.age);
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_forward_kernel(BwdKer
   a.seg_fwd[s * lanes + lane] = make_float4(x.n, x.d, lane_max_exp(x, wc), 0.0f);
 }
 
-template <bool G>
+template <bool G, bool GIVEN>
 __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernelArgs a) {
   const int64_t lanes = a.B * a.C;
   const int64_t id = static_cast<int64_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
@@ -412,22 +413,30 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   const LaneIo io = lane_io(a, lane);
   int64_t j0, j1;
   seg_bounds(a, io, s, j0, j1);
-  // start state: the initial state, then every earlier segment (all full)
-  Lane x = initial_lane(a, lanes, lane);
-  const float seg_len = static_cast<float>(a.seg_chunks * kLc);
-  // (summaries fetched kFoldBatch at a time so that their loads overlap; the
-  // fold order is unchanged)
-  int64_t sr = 0;
-  for (; sr + kFoldBatch <= s; sr += kFoldBatch) {
-    float4 f[kFoldBatch];
+  // start state: the forward's checkpoint (GIVEN), else the initial state,
+  // then every earlier segment (all full)
+  Lane x;
+  if constexpr (GIVEN) {
+    const float4 cp = a.ckpt[j0 * lanes + lane];
+    x = Lane{cp.x, cp.y, cp.z, cp.w};
+  } else {
+    x = initial_lane(a, lanes, lane);
+    const float seg_len = static_cast<float>(a.seg_chunks * kLc);
+    // (summaries fetched kFoldBatch at a time so that their loads overlap;
+    // the fold order is unchanged)
+    int64_t sr = 0;
+    for (; sr + kFoldBatch <= s; sr += kFoldBatch) {
+      float4 f[kFoldBatch];
 #pragma unroll
-    for (int m = 0; m < kFoldBatch; ++m) f[m] = a.seg_fwd[(sr + m) * lanes + lane];
+      for (int m = 0; m < kFoldBatch; ++m) f[m] = a.seg_fwd[(sr + m) * lanes + lane];
 #pragma unroll
-    for (int m = 0; m < kFoldBatch; ++m) lane_absorb(x, Seg{f[m].x, f[m].y, f[m].z, seg_len}, wc);
-  }
-  for (; sr < s; ++sr) {
-    const float4 f = a.seg_fwd[sr * lanes + lane];
-    lane_absorb(x, Seg{f.x, f.y, f.z, seg_len}, wc);
+      for (int m = 0; m < kFoldBatch; ++m)
+        lane_absorb(x, Seg{f[m].x, f[m].y, f[m].z, seg_len}, wc);
+    }
+    for (; sr < s; ++sr) {
+      const float4 f = a.seg_fwd[sr * lanes + lane];
+      lane_absorb(x, Seg{f.x, f.y, f.z, seg_len}, wc);
+    }
   }
   // forward over the segment: checkpoints, and the segment's own suffix sums
   // at the position before it, sum over its tokens t (j = t - first) of
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   float p = 0.0f, q = 0.0f, r = 0.0f, rq = 0.0f, zl = kEmpty;
   float jj = 0.0f;
   for (int64_t j = j0; j < j1; ++j) {
-    a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
+    if constexpr (!GIVEN) a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
     const int n = j < io.nfull ? kLc : io.rest;
     Chunk<G> ch;
     const int64_t off = io.row + j * io.step;
@@ -632,9 +641,14 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
   const SegPlan sp = seg_plan(lanes, a.T);
   const WsLayout l = ws_layout(a.B, a.T, a.C);
   char* base = static_cast<char*>(ws);
+  // the forward's checkpoints when given (read only: the kernels that write
+  // checkpoints are not launched then), else the workspace's
+  const bool given = a.ckpt != nullptr;
+  float4* ck = given ? const_cast<float4*>(reinterpret_cast<const float4*>(a.ckpt))
+                     : reinterpret_cast<float4*>(base + l.ckpt);
   BwdKernelArgs k{a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.gout, a.state_in, a.state_out,
                   a.gstate_out, a.r, a.gk, a.gv, a.gr, a.gstate_in,
-                  reinterpret_cast<float4*>(base + l.ckpt),
+                  ck,
                   reinterpret_cast<float*>(base + l.part),
                   reinterpret_cast<float*>(base + l.part) + sp.segments * lanes,
                   reinterpret_cast<float4*>(base + l.seg_fwd),
@@ -648,17 +662,35 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     const bool gated = a.r != nullptr;
     if (sp.segments == 1) {
       if (gated) {
-        hipLaunchKernelGGL(wkv_backward_kernel<true>, grid, block, 0, st, k);
+        if (given) {
+          hipLaunchKernelGGL((wkv_backward_kernel<true, true>), grid, block, 0, st, k);
+        } else {
+          hipLaunchKernelGGL((wkv_backward_kernel<true, false>), grid, block, 0, st, k);
+        }
       } else {
-        hipLaunchKernelGGL(wkv_backward_kernel<false>, grid, block, 0, st, k);
+        if (given) {
+          hipLaunchKernelGGL((wkv_backward_kernel<false, true>), grid, block, 0, st, k);
+        } else {
+          hipLaunchKernelGGL((wkv_backward_kernel<false, false>), grid, block, 0, st, k);
+        }
       }
     } else {
-      hipLaunchKernelGGL(wkv_bwd_seg_forward_kernel, grid, block, 0, st, k);
+      // with the forward's checkpoints every segment starts from its own: no
+      // summaries to fold
+      if (!given) hipLaunchKernelGGL(wkv_bwd_seg_forward_kernel, grid, block, 0, st, k);
       if (gated) {
-        hipLaunchKernelGGL(wkv_bwd_seg_sums_kernel<true>, grid, block, 0, st, k);
+        if (given) {
+          hipLaunchKernelGGL((wkv_bwd_seg_sums_kernel<true, true>), grid, block, 0, st, k);
+        } else {
+          hipLaunchKernelGGL((wkv_bwd_seg_sums_kernel<true, false>), grid, block, 0, st, k);
+        }
         hipLaunchKernelGGL(wkv_bwd_seg_backward_kernel<true>, grid, block, 0, st, k);
       } else {
-        hipLaunchKernelGGL(wkv_bwd_seg_sums_kernel<false>, grid, block, 0, st, k);
+        if (given) {
+          hipLaunchKernelGGL((wkv_bwd_seg_sums_kernel<false, true>), grid, block, 0, st, k);
+        } else {
+          hipLaunchKernelGGL((wkv_bwd_seg_sums_kernel<false, false>), grid, block, 0, st, k);
+        }
         hipLaunchKernelGGL(wkv_bwd_seg_backward_kernel<false>, grid, block, 0, st, k);
       }
     }

@@ -33,15 +33,18 @@
 #include "wkv_internal.h"
 #include "wkv_tile.h"
 
+#include <type_traits>
+
 namespace wkv {
 namespace {
 
-template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED, bool G>
+template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED, bool G, bool CK>
 __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L, G>& r, int nvalid, Lane (&carry)[V],
                                            const float (&wd)[V], const float (&ub)[V],
                                            const float (&cb)[V], bool fast, Seg (*tot)[LC * V],
                                            typename IoT::elem* __restrict__ op, int64_t C,
-                                           bool cvalid, int wave, int sl, int cl) {
+                                           bool cvalid, int wave, int sl, int cl,
+                                           const CkOut& ck) {
   // 1. own summary, 2. inclusive scan over the wave's sub-chunks
   Seg inc[V];
 #pragma unroll
@@ -87,16 +90,16 @@ __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L, G>& r, int nval
 #pragma unroll
   for (int j = 0; j < V; ++j) lane_absorb(pre[j], exc[j], wd[j]);
   // 4. rescan own tokens from the prefix
-  rescan_sel<IoT, V, L, MASKED, G>(fast, pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+  rescan_sel<IoT, V, L, MASKED, G, CK>(fast, pre, r, wd, ub, cb, nvalid, cvalid, op, C, ck);
 }
 
-template <typename IoT, int V, int LC, int PS, int W, int L, bool G>
+template <typename IoT, int V, int LC, int PS, int W, int L, bool G, bool CK>
 __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
     const typename IoT::elem* __restrict__ rg, const float* __restrict__ state_in,
     typename IoT::elem* __restrict__ out, float* __restrict__ state_out,
-    int64_t groups_per_row) {
+    int64_t groups_per_row, float4* __restrict__ ckpt) {
   static_assert(LC * PS == 64, "a wave is LC channel groups by PS sub-chunks");
   constexpr int CH = LC * V;          // channels per workgroup
   constexpr int TL = W * PS * L;      // tokens per tile
@@ -142,6 +145,10 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   const typename IoT::elem* rp = G ? rg + base : nullptr;
   typename IoT::elem* op = out + base;
   const int64_t step = static_cast<int64_t>(TL) * C;
+  // checkpoints (CK): this thread's first token of a tile
+  auto ck_at = [&](int64_t tile) {
+    return CkOut{ckpt, plane, lane0, tile * TL + static_cast<int64_t>(sub) * L};
+  };
 
   const int64_t full = T / TL;  // tiles with every token present
   // Software pipeline over two register buffers: the loads of the next tile
@@ -155,14 +162,15 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   for (int64_t tile = 0; tile < full; tile += 2) {
     const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
     chunk_load<IoT, V, L, false, G>(Bf, kp + nb * step, vp + nb * step, at(rp, nb), C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false, G>(A, L, carry, wd, ub, cb, fast, tot[tile & 1],
-                                               op + tile * step, C, cvalid, wave, sl, cl);
+    chunk_tile<IoT, V, LC, PS, W, L, false, G, CK>(A, L, carry, wd, ub, cb, fast, tot[tile & 1],
+                                                   op + tile * step, C, cvalid, wave, sl, cl,
+                                                   ck_at(tile));
     if (tile + 1 >= full) break;
     const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
     chunk_load<IoT, V, L, false, G>(A, kp + na * step, vp + na * step, at(rp, na), C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false, G>(Bf, L, carry, wd, ub, cb, fast,
-                                               tot[(tile + 1) & 1], op + (tile + 1) * step, C,
-                                               cvalid, wave, sl, cl);
+    chunk_tile<IoT, V, LC, PS, W, L, false, G, CK>(Bf, L, carry, wd, ub, cb, fast,
+                                                   tot[(tile + 1) & 1], op + (tile + 1) * step, C,
+                                                   cvalid, wave, sl, cl, ck_at(tile + 1));
   }
   if (full * TL < T) {  // last, partial tile
     const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
@@ -171,9 +179,9 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
     ChunkRegs<V, L, G> last;
     chunk_load<IoT, V, L, true, G>(last, kp + full * step, vp + full * step, at(rp, full), C,
                                    nvalid);
-    chunk_tile<IoT, V, LC, PS, W, L, true, G>(last, nvalid, carry, wd, ub, cb, fast,
-                                              tot[full & 1], op + full * step, C, cvalid, wave,
-                                              sl, cl);
+    chunk_tile<IoT, V, LC, PS, W, L, true, G, CK>(last, nvalid, carry, wd, ub, cb, fast,
+                                                  tot[full & 1], op + full * step, C, cvalid,
+                                                  wave, sl, cl, ck_at(full));
   }
 
   if (state_out != nullptr && sub == 0 && cvalid) {
@@ -199,25 +207,34 @@ constexpr int kLC = 32, kPS = 2;
 // us, against 25.7-27.2 for 8 x 8, 4 x 16, 16 x 8 and 4 x 32); long ones
 // smaller tiles (B=4 T=16384 C=2048: 8 x 8, 346 us, against 370-402 for
 // 16 x 8, 8 x 16, 4 x 16 and 4 x 32).
-template <typename IoT, int V, int W, int L, bool G>
+template <typename IoT, int V, int W, int L, bool G, bool CK>
 hipError_t launch_chunk_g(const FwdArgs& a, hipStream_t st) {
   constexpr int CH = kLC * V;
   const int64_t gpr = (a.C + CH - 1) / CH;
   const int64_t blocks = a.B * gpr;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L, G>),
+  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L, G, CK>),
                      dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0, st, a.B, a.T, a.C,
                      a.w, a.u, static_cast<const typename IoT::elem*>(a.k),
                      static_cast<const typename IoT::elem*>(a.v),
                      static_cast<const typename IoT::elem*>(a.r), a.state_in,
-                     static_cast<typename IoT::elem*>(a.out), a.state_out, gpr);
+                     static_cast<typename IoT::elem*>(a.out), a.state_out, gpr,
+                     reinterpret_cast<float4*>(a.ckpt));
   return hipGetLastError();
 }
 
 template <typename IoT, int V, int W, int L>
 hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
-  return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true>(a, st)
-                        : launch_chunk_g<IoT, V, W, L, false>(a, st);
+  if constexpr (std::is_same<IoT, IoF32>::value && V == 1) {
+    if (a.ckpt != nullptr) {
+      return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true, true>(a, st)
+                            : launch_chunk_g<IoT, V, W, L, false, true>(a, st);
+    }
+  } else {
+    if (a.ckpt != nullptr) return hipErrorInvalidValue;  // checkpoints: fp32 only
+  }
+  return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true, false>(a, st)
+                        : launch_chunk_g<IoT, V, W, L, false, false>(a, st);
 }
 
 constexpr int64_t kShortT = 256, kLongT = 2048;

@@ -232,12 +232,13 @@ __device__ __forceinline__ float lane_step_fast(Lane& s, float k, float v, float
   const bool tok_wins = g > 0.0f;
   const float F = tok_wins ? x : 1.0f;
   const float G = tok_wins ? 1.0f : x;
+  // every multiply-add is spelled out, so that the rounding does not depend
+  // on how the compiler splits the surrounding code into blocks
   const float fn = F * s.n;
-  const float fd = F * s.d;
   const float gc = G * c;
-  const float out = __builtin_fmaf(gc, v, fn) * fast_rcp(fd + gc);
+  const float out = __builtin_fmaf(gc, v, fn) * fast_rcp(__builtin_fmaf(F, s.d, gc));
   s.n = __builtin_fmaf(G, v, fn);
-  s.d = fd + G;
+  s.d = __builtin_fmaf(F, s.d, G);
   s.base = tok_wins ? k : s.base;
   s.age = tok_wins ? 0.0f : age1;
   return out;

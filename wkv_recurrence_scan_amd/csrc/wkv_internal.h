@@ -9,6 +9,10 @@ namespace wkv {
 
 enum Io : int { kF32 = 0, kBf16 = 1 };
 
+// Tokens per checkpoint chunk of the backward pass (and of a prefill that
+// saves its checkpoints for it).
+constexpr int kCkptTokens = 8;
+
 struct FwdArgs {
   int64_t B, T, C;
   const float* w;
@@ -19,6 +23,7 @@ struct FwdArgs {
   void* out;
   float* state_out;       // nullptr: not written
   const void* r = nullptr;  // receptance, like k; non-null: out = sigmoid(r) * wkv
+  float* ckpt = nullptr;    // fp32 only: [ceil(T/8)][B*C] float4 states for the backward
 };
 
 struct StepArgs {
@@ -67,6 +72,7 @@ struct BwdArgs {
   float* gstate_in;         // nullptr: not wanted
   const float* r = nullptr; // receptance of a gated output (out = sigmoid(r) * wkv)
   float* gr = nullptr;      // dL/dr, with r
+  const float* ckpt = nullptr;  // the forward's checkpoints ([ceil(T/8)][B*C] float4), or nullptr
 };
 // Workspace: per-lane partial sums and per-chunk checkpoints, written before
 // they are read in every launch (no clearing needed).

@@ -15,6 +15,8 @@
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
+#include <type_traits>
+
 namespace wkv {
 namespace {
 
@@ -58,15 +60,23 @@ __device__ __forceinline__ void seq_compute(const SeqBlock<IoT, V, U, G>& blk, L
   }
 }
 
-// All T tokens of one thread's channels, in order.
-template <typename IoT, int V, int U, bool FAST, bool G>
+// All T tokens of one thread's channels, in order. CK (fp32, one channel per
+// thread, U = kCkptTokens): the state in front of every block of U tokens
+// also goes to ckpt[block * lanes + lane] as (n, d, base, age), the
+// checkpoints of the backward pass.
+template <typename IoT, int V, int U, bool FAST, bool G, bool CK>
 __device__ __forceinline__ void seq_walk(Lane (&s)[V], const float (&wd)[V], const float (&ub)[V],
                                          const float (&cb)[V],
                                          const typename IoT::elem* __restrict__ kp,
                                          const typename IoT::elem* __restrict__ vp,
                                          const typename IoT::elem* __restrict__ rp,
                                          typename IoT::elem* __restrict__ op, int64_t T,
-                                         int64_t C) {
+                                         int64_t C, float4* __restrict__ ckpt, int64_t lanes,
+                                         int64_t lane) {
+  static_assert(!CK || (V == 1 && U == kCkptTokens), "checkpoint blocks are kCkptTokens tokens");
+  auto save = [&](int64_t blk) {
+    if constexpr (CK) ckpt[blk * lanes + lane] = make_float4(s[0].n, s[0].d, s[0].base, s[0].age);
+  };
   // Two register buffers, alternating; the loads for the block after the one
   // being computed are issued first, on every path (the last full block
   // re-reads itself, a cache hit), so that the compiler's counter-based waits
@@ -78,12 +88,15 @@ __device__ __forceinline__ void seq_walk(Lane (&s)[V], const float (&wd)[V], con
   for (int64_t blk = 0; blk < nblk; blk += 2) {
     const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
     seq_load<IoT, V, U, G>(Bf, kp + nb * C, vp + nb * C, at(nb), C);
+    save(blk);
     seq_compute<IoT, V, U, FAST, G>(A, s, wd, ub, cb, op + blk * U * C, C);
     if (blk + 1 >= nblk) break;
     const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
     seq_load<IoT, V, U, G>(A, kp + na * C, vp + na * C, at(na), C);
+    save(blk + 1);
     seq_compute<IoT, V, U, FAST, G>(Bf, s, wd, ub, cb, op + (blk + 1) * U * C, C);
   }
+  if (nblk * U < T) save(nblk);
   for (int64_t t = nblk * U; t < T; ++t) {
     float kk[V], vv[V], rr[V], o[V];
     IoT::template load<V, true>(kp + t * C, kk);
@@ -98,12 +111,13 @@ __device__ __forceinline__ void seq_walk(Lane (&s)[V], const float (&wd)[V], con
   }
 }
 
-template <typename IoT, int V, int U, bool G>
+template <typename IoT, int V, int U, bool G, bool CK>
 __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
     const typename IoT::elem* __restrict__ rg, const float* __restrict__ state_in,
-    typename IoT::elem* __restrict__ out, float* __restrict__ state_out) {
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out,
+    float4* __restrict__ ckpt) {
   const int64_t groups_per_row = C / V;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kSeqThreads + threadIdx.x;
   if (gid >= B * groups_per_row) return;
@@ -138,9 +152,9 @@ __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
   float cb[V];
   bonus_ratios(wd, ub, cb);
   if (wave_fast_ok(wd, ub)) {
-    seq_walk<IoT, V, U, true, G>(s, wd, ub, cb, kp, vp, rp, op, T, C);
+    seq_walk<IoT, V, U, true, G, CK>(s, wd, ub, cb, kp, vp, rp, op, T, C, ckpt, plane, lane0);
   } else {
-    seq_walk<IoT, V, U, false, G>(s, wd, ub, cb, kp, vp, rp, op, T, C);
+    seq_walk<IoT, V, U, false, G, CK>(s, wd, ub, cb, kp, vp, rp, op, T, C, ckpt, plane, lane0);
   }
 
   if (state_out != nullptr) {
@@ -157,24 +171,34 @@ __global__ __launch_bounds__(kSeqThreads) void wkv_seq_kernel(
   }
 }
 
-template <typename IoT, int V, bool G>
+template <typename IoT, int V, bool G, bool CK>
 hipError_t launch_seq_g(const FwdArgs& a, hipStream_t st) {
   constexpr int U = 8;
   const int64_t threads = a.B * (a.C / V);
   const int64_t blocks = (threads + kSeqThreads - 1) / kSeqThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_seq_kernel<IoT, V, U, G>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((wkv_seq_kernel<IoT, V, U, G, CK>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kSeqThreads), 0, st, a.B, a.T, a.C, a.w, a.u,
                      static_cast<const typename IoT::elem*>(a.k),
                      static_cast<const typename IoT::elem*>(a.v),
                      static_cast<const typename IoT::elem*>(a.r), a.state_in,
-                     static_cast<typename IoT::elem*>(a.out), a.state_out);
+                     static_cast<typename IoT::elem*>(a.out), a.state_out,
+                     reinterpret_cast<float4*>(a.ckpt));
   return hipGetLastError();
 }
 
 template <typename IoT, int V>
 hipError_t launch_seq_t(const FwdArgs& a, hipStream_t st) {
-  return a.r != nullptr ? launch_seq_g<IoT, V, true>(a, st) : launch_seq_g<IoT, V, false>(a, st);
+  if constexpr (std::is_same<IoT, IoF32>::value && V == 1) {
+    if (a.ckpt != nullptr) {
+      return a.r != nullptr ? launch_seq_g<IoT, V, true, true>(a, st)
+                            : launch_seq_g<IoT, V, false, true>(a, st);
+    }
+  } else {
+    if (a.ckpt != nullptr) return hipErrorInvalidValue;  // checkpoints: fp32 only
+  }
+  return a.r != nullptr ? launch_seq_g<IoT, V, true, false>(a, st)
+                        : launch_seq_g<IoT, V, false, false>(a, st);
 }
 
 bool aligned(const void* p, int bytes) {

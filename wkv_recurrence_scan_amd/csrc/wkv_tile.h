@@ -4,6 +4,7 @@
 #pragma once
 
 #include "wkv_device.h"
+#include "wkv_internal.h"
 
 namespace wkv {
 namespace {
@@ -141,19 +142,36 @@ __device__ __forceinline__ void tile_scan(const ChunkRegs<V, L, G>& r, const flo
   }
 }
 
+// Where a prefill saves the backward pass's checkpoints (fp32, one channel
+// per thread): the lane state in front of every token whose index is a
+// multiple of kCkptTokens goes to p[(token / kCkptTokens) * lanes + lane] as
+// (n, d, base, age); tok0 is the index of the thread's first token here.
+struct CkOut {
+  float4* p;
+  int64_t lanes, lane, tok0;
+};
+
 // Re-runs the recurrence over one thread's sub-chunk from the state in front
 // of it and writes the outputs (gated by sigmoid(r) when G). FAST selects
-// lane_step_fast.
-template <typename IoT, int V, int L, bool MASKED, bool FAST, bool G>
+// lane_step_fast; CK also saves checkpoints (see CkOut).
+template <typename IoT, int V, int L, bool MASKED, bool FAST, bool G, bool CK = false>
 __device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L, G>& r,
                                        const float (&wd)[V], const float (&ub)[V],
                                        const float (&cb)[V], int nvalid, bool cvalid,
-                                       typename IoT::elem* __restrict__ op, int64_t C) {
+                                       typename IoT::elem* __restrict__ op, int64_t C,
+                                       const CkOut& ck = CkOut{}) {
+  static_assert(!CK || V == 1, "checkpoints are saved by one-channel threads");
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     // a guard, not a break, so that the loop stays fully unrolled and the
     // register arrays keep static indices
     if (!MASKED || i < nvalid) {
+      if constexpr (CK) {
+        const int64_t t = ck.tok0 + i;
+        if (cvalid && (t % kCkptTokens) == 0)
+          ck.p[(t / kCkptTokens) * ck.lanes + ck.lane] =
+              make_float4(pre[0].n, pre[0].d, pre[0].base, pre[0].age);
+      }
       float o[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
@@ -165,15 +183,16 @@ __device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L, G>&
   }
 }
 
-template <typename IoT, int V, int L, bool MASKED, bool G>
+template <typename IoT, int V, int L, bool MASKED, bool G, bool CK = false>
 __device__ __forceinline__ void rescan_sel(bool fast, Lane (&pre)[V], const ChunkRegs<V, L, G>& r,
                                            const float (&wd)[V], const float (&ub)[V],
                                            const float (&cb)[V], int nvalid, bool cvalid,
-                                           typename IoT::elem* __restrict__ op, int64_t C) {
+                                           typename IoT::elem* __restrict__ op, int64_t C,
+                                           const CkOut& ck = CkOut{}) {
   if (fast) {
-    rescan<IoT, V, L, MASKED, true, G>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+    rescan<IoT, V, L, MASKED, true, G, CK>(pre, r, wd, ub, cb, nvalid, cvalid, op, C, ck);
   } else {
-    rescan<IoT, V, L, MASKED, false, G>(pre, r, wd, ub, cb, nvalid, cvalid, op, C);
+    rescan<IoT, V, L, MASKED, false, G, CK>(pre, r, wd, ub, cb, nvalid, cvalid, op, C, ck);
   }
 }
 
