@@ -538,10 +538,11 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKe
 }
 
 // dL/dw and dL/du: the per-lane partial sums added over the batch. A
-// workgroup owns 64 channels; its 16 row slices each add the rows
-// b = slice, slice + 16, ... in order, then slice totals are added in order
-// through LDS, so the result does not depend on timing.
-constexpr int kRedCh = 64, kRedSlices = 16;
+// workgroup owns 32 channels (128-byte row pieces); its 32 row slices each add
+// the rows b = slice, slice + 32, ... in order (eight rows' loads issued
+// together, rows past the end read as zero), then the slice totals are added
+// in order through LDS: the result does not depend on timing.
+constexpr int kRedCh = 32, kRedSlices = 32, kRedBatch = 8;
 
 __global__ __launch_bounds__(kRedCh * kRedSlices) void wkv_grad_reduce_kernel(
     int64_t B, int64_t C, const float* __restrict__ gw_part, const float* __restrict__ gu_part,
@@ -552,24 +553,19 @@ __global__ __launch_bounds__(kRedCh * kRedSlices) void wkv_grad_reduce_kernel(
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kRedCh + ch;
   float aw = 0.0f, au = 0.0f;
   if (c < C) {
-    // rows b = slice, slice + 16, ... in order, fetched four at a time
-    int64_t b = slice;
-    for (; b + 3 * kRedSlices < B; b += 4 * kRedSlices) {
-      float xw[4], xu[4];
+    for (int64_t b0 = slice; b0 < B; b0 += kRedBatch * kRedSlices) {
+      float xw[kRedBatch], xu[kRedBatch];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        xw[m] = gw_part[(b + m * kRedSlices) * C + c];
-        xu[m] = gu_part[(b + m * kRedSlices) * C + c];
+      for (int m = 0; m < kRedBatch; ++m) {
+        const int64_t b = b0 + m * kRedSlices;
+        xw[m] = b < B ? gw_part[b * C + c] : 0.0f;
+        xu[m] = b < B ? gu_part[b * C + c] : 0.0f;
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < kRedBatch; ++m) {
         aw += xw[m];
         au += xu[m];
       }
-    }
-    for (; b < B; b += kRedSlices) {
-      aw += gw_part[b * C + c];
-      au += gu_part[b * C + c];
     }
   }
   sw[slice][ch] = aw;

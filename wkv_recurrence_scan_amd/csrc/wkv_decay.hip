@@ -531,8 +531,11 @@ int dd_vec_width(int io, int64_t C, const DdArgs& a) {
   return ok ? 2 : 1;
 }
 
+// fp32: one channel per thread, as the constant-decay step (more blocks for
+// a short pass); bf16: the widest width the pointers allow.
 int dd_step_vec_width(int io, int64_t C, const DdStepArgs& a) {
-  const int elem = io == kBf16 ? 2 : 4;
+  if (io == kF32) return 1;
+  const int elem = 2;
   for (int V : {4, 2, 1}) {
     if (C % V) continue;
     if (!aligned(a.k, V * elem) || !aligned(a.v, V * elem) || !aligned(a.w, V * elem) ||
@@ -557,11 +560,7 @@ hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, hipStream_t s) {
 }
 
 hipError_t launch_dd_step(const DdStepArgs& a, int io, int vec, hipStream_t s) {
-  if (io == kF32) {
-    if (vec == 4) return launch_dd_step_t<IoF32, 4>(a, s);
-    if (vec == 2) return launch_dd_step_t<IoF32, 2>(a, s);
-    return launch_dd_step_t<IoF32, 1>(a, s);
-  }
+  if (io == kF32) return launch_dd_step_t<IoF32, 1>(a, s);
   if (vec == 4) return launch_dd_step_t<IoBf16, 4>(a, s);
   if (vec == 2) return launch_dd_step_t<IoBf16, 2>(a, s);
   return launch_dd_step_t<IoBf16, 1>(a, s);
