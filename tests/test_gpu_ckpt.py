@@ -134,9 +134,15 @@ def check_ckpt(w, u, k, v, gout, state_in=None, with_gstate=False, r=None, tol=G
     return errs
 
 
-# T < 64 runs the one-thread-per-lane plan, T >= 64 with few lanes the
-# segmented one
-BWD_SHAPES = [(1, 1, 8), (2, 7, 33), (2, 45, 24), (2, 150, 24), (1, 300, 32), (2, 1000, 16)]
+# T < 64 runs the one-thread-per-lane kernel. T >= 64 with few lanes: the
+# segmented kernels while B * ceil(C / 32) stays below three quarters of the
+# CUs (192 on MI355X), the one-pass chunked kernel from there on (tiles of
+# 128 tokens, 32 channels per workgroup). Both with a partial last tile, T
+# not a multiple of 8, tile-exact T, idle channel threads (C = 24, 70) and
+# several tiles.
+BWD_SHAPES = [(1, 1, 8), (2, 7, 33), (2, 45, 24), (2, 150, 24), (1, 300, 32), (2, 1000, 16),
+              (2, 256, 40), (1, 136, 70), (1, 1500, 8),
+              (192, 150, 24), (96, 136, 70), (192, 256, 32), (200, 400, 8)]
 
 
 @pytest.mark.parametrize("B,T,C", BWD_SHAPES)
@@ -149,11 +155,11 @@ def test_backward_ckpt_matches_oracle(B, T, C, wl):
     say("  " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
 
 
-@pytest.mark.parametrize("T", [45, 150])
+@pytest.mark.parametrize("B,T", [(2, 45), (2, 150), (192, 150)])
 @pytest.mark.parametrize("gated", [False, True])
-def test_backward_ckpt_with_states_and_gate(T, gated):
-    B, C = 2, 24
-    say(f"backward_ckpt states and gate T={T} gated={gated}")
+def test_backward_ckpt_with_states_and_gate(B, T, gated):
+    C = 24
+    say(f"backward_ckpt states and gate B={B} T={T} gated={gated}")
     w, u, k, v = make_case(WL3, B, T, C)
     gout = np.random.default_rng([46, T]).normal(0, 1, (B, T, C)).astype(np.float32)
     r = I.receptance(WL3.scaled(B=B, T=T, C=C), 1) if gated else None

@@ -450,8 +450,9 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
-  const wkv::BwdArgs a{B,  T,  C,  w,  u,         k, v,  gout, state_in, state_out, gstate_out,
-                       gk, gv, gw, gu, gstate_in, r, gr, ckpt};
+  wkv::BwdArgs a{B,  T,  C,  w,  u,         k, v,  gout, state_in, state_out, gstate_out,
+                 gk, gv, gw, gu, gstate_in, r, gr, ckpt};
+  a.cus = cu_count(dev);
   e = wkv::launch_backward(a, workspace, stream);
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }

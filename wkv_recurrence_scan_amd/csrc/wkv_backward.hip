@@ -39,8 +39,11 @@
 //
 // HBM traffic per channel-token (fp32): pass 1 reads k, v (8 B); pass 2 reads
 // k, v, g (12 B) and writes dL/dk, dL/dv (8 B); checkpoints add 2 x 16 / kLc B.
+// When the forward saved the checkpoints pass 1 is skipped; for small B*C a
+// one-pass chunked kernel (further down) then replaces the segmented ones.
 #include "wkv_device.h"
 #include "wkv_internal.h"
+#include "wkv_tile.h"
 
 namespace wkv {
 namespace {
@@ -72,19 +75,21 @@ __device__ __forceinline__ float lane_step_rec(Lane& s, float k, float v, float 
   return out;
 }
 
-// One chunk's k, v, dL/dout and, for a gated output (G), the receptance.
-template <bool G>
-struct Chunk {
-  float k[kLc], v[kLc], g[kLc], r[G ? kLc : 1];
+// L tokens' k, v, dL/dout and, for a gated output (G), the receptance.
+template <int L, bool G>
+struct ChunkL {
+  float k[L], v[L], g[L], r[G ? L : 1];
 };
+template <bool G>
+using Chunk = ChunkL<kLc, G>;
 
-template <bool MASKED, bool G>
-__device__ __forceinline__ void load_chunk(Chunk<G>& c, const float* __restrict__ kp,
+template <bool MASKED, bool G, int L>
+__device__ __forceinline__ void load_chunk(ChunkL<L, G>& c, const float* __restrict__ kp,
                                            const float* __restrict__ vp,
                                            const float* __restrict__ gp,
                                            const float* __restrict__ rp, int64_t C, int n) {
 #pragma unroll
-  for (int i = 0; i < kLc; ++i) {
+  for (int i = 0; i < L; ++i) {
     if (!MASKED || i < n) {
       c.k[i] = __builtin_nontemporal_load(kp + i * C);
       c.v[i] = __builtin_nontemporal_load(vp + i * C);
@@ -100,60 +105,135 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& c, const float* __restrict_
 }
 
 // dL/d(wkv_t) from dL/dout_t: the gate's share when the output is gated.
-template <bool G>
-__device__ __forceinline__ float wkv_grad(const Chunk<G>& c, int i) {
+template <bool G, int L>
+__device__ __forceinline__ float wkv_grad(const ChunkL<L, G>& c, int i) {
   if constexpr (G) return c.g[i] * gate(c.r[i]);
   return c.g[i];
 }
 
-// Backward walk over one chunk of n tokens (all kLc unless MASKED) starting
-// from checkpoint state st; gk, gv (and gr when G) point at the chunk's first
-// token. With a gate, dL/dr_t = dL/dout_t wkv_t s (1 - s), s = sigmoid(r_t),
-// and the WKV sees dL/dout_t s.
-template <bool MASKED, bool G>
-__device__ __forceinline__ void chunk_backward(const Chunk<G>& c, int n, Lane st, Suffix& a,
-                                               float w, float u, float& gw_acc, float& gu_acc,
-                                               float* __restrict__ gkp, float* __restrict__ gvp,
-                                               float* __restrict__ grp, int64_t C) {
-  float y[kLc], M[kLc], rho[kLc], om[kLc];
+// What the backward walk needs of each token of a chunk, from a forward run
+// over it: the output y, the log-scale M and reciprocal rho of its
+// denominator, and the current token's share om (see lane_step_rec).
+template <int L>
+struct FwdRec {
+  float y[L], M[L], rho[L], om[L];
+};
+
+// The forward over a chunk of n tokens (all L unless MASKED) from state st.
+template <int L, bool MASKED, bool G>
+__device__ __forceinline__ void chunk_record(const ChunkL<L, G>& c, int n, Lane st, float w,
+                                             float u, FwdRec<L>& f) {
 #pragma unroll
-  for (int i = 0; i < kLc; ++i) {
-    if (!MASKED || i < n) y[i] = lane_step_rec(st, c.k[i], c.v[i], w, u, M[i], rho[i], om[i]);
+  for (int i = 0; i < L; ++i) {
+    if (!MASKED || i < n) f.y[i] = lane_step_rec(st, c.k[i], c.v[i], w, u, f.M[i], f.rho[i], f.om[i]);
   }
+}
+
+// Backward walk over a recorded chunk, last token first, from the suffix
+// sums a at its end (left at the position before it); gk, gv (and gr when G)
+// point at the chunk's first token and are written only when `store`. With a
+// gate, dL/dr_t = dL/dout_t wkv_t s (1 - s), s = sigmoid(r_t), and the WKV
+// sees dL/dout_t s.
+template <int L, bool MASKED, bool G>
+__device__ __forceinline__ void chunk_walk(const ChunkL<L, G>& c, const FwdRec<L>& f, int n,
+                                           Suffix& a, float w, float& gw_acc, float& gu_acc,
+                                           float* __restrict__ gkp, float* __restrict__ gvp,
+                                           float* __restrict__ grp, int64_t C, bool store) {
 #pragma unroll
-  for (int i = kLc - 1; i >= 0; --i) {
+  for (int i = L - 1; i >= 0; --i) {
     if (!MASKED || i < n) {
       // gradients of token i from the suffix sums over t > i
       float gi = c.g[i];
       if constexpr (G) {
         const float sg = gate(c.r[i]);
-        __builtin_nontemporal_store(gi * y[i] * sg * (1.0f - sg), grp + i * C);
+        if (store) __builtin_nontemporal_store(gi * f.y[i] * sg * (1.0f - sg), grp + i * C);
         gi *= sg;
       }
-      const float e_cur = gi * om[i];
+      const float e_cur = gi * f.om[i];
       const float ex = fast_exp2(__builtin_fmaf(-a.za, w, c.k[i] + a.zb) * kLog2e);  // e^(k_i+z)
       const float gv = __builtin_fmaf(a.p, ex, e_cur);
-      const float gk = __builtin_fmaf(c.v[i], gv, -__builtin_fmaf(a.q, ex, e_cur * y[i]));
-      gu_acc = __builtin_fmaf(e_cur, c.v[i] - y[i], gu_acc);
+      const float gk = __builtin_fmaf(c.v[i], gv, -__builtin_fmaf(a.q, ex, e_cur * f.y[i]));
+      gu_acc = __builtin_fmaf(e_cur, c.v[i] - f.y[i], gu_acc);
       gw_acc = __builtin_fmaf(-ex, __builtin_fmaf(c.v[i], a.r, -a.rq), gw_acc);
-      __builtin_nontemporal_store(gk, gkp + i * C);
-      __builtin_nontemporal_store(gv, gvp + i * C);
+      if (store) {
+        __builtin_nontemporal_store(gk, gkp + i * C);
+        __builtin_nontemporal_store(gv, gvp + i * C);
+      }
       // token i joins the suffix sums: a new term g_i rho_i e^{-M_i} against
       // the old sums decayed by one step
-      const float sg = __builtin_fmaf(a.za + 1.0f, w, -M[i] - a.zb);  // -M_i - (z - w)
+      const float sg = __builtin_fmaf(a.za + 1.0f, w, -f.M[i] - a.zb);  // -M_i - (z - w)
       const float x = fast_exp2(__builtin_fabsf(sg) * -kLog2e);
       const bool new_wins = sg > 0.0f;
       const float fo = new_wins ? x : 1.0f;
       const float fn = new_wins ? 1.0f : x;
-      const float ai = gi * rho[i] * fn;
+      const float ai = gi * f.rho[i] * fn;
       a.r = fo * (a.r + a.p);
       a.rq = fo * (a.rq + a.q);
       a.p = __builtin_fmaf(fo, a.p, ai);
-      a.q = __builtin_fmaf(fo, a.q, ai * y[i]);
-      a.zb = new_wins ? -M[i] : a.zb;
+      a.q = __builtin_fmaf(fo, a.q, ai * f.y[i]);
+      a.zb = new_wins ? -f.M[i] : a.zb;
       a.za = new_wins ? 0.0f : a.za + 1.0f;
     }
   }
+}
+
+// Backward walk over one chunk of n tokens (all kLc unless MASKED) starting
+// from checkpoint state st.
+template <bool MASKED, bool G>
+__device__ __forceinline__ void chunk_backward(const Chunk<G>& c, int n, Lane st, Suffix& a,
+                                               float w, float u, float& gw_acc, float& gu_acc,
+                                               float* __restrict__ gkp, float* __restrict__ gvp,
+                                               float* __restrict__ grp, int64_t C) {
+  FwdRec<kLc> f;
+  chunk_record<kLc, MASKED, G>(c, n, st, w, u, f);
+  chunk_walk<kLc, MASKED, G>(c, f, n, a, w, gw_acc, gu_acc, gkp, gvp, grp, C, true);
+}
+
+// A chunk's own suffix sums at the position before it: the sum over its
+// tokens (j = 0, 1, ... from its first) of a_j e^{-j w} times (1, out_j, j,
+// j out_j), a_j = dL/dwkv_j / Den_j, relative to the largest exponent
+// -M_j - j w.
+template <int L, bool MASKED, bool G>
+__device__ __forceinline__ Suffix chunk_own_sums(const ChunkL<L, G>& c, const FwdRec<L>& f, int n,
+                                                 float w) {
+  float p = 0.0f, q = 0.0f, r = 0.0f, rq = 0.0f, zl = kEmpty;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (!MASKED || i < n) {
+      const float jj = static_cast<float>(i);
+      const float xe = __builtin_fmaf(-jj, w, -f.M[i]);
+      const float d = xe - zl;
+      const float e = fast_exp2(__builtin_fabsf(d) * -kLog2e);
+      const bool nw = d > 0.0f;
+      const float fo = nw ? e : 1.0f;
+      const float fn = (nw ? 1.0f : e) * wkv_grad<G>(c, i) * f.rho[i];
+      p = __builtin_fmaf(fo, p, fn);
+      q = __builtin_fmaf(fo, q, fn * f.y[i]);
+      r = __builtin_fmaf(fo, r, fn * jj);
+      rq = __builtin_fmaf(fo, rq, fn * jj * f.y[i]);
+      zl = nw ? xe : zl;
+    }
+  }
+  return Suffix{p, q, r, rq, zl, 0.0f};
+}
+
+// Suffix sums across a span X of len tokens: acc holds the sums at the end
+// of X (from the tokens after it) and leaves with the sums at the position
+// before X: decayed by len steps (their distance-weighted parts gain len times
+// the plain ones) plus X's own sums, taken against the larger exponent.
+__device__ __forceinline__ void suffix_absorb(Suffix& acc, const Suffix& X, float len, float w) {
+  // X's exponent minus acc's once decayed: (X.zb - X.za w) - (acc.zb - (acc.za + len) w)
+  const float sg = __builtin_fmaf(acc.za + len - X.za, w, X.zb - acc.zb);
+  const float e = fast_exp2(__builtin_fabsf(sg) * -kLog2e);
+  const bool xw = sg > 0.0f;
+  const float fo = xw ? e : 1.0f;
+  const float fx = xw ? 1.0f : e;
+  acc.r = __builtin_fmaf(fo, __builtin_fmaf(len, acc.p, acc.r), fx * X.r);
+  acc.rq = __builtin_fmaf(fo, __builtin_fmaf(len, acc.q, acc.rq), fx * X.rq);
+  acc.p = __builtin_fmaf(fo, acc.p, fx * X.p);
+  acc.q = __builtin_fmaf(fo, acc.q, fx * X.q);
+  acc.zb = xw ? X.zb : acc.zb;
+  acc.za = xw ? X.za : acc.za + len;
 }
 
 // Where one lane's tokens are: k, v, g and the gradients at row + t * C.
@@ -501,17 +581,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKe
     const float L = static_cast<float>((xj1 - xj0) * kLc - (xj1 > io.nfull && io.rest > 0
                                                                 ? kLc - io.rest
                                                                 : 0));
-    const float sg = __builtin_fmaf(acc.za + L, wc, zx - acc.zb);  // zx - (z - L w)
-    const float e = fast_exp2(__builtin_fabsf(sg) * -kLog2e);
-    const bool xw = sg > 0.0f;
-    const float fo = xw ? e : 1.0f;
-    const float fx = xw ? 1.0f : e;
-    acc.r = __builtin_fmaf(fo, __builtin_fmaf(L, acc.p, acc.r), fx * X.z);
-    acc.rq = __builtin_fmaf(fo, __builtin_fmaf(L, acc.q, acc.rq), fx * X.w);
-    acc.p = __builtin_fmaf(fo, acc.p, fx * X.x);
-    acc.q = __builtin_fmaf(fo, acc.q, fx * X.y);
-    acc.zb = xw ? zx : acc.zb;
-    acc.za = xw ? 0.0f : acc.za + L;
+    suffix_absorb(acc, Suffix{X.x, X.y, X.z, X.w, zx, 0.0f}, L, wc);
   };
   // later segments, last first, their sums fetched kFoldBatch at a time
   int64_t x = a.segments - 1;
@@ -535,6 +605,163 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_backward_kernel(BwdKe
   }
   a.gw_part[s * lanes + lane] = gw_acc;
   a.gu_part[s * lanes + lane] = gu_acc;
+}
+
+// Small B*C with the forward's checkpoints: one pass. One workgroup owns
+// kBcLC adjacent channels of one batch row and walks the sequence from its
+// end in tiles of P = 2W sub-chunks of L tokens (whole checkpoint chunks);
+// lane (sl, cl) of wave `wave` holds sub-chunk 2 wave + sl of channel cl.
+// Per tile:
+//   1. each thread loads its sub-chunk's k, v, dL/dout (and r) and the
+//      checkpoint in front of it, re-runs the forward over it in registers
+//      and forms the sub-chunk's own suffix sums;
+//   2. the two sub-chunks of a wave combine through a lane shuffle, the wave
+//      totals go through LDS; every thread folds the carry (the sums at the
+//      tile's end) with the totals of the waves after its own, last first,
+//      then with the later sub-chunk of its wave: the sums at its sub-chunk's
+//      end;
+//   3. each thread walks its sub-chunk backwards from there, writing dL/dk,
+//      dL/dv; the carry moves to the tile's start.
+// k, v and dL/dout are read once. The per-thread partial sums of dL/dw and
+// dL/du are added per channel in a fixed order at the end.
+constexpr int kBcLC = 32, kBcPS = 2;
+constexpr int kBcW = 8, kBcL = 8;  // waves per workgroup, tokens per sub-chunk
+
+template <int W, int L, bool MASKED, bool G>
+__device__ __forceinline__ void bwd_tile(const ChunkL<L, G>& ch, const float4& cp, int n,
+                                         int64_t t0, int64_t T, Suffix& carry,
+                                         Suffix (*tot)[kBcLC], float wc, float uc,
+                                         float& gw_acc, float& gu_acc, const BwdKernelArgs& a,
+                                         int64_t off, bool cvalid, int wave, int sl, int cl) {
+  constexpr int TL = W * kBcPS * L;
+  // 1. forward from the checkpoint, own sums
+  FwdRec<L> f;
+  const Lane st = n > 0 ? Lane{cp.x, cp.y, cp.z, cp.w} : lane_empty();
+  chunk_record<L, MASKED, G>(ch, n, st, wc, uc, f);
+  const Suffix own = chunk_own_sums<L, MASKED, G>(ch, f, n, wc);
+  // 2. the wave's later sub-chunk, the wave total
+  Suffix later;
+  later.p = __shfl_down(own.p, kBcLC, 64);
+  later.q = __shfl_down(own.q, kBcLC, 64);
+  later.r = __shfl_down(own.r, kBcLC, 64);
+  later.rq = __shfl_down(own.rq, kBcLC, 64);
+  later.zb = __shfl_down(own.zb, kBcLC, 64);
+  later.za = __shfl_down(own.za, kBcLC, 64);
+  // tokens of sub-chunk s of this tile (all L in a full tile)
+  const int64_t tile0 = t0 - static_cast<int64_t>(wave * kBcPS + sl) * L;
+  auto sub_len = [&](int s) -> float {
+    if constexpr (!MASKED) {
+      return static_cast<float>(L);
+    } else {
+      const int64_t left = T - (tile0 + static_cast<int64_t>(s) * L);
+      return static_cast<float>(left <= 0 ? 0 : (left >= L ? L : left));
+    }
+  };
+  if (sl == 0) {
+    Suffix t = later;
+    suffix_absorb(t, own, static_cast<float>(n), wc);
+    tot[wave][cl] = t;
+  }
+  __syncthreads();
+  Suffix mine = carry;
+#pragma unroll
+  for (int jj = W - 1; jj >= 0; --jj) {
+    if (jj == wave) mine = carry;
+    suffix_absorb(carry, tot[jj][cl], sub_len(kBcPS * jj) + sub_len(kBcPS * jj + 1), wc);
+  }
+  if (sl == 0) suffix_absorb(mine, later, sub_len(kBcPS * wave + 1), wc);
+  static_assert(TL % kLc == 0, "tiles are whole checkpoint chunks");
+  // 3. walk back over the sub-chunk
+  float* grp = G ? a.gr + off : a.gr;
+  chunk_walk<L, MASKED, G>(ch, f, n, mine, wc, gw_acc, gu_acc, a.gk + off, a.gv + off, grp, a.C,
+                           cvalid);
+}
+
+template <int W, int L, bool G>
+__global__ __launch_bounds__(64 * W) void wkv_bwd_chunk_kernel(BwdKernelArgs a,
+                                                               int64_t groups_per_row) {
+  static_assert(L % kLc == 0, "a sub-chunk starts at a checkpoint");
+  constexpr int TL = W * kBcPS * L;  // tokens per tile
+  constexpr int SUBS = W * kBcPS;
+  __shared__ Suffix tot[2][W][kBcLC];
+  __shared__ float red[2][SUBS][kBcLC];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int cl = lane % kBcLC;
+  const int sl = lane / kBcLC;
+  const int sub = wave * kBcPS + sl;
+
+  const int64_t g = xcd_swizzle(blockIdx.x, a.B * groups_per_row);
+  const int64_t b = g / groups_per_row;
+  const int64_t c0 = (g - b * groups_per_row) * kBcLC + cl;
+  const bool cvalid = c0 < a.C;
+  const int64_t c = cvalid ? c0 : a.C - 1;  // idle tail threads mirror the last channel
+  const int64_t lanes = a.B * a.C;
+  const int64_t lane_id = b * a.C + c;
+  const float wc = a.w[c], uc = a.u[c];
+  const int64_t T = a.T, C = a.C;
+  const int64_t row = b * T * C + c;
+  const int64_t full = T / TL;  // tiles with every token present
+
+  Suffix carry = suffix_init(a.state_out, a.gstate_out, lanes, lane_id);
+  float gw_acc = 0.0f, gu_acc = 0.0f;
+  auto first = [&](int64_t tile) { return tile * TL + static_cast<int64_t>(sub) * L; };
+  auto rp = [&](int64_t o) { return G ? a.r + o : a.r; };
+  auto load = [&](ChunkL<L, G>& ch, float4& cp, int64_t tile) {
+    const int64_t o = row + first(tile) * C;
+    load_chunk<false, G>(ch, a.k + o, a.v + o, a.gout + o, rp(o), C, L);
+    cp = a.ckpt[(first(tile) / kLc) * lanes + lane_id];
+  };
+  int parity = 0;
+  if (full * TL < T) {  // the last, partial tile comes first here
+    const int64_t t0 = first(full);
+    const int64_t left = T - t0;
+    const int n = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
+    ChunkL<L, G> last;
+    const int64_t o = row + (n > 0 ? t0 : 0) * C;
+    load_chunk<true, G>(last, a.k + o, a.v + o, a.gout + o, rp(o), C, n);
+    const float4 cp = n > 0 ? a.ckpt[(t0 / kLc) * lanes + lane_id] : make_float4(0, 0, 0, 0);
+    bwd_tile<W, L, true, G>(last, cp, n, t0, T, carry, tot[parity], wc, uc, gw_acc, gu_acc, a, o,
+                            cvalid, wave, sl, cl);
+    parity ^= 1;
+  }
+  // full tiles, last first; the next one's loads are issued before the
+  // current one is processed (tile 0 re-reads itself at the end, so the loads
+  // are unconditional)
+  ChunkL<L, G> A, Bf;
+  float4 ca, cb;
+  if (full > 0) load(A, ca, full - 1);
+  for (int64_t tile = full - 1; tile >= 0; tile -= 2) {
+    load(Bf, cb, tile >= 1 ? tile - 1 : 0);
+    bwd_tile<W, L, false, G>(A, ca, L, first(tile), T, carry, tot[parity], wc, uc, gw_acc, gu_acc,
+                             a, row + first(tile) * C, cvalid, wave, sl, cl);
+    parity ^= 1;
+    if (tile < 1) break;
+    load(A, ca, tile >= 2 ? tile - 2 : 0);
+    bwd_tile<W, L, false, G>(Bf, cb, L, first(tile - 1), T, carry, tot[parity], wc, uc, gw_acc,
+                             gu_acc, a, row + first(tile - 1) * C, cvalid, wave, sl, cl);
+    parity ^= 1;
+  }
+  // carry: the sums at position -1 (every thread holds the same)
+  if (sub == 0) {
+    initial_state_grad(initial_lane(a, lanes, lane_id), a.state_in != nullptr, carry, wc, gw_acc,
+                       cvalid ? a.gstate_in : nullptr, lanes, lane_id);
+  }
+  red[0][sub][cl] = gw_acc;
+  red[1][sub][cl] = gu_acc;
+  __syncthreads();
+  if (sub == 0 && cvalid) {
+    float tw = 0.0f, tu = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < SUBS; ++s2) {
+      tw += red[0][s2][cl];
+      tu += red[1][s2][cl];
+    }
+    a.gw_part[lane_id] = tw;
+    a.gu_part[lane_id] = tu;
+  }
 }
 
 // dL/dw and dL/du: the per-lane partial sums added over the batch. A
@@ -640,13 +867,23 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
   // the forward's checkpoints when given (read only: the kernels that write
   // checkpoints are not launched then), else the workspace's
   const bool given = a.ckpt != nullptr;
+  // small B*C with the forward's checkpoints: the one-pass chunked kernel
+  // (one partial-sum row per batch row) while its workgroups fill at least
+  // three quarters of the CUs. It walks the whole sequence per workgroup, so
+  // with fewer the segmented kernels, which split time as well, are faster.
+  // Measured on MI355X, with checkpoints: B=8 T=1024 C=768 (192 workgroups)
+  // 45 against 53 us, B=16 T=2048 C=1024 164 against 220, B=4 T=16384
+  // C=2048 668 against 895; B=1 T=4096 C=768 (24 workgroups) 129 against 52.
+  const int64_t groups = a.B * ((a.C + kBcLC - 1) / kBcLC);
+  const bool one_pass = given && sp.segments > 1 && 4 * groups >= 3 * static_cast<int64_t>(a.cus);
+  const int64_t rows = one_pass ? 1 : sp.segments;
   float4* ck = given ? const_cast<float4*>(reinterpret_cast<const float4*>(a.ckpt))
                      : reinterpret_cast<float4*>(base + l.ckpt);
   BwdKernelArgs k{a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.gout, a.state_in, a.state_out,
                   a.gstate_out, a.r, a.gk, a.gv, a.gr, a.gstate_in,
                   ck,
                   reinterpret_cast<float*>(base + l.part),
-                  reinterpret_cast<float*>(base + l.part) + sp.segments * lanes,
+                  reinterpret_cast<float*>(base + l.part) + rows * lanes,
                   reinterpret_cast<float4*>(base + l.seg_fwd),
                   reinterpret_cast<float4*>(base + l.seg_rev),
                   reinterpret_cast<float*>(base + l.seg_rev_z), sp.segments, sp.seg_chunks};
@@ -656,7 +893,18 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kBwdThreads);
     const bool gated = a.r != nullptr;
-    if (sp.segments == 1) {
+    if (one_pass) {
+      const int64_t gpr = (a.C + kBcLC - 1) / kBcLC;
+      const int64_t wgs = a.B * gpr;
+      if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+      const dim3 cgrid(static_cast<unsigned>(wgs)), cblock(64 * kBcW);
+      if (gated) {
+        hipLaunchKernelGGL((wkv_bwd_chunk_kernel<kBcW, kBcL, true>), cgrid, cblock, 0, st, k, gpr);
+      } else {
+        hipLaunchKernelGGL((wkv_bwd_chunk_kernel<kBcW, kBcL, false>), cgrid, cblock, 0, st, k,
+                           gpr);
+      }
+    } else if (sp.segments == 1) {
       if (gated) {
         if (given) {
           hipLaunchKernelGGL((wkv_backward_kernel<true, true>), grid, block, 0, st, k);
@@ -696,7 +944,7 @@ hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t st) {
   const int64_t rblocks = (a.C + kRedCh - 1) / kRedCh;
   if (rblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(wkv_grad_reduce_kernel, dim3(static_cast<unsigned>(rblocks)),
-                     dim3(kRedCh * kRedSlices), 0, st, a.B * sp.segments, a.C, k.gw_part,
+                     dim3(kRedCh * kRedSlices), 0, st, a.B * rows, a.C, k.gw_part,
                      k.gu_part, a.gw, a.gu);
   return hipGetLastError();
 }

@@ -73,6 +73,7 @@ struct BwdArgs {
   const float* r = nullptr; // receptance of a gated output (out = sigmoid(r) * wkv)
   float* gr = nullptr;      // dL/dr, with r
   const float* ckpt = nullptr;  // the forward's checkpoints ([ceil(T/8)][B*C] float4), or nullptr
+  int cus = 256;                // compute units of the device
 };
 // Workspace: per-lane partial sums and per-chunk checkpoints, written before
 // they are read in every launch (no clearing needed).
