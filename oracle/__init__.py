@@ -17,7 +17,8 @@ closed forms and invariants. None is "parity unpinned".
 """
 
 from .wkv_decay import wkv_dd_direct, wkv_dd_recurrent, wkv_dd_step_ref  # noqa: F401
-from .wkv_grad import wkv_backward_direct, wkv_gated_backward_direct  # noqa: F401
+from .wkv_grad import (  # noqa: F401
+    wkv_backward_direct, wkv_dd_backward_direct, wkv_gated_backward_direct)
 from .wkv_matrix import wkv6_direct, wkv6_recurrent, wkv6_step_ref  # noqa: F401
 from .wkv_oracle import (  # noqa: F401
     EMPTY_MAX_EXP,

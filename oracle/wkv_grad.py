@@ -163,3 +163,102 @@ def wkv_gated_backward_direct(w, u, k, v, r, gout, state_in=None, gstate_out=Non
     g = _f64(gout)
     gw, gu, gk, gv, gs = wkv_backward_direct(w, u, k, v, g * s, state_in, gstate_out, state_out)
     return gw, gu, gk, gv, gs, g * y * s * (1.0 - s)
+
+
+# ---------------------------------------------------------------------------
+# Per-token (data-dependent) decay (see wkv_decay.wkv_dd_direct).
+# ---------------------------------------------------------------------------
+
+def wkv_dd_backward_direct(w, u, k, v, gout, state_in=None, gstate_out=None, state_out=None):
+    """Gradients of sum(gout * out) (+ the final-state term, as in
+    wkv_backward_direct) for the operator with a decay rate per token,
+    w (B, T, C). The terms are those of wkv_decay.wkv_dd_direct: at output t
+    the initial state has exponent m0 - sum_{j<t} w_j, past token i < t
+    exponent k_i - sum_{j=i+1}^{t-1} w_j, the current token u + k_t; the final
+    state holds token i at k_i - sum_{j=i+1}^{T-1} w_j and the initial state at
+    m0 - sum_{j<T} w_j. The quotient-rule derivatives of wkv_backward_direct
+    apply unchanged; a rate w_j enters (with derivative -1) the exponent of
+    every term whose decay range contains step j. Term by term, O(T^2) per
+    lane. Returns (gw (B, T, C), gu (C,), gk, gv, gstate_in)."""
+    from .wkv_decay import _check
+
+    w, u, k, v, s0 = _check(w, u, k, v, state_in)
+    g = _f64(gout)
+    B, T, C = k.shape
+    if g.shape != k.shape:
+        raise ValueError("gout must be (B, T, C)")
+    if (gstate_out is None) != (state_out is None):
+        raise ValueError("gstate_out and state_out go together")
+    have_init = state_in is not None
+    n0, d0, m0 = s0
+    # cum[:, t] = sum_{j<t} w_j; the rates of steps lo .. hi-1 are cum[hi] - cum[lo]
+    cum = np.concatenate([np.zeros((B, 1, C)), np.cumsum(w, axis=1)], axis=1)
+
+    gw = np.zeros((B, T, C))
+    gu = np.zeros((B, C))
+    gk = np.zeros((B, T, C))
+    gv = np.zeros((B, T, C))
+    gn0 = np.zeros((B, C))
+    gd0 = np.zeros((B, C))
+    gm0 = np.zeros((B, C))
+
+    def to_rates(dx, upto):
+        """Terms 0 .. n-1 of past tokens i whose exponents hold the rates of
+        steps i+1 .. upto-1: rate j collects -dx_i from every token i < j,
+        i.e. minus the running sum of dx up to token j-1."""
+        if upto > 1:
+            gw[:, 1:upto] -= np.cumsum(dx, axis=1)[:, :upto - 1]
+
+    for t in range(T):
+        past = np.arange(t)
+        x_past = k[:, :t] - (cum[:, t][:, None] - cum[:, past + 1])   # steps i+1 .. t-1
+        x_cur = u + k[:, t]
+        x_init = m0 - cum[:, t]                                        # steps 0 .. t-1
+        top = np.maximum(x_cur, x_init)
+        if t > 0:
+            top = np.maximum(top, x_past.max(axis=1))
+        e_past = np.exp(x_past - top[:, None])
+        e_cur = np.exp(x_cur - top)
+        e_init = np.exp(x_init - top) if have_init else np.zeros((B, C))
+        den = e_past.sum(axis=1) + e_cur + e_init * d0
+        num = (e_past * v[:, :t]).sum(axis=1) + e_cur * v[:, t] + e_init * n0
+        y = num / den
+        gt = g[:, t]
+        r_past = e_past / den[:, None]
+        r_cur = e_cur / den
+        r_init = e_init / den
+
+        dx_past = gt[:, None] * r_past * (v[:, :t] - y[:, None])
+        gk[:, :t] += dx_past
+        gv[:, :t] += gt[:, None] * r_past
+        to_rates(dx_past, t)
+        dx_cur = gt * r_cur * (v[:, t] - y)
+        gk[:, t] += dx_cur
+        gv[:, t] += gt * r_cur
+        gu += dx_cur
+        if have_init:
+            dx_init = gt * r_init * (n0 - y * d0)
+            gm0 += dx_init
+            gw[:, :t] -= dx_init[:, None, :]
+            gn0 += gt * r_init
+            gd0 += -gt * y * r_init
+
+    if gstate_out is not None:
+        gn, gd = _f64(gstate_out)[0], _f64(gstate_out)[1]
+        m_out = _f64(state_out)[2]
+        idx = np.arange(T)
+        e_tok = np.exp(k - (cum[:, T][:, None] - cum[:, idx + 1]) - m_out[:, None])
+        gv += gn[:, None] * e_tok
+        dx_tok = e_tok * (gn[:, None] * v + gd[:, None])
+        gk += dx_tok
+        to_rates(dx_tok, T)
+        if have_init:
+            e0 = np.exp(m0 - cum[:, T] - m_out)
+            gn0 += gn * e0
+            gd0 += gd * e0
+            dx0 = e0 * (gn * n0 + gd * d0)
+            gm0 += dx0
+            gw -= dx0[:, None, :]
+
+    gstate_in = np.stack([gn0, gd0, gm0])
+    return gw, gu.sum(axis=0), gk, gv, gstate_in
