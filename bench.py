@@ -20,6 +20,8 @@ Default run (one JSON line on stdout):
   * per_token_decay: wkv_forward_dd (a decay rate per token and channel) on
     one layer of the prefill shape and on the decode workload's B=256 T=512
     prefill shape.
+  * per_token_decay_backward: wkv_backward_dd (the gradients, a rate per
+    token) on the same two shapes.
   * matrix_state: wkv_matrix_forward (a 64 x 64 state per head of 64
     channels) on the same two shapes.
   * backward: wkv_backward (the gradients) on one layer of the prefill shape
@@ -343,6 +345,53 @@ def time_ckpt_pair(wl, dev, reps=10):
             "unit": "G channel-tokens/s (forward + backward)",
             "roofline_forward_ckpt": roof(fbytes, us["forward_ckpt"]),
             "roofline_backward_ckpt": roof(bbytes, us["backward_ckpt"])}
+
+
+def time_dd_backward(wl, dev, reps=10):
+    """wkv_backward_dd (fp32) on workload wl's first layer with per-token
+    rates and a seeded upstream gradient: microseconds per call (event pair
+    around `reps` calls after two warm-up calls) and the roofline on its
+    algorithmic bytes (read w, k, v, dL/dout; write dL/dk, dL/dv, dL/dw; u in
+    and dL/du out)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    _, u = I.params(wl)
+    k, v = I.kv(wl)
+    g = I.grad_out(wl)
+    rates = I.decay_rates(wl)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    du, dk, dv, dg, dr = t(u), t(k), t(v), t(g), t(rates)
+    del k, v, g, rates
+    grads = (torch.empty_like(dk), torch.empty_like(dk), torch.empty_like(dk),
+             torch.empty_like(du), None)
+    ws = torch.empty(max(W.wkv_backward_dd_workspace_size(wl.B, wl.T, wl.C), 1),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: W.wkv_backward_dd(dr, du, dk, dv, dg, want_gstate_in=False, workspace=ws,
+                                     out=grads)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ct = wl.B * wl.T * wl.C
+    abytes = 28 * ct + 8 * wl.C
+    achieved = abytes / (us * 1e-6) / 1e9
+    return {"workload": f"{wl.name}, one layer, per-token decay backward", "B": wl.B, "T": wl.T,
+            "C": wl.C, "io": "f32",
+            "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
+            "us_per_call": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": abytes},
+            "workspace_bytes": int(ws.numel())}
 
 
 def time_gated(wl, dev, path, reps=50):
@@ -758,6 +807,11 @@ def main():
         for dwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
             _log(f"per-token decay forward: {dwl.name} (one layer)")
             rec["per_token_decay"].append(time_decay(dwl, dev))
+            torch.cuda.empty_cache()
+        rec["per_token_decay_backward"] = []
+        for dwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+            _log(f"per-token decay backward: {dwl.name} (one layer)")
+            rec["per_token_decay_backward"].append(time_dd_backward(dwl, dev))
             torch.cuda.empty_cache()
 
     if args.config == 1 and not args.no_backward:

@@ -290,6 +290,34 @@ int wkv_forward_dd(int64_t B, int64_t T, int64_t C, const void* w, const float* 
 int wkv_step_dd(int64_t B, int64_t C, const void* w, const float* u, const void* k,
                 const void* v, float* state, void* out, int io, hipStream_t stream);
 
+/* Gradients of the per-token-decay prefill (fp32): dL/dw for every rate,
+ * dL/du, dL/dk, dL/dv and dL/dstate_in from dL/dout and optionally
+ * dL/dstate_out. The derivatives are those of wkv_forward_dd's operator (the
+ * per-token decay of the page "RWKV-v6 Architecture: Attention-Free Linear
+ * Transformers", section "The Core Components of the RWKV-v6 Time-Mixing
+ * Block", on the wkv_t ratio of the page "Linear attention without writing
+ * a CUDA kernel", section "The recurrence"); a rate w[b][t][c] decays
+ * every earlier token's term in the outputs after step t.
+ *
+ *   w           [B][T][C] fp32 the forward's rates; u [C] its bonus.
+ *   k, v, gout  [B][T][C] fp32 keys, values and dL/dout.
+ *   state_in, state_out, gstate_out, gstate_in: as wkv_backward.
+ *   gk, gv, gw  [B][T][C] out: dL/dk, dL/dv, dL/dw.
+ *   gu          [C] out: dL/du summed over the batch.
+ *   workspace   wkv_backward_dd_workspace_size(B, T, C) bytes, 256-byte
+ *               aligned, owned by the caller, no clearing needed; calls that
+ *               may run concurrently must not share it.
+ * Sizes, errors and overlap rules as wkv_backward; deterministic. */
+int wkv_backward_dd(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                    const float* k, const float* v, const float* state_in, const float* state_out,
+                    const float* gstate_out, const float* gout, float* gk, float* gv, float* gw,
+                    float* gu, float* gstate_in, void* workspace, int64_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Bytes of workspace wkv_backward_dd needs for these sizes, or a negative
+ * wkv_status on error. */
+int64_t wkv_backward_dd_workspace_size(int64_t B, int64_t T, int64_t C);
+
 /* Matrix-valued-state recurrence (page "RWKV-v6 Architecture: Attention-Free
  * Linear Transformers", section "The Core Components of the RWKV-v6
  * Time-Mixing Block", item "Matrix-Valued Hidden State", and the step

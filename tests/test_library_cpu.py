@@ -215,6 +215,43 @@ def test_checkpoint_entry_points_validate_without_device():
     assert lib.wkv_backward_ckpt(*bwd, gk, *rest) == 4
 
 
+def test_decay_backward_entry_points_validate_without_device():
+    """wkv_backward_dd's host-side checks (they run before any device call):
+    sizes, missing pointers, alignment, overlaps and the workspace."""
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    B, T, C = 2, 100, 16  # few lanes, T >= 64: the segmented plan needs a workspace
+    need = lib.wkv_backward_dd_workspace_size(B, T, C)
+    assert need > 0
+    assert lib.wkv_backward_dd_workspace_size(-1, T, C) < 0
+    assert lib.wkv_backward_dd_workspace_size(B, T, 0) == 0
+    a = 0x10000000
+    seq = B * T * C * 4
+    w, k, v, g, gk, gv, gw = (P(a + i * seq) for i in range(7))
+    u, gu = P(a + 7 * seq), P(a + 7 * seq + 256)
+    ws = P(a + (1 << 24))
+    # B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw, gu, gstate_in,
+    # workspace, bytes, stream
+    base = [B, T, C, w, u, k, v, nul, nul, nul, g, gk, gv, gw, gu, nul]
+    bad = list(base)
+    bad[3] = nul                                                         # w missing
+    assert lib.wkv_backward_dd(*bad, ws, need, nul) == 1
+    bad = list(base)
+    bad[8] = P(a + (1 << 23))                                            # state_out without gradient
+    assert lib.wkv_backward_dd(*bad, ws, need, nul) == 1
+    bad = list(base)
+    bad[13] = P(a + 3 * seq + 2)                                         # gw misaligned
+    assert lib.wkv_backward_dd(*bad, ws, need, nul) == 3
+    bad = list(base)
+    bad[13] = k                                                          # gw on top of k
+    assert lib.wkv_backward_dd(*bad, ws, need, nul) == 4
+    assert lib.wkv_backward_dd(*base, ws, need - 8, nul) == 8            # workspace too small
+    assert lib.wkv_backward_dd(*base, nul, 0, nul) == 8
+    assert lib.wkv_backward_dd(*base, P(a + (1 << 24) + 8), need, nul) == 3  # not 256-aligned
+    assert lib.wkv_backward_dd(-1, T, C, *base[3:], ws, need, nul) == 2
+
+
 def test_per_token_decay_rates_are_seeded_and_positive():
     wl = I.WORKLOADS[1].scaled(B=3, T=50, C=32)
     r1 = I.decay_rates(wl)

@@ -52,6 +52,19 @@ def rms(v) -> float:
     return float(np.sqrt(np.mean(v * v))) if v.size else 1.0
 
 
+def assert_grad_close(got, ref, tol, what, scale=0.0):
+    """Elementwise |got - ref| / (|ref| + max(rms(ref), scale)) <= tol: a
+    relative error that falls back to the gradient's typical size (or that of
+    a companion gradient, `scale`) where an element itself is near zero."""
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite gradient"
+    err = np.abs(got - ref) / (np.abs(ref) + max(rms(ref), scale, 1e-30))
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max normalised error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
 def tol_for(io: str) -> float:
     return BF16_TOL if io == "bf16" else F32_TOL
 

@@ -10,6 +10,7 @@ into that interface (see _lib). Build the library with
     y = wkv_step(w, u, k_t, v_t, state)             # decode, state in place
     gw, gu, gk, gv, gs = wkv_backward(w, u, k, v, gout)  # gradients
     out, state = wkv_forward_dd(w_t, u, k, v)     # per-token decay w_t (B, T, C)
+    gw_t, gu, gk, gv, gs = wkv_backward_dd(w_t, u, k, v, gout)  # its gradients
     y, S = wkv_matrix_forward(w_t, k, v, r, H)     # matrix-valued state per head
 """
 
@@ -31,6 +32,8 @@ from ._lib import (  # noqa: F401
     step,
     wkv_abi_version,
     wkv_backward,
+    wkv_backward_dd,
+    wkv_backward_dd_workspace_size,
     wkv_forward_ckpt,
     wkv_ckpt_bytes,
     ckpt_shape,

@@ -74,6 +74,8 @@ def load_library() -> ctypes.CDLL:
         "wkv_matrix_workspace_size": [i64, i64, i64, i64],
         "wkv_matrix_step": [i64, i64, i64] + [vp] * 6 + [vp],
         "wkv_ckpt_bytes": [i64, i64, i64],
+        "wkv_backward_dd": [i64, i64, i64] + [vp] * 13 + [vp, i64, vp],
+        "wkv_backward_dd_workspace_size": [i64, i64, i64],
         "wkv_forward_ckpt": [i64, i64, i64] + [vp] * 9 + [ci, vp],
         "wkv_backward_ckpt": [i64, i64, i64] + [vp] * 16 + [vp, i64, vp],
     }
@@ -84,6 +86,7 @@ def load_library() -> ctypes.CDLL:
                       "wkv_workspace_size": ctypes.c_int64,
                       "wkv_backward_workspace_size": ctypes.c_int64,
                       "wkv_ckpt_bytes": ctypes.c_int64,
+                      "wkv_backward_dd_workspace_size": ctypes.c_int64,
                       "wkv_matrix_workspace_size": ctypes.c_int64}.get(name, ctypes.c_int)
     if lib.wkv_abi_version() != 1:
         raise RuntimeError(f"{LIBRARY_PATH}: unexpected ABI version {lib.wkv_abi_version()}")
@@ -509,6 +512,62 @@ def wkv_step_gated(w, u, k, v, r, state, out=None, stream=None):
                                 _ptr(out), io, _stream_handle(dev, stream))
     _check(st, "wkv_step_gated")
     return out
+
+
+def wkv_backward_dd_workspace_size(B: int, T: int, C: int) -> int:
+    """Bytes of workspace wkv_backward_dd needs."""
+    r = load_library().wkv_backward_dd_workspace_size(B, T, C)
+    if r < 0:
+        raise WKVError("wkv_backward_dd_workspace_size", -r)
+    return int(r)
+
+
+def wkv_backward_dd(w, u, k, v, gout, state_in=None, state_out=None, gstate_out=None, *,
+                    want_gstate_in=True, workspace=None, out=None, stream=None):
+    """Gradients of the per-token-decay prefill (float32): returns
+    (gw, gu, gk, gv, gstate_in) with gw shaped like w (B, T, C), gu (C,)
+    summed over the batch, gstate_in None when want_gstate_in is False.
+    `out` may hold preallocated (gk, gv, gw, gu, gstate_in) tensors;
+    `workspace` a uint8 tensor of at least wkv_backward_dd_workspace_size
+    bytes (else one is allocated for the call)."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    f32 = torch.float32
+    for name, t in (("w", w), ("k", k), ("v", v), ("gout", gout)):
+        _need(t, name, f32, (B, T, C), dev)
+    _need(u, "u", f32, (C,), dev)
+    for name, t in (("state_in", state_in), ("state_out", state_out), ("gstate_out", gstate_out)):
+        if t is not None:
+            _need(t, name, f32, (3, B, C), dev)
+    if out is None:
+        gk, gv, gw = (torch.empty((B, T, C), dtype=f32, device=dev) for _ in range(3))
+        gu = torch.empty((C,), dtype=f32, device=dev)
+        gs = torch.empty((3, B, C), dtype=f32, device=dev) if want_gstate_in else None
+    else:
+        gk, gv, gw, gu, gs = out
+    for name, t, shape in (("gk", gk, (B, T, C)), ("gv", gv, (B, T, C)), ("gw", gw, (B, T, C)),
+                           ("gu", gu, (C,))):
+        _need(t, name, f32, shape, dev)
+    if gs is not None:
+        _need(gs, "gstate_in", f32, (3, B, C), dev)
+    with torch.cuda.device(dev):
+        strm = torch.cuda.current_stream(dev) if stream is None else stream
+        nbytes = wkv_backward_dd_workspace_size(B, T, C)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
+        st = lib.wkv_backward_dd(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                                 _ptr(state_out), _ptr(gstate_out), _ptr(gout), _ptr(gk),
+                                 _ptr(gv), _ptr(gw), _ptr(gu), _ptr(gs), _ptr(workspace),
+                                 workspace.numel(), ctypes.c_void_p(strm.cuda_stream))
+    _check(st, "wkv_backward_dd")
+    return gw, gu, gk, gv, gs
 
 
 def wkv_forward_dd(w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",

@@ -25,14 +25,15 @@ LIB = os.path.join(PKG, "libwkv.so")
 
 ARCH = "gfx950"
 SOURCES = ["wkv_api.cpp", "wkv_seq.hip", "wkv_chunk.hip", "wkv_lookback.hip", "wkv_step.hip",
-           "wkv_backward.hip", "wkv_decay.hip", "wkv_matrix.hip"]
+           "wkv_backward.hip", "wkv_decay.hip", "wkv_decay_backward.hip", "wkv_matrix.hip"]
 EXPORTS = [
     "wkv_forward", "wkv_forward_bf16", "wkv_forward_ex", "wkv_forward_ws", "wkv_workspace_size",
     "wkv_select_path",
     "wkv_step", "wkv_step_bf16", "wkv_status_string", "wkv_last_hip_error",
     "wkv_abi_version", "wkv_backward", "wkv_backward_workspace_size", "wkv_backward_ckpt",
     "wkv_ckpt_bytes", "wkv_forward_ckpt", "wkv_forward_gated",
-    "wkv_step_gated", "wkv_forward_dd", "wkv_step_dd",
+    "wkv_step_gated", "wkv_forward_dd", "wkv_step_dd", "wkv_backward_dd",
+    "wkv_backward_dd_workspace_size",
     "wkv_matrix_forward", "wkv_matrix_workspace_size", "wkv_matrix_step",
 ]
 

@@ -457,6 +457,68 @@ int backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* 
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
 
+// Backward of the per-token-decay operator (fp32; gw shaped like k).
+int backward_dd_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                     const float* k, const float* v, const float* state_in,
+                     const float* state_out, const float* gstate_out, const float* gout,
+                     float* gk, float* gv, float* gw, float* gu, float* gstate_in,
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+  int64_t seq_bytes, state_bytes;
+  if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, 4, &seq_bytes) ||
+      seq_bytes > kMaxBytes)
+    return WKV_ERR_DIM;
+  if (!mul3(B, C, 12, &state_bytes) || state_bytes > kMaxBytes) return WKV_ERR_DIM;
+  if (C == 0) return WKV_OK;
+  const int64_t need = wkv::dd_backward_workspace_bytes(B, T, C);
+  if (need < 0 || need > kMaxBytes) return WKV_ERR_DIM;
+
+  if (u == nullptr || gu == nullptr) return WKV_ERR_NULL;
+  const bool tokens = B > 0 && T > 0;
+  if (tokens && (w == nullptr || k == nullptr || v == nullptr || gout == nullptr ||
+                 gk == nullptr || gv == nullptr || gw == nullptr))
+    return WKV_ERR_NULL;
+  if ((gstate_out == nullptr) != (state_out == nullptr)) return WKV_ERR_NULL;
+  const void* all[] = {w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw, gu,
+                       gstate_in};
+  for (const void* p : all)
+    if (misaligned(p, 4)) return WKV_ERR_ALIGN;
+
+  const int64_t pbytes = C * 4;
+  const int64_t sbytes = tokens ? seq_bytes : 0;
+  struct Range {
+    const void* p;
+    int64_t n;
+  };
+  const Range inputs[] = {{w, sbytes},        {u, pbytes},          {k, sbytes},
+                          {v, sbytes},        {gout, sbytes},       {state_in, state_bytes},
+                          {state_out, state_bytes}, {gstate_out, state_bytes}};
+  const Range outputs[] = {{gk, sbytes}, {gv, sbytes}, {gw, sbytes}, {gu, pbytes},
+                           {gstate_in, state_bytes}};
+  for (int i = 0; i < 5; ++i) {
+    for (const Range& r : inputs)
+      if (overlaps(outputs[i].p, outputs[i].n, r.p, r.n)) return WKV_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outputs[i].p, outputs[i].n, outputs[j].p, outputs[j].n)) return WKV_ERR_ALIAS;
+  }
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return WKV_ERR_WORKSPACE;
+    if (misaligned(workspace, 256)) return WKV_ERR_ALIGN;
+    for (const Range& r : inputs)
+      if (overlaps(workspace, workspace_bytes, r.p, r.n)) return WKV_ERR_ALIAS;
+    for (const Range& r : outputs)
+      if (overlaps(workspace, workspace_bytes, r.p, r.n)) return WKV_ERR_ALIAS;
+  }
+
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  const wkv::DdBwdArgs a{B, T, C, w, u, k, v, gout, state_in, state_out, gstate_out,
+                         gk, gv, gw, gu, gstate_in};
+  e = wkv::launch_dd_backward(a, workspace, stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -502,6 +564,24 @@ int64_t wkv_backward_workspace_size(int64_t B, int64_t T, int64_t C) {
   if (!mul3(B, T, C, &cells) || cells > kMaxBytes) return -WKV_ERR_DIM;
   if (C == 0) return 0;
   const int64_t n = wkv::backward_workspace_bytes(B, T, C);
+  return n < 0 || n > kMaxBytes ? -WKV_ERR_DIM : n;
+}
+
+int wkv_backward_dd(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                    const float* k, const float* v, const float* state_in, const float* state_out,
+                    const float* gstate_out, const float* gout, float* gk, float* gv, float* gw,
+                    float* gu, float* gstate_in, void* workspace, int64_t workspace_bytes,
+                    hipStream_t stream) {
+  return backward_dd_impl(B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw,
+                          gu, gstate_in, workspace, workspace_bytes, stream);
+}
+
+int64_t wkv_backward_dd_workspace_size(int64_t B, int64_t T, int64_t C) {
+  if (B < 0 || T < 0 || C < 0) return -WKV_ERR_DIM;
+  int64_t cells;
+  if (!mul3(B, T, C, &cells) || cells > kMaxBytes) return -WKV_ERR_DIM;
+  if (C == 0) return 0;
+  const int64_t n = wkv::dd_backward_workspace_bytes(B, T, C);
   return n < 0 || n > kMaxBytes ? -WKV_ERR_DIM : n;
 }
 

@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kRedCh * kRedSlices) void wkv_grad_reduce_kernel(
 #pragma unroll
       for (int m = 0; m < kRedBatch; ++m) {
         const int64_t b = b0 + m * kRedSlices;
-        xw[m] = b < B ? gw_part[b * C + c] : 0.0f;
+        xw[m] = b < B && gw_part != nullptr ? gw_part[b * C + c] : 0.0f;
         xu[m] = b < B ? gu_part[b * C + c] : 0.0f;
       }
 #pragma unroll
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(kRedCh * kRedSlices) void wkv_grad_reduce_kernel(
       tw += sw[i][ch];
       tu += su[i][ch];
     }
-    gw[c] = tw;
+    if (gw != nullptr) gw[c] = tw;
     gu[c] = tu;
   }
 }
@@ -854,6 +854,22 @@ WsLayout ws_layout(int64_t B, int64_t T, int64_t C) {
 }
 
 }  // namespace
+
+int64_t backward_segments(int64_t lanes, int64_t T, int64_t* seg_chunks) {
+  const SegPlan p = seg_plan(lanes, T);
+  *seg_chunks = p.seg_chunks;
+  return p.segments;
+}
+
+hipError_t launch_grad_reduce(int64_t rows, int64_t C, const float* gw_part, const float* gu_part,
+                              float* gw, float* gu, hipStream_t st) {
+  const int64_t rblocks = (C + kRedCh - 1) / kRedCh;
+  if (rblocks == 0) return hipSuccess;
+  if (rblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(wkv_grad_reduce_kernel, dim3(static_cast<unsigned>(rblocks)),
+                     dim3(kRedCh * kRedSlices), 0, st, rows, C, gw_part, gu_part, gw, gu);
+  return hipGetLastError();
+}
 
 int64_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C) {
   return B * C > 0 ? ws_layout(B, T, C).total : 0;

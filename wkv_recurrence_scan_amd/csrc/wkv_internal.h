@@ -80,6 +80,35 @@ struct BwdArgs {
 int64_t backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
 hipError_t launch_backward(const BwdArgs& a, void* ws, hipStream_t s);
 
+// Segments per lane of the backward passes for B*C lanes and T tokens (1: one
+// thread per lane) and the checkpoint chunks per segment.
+int64_t backward_segments(int64_t lanes, int64_t T, int64_t* seg_chunks);
+// dL/du (and dL/dw when gw is not null) added over `rows` rows of C per-lane
+// partial sums, in a fixed order; zero rows give zeros.
+hipError_t launch_grad_reduce(int64_t rows, int64_t C, const float* gw_part, const float* gu_part,
+                              float* gw, float* gu, hipStream_t s);
+
+// Backward pass of the per-token-decay operator (fp32): w, k, v, gout, gk, gv
+// and gw are [B][T][C]; gu is [C], summed over the batch.
+struct DdBwdArgs {
+  int64_t B, T, C;
+  const float* w;
+  const float* u;
+  const float* k;
+  const float* v;
+  const float* gout;
+  const float* state_in;    // nullptr: empty initial state
+  const float* state_out;   // with gstate_out: the forward's final state
+  const float* gstate_out;  // nullptr: no gradient on the final state
+  float* gk;
+  float* gv;
+  float* gw;
+  float* gu;
+  float* gstate_in;         // nullptr: not wanted
+};
+int64_t dd_backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
+hipError_t launch_dd_backward(const DdBwdArgs& a, void* ws, hipStream_t s);
+
 // Per-token (data-dependent) decay: w has k's layout and element type.
 struct DdArgs {
   int64_t B, T, C;
