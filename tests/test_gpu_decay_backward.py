@@ -136,3 +136,42 @@ def test_dd_backward_constant_rate_equals_constant_decay_backward():
     assert_grad_close(gw_sum, host64(b[0]), GRAD_TOL, "gw", rms(host64(b[1])))
     for i, name in ((1, "gu"), (2, "gk"), (3, "gv")):
         assert_grad_close(host64(a[i]), host64(b[i]), GRAD_TOL, name)
+
+
+def test_dd_backward_deterministic_and_in_hip_graph():
+    """Two eager calls agree bit for bit (fixed summation orders), and a call
+    captured in a HIP graph reproduces them on every replay, with the outputs
+    cleared and unrelated eager work in between; the segmented plan (B=8
+    T=1024 C=768) and the one-thread-per-lane plan (B=90 T=40 C=768)."""
+    for B, T, C in ((8, 1024, 768), (90, 40, 768)):
+        say(f"dd backward determinism and graph B={B} T={T} C={C}")
+        wt, u, k, v, g = (dev_f32(a) for a in dd_case(WL0, B, T, C))
+        s0 = dev_f32(random_state(B, C, 15))
+        outs = (torch.empty_like(k), torch.empty_like(k), torch.empty_like(k),
+                torch.empty_like(u), torch.empty((3, B, C), device="cuda"))
+        ws = torch.empty(max(W.wkv_backward_dd_workspace_size(B, T, C), 1), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            W.wkv_backward_dd(wt, u, k, v, g, s0, workspace=ws, out=outs)
+
+        run()
+        torch.cuda.synchronize()
+        first = [t.clone() for t in outs]
+        run()
+        torch.cuda.synchronize()
+        bits = lambda t: t.view(torch.int32)
+        for got, ref in zip(outs, first):
+            assert torch.equal(bits(got), bits(ref)), "eager rerun"
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        for rep in range(3):
+            for t in outs:
+                t.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for got, ref in zip(outs, first):
+                assert torch.equal(bits(got), bits(ref)), f"replay {rep}"
+            _ = W.wkv_backward_dd(wt, u, k, v, g)  # unrelated eager work

@@ -43,6 +43,8 @@
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
+#include <type_traits>
+
 namespace wkv {
 namespace {
 
@@ -128,12 +130,12 @@ struct DbChunk {
   float k[kDbLc], v[kDbLc], w[kDbLc], g[G ? kDbLc : 1];
 };
 
-template <bool G>
+template <bool G, bool MASKED>
 __device__ __forceinline__ void db_load(DbChunk<G>& c, const DdBwdKernelArgs& a, int64_t o,
                                         int n) {
 #pragma unroll
   for (int i = 0; i < kDbLc; ++i) {
-    if (i < n) {
+    if (!MASKED || i < n) {
       c.k[i] = __builtin_nontemporal_load(a.k + o + i * a.C);
       c.v[i] = __builtin_nontemporal_load(a.v + o + i * a.C);
       c.w[i] = __builtin_nontemporal_load(a.w + o + i * a.C);
@@ -169,11 +171,13 @@ __device__ __forceinline__ int chunk_tokens(const DdBwdKernelArgs& a, int64_t j)
   return left >= kDbLc ? kDbLc : static_cast<int>(left);
 }
 
-// Calls body(chunk, j, tokens) for the thread's chunks j0 .. j1-1 in order
-// (REV: last first), with two register buffers: the next chunk's loads are
-// issued before the current one is processed. They are issued on every path
-// (past the end the last chunk re-reads itself), so the compiler's counter
-// waits stop at the chunk about to be used.
+// Calls body(chunk, j, tokens, full) for the thread's chunks j0 .. j1-1 in
+// order (REV: last first), with two register buffers: the next chunk's loads
+// are issued before the current one is processed. They are issued on every
+// path (past the end the last chunk re-reads itself), so the compiler's
+// counter waits stop at the chunk about to be used. `full` is a compile-time
+// flag: only the sequence's last chunk can be partial, and only its code
+// tests each token.
 template <bool G, bool REV, typename F>
 __device__ __forceinline__ void db_walk(const DdBwdKernelArgs& a, const DbThread& th, F&& body) {
   const int64_t n = th.j1 - th.j0;
@@ -181,16 +185,29 @@ __device__ __forceinline__ void db_walk(const DdBwdKernelArgs& a, const DbThread
   auto chunk = [&](int64_t q) { return REV ? th.j1 - 1 - q : th.j0 + q; };
   auto load = [&](DbChunk<G>& c, int64_t q) {
     const int64_t j = chunk(q < n ? q : n - 1);
-    db_load<G>(c, a, th.row + j * kDbLc * a.C, chunk_tokens(a, j));
+    const int nt = chunk_tokens(a, j);
+    if (nt == kDbLc) {
+      db_load<G, false>(c, a, th.row + j * kDbLc * a.C, nt);
+    } else {
+      db_load<G, true>(c, a, th.row + j * kDbLc * a.C, nt);
+    }
+  };
+  auto run = [&](const DbChunk<G>& c, int64_t j) {
+    const int nt = chunk_tokens(a, j);
+    if (nt == kDbLc) {
+      body(c, j, nt, std::true_type{});
+    } else {
+      body(c, j, nt, std::false_type{});
+    }
   };
   DbChunk<G> A, Bf;
   load(A, 0);
   for (int64_t q = 0; q < n; q += 2) {
     load(Bf, q + 1);
-    body(A, chunk(q), chunk_tokens(a, chunk(q)));
+    run(A, chunk(q));
     if (q + 1 >= n) break;
     load(A, q + 2);
-    body(Bf, chunk(q + 1), chunk_tokens(a, chunk(q + 1)));
+    run(Bf, chunk(q + 1));
   }
 }
 
@@ -200,10 +217,10 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_forward_kernel(DdBw
   if (!db_thread(a, th)) return;
   LaneD x = laned_empty();
   double ws = 0.0;
-  db_walk<false, false>(a, th, [&](const DbChunk<false>& ch, int64_t, int n) {
+  db_walk<false, false>(a, th, [&](const DbChunk<false>& ch, int64_t, int n, auto full) {
 #pragma unroll
     for (int i = 0; i < kDbLc; ++i) {
-      if (i < n) {
+      if (decltype(full)::value || i < n) {
         laned_advance(x, ch.k[i], ch.v[i], ch.w[i]);
         ws += static_cast<double>(ch.w[i]);
       }
@@ -235,11 +252,11 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_sums_kernel(DdBwdKe
   }
   float p = 0.0f, q = 0.0f;
   double zl = kEmptyD, cw = 0.0;
-  db_walk<OWN, false>(a, th, [&](const DbChunk<OWN>& ch, int64_t j, int n) {
+  db_walk<OWN, false>(a, th, [&](const DbChunk<OWN>& ch, int64_t j, int n, auto full) {
     a.ckpt[j * th.lanes + th.lane] = CkD{x.n, x.d, x.m};
 #pragma unroll
     for (int i = 0; i < kDbLc; ++i) {
-      if (i < n) {
+      if (decltype(full)::value || i < n) {
         if constexpr (OWN) {
           double M;
           float rho, om;
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_backward_kernel(DdB
     acc.z = xw ? a.own_z[at] : zd;
   }
   float gu_acc = 0.0f;
-  db_walk<true, true>(a, th, [&](const DbChunk<true>& ch, int64_t j, int n) {
+  db_walk<true, true>(a, th, [&](const DbChunk<true>& ch, int64_t j, int n, auto full) {
     const int64_t o = th.row + j * kDbLc * a.C;
     const CkD cp = a.ckpt[j * th.lanes + th.lane];
     LaneD st{cp.n, cp.d, cp.m};
@@ -300,7 +317,7 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_backward_kernel(DdB
     double M[kDbLc], pm[kDbLc];
 #pragma unroll
     for (int i = 0; i < kDbLc; ++i) {
-      if (i < n) {
+      if (decltype(full)::value || i < n) {
         pn[i] = st.n;
         pd[i] = st.d;
         pm[i] = st.m;
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_backward_kernel(DdB
     }
 #pragma unroll
     for (int i = kDbLc - 1; i >= 0; --i) {
-      if (i < n) {
+      if (decltype(full)::value || i < n) {
         // token i from the sums over t > i
         const float e_cur = ch.g[i] * om[i];
         const float ex = exp_d(static_cast<double>(ch.k[i]) + acc.z);  // e^(k_i + z)
