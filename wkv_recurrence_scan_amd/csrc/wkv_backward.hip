@@ -45,6 +45,8 @@
 #include "wkv_internal.h"
 #include "wkv_tile.h"
 
+#include <type_traits>
+
 namespace wkv {
 namespace {
 
@@ -524,20 +526,12 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   // relative to the largest exponent -M_t - j w seen so far
   float p = 0.0f, q = 0.0f, r = 0.0f, rq = 0.0f, zl = kEmpty;
   float jj = 0.0f;
-  for (int64_t j = j0; j < j1; ++j) {
-    if constexpr (!GIVEN) a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
-    const int n = j < io.nfull ? kLc : io.rest;
-    Chunk<G> ch;
-    const int64_t off = io.row + j * io.step;
-    const float* rp = G ? io.r + off : io.r;
-    if (n == kLc) {
-      load_chunk<false, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, kLc);
-    } else {
-      load_chunk<true, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, n);
-    }
+  // chunks with their loads double-buffered; only a partial last chunk is
+  // compiled with a test per token
+  auto process = [&](const Chunk<G>& ch, int n, auto full) {
 #pragma unroll
     for (int i = 0; i < kLc; ++i) {
-      if (i < n) {
+      if (decltype(full)::value || i < n) {
         float M, rho, om;
         const float y = lane_step_rec(x, ch.k[i], ch.v[i], wc, uc, M, rho, om);
         const float xe = __builtin_fmaf(-jj, wc, -M);  // exponent of a_t e^{-j w}
@@ -553,6 +547,37 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
         zl = nw ? xe : zl;
         jj += 1.0f;
       }
+    }
+  };
+  auto load = [&](Chunk<G>& ch, int64_t j) {
+    const int n = j < io.nfull ? kLc : io.rest;
+    const int64_t off = io.row + j * io.step;
+    const float* rp = G ? io.r + off : io.r;
+    if (n == kLc) {
+      load_chunk<false, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, kLc);
+    } else {
+      load_chunk<true, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, n);
+    }
+  };
+  auto run = [&](const Chunk<G>& ch, int64_t j) {
+    if constexpr (!GIVEN) a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
+    const int n = j < io.nfull ? kLc : io.rest;
+    if (n == kLc) {
+      process(ch, n, std::true_type{});
+    } else {
+      process(ch, n, std::false_type{});
+    }
+  };
+  if (j0 < j1) {
+    // the last chunk re-reads itself, so the loads are unconditional
+    Chunk<G> A, Bf;
+    load(A, j0);
+    for (int64_t j = j0; j < j1; j += 2) {
+      load(Bf, j + 1 < j1 ? j + 1 : j);
+      run(A, j);
+      if (j + 1 >= j1) break;
+      load(A, j + 2 < j1 ? j + 2 : j + 1);
+      run(Bf, j + 1);
     }
   }
   a.seg_rev[s * lanes + lane] = make_float4(p, q, r, rq);
