@@ -21,7 +21,8 @@ Default run (one JSON line on stdout):
     one layer of the prefill shape and on the decode workload's B=256 T=512
     prefill shape.
   * per_token_decay_backward: wkv_backward_dd (the gradients, a rate per
-    token) on the same two shapes.
+    token) on the same two shapes, and the training pair with and without
+    the checkpoints wkv_forward_dd_ckpt saves.
   * matrix_state: wkv_matrix_forward (a 64 x 64 state per head of 64
     channels) on the same two shapes.
   * backward: wkv_backward (the gradients) on one layer of the prefill shape
@@ -381,6 +382,28 @@ def time_dd_backward(wl, dev, reps=10):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
+    # the training pair both ways: the plain prefill then this backward,
+    # against the prefill that saves checkpoints then the backward from them
+    out, st = torch.empty_like(dk), torch.empty((3, wl.B, wl.C), device=dev)
+    ck = torch.empty(W.ckpt_shape(wl.B, wl.T, wl.C), device=dev)
+    pair = {
+        "forward": lambda: W.wkv_forward_dd(dr, du, dk, dv, out=out, state_out=st),
+        "forward_ckpt": lambda: W.wkv_forward_dd_ckpt(dr, du, dk, dv, out=out, state_out=st,
+                                                      ckpt=ck),
+        "backward_ckpt": lambda: W.wkv_backward_dd(dr, du, dk, dv, dg, want_gstate_in=False,
+                                                   workspace=ws, out=grads, ckpt=ck),
+    }
+    pus = {"backward": us}
+    for name, fn in pair.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pus[name] = e0.elapsed_time(e1) * 1e3 / reps
     ct = wl.B * wl.T * wl.C
     abytes = 28 * ct + 8 * wl.C
     achieved = abytes / (us * 1e-6) / 1e9
@@ -391,7 +414,14 @@ def time_dd_backward(wl, dev, reps=10):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes_per_launch": abytes},
-            "workspace_bytes": int(ws.numel())}
+            "workspace_bytes": int(ws.numel()),
+            "with_checkpoints": {
+                "us_per_call": {k_: round(x, 2) for k_, x in pus.items()},
+                "pair_value": round(ct / ((pus["forward_ckpt"] + pus["backward_ckpt"]) * 1e-6)
+                                    / 1e9, 3),
+                "plain_pair_value": round(ct / ((pus["forward"] + pus["backward"]) * 1e-6) / 1e9,
+                                          3),
+                "unit": "G channel-tokens/s (forward + backward)"}}
 
 
 def time_gated(wl, dev, path, reps=50):

@@ -318,6 +318,32 @@ int wkv_backward_dd(int64_t B, int64_t T, int64_t C, const float* w, const float
  * wkv_status on error. */
 int64_t wkv_backward_dd_workspace_size(int64_t B, int64_t T, int64_t C);
 
+/* Training pair for the per-token-decay prefill (fp32), as wkv_forward_ckpt /
+ * wkv_backward_ckpt for the constant decay: the forward saves the state in
+ * front of every chunk of 8 tokens, and the backward starts from those
+ * states instead of re-running the forward to rebuild them.
+ *
+ * wkv_forward_dd_ckpt: as wkv_forward_dd (fp32 only) with
+ *   ckpt   out: [ceil(T / 8)][B][C] records of 16 bytes (float num, float
+ *          den, double max_exp), the lane state in front of token 8j at
+ *          [j][b][c]; wkv_ckpt_bytes(B, T, C) bytes, 16-byte aligned, owned
+ *          by the caller; must not overlap any other argument. Required when
+ *          B, T, C > 0 (WKV_ERR_NULL). The outputs equal those of
+ *          wkv_forward_dd on the same path bit for bit.
+ * wkv_backward_dd_ckpt: as wkv_backward_dd with ckpt, what
+ *   wkv_forward_dd_ckpt wrote for the same w, u, k, v and state_in (other
+ *   checkpoints give wrong gradients; this is not detected); read only. The
+ *   workspace is as for wkv_backward_dd. */
+int wkv_forward_dd_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                        const float* k, const float* v, const float* state_in, float* out,
+                        float* state_out, void* ckpt, int path, hipStream_t stream);
+int wkv_backward_dd_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                         const float* k, const float* v, const float* state_in,
+                         const float* state_out, const float* gstate_out, const float* gout,
+                         const void* ckpt, float* gk, float* gv, float* gw, float* gu,
+                         float* gstate_in, void* workspace, int64_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Matrix-valued-state recurrence (page "RWKV-v6 Architecture: Attention-Free
  * Linear Transformers", section "The Core Components of the RWKV-v6
  * Time-Mixing Block", item "Matrix-Valued Hidden State", and the step

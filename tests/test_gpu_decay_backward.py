@@ -14,7 +14,8 @@ import pytest
 import torch
 
 from oracle import wkv_dd_backward_direct, wkv_dd_recurrent
-from wkvtest import (I, W, assert_grad_close, dev_f32, host64, make_case, random_state, rms,
+from wkvtest import (I, W, assert_grad_close, assert_state_close, dev_f32, host64, make_case,
+                     random_state, rms,
                      say)
 
 pytestmark = pytest.mark.gpu
@@ -175,3 +176,89 @@ def test_dd_backward_deterministic_and_in_hip_graph():
             for got, ref in zip(outs, first):
                 assert torch.equal(bits(got), bits(ref)), f"replay {rep}"
             _ = W.wkv_backward_dd(wt, u, k, v, g)  # unrelated eager work
+
+
+# ---------------------------------------------------------------- checkpoints
+
+CK_SHAPES = [(1, 1, 8), (2, 7, 33), (2, 63, 24), (1, 257, 32), (2, 300, 40), (1, 2100, 16)]
+
+
+def ck_records(ck):
+    """(num, den, max_exp) planes of wkv_forward_dd_ckpt's 16-byte records:
+    two float32 values, then a float64."""
+    ck = ck.contiguous()
+    nd = host64(ck[..., :2])
+    m = ck.view(torch.float64)[..., 1].double().cpu().numpy()
+    return nd[..., 0], nd[..., 1], m
+
+
+@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("B,T,C", CK_SHAPES)
+def test_dd_forward_ckpt_outputs_equal_plain_forward(B, T, C, path):
+    say(f"dd forward_ckpt vs forward path={path} B={B} T={T} C={C}")
+    wt, u, k, v, _ = (dev_f32(a) for a in dd_case(WL3, B, T, C))
+    s0 = dev_f32(random_state(B, C, 16))
+    out, st, ck = W.wkv_forward_dd_ckpt(wt, u, k, v, s0, path=path)
+    ref, rst = W.wkv_forward_dd(wt, u, k, v, s0, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(st.view(torch.int32), rst.view(torch.int32))
+
+
+@pytest.mark.parametrize("path", ["seq", "chunk"])
+def test_dd_checkpoints_are_the_forward_states(path):
+    """Record j holds the state in front of token 8j: the oracle's state after
+    the first 8j tokens (the initial state for j = 0)."""
+    B, T, C = 2, 150, 40
+    say(f"dd checkpoints vs oracle states path={path}")
+    wt, u, k, v, _ = dd_case(WL0, B, T, C)
+    s0 = random_state(B, C, 17)
+    _, _, ck = W.wkv_forward_dd_ckpt(dev_f32(wt), dev_f32(u), dev_f32(k), dev_f32(v),
+                                     dev_f32(s0), path=path)
+    torch.cuda.synchronize()
+    n, d, m = ck_records(ck)
+    for j in range(n.shape[0]):
+        t = 8 * j
+        if t == 0:
+            ref = s0.astype(np.float64)
+        else:
+            _, ref = wkv_dd_recurrent(wt[:, :t], u, k[:, :t], v[:, :t], s0)
+        assert_state_close(np.stack([n[j], d[j], m[j]]), ref, 1e-5, f"checkpoint {j}")
+
+
+@pytest.mark.parametrize("B,T,C", [(2, 45, 24), (2, 150, 24), (1, 300, 32), (2, 777, 16)])
+def test_dd_backward_ckpt_matches_oracle(B, T, C):
+    say(f"dd backward_ckpt B={B} T={T} C={C}")
+    wt, u, k, v, g = dd_case(WL3, B, T, C, 3)
+    s0 = random_state(B, C, 18)
+    dev = lambda a: None if a is None else dev_f32(a)
+    _, st, ck = W.wkv_forward_dd_ckpt(dev(wt), dev(u), dev(k), dev(v), dev(s0))
+    st_out = host64(st)
+    gen = np.random.default_rng([63, T])
+    gs_out = np.stack([gen.normal(0, 1, (B, C)), gen.normal(0, 1, (B, C)), np.zeros((B, C))])
+    got = W.wkv_backward_dd(dev(wt), dev(u), dev(k), dev(v), dev(g), dev(s0), st,
+                            dev(gs_out), ckpt=ck)
+    torch.cuda.synchronize()
+    got = [host64(x) for x in got]
+    ref = wkv_dd_backward_direct(wt, u, k, v, g, s0, gs_out, st_out)
+    for i, name in enumerate(("gw", "gu", "gk", "gv", "gstate_in")):
+        scale = rms(ref[3]) if name in ("gk", "gw") else 0.0
+        assert_grad_close(got[i], ref[i], GRAD_TOL, name, scale)
+
+
+@pytest.mark.parametrize("B,T,C", [(8, 1024, 768), (90, 100, 768)])
+def test_dd_backward_ckpt_agrees_with_plain_backward(B, T, C):
+    """The 8-layer model's layer (segmented plan) and B*C >= 2^16 (one thread
+    per lane): gradients from the forward's checkpoints against those of the
+    backward that rebuilds its own, to the oracle tolerance."""
+    say(f"dd backward_ckpt vs backward B={B} T={T} C={C}")
+    wt, u, k, v, g = (dev_f32(a) for a in dd_case(WL0, B, T, C))
+    _, _, ck = W.wkv_forward_dd_ckpt(wt, u, k, v)
+    a = W.wkv_backward_dd(wt, u, k, v, g, ckpt=ck)
+    b = W.wkv_backward_dd(wt, u, k, v, g)
+    torch.cuda.synchronize()
+    a = [host64(x) for x in a[:4]]
+    b = [host64(x) for x in b[:4]]
+    for i, name in enumerate(("gw", "gu", "gk", "gv")):
+        scale = rms(b[3]) if name in ("gk", "gw") else 0.0
+        assert_grad_close(a[i], b[i], GRAD_TOL, name, scale)

@@ -42,6 +42,7 @@ from ._lib import (  # noqa: F401
     wkv_forward,
     wkv_forward_bf16,
     wkv_forward_dd,
+    wkv_forward_dd_ckpt,
     wkv_forward_ex,
     wkv_forward_gated,
     wkv_forward_ws,

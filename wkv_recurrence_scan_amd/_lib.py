@@ -76,6 +76,8 @@ def load_library() -> ctypes.CDLL:
         "wkv_ckpt_bytes": [i64, i64, i64],
         "wkv_backward_dd": [i64, i64, i64] + [vp] * 13 + [vp, i64, vp],
         "wkv_backward_dd_workspace_size": [i64, i64, i64],
+        "wkv_forward_dd_ckpt": [i64, i64, i64] + [vp] * 8 + [ci, vp],
+        "wkv_backward_dd_ckpt": [i64, i64, i64] + [vp] * 14 + [vp, i64, vp],
         "wkv_forward_ckpt": [i64, i64, i64] + [vp] * 9 + [ci, vp],
         "wkv_backward_ckpt": [i64, i64, i64] + [vp] * 16 + [vp, i64, vp],
     }
@@ -523,13 +525,15 @@ def wkv_backward_dd_workspace_size(B: int, T: int, C: int) -> int:
 
 
 def wkv_backward_dd(w, u, k, v, gout, state_in=None, state_out=None, gstate_out=None, *,
-                    want_gstate_in=True, workspace=None, out=None, stream=None):
+                    want_gstate_in=True, workspace=None, out=None, ckpt=None, stream=None):
     """Gradients of the per-token-decay prefill (float32): returns
     (gw, gu, gk, gv, gstate_in) with gw shaped like w (B, T, C), gu (C,)
     summed over the batch, gstate_in None when want_gstate_in is False.
     `out` may hold preallocated (gk, gv, gw, gu, gstate_in) tensors;
     `workspace` a uint8 tensor of at least wkv_backward_dd_workspace_size
-    bytes (else one is allocated for the call)."""
+    bytes (else one is allocated for the call). `ckpt`: the checkpoints
+    wkv_forward_dd_ckpt saved for the same inputs (wkv_backward_dd_ckpt), or
+    None."""
     lib = load_library()
     if k.dim() != 3:
         raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
@@ -562,12 +566,61 @@ def wkv_backward_dd(w, u, k, v, gout, state_in=None, state_out=None, gstate_out=
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
-        st = lib.wkv_backward_dd(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
-                                 _ptr(state_out), _ptr(gstate_out), _ptr(gout), _ptr(gk),
-                                 _ptr(gv), _ptr(gw), _ptr(gu), _ptr(gs), _ptr(workspace),
-                                 workspace.numel(), ctypes.c_void_p(strm.cuda_stream))
-    _check(st, "wkv_backward_dd")
+        if ckpt is None:
+            st = lib.wkv_backward_dd(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                     _ptr(state_in), _ptr(state_out), _ptr(gstate_out),
+                                     _ptr(gout), _ptr(gk), _ptr(gv), _ptr(gw), _ptr(gu), _ptr(gs),
+                                     _ptr(workspace), workspace.numel(),
+                                     ctypes.c_void_p(strm.cuda_stream))
+            _check(st, "wkv_backward_dd")
+        else:
+            _need(ckpt, "ckpt", f32, ckpt_shape(B, T, C), dev)
+            st = lib.wkv_backward_dd_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v),
+                                          _ptr(state_in), _ptr(state_out), _ptr(gstate_out),
+                                          _ptr(gout), _ptr(ckpt), _ptr(gk), _ptr(gv), _ptr(gw),
+                                          _ptr(gu), _ptr(gs), _ptr(workspace), workspace.numel(),
+                                          ctypes.c_void_p(strm.cuda_stream))
+            _check(st, "wkv_backward_dd_ckpt")
     return gw, gu, gk, gv, gs
+
+
+def wkv_forward_dd_ckpt(w, u, k, v, state_in=None, out=None, state_out=None, ckpt=None, *,
+                        path="auto", want_state=True, stream=None):
+    """wkv_forward_dd_ckpt: the float32 per-token-decay prefill that also
+    saves the backward's checkpoints. Returns (out, state_out, ckpt); ckpt is
+    a float32 tensor of ckpt_shape(B, T, C) holding 16-byte records (num, den
+    and a float64 max_exp); pass it to wkv_backward_dd(..., ckpt=ckpt)."""
+    lib = load_library()
+    if k.dim() != 3:
+        raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
+    if path not in ("auto", "seq", "chunk"):
+        raise ValueError("path must be 'auto', 'seq' or 'chunk'")
+    B, T, C = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    f32 = torch.float32
+    for name, t in (("w", w), ("k", k), ("v", v)):
+        _need(t, name, f32, (B, T, C), dev)
+    _need(u, "u", f32, (C,), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", f32, (3, B, C), dev)
+    if out is None:
+        out = torch.empty((B, T, C), dtype=f32, device=dev)
+    _need(out, "out", f32, (B, T, C), dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((3, B, C), dtype=f32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", f32, (3, B, C), dev)
+    if ckpt is None:
+        ckpt = torch.empty(ckpt_shape(B, T, C), dtype=f32, device=dev)
+    _need(ckpt, "ckpt", f32, ckpt_shape(B, T, C), dev)
+    with torch.cuda.device(dev):
+        st = lib.wkv_forward_dd_ckpt(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
+                                     _ptr(out), _ptr(state_out), _ptr(ckpt), _PATHS[path],
+                                     _stream_handle(dev, stream))
+    _check(st, "wkv_forward_dd_ckpt")
+    return out, state_out, ckpt
 
 
 def wkv_forward_dd(w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",

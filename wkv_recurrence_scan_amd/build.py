@@ -33,7 +33,7 @@ EXPORTS = [
     "wkv_abi_version", "wkv_backward", "wkv_backward_workspace_size", "wkv_backward_ckpt",
     "wkv_ckpt_bytes", "wkv_forward_ckpt", "wkv_forward_gated",
     "wkv_step_gated", "wkv_forward_dd", "wkv_step_dd", "wkv_backward_dd",
-    "wkv_backward_dd_workspace_size",
+    "wkv_backward_dd_workspace_size", "wkv_forward_dd_ckpt", "wkv_backward_dd_ckpt",
     "wkv_matrix_forward", "wkv_matrix_workspace_size", "wkv_matrix_step",
 ]
 

@@ -220,7 +220,7 @@ int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* 
 // Per-token decay: w is a sequence like k (same element type), u per channel.
 int forward_dd_impl(int64_t B, int64_t T, int64_t C, const void* w, const float* u, const void* k,
                     const void* v, const float* state_in, void* out, float* state_out, int io,
-                    int path, hipStream_t stream) {
+                    int path, hipStream_t stream, void* ckpt = nullptr, bool want_ckpt = false) {
   if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
   if (path != WKV_PATH_AUTO && path != WKV_PATH_SEQ && path != WKV_PATH_CHUNK) return WKV_ERR_ARG;
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
@@ -240,6 +240,19 @@ int forward_dd_impl(int64_t B, int64_t T, int64_t C, const void* w, const float*
     return WKV_ERR_ALIGN;
   const int64_t pbytes = C * 4;
   const int64_t sbytes = T > 0 ? seq_bytes : 0;
+  if (want_ckpt) {
+    // checkpoints for the backward: fp32 only, 16-byte records
+    if (io != WKV_IO_F32) return WKV_ERR_ARG;
+    if (T == 0) ckpt = nullptr;
+    if (T > 0 && ckpt == nullptr) return WKV_ERR_NULL;
+    if (misaligned(ckpt, 16)) return WKV_ERR_ALIGN;
+    const int64_t cbytes = T > 0 ? ckpt_bytes(B, T, C) : 0;
+    if (cbytes < 0) return WKV_ERR_DIM;
+    const void* others[] = {w, u, k, v, out, state_in, state_out};
+    const int64_t sizes[] = {sbytes, pbytes, sbytes, sbytes, sbytes, state_bytes, state_bytes};
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(ckpt, cbytes, others[i], sizes[i])) return WKV_ERR_ALIAS;
+  }
   if (overlaps(out, sbytes, w, sbytes) || overlaps(out, sbytes, k, sbytes) ||
       overlaps(out, sbytes, v, sbytes) || overlaps(out, sbytes, u, pbytes) ||
       overlaps(out, sbytes, state_in, state_bytes) || overlaps(out, sbytes, state_out, state_bytes))
@@ -258,7 +271,7 @@ int forward_dd_impl(int64_t B, int64_t T, int64_t C, const void* w, const float*
     e = wkv::launch_state_copy(B, C, state_in, state_out, stream);
     return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
   }
-  const wkv::DdArgs a{B, T, C, w, u, k, v, state_in, out, state_out};
+  const wkv::DdArgs a{B, T, C, w, u, k, v, state_in, out, state_out, ckpt};
   if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, false);
   const int vec = wkv::dd_vec_width(io, C, a);
   e = path == WKV_PATH_SEQ ? wkv::launch_dd_seq(a, io, vec, stream)
@@ -462,7 +475,8 @@ int backward_dd_impl(int64_t B, int64_t T, int64_t C, const float* w, const floa
                      const float* k, const float* v, const float* state_in,
                      const float* state_out, const float* gstate_out, const float* gout,
                      float* gk, float* gv, float* gw, float* gu, float* gstate_in,
-                     void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                     const void* ckpt = nullptr, bool want_ckpt = false) {
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
   int64_t seq_bytes, state_bytes;
   if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, 4, &seq_bytes) ||
@@ -483,6 +497,11 @@ int backward_dd_impl(int64_t B, int64_t T, int64_t C, const float* w, const floa
                        gstate_in};
   for (const void* p : all)
     if (misaligned(p, 4)) return WKV_ERR_ALIGN;
+  if (!tokens) ckpt = nullptr;
+  if (want_ckpt && tokens && ckpt == nullptr) return WKV_ERR_NULL;
+  if (misaligned(ckpt, 16)) return WKV_ERR_ALIGN;
+  const int64_t cbytes = ckpt != nullptr ? ckpt_bytes(B, T, C) : 0;
+  if (cbytes < 0) return WKV_ERR_DIM;
 
   const int64_t pbytes = C * 4;
   const int64_t sbytes = tokens ? seq_bytes : 0;
@@ -492,7 +511,7 @@ int backward_dd_impl(int64_t B, int64_t T, int64_t C, const float* w, const floa
   };
   const Range inputs[] = {{w, sbytes},        {u, pbytes},          {k, sbytes},
                           {v, sbytes},        {gout, sbytes},       {state_in, state_bytes},
-                          {state_out, state_bytes}, {gstate_out, state_bytes}};
+                          {state_out, state_bytes}, {gstate_out, state_bytes}, {ckpt, cbytes}};
   const Range outputs[] = {{gk, sbytes}, {gv, sbytes}, {gw, sbytes}, {gu, pbytes},
                            {gstate_in, state_bytes}};
   for (int i = 0; i < 5; ++i) {
@@ -514,7 +533,7 @@ int backward_dd_impl(int64_t B, int64_t T, int64_t C, const float* w, const floa
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
   const wkv::DdBwdArgs a{B, T, C, w, u, k, v, gout, state_in, state_out, gstate_out,
-                         gk, gv, gw, gu, gstate_in};
+                         gk, gv, gw, gu, gstate_in, ckpt};
   e = wkv::launch_dd_backward(a, workspace, stream);
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
@@ -574,6 +593,23 @@ int wkv_backward_dd(int64_t B, int64_t T, int64_t C, const float* w, const float
                     hipStream_t stream) {
   return backward_dd_impl(B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw,
                           gu, gstate_in, workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_dd_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                        const float* k, const float* v, const float* state_in, float* out,
+                        float* state_out, void* ckpt, int path, hipStream_t stream) {
+  return forward_dd_impl(B, T, C, w, u, k, v, state_in, out, state_out, WKV_IO_F32, path, stream,
+                         ckpt, true);
+}
+
+int wkv_backward_dd_ckpt(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                         const float* k, const float* v, const float* state_in,
+                         const float* state_out, const float* gstate_out, const float* gout,
+                         const void* ckpt, float* gk, float* gv, float* gw, float* gu,
+                         float* gstate_in, void* workspace, int64_t workspace_bytes,
+                         hipStream_t stream) {
+  return backward_dd_impl(B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, gk, gv, gw,
+                          gu, gstate_in, workspace, workspace_bytes, stream, ckpt, true);
 }
 
 int64_t wkv_backward_dd_workspace_size(int64_t B, int64_t T, int64_t C) {

@@ -27,6 +27,8 @@
 #include "wkv_tile.h"
 #include "wkv_decay_lane.h"
 
+#include <type_traits>
+
 namespace wkv {
 namespace {
 
@@ -137,12 +139,16 @@ __device__ __forceinline__ void dd_seq_compute(const DdBlock<V, U>& blk, LaneD (
   }
 }
 
-template <typename IoT, int V, int U>
+// CK: also save the backward's checkpoints (one channel per thread; the
+// blocks of U = kCkptTokens tokens are the checkpoint chunks).
+template <typename IoT, int V, int U, bool CK>
 __global__ __launch_bounds__(kDdSeqThreads) void wkv_dd_seq_kernel(
     int64_t B, int64_t T, int64_t C, const typename IoT::elem* __restrict__ w,
     const float* __restrict__ u, const typename IoT::elem* __restrict__ k,
     const typename IoT::elem* __restrict__ v, const float* __restrict__ state_in,
-    typename IoT::elem* __restrict__ out, float* __restrict__ state_out) {
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out,
+    LaneCk* __restrict__ ckpt) {
+  static_assert(!CK || (V == 1 && U == kCkptTokens), "checkpoints: one channel, 8-token blocks");
   const int64_t groups_per_row = C / V;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kDdSeqThreads + threadIdx.x;
   if (gid >= B * groups_per_row) return;
@@ -174,11 +180,16 @@ __global__ __launch_bounds__(kDdSeqThreads) void wkv_dd_seq_kernel(
   for (int64_t blk = 0; blk < nblk; blk += 2) {
     const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
     dd_seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, wp + nb * C, C);
+    if constexpr (CK) ckpt[blk * plane + lane0] = LaneCk{s[0].n, s[0].d, s[0].m};
     dd_seq_compute<IoT, V, U>(A, s, ud, op + blk * U * C, C);
     if (blk + 1 >= nblk) break;
     const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
     dd_seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, wp + na * C, C);
+    if constexpr (CK) ckpt[(blk + 1) * plane + lane0] = LaneCk{s[0].n, s[0].d, s[0].m};
     dd_seq_compute<IoT, V, U>(Bf, s, ud, op + (blk + 1) * U * C, C);
+  }
+  if constexpr (CK) {
+    if (nblk * U < T) ckpt[nblk * plane + lane0] = LaneCk{s[0].n, s[0].d, s[0].m};
   }
   for (int64_t t = nblk * U; t < T; ++t) {
     float kk[V], vv[V], ww[V], o[V];
@@ -224,11 +235,17 @@ __device__ __forceinline__ void dd_chunk_load(DdRegs<V, L>& r,
 
 // One tile: summaries, scan inside the wave, wave totals through LDS, the
 // state in front of every sub-chunk, then the rescan of each thread's tokens.
-template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED>
+// CK: the re-scan also saves the state in front of every token whose index
+// is a multiple of kCkptTokens to ck[(index / kCkptTokens) * lanes + lane]
+// (one channel per thread); tok0 is the index of the thread's first token.
+template <typename IoT, int V, int LC, int PS, int W, int L, bool MASKED, bool CK>
 __device__ __forceinline__ void dd_chunk_tile(const DdRegs<V, L>& r, int nvalid, LaneD (&carry)[V],
                                               const double (&ud)[V], SegD (*tot)[LC * V],
                                               typename IoT::elem* __restrict__ op, int64_t C,
-                                              bool cvalid, int wave, int sl, int cl) {
+                                              bool cvalid, int wave, int sl, int cl,
+                                              LaneCk* __restrict__ ck, int64_t lanes,
+                                              int64_t lane, int64_t tok0) {
+  static_assert(!CK || V == 1, "checkpoints are saved by one-channel threads");
   SegD inc[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
@@ -275,6 +292,11 @@ __device__ __forceinline__ void dd_chunk_tile(const DdRegs<V, L>& r, int nvalid,
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     if (!MASKED || i < nvalid) {
+      if constexpr (CK) {
+        const int64_t t = tok0 + i;
+        if (cvalid && (t % kCkptTokens) == 0)
+          ck[(t / kCkptTokens) * lanes + lane] = LaneCk{pre[0].n, pre[0].d, pre[0].m};
+      }
       float o[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) o[j] = laned_step(pre[j], r.k[i][j], r.v[i][j], r.w[i][j], ud[j]);
@@ -283,12 +305,13 @@ __device__ __forceinline__ void dd_chunk_tile(const DdRegs<V, L>& r, int nvalid,
   }
 }
 
-template <typename IoT, int V, int LC, int PS, int W, int L>
+template <typename IoT, int V, int LC, int PS, int W, int L, bool CK>
 __global__ __launch_bounds__(64 * W) void wkv_dd_chunk_kernel(
     int64_t B, int64_t T, int64_t C, const typename IoT::elem* __restrict__ w,
     const float* __restrict__ u, const typename IoT::elem* __restrict__ k,
     const typename IoT::elem* __restrict__ v, const float* __restrict__ state_in,
-    typename IoT::elem* __restrict__ out, float* __restrict__ state_out, int64_t groups_per_row) {
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out, int64_t groups_per_row,
+    LaneCk* __restrict__ ckpt) {
   static_assert(LC * PS == 64, "a wave is LC channel groups by PS sub-chunks");
   constexpr int CH = LC * V;
   constexpr int TL = W * PS * L;
@@ -325,18 +348,21 @@ __global__ __launch_bounds__(64 * W) void wkv_dd_chunk_kernel(
   const int64_t step = static_cast<int64_t>(TL) * C;
 
   const int64_t full = T / TL;
+  auto tok0 = [&](int64_t tile) { return tile * TL + static_cast<int64_t>(sub) * L; };
   DdRegs<V, L> A, Bf;
   if (full > 0) dd_chunk_load<IoT, V, L, false>(A, kp, vp, wp, C, L);
   for (int64_t tile = 0; tile < full; tile += 2) {
     const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
     dd_chunk_load<IoT, V, L, false>(Bf, kp + nb * step, vp + nb * step, wp + nb * step, C, L);
-    dd_chunk_tile<IoT, V, LC, PS, W, L, false>(A, L, carry, ud, tot[tile & 1], op + tile * step,
-                                               C, cvalid, wave, sl, cl);
+    dd_chunk_tile<IoT, V, LC, PS, W, L, false, CK>(A, L, carry, ud, tot[tile & 1],
+                                                   op + tile * step, C, cvalid, wave, sl, cl,
+                                                   ckpt, plane, lane0, tok0(tile));
     if (tile + 1 >= full) break;
     const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
     dd_chunk_load<IoT, V, L, false>(A, kp + na * step, vp + na * step, wp + na * step, C, L);
-    dd_chunk_tile<IoT, V, LC, PS, W, L, false>(Bf, L, carry, ud, tot[(tile + 1) & 1],
-                                               op + (tile + 1) * step, C, cvalid, wave, sl, cl);
+    dd_chunk_tile<IoT, V, LC, PS, W, L, false, CK>(Bf, L, carry, ud, tot[(tile + 1) & 1],
+                                                   op + (tile + 1) * step, C, cvalid, wave, sl,
+                                                   cl, ckpt, plane, lane0, tok0(tile + 1));
   }
   if (full * TL < T) {  // last, partial tile
     const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
@@ -345,8 +371,9 @@ __global__ __launch_bounds__(64 * W) void wkv_dd_chunk_kernel(
     DdRegs<V, L> last;
     dd_chunk_load<IoT, V, L, true>(last, kp + full * step, vp + full * step, wp + full * step, C,
                                    nvalid);
-    dd_chunk_tile<IoT, V, LC, PS, W, L, true>(last, nvalid, carry, ud, tot[full & 1],
-                                              op + full * step, C, cvalid, wave, sl, cl);
+    dd_chunk_tile<IoT, V, LC, PS, W, L, true, CK>(last, nvalid, carry, ud, tot[full & 1],
+                                                  op + full * step, C, cvalid, wave, sl, cl, ckpt,
+                                                  plane, lane0, tok0(full));
   }
   if (state_out != nullptr && sub == 0 && cvalid) store_state_d<V>(state_out, lane0, plane, carry);
 }
@@ -395,9 +422,21 @@ hipError_t launch_dd_seq_t(const DdArgs& a, hipStream_t st) {
   const int64_t blocks = (threads + kDdSeqThreads - 1) / kDdSeqThreads;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   using E = typename IoT::elem;
-  hipLaunchKernelGGL((wkv_dd_seq_kernel<IoT, V, U>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kDdSeqThreads), 0, st, a.B, a.T, a.C, cp<E>(a.w), a.u, cp<E>(a.k),
-                     cp<E>(a.v), a.state_in, static_cast<E*>(a.out), a.state_out);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kDdSeqThreads);
+  auto* ck = static_cast<LaneCk*>(a.ckpt);
+  if constexpr (std::is_same<IoT, IoF32>::value && V == 1) {
+    if (ck != nullptr) {
+      hipLaunchKernelGGL((wkv_dd_seq_kernel<IoT, V, U, true>), grid, block, 0, st, a.B, a.T, a.C,
+                         cp<E>(a.w), a.u, cp<E>(a.k), cp<E>(a.v), a.state_in,
+                         static_cast<E*>(a.out), a.state_out, ck);
+      return hipGetLastError();
+    }
+  } else {
+    if (ck != nullptr) return hipErrorInvalidValue;  // checkpoints: fp32 only
+  }
+  hipLaunchKernelGGL((wkv_dd_seq_kernel<IoT, V, U, false>), grid, block, 0, st, a.B, a.T, a.C,
+                     cp<E>(a.w), a.u, cp<E>(a.k), cp<E>(a.v), a.state_in, static_cast<E*>(a.out),
+                     a.state_out, nullptr);
   return hipGetLastError();
 }
 
@@ -408,10 +447,21 @@ hipError_t launch_dd_chunk_t(const DdArgs& a, hipStream_t st) {
   const int64_t blocks = a.B * gpr;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   using E = typename IoT::elem;
-  hipLaunchKernelGGL((wkv_dd_chunk_kernel<IoT, V, kDdLC, kDdPS, W, L>),
-                     dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0, st, a.B, a.T, a.C,
-                     cp<E>(a.w), a.u, cp<E>(a.k), cp<E>(a.v), a.state_in, static_cast<E*>(a.out),
-                     a.state_out, gpr);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * W);
+  auto* ck = static_cast<LaneCk*>(a.ckpt);
+  if constexpr (std::is_same<IoT, IoF32>::value && V == 1) {
+    if (ck != nullptr) {
+      hipLaunchKernelGGL((wkv_dd_chunk_kernel<IoT, V, kDdLC, kDdPS, W, L, true>), grid, block, 0,
+                         st, a.B, a.T, a.C, cp<E>(a.w), a.u, cp<E>(a.k), cp<E>(a.v), a.state_in,
+                         static_cast<E*>(a.out), a.state_out, gpr, ck);
+      return hipGetLastError();
+    }
+  } else {
+    if (ck != nullptr) return hipErrorInvalidValue;  // checkpoints: fp32 only
+  }
+  hipLaunchKernelGGL((wkv_dd_chunk_kernel<IoT, V, kDdLC, kDdPS, W, L, false>), grid, block, 0, st,
+                     a.B, a.T, a.C, cp<E>(a.w), a.u, cp<E>(a.k), cp<E>(a.v), a.state_in,
+                     static_cast<E*>(a.out), a.state_out, gpr, nullptr);
   return hipGetLastError();
 }
 

@@ -23,7 +23,9 @@
 // defining sums term by term instead.
 //
 // Layout as in the constant-decay backward: every (segment, lane) pair is a
-// thread; one segment per lane when B*C alone fills the GPU. Launches:
+// thread; one segment per lane when B*C alone fills the GPU. When the forward
+// saved the checkpoints, A and the checkpoint writes are skipped (B runs only
+// with several segments, each starting from its first checkpoint). Launches:
 //   A (several segments only): each segment's forward summary from the empty
 //     state (sums, maximum exponent, total rate);
 //   B: each segment's start state (the initial state, then the earlier
@@ -51,12 +53,6 @@ namespace {
 constexpr int kDbThreads = 256;
 constexpr int kDbLc = kCkptTokens;  // tokens per checkpoint chunk
 
-// A checkpoint: the state in front of a chunk.
-struct CkD {
-  float n, d;
-  double m;
-};
-
 // Suffix sums P = p e^z, Q = q e^z.
 struct SufD {
   float p, q;
@@ -78,7 +74,7 @@ struct DdBwdKernelArgs {
   float* gw;
   float* gstate_in;
   float* gu_part;   // [segments][lanes]
-  CkD* ckpt;        // [chunks][lanes]
+  LaneCk* ckpt;        // [chunks][lanes]
   float2* seg_nd;   // [segments][lanes] forward summary: sums,
   double* seg_m;    //   maximum exponent,
   double* seg_ws;   //   total rate
@@ -234,26 +230,32 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_forward_kernel(DdBw
 
 // B: start state, checkpoints and (OWN) the segment's own suffix sums: the sum
 // over its tokens t of a_t W(first - 1, t) (1, out_t), relative to the largest
-// exponent -M_t - (rates of the segment's steps before t).
-template <bool OWN>
+// exponent -M_t - (rates of the segment's steps before t). GIVEN: the forward
+// saved the checkpoints; the segment starts from its first one and writes none.
+template <bool OWN, bool GIVEN>
 __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_sums_kernel(DdBwdKernelArgs a) {
   DbThread th;
   if (!db_thread(a, th)) return;
   const double ud = static_cast<double>(a.u[th.c]);
   LaneD x = laned_empty();
-  if (a.state_in != nullptr) {
-    x = LaneD{a.state_in[th.lane], a.state_in[th.lanes + th.lane],
-              static_cast<double>(a.state_in[2 * th.lanes + th.lane])};
-  }
-  for (int64_t sr = 0; sr < th.s; ++sr) {
-    const int64_t at = sr * th.lanes + th.lane;
-    const float2 nd = a.seg_nd[at];
-    laned_absorb(x, SegD{nd.x, nd.y, a.seg_m[at], a.seg_ws[at]});
+  if constexpr (GIVEN) {
+    const LaneCk cp = a.ckpt[th.j0 * th.lanes + th.lane];
+    x = LaneD{cp.n, cp.d, cp.m};
+  } else {
+    if (a.state_in != nullptr) {
+      x = LaneD{a.state_in[th.lane], a.state_in[th.lanes + th.lane],
+                static_cast<double>(a.state_in[2 * th.lanes + th.lane])};
+    }
+    for (int64_t sr = 0; sr < th.s; ++sr) {
+      const int64_t at = sr * th.lanes + th.lane;
+      const float2 nd = a.seg_nd[at];
+      laned_absorb(x, SegD{nd.x, nd.y, a.seg_m[at], a.seg_ws[at]});
+    }
   }
   float p = 0.0f, q = 0.0f;
   double zl = kEmptyD, cw = 0.0;
   db_walk<OWN, false>(a, th, [&](const DbChunk<OWN>& ch, int64_t j, int n, auto full) {
-    a.ckpt[j * th.lanes + th.lane] = CkD{x.n, x.d, x.m};
+    if constexpr (!GIVEN) a.ckpt[j * th.lanes + th.lane] = LaneCk{x.n, x.d, x.m};
 #pragma unroll
     for (int i = 0; i < kDbLc; ++i) {
       if (decltype(full)::value || i < n) {
@@ -281,6 +283,10 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_sums_kernel(DdBwdKe
     const int64_t at = th.s * th.lanes + th.lane;
     a.own_pq[at] = make_float2(p, q);
     a.own_z[at] = zl;
+    // the segment's total rate, which the walk back needs to cross it (A,
+    // which also writes it, does not run when the checkpoints are given;
+    // otherwise this launch reads the earlier segments' totals and leaves them)
+    if constexpr (GIVEN) a.seg_ws[at] = cw;
   }
 }
 
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(kDbThreads) void wkv_dd_bwd_seg_backward_kernel(DdB
   float gu_acc = 0.0f;
   db_walk<true, true>(a, th, [&](const DbChunk<true>& ch, int64_t j, int n, auto full) {
     const int64_t o = th.row + j * kDbLc * a.C;
-    const CkD cp = a.ckpt[j * th.lanes + th.lane];
+    const LaneCk cp = a.ckpt[j * th.lanes + th.lane];
     LaneD st{cp.n, cp.d, cp.m};
     float y[kDbLc], rho[kDbLc], om[kDbLc], pn[kDbLc], pd[kDbLc];
     double M[kDbLc], pm[kDbLc];
@@ -406,10 +412,15 @@ hipError_t launch_dd_backward(const DdBwdArgs& a, void* ws, hipStream_t st) {
   const int64_t S = backward_segments(lanes, a.T, &seg_chunks);
   const DbLayout l = db_layout(a.B, a.T, a.C, S);
   char* base = static_cast<char*>(ws);
+  // the forward's checkpoints when given (read only: nothing that writes
+  // checkpoints is launched then), else the workspace's
+  const bool given = a.ckpt != nullptr;
+  LaneCk* ck = given ? const_cast<LaneCk*>(static_cast<const LaneCk*>(a.ckpt))
+                     : reinterpret_cast<LaneCk*>(base + l.ckpt);
   DdBwdKernelArgs k{a.B, a.T, a.C, a.w, a.u, a.k, a.v, a.gout, a.state_in, a.state_out,
                     a.gstate_out, a.gk, a.gv, a.gw, a.gstate_in,
                     reinterpret_cast<float*>(base + l.gu_part),
-                    reinterpret_cast<CkD*>(base + l.ckpt),
+                    ck,
                     reinterpret_cast<float2*>(base + l.seg_nd),
                     reinterpret_cast<double*>(base + l.seg_m),
                     reinterpret_cast<double*>(base + l.seg_ws),
@@ -421,10 +432,14 @@ hipError_t launch_dd_backward(const DdBwdArgs& a, void* ws, hipStream_t st) {
   if (blocks > 0) {
     const dim3 grid(static_cast<unsigned>(blocks)), block(kDbThreads);
     if (S > 1) {
-      hipLaunchKernelGGL(wkv_dd_bwd_seg_forward_kernel, grid, block, 0, st, k);
-      hipLaunchKernelGGL(wkv_dd_bwd_seg_sums_kernel<true>, grid, block, 0, st, k);
-    } else {
-      hipLaunchKernelGGL(wkv_dd_bwd_seg_sums_kernel<false>, grid, block, 0, st, k);
+      if (given) {
+        hipLaunchKernelGGL((wkv_dd_bwd_seg_sums_kernel<true, true>), grid, block, 0, st, k);
+      } else {
+        hipLaunchKernelGGL(wkv_dd_bwd_seg_forward_kernel, grid, block, 0, st, k);
+        hipLaunchKernelGGL((wkv_dd_bwd_seg_sums_kernel<true, false>), grid, block, 0, st, k);
+      }
+    } else if (!given) {
+      hipLaunchKernelGGL((wkv_dd_bwd_seg_sums_kernel<false, false>), grid, block, 0, st, k);
     }
     hipLaunchKernelGGL(wkv_dd_bwd_seg_backward_kernel, grid, block, 0, st, k);
     const hipError_t e = hipGetLastError();

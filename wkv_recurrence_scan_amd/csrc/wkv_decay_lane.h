@@ -25,6 +25,13 @@ struct LaneD {
 
 __device__ __forceinline__ LaneD laned_empty() { return LaneD{0.0f, 0.0f, kEmptyD}; }
 
+// A checkpoint for the backward pass: the lane state in front of a chunk of
+// kCkptTokens tokens, 16 bytes, stored at [chunk][b * C + c].
+struct LaneCk {
+  float n, d;
+  double m;
+};
+
 // One token. Output: the state as it stands mixed with the token at weight
 // e^(u + k); then the state decays by e^(-w) and the token is added at e^k.
 // Of each pair of weights, taken against the larger exponent, one is 1.

@@ -105,6 +105,7 @@ struct DdBwdArgs {
   float* gw;
   float* gu;
   float* gstate_in;         // nullptr: not wanted
+  const void* ckpt = nullptr;  // the forward's checkpoints (see DdArgs), or nullptr
 };
 int64_t dd_backward_workspace_bytes(int64_t B, int64_t T, int64_t C);
 hipError_t launch_dd_backward(const DdBwdArgs& a, void* ws, hipStream_t s);
@@ -119,6 +120,7 @@ struct DdArgs {
   const float* state_in;  // nullptr: empty state
   void* out;
   float* state_out;       // nullptr: not written
+  void* ckpt = nullptr;   // fp32 only: [ceil(T/8)][B*C] states (n, d, fp64 m) for the backward
 };
 struct DdStepArgs {
   int64_t B, C;
