@@ -252,6 +252,32 @@ def test_decay_backward_entry_points_validate_without_device():
     assert lib.wkv_backward_dd(-1, T, C, *base[3:], ws, need, nul) == 2
 
 
+def test_decay_checkpoint_entry_points_validate_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    a = 0x10000000
+    B, T, C = 1, 16, 64
+    seq = B * T * C * 4
+    w, k, v, out = (P(a + i * seq) for i in range(4))
+    u, ck = P(a + 4 * seq), P(a + 65536)
+    # B, T, C, w, u, k, v, state_in, out, state_out, ckpt, path, stream
+    base = [B, T, C, w, u, k, v, nul, out, nul]
+    assert lib.wkv_forward_dd_ckpt(*base, ck, W.WKV_PATH_LOOKBACK, nul) == 7  # no look-back
+    assert lib.wkv_forward_dd_ckpt(*base, nul, W.WKV_PATH_AUTO, nul) == 1     # ckpt missing
+    assert lib.wkv_forward_dd_ckpt(*base, P(a + 65536 + 8), W.WKV_PATH_AUTO, nul) == 3
+    assert lib.wkv_forward_dd_ckpt(*base, out, W.WKV_PATH_AUTO, nul) == 4     # ckpt on out
+    # B, T, C, w, u, k, v, state_in, state_out, gstate_out, gout, ckpt, gk, gv, gw, gu,
+    # gstate_in, workspace, bytes, stream
+    g, gk, gv, gw = (P(a + (8 + i) * seq) for i in range(4))
+    gu = P(a + 12 * seq)
+    bwd = [B, T, C, w, u, k, v, nul, nul, nul, g]
+    rest = [gk, gv, gw, gu, nul, P(a + (1 << 24)), 1 << 20, nul]
+    assert lib.wkv_backward_dd_ckpt(*bwd, nul, *rest) == 1                   # ckpt missing
+    assert lib.wkv_backward_dd_ckpt(*bwd, P(a + 65536 + 4), *rest) == 3      # misaligned
+    assert lib.wkv_backward_dd_ckpt(*bwd, gk, *rest) == 4                    # an output on it
+
+
 def test_per_token_decay_rates_are_seeded_and_positive():
     wl = I.WORKLOADS[1].scaled(B=3, T=50, C=32)
     r1 = I.decay_rates(wl)
