@@ -168,43 +168,41 @@ __device__ __forceinline__ int chunk_tokens(const DdBwdKernelArgs& a, int64_t j)
 }
 
 // Calls body(chunk, j, tokens, full) for the thread's chunks j0 .. j1-1 in
-// order (REV: last first), with two register buffers: the next chunk's loads
-// are issued before the current one is processed. They are issued on every
-// path (past the end the last chunk re-reads itself), so the compiler's
-// counter waits stop at the chunk about to be used. `full` is a compile-time
-// flag: only the sequence's last chunk can be partial, and only its code
-// tests each token.
+// order (REV: last first). `full` is a compile-time flag: only the
+// sequence's last chunk can be partial; it is loaded and processed on its own
+// (first when REV), with a test per token. The full chunks run through two
+// register buffers with no branch around their loads: the next chunk's loads
+// are issued before the current one is processed, and past the end the last
+// chunk re-reads itself, so the compiler's counter waits stop at the chunk
+// about to be used.
 template <bool G, bool REV, typename F>
 __device__ __forceinline__ void db_walk(const DdBwdKernelArgs& a, const DbThread& th, F&& body) {
-  const int64_t n = th.j1 - th.j0;
-  if (n <= 0) return;
-  auto chunk = [&](int64_t q) { return REV ? th.j1 - 1 - q : th.j0 + q; };
-  auto load = [&](DbChunk<G>& c, int64_t q) {
-    const int64_t j = chunk(q < n ? q : n - 1);
-    const int nt = chunk_tokens(a, j);
-    if (nt == kDbLc) {
-      db_load<G, false>(c, a, th.row + j * kDbLc * a.C, nt);
-    } else {
-      db_load<G, true>(c, a, th.row + j * kDbLc * a.C, nt);
-    }
+  const int64_t jf = th.j1 < a.T / kDbLc ? th.j1 : a.T / kDbLc;  // end of the full chunks
+  const bool partial = th.j1 > jf;                               // chunk jf is partial
+  auto partial_chunk = [&]() {
+    const int nt = chunk_tokens(a, jf);
+    DbChunk<G> c;
+    db_load<G, true>(c, a, th.row + jf * kDbLc * a.C, nt);
+    body(c, jf, nt, std::false_type{});
   };
-  auto run = [&](const DbChunk<G>& c, int64_t j) {
-    const int nt = chunk_tokens(a, j);
-    if (nt == kDbLc) {
-      body(c, j, nt, std::true_type{});
-    } else {
-      body(c, j, nt, std::false_type{});
+  if (REV && partial) partial_chunk();
+  const int64_t n = jf - th.j0;
+  if (n > 0) {
+    auto chunk = [&](int64_t q) { return REV ? jf - 1 - q : th.j0 + q; };
+    auto load = [&](DbChunk<G>& c, int64_t q) {
+      db_load<G, false>(c, a, th.row + chunk(q < n ? q : n - 1) * kDbLc * a.C, kDbLc);
+    };
+    DbChunk<G> A, Bf;
+    load(A, 0);
+    for (int64_t q = 0; q < n; q += 2) {
+      load(Bf, q + 1);
+      body(A, chunk(q), kDbLc, std::true_type{});
+      if (q + 1 >= n) break;
+      load(A, q + 2);
+      body(Bf, chunk(q + 1), kDbLc, std::true_type{});
     }
-  };
-  DbChunk<G> A, Bf;
-  load(A, 0);
-  for (int64_t q = 0; q < n; q += 2) {
-    load(Bf, q + 1);
-    run(A, chunk(q));
-    if (q + 1 >= n) break;
-    load(A, q + 2);
-    run(Bf, chunk(q + 1));
   }
+  if (!REV && partial) partial_chunk();
 }
 
 // A: forward summary of every segment but the last from the empty state.
