@@ -549,8 +549,7 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
       }
     }
   };
-  auto load = [&](Chunk<G>& ch, int64_t j) {
-    const int n = j < io.nfull ? kLc : io.rest;
+  auto load = [&](Chunk<G>& ch, int64_t j, int n) {
     const int64_t off = io.row + j * io.step;
     const float* rp = G ? io.r + off : io.r;
     if (n == kLc) {
@@ -559,26 +558,30 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
       load_chunk<true, G>(ch, io.k + off, io.v + off, io.g + off, rp, io.C, n);
     }
   };
-  auto run = [&](const Chunk<G>& ch, int64_t j) {
+  auto save = [&](int64_t j) {
     if constexpr (!GIVEN) a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
-    const int n = j < io.nfull ? kLc : io.rest;
-    if (n == kLc) {
-      process(ch, n, std::true_type{});
-    } else {
-      process(ch, n, std::false_type{});
-    }
   };
-  if (j0 < j1) {
-    // the last chunk re-reads itself, so the loads are unconditional
+  // full chunks through two buffers with no branch around their loads (the
+  // last re-reads itself), then the sequence's partial last chunk on its own
+  const int64_t jf = j1 < io.nfull ? j1 : io.nfull;
+  if (j0 < jf) {
     Chunk<G> A, Bf;
-    load(A, j0);
-    for (int64_t j = j0; j < j1; j += 2) {
-      load(Bf, j + 1 < j1 ? j + 1 : j);
-      run(A, j);
-      if (j + 1 >= j1) break;
-      load(A, j + 2 < j1 ? j + 2 : j + 1);
-      run(Bf, j + 1);
+    load(A, j0, kLc);
+    for (int64_t j = j0; j < jf; j += 2) {
+      load(Bf, j + 1 < jf ? j + 1 : j, kLc);
+      save(j);
+      process(A, kLc, std::true_type{});
+      if (j + 1 >= jf) break;
+      load(A, j + 2 < jf ? j + 2 : j + 1, kLc);
+      save(j + 1);
+      process(Bf, kLc, std::true_type{});
     }
+  }
+  if (j1 > jf) {
+    Chunk<G> last;
+    load(last, jf, io.rest);
+    save(jf);
+    process(last, io.rest, std::false_type{});
   }
   a.seg_rev[s * lanes + lane] = make_float4(p, q, r, rq);
   a.seg_rev_z[s * lanes + lane] = zl;
