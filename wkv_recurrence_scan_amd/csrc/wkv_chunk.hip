@@ -152,25 +152,35 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
 
   const int64_t full = T / TL;  // tiles with every token present
   // Software pipeline over two register buffers: the loads of the next tile
-  // are issued before the current one is processed. They are issued on every
-  // path (the last full tile re-reads itself, a harmless cache hit), so the
-  // compiler's counter-based waits stop at the current tile's loads instead
-  // of draining the prefetch as well.
+  // are issued before the current one is processed. Inside the loop every
+  // load is a real one and unconditional, so the compiler's counter-based
+  // waits stop at the current tile's loads instead of draining the prefetch;
+  // the last one or two tiles are processed after it (two: both loaded up
+  // front), so no tile is read twice.
   ChunkRegs<V, L, G> A, Bf;
   auto at = [&](const typename IoT::elem* p, int64_t t) { return G ? p + t * step : p; };
-  if (full > 0) chunk_load<IoT, V, L, false, G>(A, kp, vp, rp, C, L);
-  for (int64_t tile = 0; tile < full; tile += 2) {
-    const int64_t nb = tile + 1 < full ? tile + 1 : full - 1;
-    chunk_load<IoT, V, L, false, G>(Bf, kp + nb * step, vp + nb * step, at(rp, nb), C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false, G, CK>(A, L, carry, wd, ub, cb, fast, tot[tile & 1],
-                                                   op + tile * step, C, cvalid, wave, sl, cl,
-                                                   ck_at(tile));
-    if (tile + 1 >= full) break;
-    const int64_t na = tile + 2 < full ? tile + 2 : full - 1;
-    chunk_load<IoT, V, L, false, G>(A, kp + na * step, vp + na * step, at(rp, na), C, L);
-    chunk_tile<IoT, V, LC, PS, W, L, false, G, CK>(Bf, L, carry, wd, ub, cb, fast,
-                                                   tot[(tile + 1) & 1], op + (tile + 1) * step, C,
-                                                   cvalid, wave, sl, cl, ck_at(tile + 1));
+  auto load = [&](ChunkRegs<V, L, G>& r, int64_t t) {
+    chunk_load<IoT, V, L, false, G>(r, kp + t * step, vp + t * step, at(rp, t), C, L);
+  };
+  auto tile_of = [&](const ChunkRegs<V, L, G>& r, int64_t t) {
+    chunk_tile<IoT, V, LC, PS, W, L, false, G, CK>(r, L, carry, wd, ub, cb, fast, tot[t & 1],
+                                                   op + t * step, C, cvalid, wave, sl, cl,
+                                                   ck_at(t));
+  };
+  if (full > 0) load(A, 0);
+  int64_t tile = 0;
+  for (; tile + 2 < full; tile += 2) {
+    load(Bf, tile + 1);
+    tile_of(A, tile);
+    load(A, tile + 2);
+    tile_of(Bf, tile + 1);
+  }
+  if (tile + 1 < full) {  // two left
+    load(Bf, tile + 1);
+    tile_of(A, tile);
+    tile_of(Bf, tile + 1);
+  } else if (tile < full) {  // one left
+    tile_of(A, tile);
   }
   if (full * TL < T) {  // last, partial tile
     const int64_t first = full * TL + static_cast<int64_t>(sub) * L;

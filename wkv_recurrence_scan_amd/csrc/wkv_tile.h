@@ -62,7 +62,9 @@ struct ChunkRegs {
   float r[G ? L : 1][V];
 };
 
-// rp is read only when G.
+// rp is read only when G. The loads are non-temporal: a tile is read once
+// (measured on MI355X: B=8 T=1024 C=768 22.9 against 23.5 us per layer,
+// B=4 T=16384 C=2048 look-back 315 against 337 us).
 template <typename IoT, int V, int L, bool MASKED, bool G>
 __device__ __forceinline__ void chunk_load(ChunkRegs<V, L, G>& r,
                                            const typename IoT::elem* __restrict__ kp,
@@ -72,9 +74,9 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<V, L, G>& r,
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     if (!MASKED || i < nvalid) {
-      IoT::template load<V, false>(kp + i * C, r.k[i]);
-      IoT::template load<V, false>(vp + i * C, r.v[i]);
-      if constexpr (G) IoT::template load<V, false>(rp + i * C, r.r[i]);
+      IoT::template load<V, true>(kp + i * C, r.k[i]);
+      IoT::template load<V, true>(vp + i * C, r.v[i]);
+      if constexpr (G) IoT::template load<V, true>(rp + i * C, r.r[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
