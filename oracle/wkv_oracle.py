@@ -148,36 +148,52 @@ def _summary_by_definition(w, k, v, n0, d0, m0):
 # O2: the stabilised recurrence (one step per token, vectorised over lanes).
 # ---------------------------------------------------------------------------
 
+def _share(x):
+    """1 / (1 + e^-x) for x in [-inf, inf], as exp(-log(1 + e^-x)) so that no
+    branch is needed and neither tail overflows."""
+    return np.exp(-np.logaddexp(0.0, -x))
+
+
 def wkv_step_ref(w, u, k_t, v_t, state):
-    """One decode step (page "Linear attention without writing a CUDA kernel",
-    section "The recurrence", the step function that carries num, den and
-    max_exp).
+    """One decode step, from the sum definition (page "Linear attention
+    without writing a CUDA kernel", section "The recurrence", the wkv_t
+    equation and its running-state form).
 
     k_t, v_t: (B, C) for one position; state: (3, B, C). Returns (out_t, new
-    state). The output mixes the state as it stands with the current token
-    weighted by exp(u + k_t); the new state is the old one decayed by exp(-w)
-    plus the current token weighted by exp(k_t). Each mix is done relative to
-    the larger of its two exponents, so one of the two factors is exactly 1 and
-    neither can overflow.
+    state).
+
+    Written as a running weighted mean rather than as rescaled sums: the state
+    (num, den, max_exp) stands for the sums N = num e^max_exp and
+    D = den e^max_exp, so it is read as two numbers per lane, the total weight
+    of the past as its logarithm, log D = max_exp + ln den, and the mean of the
+    past values under those weights, r = N / D = num / den (an empty state has
+    log D = -inf). The output at this position is then the mean of two groups,
+    the past (weight D, mean r) and the current token (weight e^(u + k_t),
+    value v_t); the past's share of the total is
+    D / (D + e^(u + k_t)) = 1 / (1 + e^-(log D - u - k_t)). After the output
+    the past weight decays by e^-w and the token joins it at weight e^(k_t),
+    without the bonus: log D' = log(e^(log D - w) + e^(k_t)), and r' is again
+    a two-group mean with the past's share taken at exponents log D - w and
+    k_t. The new state is handed back as (num, den, max_exp) = (r', 1, log D'),
+    which stands for the same two sums.
     """
     w, u = _f64(w), _f64(u)
     k_t, v_t = _f64(k_t), _f64(v_t)
     num, den, mx = (_f64(p) for p in state)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        filled = den > 0
+        log_d = np.where(filled, mx + np.log(np.where(filled, den, 1.0)), -np.inf)
+        mean = np.where(filled, num / np.where(filled, den, 1.0), 0.0)
 
-    # output: past state against the bonus-weighted current token
-    cur = u + k_t
-    ref = np.maximum(mx, cur)
-    f_past = np.exp(mx - ref)
-    f_cur = np.exp(cur - ref)
-    out_t = (f_past * num + f_cur * v_t) / (f_past * den + f_cur)
+    # output: past (weight D) against the current token (weight e^(u + k_t))
+    gap = log_d - (u + k_t)
+    out_t = _share(gap) * mean + _share(-gap) * v_t
 
-    # advance: decayed past against the current token without bonus
-    decayed = mx - w
-    ref2 = np.maximum(decayed, k_t)
-    g_past = np.exp(decayed - ref2)
-    g_cur = np.exp(k_t - ref2)
-    new_state = np.stack([g_past * num + g_cur * v_t, g_past * den + g_cur, ref2])
-    return out_t, new_state
+    # the past decays by one step, the token joins without the bonus
+    gap2 = (log_d - w) - k_t
+    new_mean = _share(gap2) * mean + _share(-gap2) * v_t
+    new_log_d = np.logaddexp(log_d - w, k_t)
+    return out_t, np.stack([new_mean, np.ones_like(new_mean), new_log_d])
 
 
 def wkv_recurrent(w, u, k, v, state_in=None):
