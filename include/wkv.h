@@ -67,7 +67,9 @@ typedef enum wkv_status {
   WKV_ERR_LAUNCH = 5, /* the kernel launch failed (see wkv_last_hip_error)        */
   WKV_ERR_DEVICE = 6, /* no usable HIP device is current                          */
   WKV_ERR_ARG = 7,    /* an enumerated argument (io, path) is out of range        */
-  WKV_ERR_WORKSPACE = 8 /* the kernel needs a workspace: missing or too small     */
+  WKV_ERR_WORKSPACE = 8, /* the kernel needs a workspace: missing or too small    */
+  WKV_ERR_LOOKBACK = 9  /* reported by wkv_workspace_status only: a LOOKBACK launch
+                           could not chain its segments (see there)                */
 } wkv_status;
 
 /* Element type of k, v and out (w, u and the state are always fp32). */
@@ -121,19 +123,41 @@ int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float*
 /* As wkv_forward_ex with a device workspace, which the LOOKBACK kernel needs
  * (and AUTO then may choose).
  *   workspace        device memory of at least wkv_workspace_size(...) bytes,
- *                    256-byte aligned, owned by the caller. It must be zero-filled
- *                    before its first use with given (B, T, C, io); every call
- *                    leaves it ready for the next call with the same sizes (no
- *                    clearing needed in between, HIP graph replays included).
- *                    Before reuse with other sizes, zero-fill it again. Calls
- *                    that may run concurrently must not share a workspace. It
- *                    must not overlap any other argument.
+ *                    256-byte aligned, owned by the caller. Zero-fill it once
+ *                    before its first use; after that every call leaves it
+ *                    ready for the next one, with the same sizes or others
+ *                    (no clearing in between, HIP graph replays included).
+ *                    Calls that may run concurrently must not share a
+ *                    workspace. It must not overlap any other argument.
  *   workspace_bytes  its size in bytes.
- * A call whose kernel needs no workspace ignores it (it may be NULL). */
+ * A call whose kernel needs no workspace ignores it (it may be NULL).
+ *
+ * Layout of the workspace's first 16 bytes (32-bit words): [0] the sticky
+ * error word read by wkv_workspace_status (bit 0: a wait for an earlier
+ * segment ran out; bit 1: overlapping calls shared the workspace), [1] the
+ * epoch of the latest launch, [2] and [3] zero in normal use (tests set [2]
+ * bit 0, "publish nothing", and [3], a smaller bound on each wait, to force
+ * the failure path). Each LOOKBACK launch enqueues a one-block set-up kernel
+ * (next epoch, ticket counters rewound) before the scan itself. A wait that
+ * runs out (it cannot in a correct launch) does not hang the kernel: it sets
+ * the error word and continues with NaN in place of the missing prefix, so
+ * every output that depended on it is NaN. */
 int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                    const void* k, const void* v, const float* state_in, void* out,
                    float* state_out, int io, int path, void* workspace,
                    int64_t workspace_bytes, hipStream_t stream);
+
+/* Reads the error word of a workspace used by wkv_forward_ws (and friends)
+ * after the work enqueued on `stream` so far has finished: waits for the
+ * stream, then returns WKV_OK if no LOOKBACK launch with this workspace ever
+ * failed to chain its segments (since the word was last cleared), or
+ * WKV_ERR_LOOKBACK if one did; with clear != 0 the word is then reset to 0.
+ * Blocking (it synchronises the stream), so not for use under HIP graph
+ * capture. WKV_ERR_NULL / WKV_ERR_WORKSPACE (fewer than 16 bytes) /
+ * WKV_ERR_ALIGN (not 256-byte aligned) for a bad workspace argument,
+ * WKV_ERR_LAUNCH if the copy or the synchronisation fails. */
+int wkv_workspace_status(void* workspace, int64_t workspace_bytes, int clear,
+                         hipStream_t stream);
 
 /* As wkv_forward_ws with the output gated by the receptance:
  * out_t = sigmoid(r_t) * wkv_t per element (page "RWKV-v6 Architecture:

@@ -194,12 +194,18 @@ def test_auto_path_choice():
     assert W.wkv_select_path(4, 8, 64) == "seq"
 
 
-def test_lookback_workspace_counters_and_error_word():
-    """The look-back kernel's workspace after n launches: every channel
-    group's ticket counter advanced by exactly S (segments per group) per
-    launch, which is what gives each launch its own epoch, and the error word
-    (set only if a bounded wait timed out) still zero. T = 3000 uses
-    256-token segments, so S = 12."""
+def _ctrl_words(ws, groups):
+    """The look-back workspace's control words: error, epoch, test flags, test
+    spin limit, then each channel group's ticket counter (16 bytes apart)."""
+    words = ws[:16 + 16 * groups].view(torch.int32).cpu().numpy().astype(np.int64) & 0xffffffff
+    return words[:4], words[4:].reshape(groups, 4)[:, 0]
+
+
+def test_lookback_workspace_epoch_tickets_and_error_word():
+    """The look-back workspace after n launches: the epoch word counts the
+    launches, every channel group's ticket counter ends at S (segments per
+    group: the set-up kernel rewinds it before each launch), and the error
+    word stays zero. T = 3000 uses 256-token segments, so S = 12."""
     wl = WL3.scaled(B=2, T=3000, C=96)
     w, u = I.params(wl)
     k, v = I.kv(wl)
@@ -212,10 +218,72 @@ def test_lookback_workspace_counters_and_error_word():
                                   workspace=ws)
         torch.cuda.synchronize()
         assert_out_close(host64(out), ref, v, F32_TOL)
-        words = ws[:16 + 16 * groups].view(torch.int64).cpu().numpy()
-        assert int(words[0]) & 0xffffffff == 0, "a bounded wait timed out"
-        tickets = words[2:].reshape(groups, 2)[:, 0]
-        assert np.all(tickets == (n + 1) * S), tickets
+        ctrl, tickets = _ctrl_words(ws, groups)
+        assert ctrl[0] == 0, "a look-back launch failed to chain its segments"
+        assert ctrl[1] == n + 1, ctrl
+        assert np.all(tickets == S), tickets
+        assert W.wkv_workspace_status(ws) == 0
+
+
+def test_lookback_workspace_reused_across_sizes_without_clearing():
+    """One workspace (zero-filled once) serves look-back launches of other
+    sizes in turn, and the first size again: every result matches the oracle
+    (words a launch of other sizes left behind carry an older epoch)."""
+    cases = [(2, 3000, 96), (1, 4097, 40), (3, 600, 64), (2, 3000, 96)]
+    nbytes = max(W.wkv_workspace_size(B, T, C, W.WKV_IO_F32, "lookback") for B, T, C in cases)
+    ws = W.new_workspace(nbytes, "cuda")
+    for i, (B, T, C) in enumerate(cases):
+        say(f"look-back workspace reuse {i}: B={B} T={T} C={C}")
+        w, u, k, v = make_case(WL3, B, T, C, layer=i)
+        ref, rst = wkv_recurrent(w, u, k, v)
+        out, st = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        assert_out_close(host64(out), ref, v, F32_TOL)
+        assert_state_close(host64(st), rst, F32_TOL)
+        assert W.wkv_workspace_status(ws) == 0
+
+
+def test_lookback_wait_that_runs_out_is_reported_and_poisons_outputs():
+    """Forced from the host through the workspace's test words: with nothing
+    published and a bound of 64 polls, every wait for an earlier segment runs
+    out. The launch still finishes, wkv_workspace_status reports
+    WKV_ERR_LOOKBACK, the first segment's outputs are right and every later
+    one is NaN (never a plausible value); with the test words cleared the same
+    workspace works again."""
+    B, T, C = 2, 3000, 96
+    w, u, k, v = make_case(WL3, B, T, C)
+    ref, _ = wkv_recurrent(w, u, k, v)
+    ws = W.new_workspace(W.wkv_workspace_size(B, T, C, W.WKV_IO_F32, "lookback"), "cuda")
+    ctl = ws[:16].view(torch.int32)
+    ctl[2] = 1    # publish nothing
+    ctl[3] = 64   # polls before a wait gives up
+    say("look-back forced wait time-out")
+    out, _ = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
+                              workspace=ws)
+    torch.cuda.synchronize()
+    got = host64(out)
+    assert W.wkv_workspace_status(ws) == W.WKV_ERR_LOOKBACK
+    assert W.wkv_workspace_status(ws, clear=True) == W.WKV_ERR_LOOKBACK
+    assert W.wkv_workspace_status(ws) == 0
+    assert_out_close(got[:, :256], ref[:, :256], v[:, :256], F32_TOL)
+    assert np.isnan(got[:, 256:]).all()
+    with pytest.raises(W.WKVError):
+        W.check_workspace(_poisoned_again(ws, w, u, k, v))
+    ctl[2] = 0
+    ctl[3] = 0
+    W.wkv_workspace_status(ws, clear=True)
+    out, _ = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
+                              workspace=ws)
+    torch.cuda.synchronize()
+    assert_out_close(host64(out), ref, v, F32_TOL)
+    assert W.wkv_workspace_status(ws) == 0
+
+
+def _poisoned_again(ws, w, u, k, v):
+    """One more launch with the test words still set; returns the workspace."""
+    W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback", workspace=ws)
+    return ws
 
 
 def test_decode_in_hip_graph_replays_match_eager():

@@ -25,7 +25,9 @@ from ._lib import (  # noqa: F401
     WKV_PATH_SEQ,
     ForwardCall,
     StepCall,
+    WKV_ERR_LOOKBACK,
     WKVError,
+    check_workspace,
     forward,
     load_library,
     new_workspace,
@@ -56,4 +58,5 @@ from ._lib import (  # noqa: F401
     wkv_step_dd,
     wkv_step_gated,
     wkv_workspace_size,
+    wkv_workspace_status,
 )

@@ -58,6 +58,7 @@ def load_library() -> ctypes.CDLL:
         "wkv_forward_ex": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp],
         "wkv_forward_ws": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp, i64, vp],
         "wkv_workspace_size": [i64, i64, i64, ci, ci],
+        "wkv_workspace_status": [vp, i64, ci, vp],
         "wkv_select_path": [i64, i64, i64, ci],
         "wkv_step": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
         "wkv_step_bf16": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
@@ -139,6 +140,33 @@ def wkv_workspace_size(B: int, T: int, C: int, io: int = WKV_IO_F32, path: str =
     return int(r)
 
 
+WKV_ERR_LOOKBACK = 9
+
+
+def wkv_workspace_status(workspace: torch.Tensor, clear: bool = False, stream=None) -> int:
+    """wkv_workspace_status: waits for `stream` (default: the current one) and
+    returns 0 if no look-back launch with this workspace failed to chain its
+    segments since its error word was last cleared, WKV_ERR_LOOKBACK if one did
+    (clear=True then resets the word). Other codes raise WKVError."""
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    with torch.cuda.device(workspace.device):
+        strm = torch.cuda.current_stream(workspace.device) if stream is None else stream
+        st = load_library().wkv_workspace_status(_ptr(workspace), workspace.numel(), int(clear),
+                                                 ctypes.c_void_p(strm.cuda_stream))
+    if st not in (0, WKV_ERR_LOOKBACK):
+        _check(st, "wkv_workspace_status")
+    return st
+
+
+def check_workspace(workspace: Optional[torch.Tensor], stream=None) -> None:
+    """Raises WKVError (and clears the word) if a look-back launch with this
+    workspace failed to chain its segments; its outputs past the failure are
+    NaN. Synchronises the stream."""
+    if workspace is not None and wkv_workspace_status(workspace, True, stream) != 0:
+        raise WKVError("wkv_forward_ws", WKV_ERR_LOOKBACK)
+
+
 def new_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     """A zero-filled device workspace of at least nbytes (None for 0 bytes).
     torch's allocator returns blocks aligned to at least 256 bytes."""
@@ -169,8 +197,9 @@ def _cached_workspace(nbytes: int, device, stream, shape) -> Optional[torch.Tens
 def wkv_forward_ws(w, u, k, v, state_in=None, out=None, state_out=None, *, path="auto",
                    workspace=None, want_state=True, stream=None):
     """wkv_forward_ws: wkv_forward_ex with a device workspace (a uint8 tensor from
-    new_workspace, zero-filled before its first use with these sizes). With
-    workspace=None one is taken from a per-(stream, sizes) cache."""
+    new_workspace, zero-filled once before its first use). With workspace=None
+    one is taken from a per-(stream, sizes) cache and checked after the call
+    (see wkv_forward_ex)."""
     return wkv_forward_ex(w, u, k, v, state_in, out, state_out, path=path, workspace=workspace,
                           want_state=want_state, stream=stream)
 
@@ -185,7 +214,10 @@ def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.T
     (out, state_out); state_out is None when want_state is False and none was
     given. path: "auto", "seq", "chunk" or "lookback". Calls go through
     wkv_forward_ws, so "auto" may pick the look-back scan; its workspace is
-    `workspace` or one cached for the stream."""
+    `workspace` or one cached for the stream. A cached workspace is checked
+    after the call (check_workspace: the stream is synchronised and a failed
+    look-back chain raises WKVError); a workspace passed in is the caller's to
+    check with wkv_workspace_status."""
     lib = load_library()
     if k.dim() != 3:
         raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
@@ -213,7 +245,8 @@ def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.T
     io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
     with torch.cuda.device(dev):
         strm = torch.cuda.current_stream(dev) if stream is None else stream
-        if workspace is None:
+        owned = workspace is None
+        if owned:
             workspace = _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
                                           (B, T, C, io, path))
         elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -222,7 +255,9 @@ def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.T
                                 _ptr(out), _ptr(state_out), io, _PATHS[path], _ptr(workspace),
                                 0 if workspace is None else workspace.numel(),
                                 ctypes.c_void_p(strm.cuda_stream))
-    _check(st, "wkv_forward_ws")
+        _check(st, "wkv_forward_ws")
+        if owned:
+            check_workspace(workspace, strm)
     return out, state_out
 
 
@@ -484,14 +519,17 @@ def wkv_forward_gated(w, u, k, v, r, state_in=None, out=None, state_out=None, *,
     io = WKV_IO_BF16 if k.dtype == torch.bfloat16 else WKV_IO_F32
     with torch.cuda.device(dev):
         strm = torch.cuda.current_stream(dev) if stream is None else stream
-        if workspace is None:
+        owned = workspace is None
+        if owned:
             workspace = _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
                                           (B, T, C, io, path))
         st = lib.wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                    _ptr(state_in), _ptr(out), _ptr(state_out), io, _PATHS[path],
                                    _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                    ctypes.c_void_p(strm.cuda_stream))
-    _check(st, "wkv_forward_gated")
+        _check(st, "wkv_forward_gated")
+        if owned:
+            check_workspace(workspace, strm)
     return out, state_out
 
 
@@ -819,6 +857,11 @@ class ForwardCall:
         if st != 0:
             _check(st, "wkv_forward_ws")
         return self.out, self.state_out
+
+    def check(self, stream=None) -> None:
+        """Raises WKVError if a look-back launch of this call failed to chain
+        its segments since the last check (synchronises the stream)."""
+        check_workspace(self.workspace, stream)
 
 
 class StepCall:

@@ -749,8 +749,30 @@ const char* wkv_status_string(int status) {
     case WKV_ERR_DEVICE: return "WKV_ERR_DEVICE: no usable HIP device";
     case WKV_ERR_ARG: return "WKV_ERR_ARG: io or path out of range";
     case WKV_ERR_WORKSPACE: return "WKV_ERR_WORKSPACE: the kernel needs a (larger) workspace";
+    case WKV_ERR_LOOKBACK:
+      return "WKV_ERR_LOOKBACK: a look-back launch could not chain its segments; outputs past the "
+             "failure are NaN or unwritten";
     default: return "unknown wkv_status";
   }
+}
+
+int wkv_workspace_status(void* workspace, int64_t workspace_bytes, int clear,
+                         hipStream_t stream) {
+  if (workspace == nullptr) return WKV_ERR_NULL;
+  if (workspace_bytes < 16) return WKV_ERR_WORKSPACE;
+  if (misaligned(workspace, 256)) return WKV_ERR_ALIGN;
+  // the error word is the first 32-bit word of the workspace
+  uint32_t err = 0;
+  hipError_t e = hipMemcpyAsync(&err, workspace, sizeof(err), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(WKV_ERR_LAUNCH, e);
+  if (err != 0 && clear != 0) {
+    const uint32_t zero = 0;
+    e = hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(WKV_ERR_LAUNCH, e);
+  }
+  return err != 0 ? WKV_ERR_LOOKBACK : WKV_OK;
 }
 
 int wkv_last_hip_error(void) { return g_last_hip_error; }

@@ -30,20 +30,21 @@
 //   4. every thread re-runs the recurrence over its registers from its
 //      sub-chunk's start state and writes the outputs.
 //
-// Publication uses 64-bit words tagged with a per-launch epoch in their high
+// Publication uses 64-bit words tagged with the launch's epoch in their high
 // half and written/read with device-scope relaxed atomics: a value is
 // accepted only when its tag is the current epoch, so the words need no
-// fences and nothing has to be cleared between launches. Each channel group's
-// ticket counter is never reset: every launch advances it by exactly S (the
-// segments per group), so ticket t means segment t mod S of launch t / S, and
-// the launch number gives the epoch (a launch replayed from a HIP graph gets
-// a fresh one too, and a workgroup needs no second counter to read or to
-// update on exit). Tags are never 0, so a zero-filled workspace holds no valid
-// word. The workspace's layout depends on the problem's sizes: reusing it for
-// other sizes needs it zero-filled again. Inclusive prefixes keep their
-// maximum index-tracked (base, age), so chains of segments do not accumulate
-// rounding. Every wait is bounded: past the limit a workgroup flags an error
-// word in the workspace and proceeds, so the kernel always finishes.
+// fences and nothing has to be cleared between launches. Every launch first
+// runs a one-block set-up kernel that advances the workspace's epoch word and
+// rewinds the per-group ticket counters, so the epoch is unique over the
+// workspace's whole life (whatever sizes it served before) and a group's
+// tickets are its segment numbers. Tags are never 0, so a zero-filled
+// workspace holds no valid word. Inclusive prefixes keep their maximum
+// index-tracked (base, age), so chains of segments do not accumulate
+// rounding. Every wait is bounded: past the limit a workgroup sets the
+// workspace's sticky error word and carries on with a NaN prefix, so the
+// kernel always finishes and the outputs that depended on the missing words
+// are NaN, never plausible values; the host reads the error word back with
+// wkv_workspace_status.
 //
 // While its ticket is in flight a workgroup already loads the tile of the
 // segment it will most likely get (blocks of a group start in index order),
@@ -69,6 +70,16 @@ constexpr int64_t anchor_spacing() { return (64 * W) / (kLbLC * V); }
 // launch sees (microseconds), small enough that a broken one still ends fast.
 constexpr uint32_t kSpinLimit = 1u << 14;
 
+// Control words at the start of the workspace (32-bit each): the sticky error
+// word (bit 0: a wait ran out; bit 1: a ticket beyond the last segment, i.e.
+// overlapping launches shared the workspace), the epoch of the latest launch, and two words only tests write: flags
+// (bit 0: publish nothing, so that every wait runs out) and a replacement for
+// kSpinLimit (0: none). Then one ticket counter per channel group, 16 bytes
+// apart.
+constexpr int kCtrlErr = 0, kCtrlEpoch = 1, kCtrlFlags = 2, kCtrlSpin = 3;
+constexpr uint32_t kFlagNoPublish = 1u;
+constexpr int kTicketStride = 4;  // in 32-bit words
+
 __device__ __forceinline__ void put(uint64_t* p, float x, uint32_t epoch) {
   const uint64_t word = (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(x);
   __hip_atomic_store(p, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -84,16 +95,28 @@ struct LbArgs {
   int64_t groups;       // G: channel groups (B * groups_per_row)
   int64_t segments;     // S: segments per lane
   int64_t gpr;          // channel groups per batch row
-  uint32_t* err;        // error word: bit 0 set when a wait ran out
-  uint64_t* tickets;    // ticket counter of group g at tickets[2 g]
+  uint32_t* ctrl;       // control words (kCtrl*), then the ticket counters
   uint64_t* agg;        // [S][G][CH][3] tile aggregates (n, d, m)
   uint64_t* inc;        // [S][G][CH][4] inclusive prefixes (n, d, base, age)
-  uint32_t epoch;       // tag of this launch's words (never 0)
+  uint32_t epoch;       // tag of this launch's words (never 0), read by the kernel
+  uint32_t spin_limit;  // polls before a wait gives up, read by the kernel
+  bool publish;         // false only when a test asked for it, read by the kernel
 };
 
+// Set-up before every look-back launch (one block): the next epoch (never 0)
+// and every group's ticket counter back to 0.
+__global__ __launch_bounds__(256) void wkv_lb_prepare(uint32_t* __restrict__ ctrl, int64_t groups) {
+  uint32_t* tickets = ctrl + kTicketStride;
+  for (int64_t g = threadIdx.x; g < groups; g += 256) tickets[g * kTicketStride] = 0u;
+  if (threadIdx.x == 0) {
+    const uint32_t e = ctrl[kCtrlEpoch] + 1u;
+    ctrl[kCtrlEpoch] = e == 0u ? 1u : e;
+  }
+}
+
 // Wait (bounded) until the n tagged words at p carry this launch's epoch and
-// return their values. Past the limit the error word is set and zeros are
-// returned, so the kernel still finishes.
+// return their values. Past the limit the error word is set and NaNs are
+// returned, so the kernel still finishes and what depends on them is NaN.
 template <int N>
 __device__ __forceinline__ void wait_words(const LbArgs& a, uint64_t* p, float (&x)[N]) {
   for (uint32_t spin = 0;; ++spin) {
@@ -101,10 +124,10 @@ __device__ __forceinline__ void wait_words(const LbArgs& a, uint64_t* p, float (
 #pragma unroll
     for (int i = 0; i < N; ++i) ok = get(p + i, a.epoch, x[i]) && ok;
     if (ok) return;
-    if (spin >= kSpinLimit) {
-      __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (spin >= a.spin_limit) {
+      __hip_atomic_fetch_or(a.ctrl + kCtrlErr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int i = 0; i < N; ++i) x[i] = 0.0f;
+      for (int i = 0; i < N; ++i) x[i] = __builtin_nanf("");
       return;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -166,7 +189,7 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   constexpr int64_t K = anchor_spacing<V, W>();
   const bool is_anchor = s % K == 0;
   const int64_t anchor = s == 0 ? 0 : ((s - 1) / K) * K;
-  if (s > 0 && !is_anchor && wave == 0 && sl == 0) {
+  if (a.publish && s > 0 && !is_anchor && wave == 0 && sl == 0) {
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint64_t* pa = a.agg + ((s * a.groups + g) * CH + cl * V + j) * 3;
@@ -208,7 +231,7 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
       }
       Lane incl = x;
       lane_absorb(incl, whole[j], wd[j]);
-      if (is_anchor) {
+      if (is_anchor && a.publish) {
         uint64_t* pi = a.inc + ((s * a.groups + g) * CH + idx) * 4;
         put(pi, incl.n, a.epoch);
         put(pi + 1, incl.d, a.epoch);
@@ -275,12 +298,14 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
                         ? o
                         : (o & ~int64_t{kNumXcd - 1}) | (((o & (kNumXcd - 1)) + (o / kNumXcd)) &
                                                          (kNumXcd - 1));
-  const int64_t S = a.segments;
+  __shared__ uint32_t spin_s, flags_s;
   if (threadIdx.x == 0) {
-    const uint64_t t =
-        __hip_atomic_fetch_add(a.tickets + 2 * g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    seg_s = static_cast<uint32_t>(t % static_cast<uint64_t>(S));
-    epoch_s = static_cast<uint32_t>((t / static_cast<uint64_t>(S)) % 0xffffffffull) + 1u;
+    uint32_t* tickets = a.ctrl + kTicketStride;
+    seg_s = __hip_atomic_fetch_add(tickets + g * kTicketStride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    epoch_s = __hip_atomic_load(a.ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flags_s = __hip_atomic_load(a.ctrl + kCtrlFlags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    spin_s = __hip_atomic_load(a.ctrl + kCtrlSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // prefetch the likely segment's tile while the ticket is in flight: the
   // group's blocks are one per row, so this block is most likely its row-th
@@ -294,6 +319,17 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   }
   __syncthreads();
   a.epoch = epoch_s;
+  a.spin_limit = spin_s != 0u ? spin_s : kSpinLimit;
+  a.publish = (flags_s & kFlagNoPublish) == 0u;
+  // the set-up kernel rewound the counters: exactly S workgroups per group
+  // take tickets 0 .. S-1, so the ticket is the segment. A ticket beyond that
+  // means another launch shares the workspace at the same time: flag it and
+  // leave (the waits that depended on this workgroup run out and flag too).
+  if (seg_s >= static_cast<uint64_t>(a.segments)) {
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_or(a.ctrl + kCtrlErr, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   const int64_t s = seg_s;
   const int64_t off = lb_offset<V, W, L>(s, g, a.gpr, T, C);
   if ((s + 1) * TL <= T) {
@@ -325,10 +361,12 @@ auto lb_dispatch(int64_t T, F&& f) {
   return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 32>{});
 }
 
-// Control words: the error word, then one 64-bit ticket counter per channel
-// group (16 bytes apart), rounded up to 256 bytes so the tagged words after
-// them stay aligned.
-int64_t lookback_ctrl_bytes(int64_t groups) { return ((16 + 16 * groups + 255) / 256) * 256; }
+// Control words (16 bytes), then one ticket counter per channel group (16
+// bytes apart), rounded up to 256 bytes so the tagged words after them stay
+// aligned.
+int64_t lookback_ctrl_bytes(int64_t groups) {
+  return ((16 + 4 * kTicketStride * groups + 255) / 256) * 256;
+}
 
 template <int V, int W, int L>
 int64_t lb_bytes(int64_t B, int64_t T, int64_t C) {
@@ -353,13 +391,15 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
   la.groups = groups;
   la.segments = segments;
   la.gpr = gpr;
-  la.err = ws.ctrl;
-  la.tickets = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.ctrl) + 16);
+  la.ctrl = ws.ctrl;
   uint64_t* slots = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws.ctrl) +
                                                 lookback_ctrl_bytes(groups));
   la.agg = slots;
   la.inc = slots + items * CH * 3;
-  la.epoch = 0;  // derived from the ticket by the kernel
+  la.epoch = 0;          // these three are read from the control words by the kernel
+  la.spin_limit = kSpinLimit;
+  la.publish = true;
+  hipLaunchKernelGGL(wkv_lb_prepare, dim3(1), dim3(256), 0, st, ws.ctrl, groups);
   const auto* kk = static_cast<const typename IoT::elem*>(a.k);
   const auto* vv = static_cast<const typename IoT::elem*>(a.v);
   const auto* rr = static_cast<const typename IoT::elem*>(a.r);
