@@ -159,6 +159,27 @@ int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float*
 int wkv_workspace_status(void* workspace, int64_t workspace_bytes, int clear,
                          hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * wkv_forward_ws without the workspace argument. The look-back scan's
+ * workspace is instead a static device array inside the library, 32 MiB per
+ * device (held from the library's load to the end of the process), found with
+ * hipGetSymbolAddress on the first call on each device, which also enqueues a
+ * one-time zero fill of it on `stream`. No call allocates memory.
+ *   path LOOKBACK whose workspace (wkv_workspace_size) exceeds 32 MiB:
+ *        WKV_ERR_WORKSPACE. AUTO uses the array when its choice is the
+ *        look-back scan and it fits, and otherwise picks among the kernels
+ *        that need no workspace; SEQ and CHUNK never touch it.
+ * Every call on one device shares that device's array: calls that may
+ * overlap in time on one device (other streams, other threads) race on it
+ * and must not be made; calls in order on one stream are fine, with any
+ * sizes. A look-back chain that fails anyway (possible only when calls
+ * overlap) leaves NaN in the affected outputs. Other arguments, layout and
+ * errors as wkv_forward_ws. */
+int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                        const void* k, const void* v, const float* state_in, void* out,
+                        float* state_out, int io, int path, hipStream_t stream);
+
 /* As wkv_forward_ws with the output gated by the receptance:
  * out_t = sigmoid(r_t) * wkv_t per element (page "RWKV-v6 Architecture:
  * Attention-Free Linear Transformers", the output equation of its recurrence;

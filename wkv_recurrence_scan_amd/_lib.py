@@ -59,6 +59,7 @@ def load_library() -> ctypes.CDLL:
         "wkv_forward_ws": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp, i64, vp],
         "wkv_workspace_size": [i64, i64, i64, ci, ci],
         "wkv_workspace_status": [vp, i64, ci, vp],
+        "wkv_forward_noalloc": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp],
         "wkv_select_path": [i64, i64, i64, ci],
         "wkv_step": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
         "wkv_step_bf16": [i64, i64, vp, vp, vp, vp, vp, vp, vp],

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "wkv_internal.h"
 
@@ -183,6 +184,42 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
     e = wkv::launch_lookback(a, io, vec, ws, stream);
   }
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
+// Device scratch of wkv_forward_noalloc, for callers that cannot allocate:
+// the look-back scan's workspace, one copy per device (each device that loads
+// the library holds it until the process ends). Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, once per device, and is
+// kept in g_scratch.
+constexpr int64_t kScratchBytes = int64_t{32} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// This device's scratch (dev must be current), or nullptr with *e set. The
+// first use on a device also enqueues one zero fill of the whole array on
+// `stream` (a kernel: the look-back words' tags must start at 0).
+void* scratch_on(int dev, hipStream_t stream, hipError_t* e) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  *e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*e != hipSuccess || p == nullptr) {
+    if (*e == hipSuccess) *e = hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  *e = wkv::launch_zero_fill(p, kScratchBytes, stream);
+  if (*e != hipSuccess) return nullptr;
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* k, const void* v,
@@ -648,6 +685,34 @@ int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float*
                    int path, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
                       workspace, workspace_bytes, stream);
+}
+
+int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                        const void* k, const void* v, const float* state_in, void* out,
+                        float* state_out, int io, int path, hipStream_t stream) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
+  if (path < WKV_PATH_AUTO || path > WKV_PATH_LOOKBACK) return WKV_ERR_ARG;
+  if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
+  if (B == 0 || C == 0 || T == 0)
+    return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
+                        nullptr, 0, stream);
+  // the scratch serves when the look-back scan may run and fits in it: an
+  // explicit LOOKBACK beyond kScratchBytes is WKV_ERR_WORKSPACE, AUTO then
+  // chooses among the kernels that need none
+  int64_t seq;
+  if (!mul3(B, T, C, &seq) || seq > kMaxBytes) return WKV_ERR_DIM;
+  const int64_t need = lookback_bytes(io, B, T, C);
+  if (path == WKV_PATH_LOOKBACK && need > kScratchBytes) return WKV_ERR_WORKSPACE;
+  if (path == WKV_PATH_SEQ || path == WKV_PATH_CHUNK || need > kScratchBytes)
+    return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
+                        nullptr, 0, stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
+  void* ws = scratch_on(dev, stream, &e);
+  if (ws == nullptr) return fail(WKV_ERR_LAUNCH, e);
+  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
+                      ws, kScratchBytes, stream);
 }
 
 int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float* w, const float* u,

@@ -53,6 +53,8 @@ struct LbWorkspace {
 int lookback_vec_width(int io, int64_t C, const FwdArgs& a);
 int64_t lookback_workspace_bytes(int vec, int64_t B, int64_t T, int64_t C);
 hipError_t launch_lookback(const FwdArgs& a, int io, int vec, const LbWorkspace& ws, hipStream_t s);
+// Zero-fills bytes (a multiple of 16) at p with a kernel on stream s.
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s);
 
 // Backward pass (fp32): gradients for w, u, k, v and the initial state.
 struct BwdArgs {

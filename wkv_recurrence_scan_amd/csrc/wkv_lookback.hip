@@ -425,6 +425,22 @@ hipError_t launch_lb_v(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
 
 }  // namespace
 
+namespace {
+__global__ __launch_bounds__(256) void wkv_zero_fill(uint4* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t{256} + threadIdx.x; i < n; i += int64_t{gridDim.x} * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 16;
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(wkv_zero_fill, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<uint4*>(p), n);
+  return hipGetLastError();
+}
+
 int lookback_vec_width(int io, int64_t C, const FwdArgs& a) { return chunk_vec_width(io, C, a); }
 
 int64_t lookback_workspace_bytes(int vec, int64_t B, int64_t T, int64_t C) {
