@@ -123,25 +123,27 @@ int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float*
 /* As wkv_forward_ex with a device workspace, which the LOOKBACK kernel needs
  * (and AUTO then may choose).
  *   workspace        device memory of at least wkv_workspace_size(...) bytes,
- *                    256-byte aligned, owned by the caller. Zero-fill it once
- *                    before its first use; after that every call leaves it
- *                    ready for the next one, with the same sizes or others
+ *                    256-byte aligned, owned by the caller. It must be
+ *                    zero-filled before its first use, and again before it
+ *                    serves sizes with another look-back layout; every call
+ *                    leaves it ready for the next call with the same sizes
  *                    (no clearing in between, HIP graph replays included).
  *                    Calls that may run concurrently must not share a
  *                    workspace. It must not overlap any other argument.
  *   workspace_bytes  its size in bytes.
  * A call whose kernel needs no workspace ignores it (it may be NULL).
  *
- * Layout of the workspace's first 16 bytes (32-bit words): [0] the sticky
- * error word read by wkv_workspace_status (bit 0: a wait for an earlier
- * segment ran out; bit 1: overlapping calls shared the workspace), [1] the
- * epoch of the latest launch, [2] and [3] zero in normal use (tests set [2]
- * bit 0, "publish nothing", and [3], a smaller bound on each wait, to force
- * the failure path). Each LOOKBACK launch enqueues a one-block set-up kernel
- * (next epoch, ticket counters rewound) before the scan itself. A wait that
- * runs out (it cannot in a correct launch) does not hang the kernel: it sets
- * the error word and continues with NaN in place of the missing prefix, so
- * every output that depended on it is NaN. */
+ * Misuse is reported, never silent: the first LOOKBACK launch on a
+ * zero-filled workspace claims it for its layout, and a later launch with
+ * another layout (other sizes) on the same, uncleared workspace, or a wait
+ * for an earlier segment that runs out (as when overlapping calls share a
+ * workspace), sets the workspace's error word and writes NaN where the
+ * missing data would have gone, so the affected outputs are NaN rather than
+ * plausible values. wkv_workspace_status reads the word. Layout of the
+ * first 16 bytes (32-bit words): [0] the error word (bit 0: a wait ran out;
+ * bit 2: another layout's claim), [1] zero in normal use (tests set bit 0,
+ * "publish nothing", and a smaller bound on each wait in bits 8-31, to force
+ * the failure path), [2..3] the layout claim. */
 int wkv_forward_ws(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                    const void* k, const void* v, const float* state_in, void* out,
                    float* state_out, int io, int path, void* workspace,
@@ -164,8 +166,11 @@ int wkv_workspace_status(void* workspace, int64_t workspace_bytes, int clear,
  * wkv_forward_ws without the workspace argument. The look-back scan's
  * workspace is instead a static device array inside the library, 32 MiB per
  * device (held from the library's load to the end of the process), found with
- * hipGetSymbolAddress on the first call on each device, which also enqueues a
- * one-time zero fill of it on `stream`. No call allocates memory.
+ * hipGetSymbolAddress on the first call on each device. No call allocates
+ * memory. Since calls may come with any sizes and in any order (graph
+ * replays included), every call that runs the look-back scan first enqueues
+ * a kernel that zero-fills the part of the array it will use (the scan's
+ * workspace size), then the scan.
  *   path LOOKBACK whose workspace (wkv_workspace_size) exceeds 32 MiB:
  *        WKV_ERR_WORKSPACE. AUTO uses the array when its choice is the
  *        look-back scan and it fits, and otherwise picks among the kernels
@@ -173,9 +178,7 @@ int wkv_workspace_status(void* workspace, int64_t workspace_bytes, int clear,
  * Every call on one device shares that device's array: calls that may
  * overlap in time on one device (other streams, other threads) race on it
  * and must not be made; calls in order on one stream are fine, with any
- * sizes. A look-back chain that fails anyway (possible only when calls
- * overlap) leaves NaN in the affected outputs. Other arguments, layout and
- * errors as wkv_forward_ws. */
+ * sizes. Other arguments, layout and errors as wkv_forward_ws. */
 int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
                         const void* k, const void* v, const float* state_in, void* out,
                         float* state_out, int io, int path, hipStream_t stream);

@@ -77,7 +77,8 @@ def test_workspace_size_and_requirement_without_device():
     assert lib.wkv_workspace_size(8, 1024, 768, 0, chunk) == 0
     n = lib.wkv_workspace_size(8, 1024, 768, 0, lookback)
     # control words (16 B + 16 B per 32-channel group, rounded up to 256 B) and
-    # 7 tagged 8-byte words per (lane, segment); T = 1024 uses 256-token segments
+    # 7 tagged 8-byte words per (lane, segment): an aggregate (n, d, m) and an
+    # inclusive prefix (n, d, base, age); T = 1024 uses 256-token segments
     groups = 8 * 768 // 32
     assert n == ((16 + 16 * groups + 255) // 256) * 256 + 8 * 768 * (1024 // 256) * 7 * 8
     assert lib.wkv_workspace_size(8, 0, 768, 0, lookback) == 0

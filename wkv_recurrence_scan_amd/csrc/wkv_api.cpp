@@ -89,7 +89,7 @@ int64_t ckpt_bytes(int64_t B, int64_t T, int64_t C) {
 int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u, const void* k,
                  const void* v, const void* r, bool gated, const float* state_in, void* out,
                  float* state_out, int io, int path, void* workspace, int64_t workspace_bytes,
-                 hipStream_t stream, float* ckpt = nullptr) {
+                 hipStream_t stream, float* ckpt = nullptr, bool check_only = false) {
   if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
   if (path < WKV_PATH_AUTO || path > WKV_PATH_LOOKBACK) return WKV_ERR_ARG;
   if (B < 0 || T < 0 || C < 0) return WKV_ERR_DIM;
@@ -161,6 +161,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
                                          wkv::lookback_vec_width(io, C, a), B, T, C)))
     return WKV_ERR_WORKSPACE;
 
+  if (check_only) return WKV_OK;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
@@ -198,10 +199,8 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 std::mutex g_scratch_mu;
 std::atomic<void*> g_scratch[kMaxDevices];
 
-// This device's scratch (dev must be current), or nullptr with *e set. The
-// first use on a device also enqueues one zero fill of the whole array on
-// `stream` (a kernel: the look-back words' tags must start at 0).
-void* scratch_on(int dev, hipStream_t stream, hipError_t* e) {
+// This device's scratch (dev must be current), or nullptr with *e set.
+void* scratch_on(int dev, hipError_t* e) {
   if (dev < 0 || dev >= kMaxDevices) {
     *e = hipErrorInvalidDevice;
     return nullptr;
@@ -216,8 +215,6 @@ void* scratch_on(int dev, hipStream_t stream, hipError_t* e) {
     if (*e == hipSuccess) *e = hipErrorInvalidSymbol;
     return nullptr;
   }
-  *e = wkv::launch_zero_fill(p, kScratchBytes, stream);
-  if (*e != hipSuccess) return nullptr;
   g_scratch[dev].store(p, std::memory_order_release);
   return p;
 }
@@ -696,23 +693,34 @@ int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w, const f
   if (B == 0 || C == 0 || T == 0)
     return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
                         nullptr, 0, stream);
-  // the scratch serves when the look-back scan may run and fits in it: an
+  // the scratch serves when the look-back scan runs and fits in it: an
   // explicit LOOKBACK beyond kScratchBytes is WKV_ERR_WORKSPACE, AUTO then
   // chooses among the kernels that need none
   int64_t seq;
   if (!mul3(B, T, C, &seq) || seq > kMaxBytes) return WKV_ERR_DIM;
   const int64_t need = lookback_bytes(io, B, T, C);
   if (path == WKV_PATH_LOOKBACK && need > kScratchBytes) return WKV_ERR_WORKSPACE;
-  if (path == WKV_PATH_SEQ || path == WKV_PATH_CHUNK || need > kScratchBytes)
-    return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
-                        nullptr, 0, stream);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
-  void* ws = scratch_on(dev, stream, &e);
+  const bool fits = need <= kScratchBytes;
+  const int chosen = path == WKV_PATH_AUTO ? choose_path(B, T, C, io, dev, fits) : path;
+  if (chosen != WKV_PATH_LOOKBACK)
+    return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, chosen,
+                        nullptr, 0, stream);
+  void* ws = scratch_on(dev, &e);
   if (ws == nullptr) return fail(WKV_ERR_LAUNCH, e);
-  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, path,
-                      ws, kScratchBytes, stream);
+  // Calls may come with any sizes and in any order (HIP graph replays
+  // included), so every look-back call starts from a zero-filled workspace:
+  // the part of the array it uses is cleared first, in stream order, by a
+  // kernel. Arguments are validated before anything is enqueued.
+  const int pre = forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io,
+                               WKV_PATH_LOOKBACK, ws, kScratchBytes, stream, nullptr, true);
+  if (pre != WKV_OK) return pre;
+  e = wkv::launch_zero_fill(ws, (need + 15) / 16 * 16, stream);
+  if (e != hipSuccess) return fail(WKV_ERR_LAUNCH, e);
+  return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io,
+                      WKV_PATH_LOOKBACK, ws, kScratchBytes, stream);
 }
 
 int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float* w, const float* u,

@@ -265,9 +265,10 @@ __device__ __forceinline__ Suffix suffix_init(const float* __restrict__ state_ou
 
 // Forward state advance over chunks [j0, j1) (all full), storing the state in
 // front of each chunk when CKPT. Two register buffers used alternately: the
-// next chunk's loads are issued before the current one is consumed (the last
-// chunk re-reads itself, so the loads are unconditional and the compiler's
-// counter waits stay exact).
+// next chunk's loads are issued before the current one is consumed,
+// unconditionally inside the loop so that the compiler's counter waits stay
+// exact; the last one or two chunks are consumed after it, so no chunk is
+// read twice.
 template <bool CKPT>
 __device__ __forceinline__ void forward_chunks(Lane& s, const LaneIo& io, int64_t j0, int64_t j1,
                                                float w, float4* __restrict__ ckpt,
@@ -286,12 +287,19 @@ __device__ __forceinline__ void forward_chunks(Lane& s, const LaneIo& io, int64_
     for (int i = 0; i < kLc; ++i) lane_advance(s, kk[i], vv[i], w);
   };
   if (j0 < j1) load2(ka, va, j0);
-  for (int64_t j = j0; j < j1; j += 2) {
-    load2(kb, vb, j + 1 < j1 ? j + 1 : j);
+  int64_t j = j0;
+  for (; j + 2 < j1; j += 2) {
+    load2(kb, vb, j + 1);
     advance(ka, va, j);
-    if (j + 1 >= j1) break;
-    load2(ka, va, j + 2 < j1 ? j + 2 : j + 1);
+    load2(ka, va, j + 2);
     advance(kb, vb, j + 1);
+  }
+  if (j + 1 < j1) {  // two left
+    load2(kb, vb, j + 1);
+    advance(ka, va, j);
+    advance(kb, vb, j + 1);
+  } else if (j < j1) {  // one left
+    advance(ka, va, j);
   }
 }
 
@@ -561,20 +569,31 @@ __global__ __launch_bounds__(kBwdThreads) void wkv_bwd_seg_sums_kernel(BwdKernel
   auto save = [&](int64_t j) {
     if constexpr (!GIVEN) a.ckpt[j * lanes + lane] = make_float4(x.n, x.d, x.base, x.age);
   };
-  // full chunks through two buffers with no branch around their loads (the
-  // last re-reads itself), then the sequence's partial last chunk on its own
+  // full chunks through two buffers with no branch around their loads inside
+  // the loop (the last one or two after it, so none is read twice), then the
+  // sequence's partial last chunk on its own
   const int64_t jf = j1 < io.nfull ? j1 : io.nfull;
   if (j0 < jf) {
     Chunk<G> A, Bf;
     load(A, j0, kLc);
-    for (int64_t j = j0; j < jf; j += 2) {
-      load(Bf, j + 1 < jf ? j + 1 : j, kLc);
+    int64_t j = j0;
+    for (; j + 2 < jf; j += 2) {
+      load(Bf, j + 1, kLc);
       save(j);
       process(A, kLc, std::true_type{});
-      if (j + 1 >= jf) break;
-      load(A, j + 2 < jf ? j + 2 : j + 1, kLc);
+      load(A, j + 2, kLc);
       save(j + 1);
       process(Bf, kLc, std::true_type{});
+    }
+    if (j + 1 < jf) {  // two left
+      load(Bf, j + 1, kLc);
+      save(j);
+      process(A, kLc, std::true_type{});
+      save(j + 1);
+      process(Bf, kLc, std::true_type{});
+    } else if (j < jf) {  // one left
+      save(j);
+      process(A, kLc, std::true_type{});
     }
   }
   if (j1 > jf) {
@@ -756,21 +775,29 @@ __global__ __launch_bounds__(64 * W) void wkv_bwd_chunk_kernel(BwdKernelArgs a,
     parity ^= 1;
   }
   // full tiles, last first; the next one's loads are issued before the
-  // current one is processed (tile 0 re-reads itself at the end, so the loads
-  // are unconditional)
+  // current one is processed, unconditionally inside the loop, and the last
+  // one or two tiles are processed after it, so no tile is read twice
   ChunkL<L, G> A, Bf;
   float4 ca, cb;
+  auto run = [&](ChunkL<L, G>& ch, const float4& cp, int64_t tile) {
+    bwd_tile<W, L, false, G>(ch, cp, L, first(tile), T, carry, tot[parity], wc, uc, gw_acc,
+                             gu_acc, a, row + first(tile) * C, cvalid, wave, sl, cl);
+    parity ^= 1;
+  };
   if (full > 0) load(A, ca, full - 1);
-  for (int64_t tile = full - 1; tile >= 0; tile -= 2) {
-    load(Bf, cb, tile >= 1 ? tile - 1 : 0);
-    bwd_tile<W, L, false, G>(A, ca, L, first(tile), T, carry, tot[parity], wc, uc, gw_acc, gu_acc,
-                             a, row + first(tile) * C, cvalid, wave, sl, cl);
-    parity ^= 1;
-    if (tile < 1) break;
-    load(A, ca, tile >= 2 ? tile - 2 : 0);
-    bwd_tile<W, L, false, G>(Bf, cb, L, first(tile - 1), T, carry, tot[parity], wc, uc, gw_acc,
-                             gu_acc, a, row + first(tile - 1) * C, cvalid, wave, sl, cl);
-    parity ^= 1;
+  int64_t tile = full - 1;
+  for (; tile >= 2; tile -= 2) {
+    load(Bf, cb, tile - 1);
+    run(A, ca, tile);
+    load(A, ca, tile - 2);
+    run(Bf, cb, tile - 1);
+  }
+  if (tile == 1) {  // two left
+    load(Bf, cb, 0);
+    run(A, ca, 1);
+    run(Bf, cb, 0);
+  } else if (tile == 0) {  // one left
+    run(A, ca, 0);
   }
   // carry: the sums at position -1 (every thread holds the same)
   if (sub == 0) {

@@ -172,21 +172,33 @@ __global__ __launch_bounds__(kDdSeqThreads) void wkv_dd_seq_kernel(
   typename IoT::elem* op = out + row;
 
   // two register buffers; the next block's loads are issued before the
-  // current block is computed (on every path: the last full block re-reads
-  // itself), so the counter-based waits stop at the block about to be used
+  // current block is computed, unconditionally inside the loop, so the
+  // counter-based waits stop at the block about to be used; the last one or
+  // two blocks are computed after the loop, so no block is read twice
   DdBlock<V, U> A, Bf;
-  const int64_t nblk = T / U;
-  if (nblk > 0) dd_seq_load<IoT, V, U>(A, kp, vp, wp, C);
-  for (int64_t blk = 0; blk < nblk; blk += 2) {
-    const int64_t nb = (blk + 1 < nblk ? blk + 1 : nblk - 1) * U;
-    dd_seq_load<IoT, V, U>(Bf, kp + nb * C, vp + nb * C, wp + nb * C, C);
+  auto load = [&](DdBlock<V, U>& x, int64_t blk) {
+    const int64_t t = blk * U;
+    dd_seq_load<IoT, V, U>(x, kp + t * C, vp + t * C, wp + t * C, C);
+  };
+  auto run = [&](const DdBlock<V, U>& x, int64_t blk) {
     if constexpr (CK) ckpt[blk * plane + lane0] = LaneCk{s[0].n, s[0].d, s[0].m};
-    dd_seq_compute<IoT, V, U>(A, s, ud, op + blk * U * C, C);
-    if (blk + 1 >= nblk) break;
-    const int64_t na = (blk + 2 < nblk ? blk + 2 : nblk - 1) * U;
-    dd_seq_load<IoT, V, U>(A, kp + na * C, vp + na * C, wp + na * C, C);
-    if constexpr (CK) ckpt[(blk + 1) * plane + lane0] = LaneCk{s[0].n, s[0].d, s[0].m};
-    dd_seq_compute<IoT, V, U>(Bf, s, ud, op + (blk + 1) * U * C, C);
+    dd_seq_compute<IoT, V, U>(x, s, ud, op + blk * U * C, C);
+  };
+  const int64_t nblk = T / U;
+  if (nblk > 0) load(A, 0);
+  int64_t blk = 0;
+  for (; blk + 2 < nblk; blk += 2) {
+    load(Bf, blk + 1);
+    run(A, blk);
+    load(A, blk + 2);
+    run(Bf, blk + 1);
+  }
+  if (blk + 1 < nblk) {  // two left
+    load(Bf, blk + 1);
+    run(A, blk);
+    run(Bf, blk + 1);
+  } else if (blk < nblk) {  // one left
+    run(A, blk);
   }
   if constexpr (CK) {
     if (nblk * U < T) ckpt[nblk * plane + lane0] = LaneCk{s[0].n, s[0].d, s[0].m};

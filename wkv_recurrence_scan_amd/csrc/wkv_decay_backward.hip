@@ -171,10 +171,10 @@ __device__ __forceinline__ int chunk_tokens(const DdBwdKernelArgs& a, int64_t j)
 // order (REV: last first). `full` is a compile-time flag: only the
 // sequence's last chunk can be partial; it is loaded and processed on its own
 // (first when REV), with a test per token. The full chunks run through two
-// register buffers with no branch around their loads: the next chunk's loads
-// are issued before the current one is processed, and past the end the last
-// chunk re-reads itself, so the compiler's counter waits stop at the chunk
-// about to be used.
+// register buffers with no branch around their loads inside the loop: the
+// next chunk's loads are issued before the current one is processed, so the
+// compiler's counter waits stop at the chunk about to be used; the last one
+// or two chunks are processed after the loop, so none is read twice.
 template <bool G, bool REV, typename F>
 __device__ __forceinline__ void db_walk(const DdBwdKernelArgs& a, const DbThread& th, F&& body) {
   const int64_t jf = th.j1 < a.T / kDbLc ? th.j1 : a.T / kDbLc;  // end of the full chunks
@@ -190,16 +190,23 @@ __device__ __forceinline__ void db_walk(const DdBwdKernelArgs& a, const DbThread
   if (n > 0) {
     auto chunk = [&](int64_t q) { return REV ? jf - 1 - q : th.j0 + q; };
     auto load = [&](DbChunk<G>& c, int64_t q) {
-      db_load<G, false>(c, a, th.row + chunk(q < n ? q : n - 1) * kDbLc * a.C, kDbLc);
+      db_load<G, false>(c, a, th.row + chunk(q) * kDbLc * a.C, kDbLc);
     };
     DbChunk<G> A, Bf;
     load(A, 0);
-    for (int64_t q = 0; q < n; q += 2) {
+    int64_t q = 0;
+    for (; q + 2 < n; q += 2) {
       load(Bf, q + 1);
       body(A, chunk(q), kDbLc, std::true_type{});
-      if (q + 1 >= n) break;
       load(A, q + 2);
       body(Bf, chunk(q + 1), kDbLc, std::true_type{});
+    }
+    if (q + 1 < n) {  // two left
+      load(Bf, q + 1);
+      body(A, chunk(q), kDbLc, std::true_type{});
+      body(Bf, chunk(q + 1), kDbLc, std::true_type{});
+    } else if (q < n) {  // one left
+      body(A, chunk(q), kDbLc, std::true_type{});
     }
   }
   if (!REV && partial) partial_chunk();

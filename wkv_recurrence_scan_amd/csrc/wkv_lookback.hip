@@ -30,21 +30,27 @@
 //   4. every thread re-runs the recurrence over its registers from its
 //      sub-chunk's start state and writes the outputs.
 //
-// Publication uses 64-bit words tagged with the launch's epoch in their high
+// Publication uses 64-bit words tagged with a per-launch epoch in their high
 // half and written/read with device-scope relaxed atomics: a value is
 // accepted only when its tag is the current epoch, so the words need no
-// fences and nothing has to be cleared between launches. Every launch first
-// runs a one-block set-up kernel that advances the workspace's epoch word and
-// rewinds the per-group ticket counters, so the epoch is unique over the
-// workspace's whole life (whatever sizes it served before) and a group's
-// tickets are its segment numbers. Tags are never 0, so a zero-filled
-// workspace holds no valid word. Inclusive prefixes keep their maximum
-// index-tracked (base, age), so chains of segments do not accumulate
-// rounding. Every wait is bounded: past the limit a workgroup sets the
-// workspace's sticky error word and carries on with a NaN prefix, so the
-// kernel always finishes and the outputs that depended on the missing words
-// are NaN, never plausible values; the host reads the error word back with
-// wkv_workspace_status.
+// fences and nothing has to be cleared between launches. Each channel group's
+// ticket counter is never reset: every launch advances it by exactly S (the
+// segments per group), so ticket t means segment t mod S of launch t / S, and
+// the launch number gives the epoch (a launch replayed from a HIP graph gets
+// a fresh one too, and nothing has to run before or after the scan to keep
+// the counters in step). That holds while a workspace keeps its layout (the
+// number of channel groups G and of segments S): the first launch on a
+// zero-filled workspace claims it for its (G, S) (one workgroup stores the
+// claim; the others only load it), and a launch with another (G, S) on the
+// same workspace finds the claim,
+// flags the error word and produces NaN instead of mixing with the other
+// layout's words. Tags are never 0, so a zero-filled workspace holds no valid
+// word. Inclusive prefixes keep their maximum index-tracked (base, age), so
+// chains of segments do not accumulate rounding. Every wait is bounded: past
+// the limit a workgroup sets the workspace's sticky error word and carries on
+// with a NaN prefix, so the kernel always finishes and the outputs that
+// depended on the missing words are NaN, never plausible values; the host
+// reads the error word back with wkv_workspace_status.
 //
 // While its ticket is in flight a workgroup already loads the tile of the
 // segment it will most likely get (blocks of a group start in index order),
@@ -70,14 +76,14 @@ constexpr int64_t anchor_spacing() { return (64 * W) / (kLbLC * V); }
 // launch sees (microseconds), small enough that a broken one still ends fast.
 constexpr uint32_t kSpinLimit = 1u << 14;
 
-// Control words at the start of the workspace (32-bit each): the sticky error
-// word (bit 0: a wait ran out; bit 1: a ticket beyond the last segment, i.e.
-// overlapping launches shared the workspace), the epoch of the latest launch, and two words only tests write: flags
-// (bit 0: publish nothing, so that every wait runs out) and a replacement for
-// kSpinLimit (0: none). Then one ticket counter per channel group, 16 bytes
-// apart.
-constexpr int kCtrlErr = 0, kCtrlEpoch = 1, kCtrlFlags = 2, kCtrlSpin = 3;
-constexpr uint32_t kFlagNoPublish = 1u;
+// Control words at the start of the workspace (32-bit each): [0] the sticky
+// error word (bit 0: a wait ran out, as when overlapping launches share the
+// workspace; bit 2: the workspace is claimed by another layout), [1] a word only tests write (bit 0: publish
+// nothing, so that every wait runs out; bits 8-31: a replacement for
+// kSpinLimit, 0 for none), [2..3] the 64-bit claim (G << 32 | S, 0 while
+// unclaimed). Then per channel group a 64-bit ticket counter, 16 bytes apart.
+constexpr int kCtrlErr = 0, kCtrlTest = 1, kCtrlClaim = 2;
+constexpr uint32_t kTestNoPublish = 1u;
 constexpr int kTicketStride = 4;  // in 32-bit words
 
 __device__ __forceinline__ void put(uint64_t* p, float x, uint32_t epoch) {
@@ -101,24 +107,19 @@ struct LbArgs {
   uint32_t epoch;       // tag of this launch's words (never 0), read by the kernel
   uint32_t spin_limit;  // polls before a wait gives up, read by the kernel
   bool publish;         // false only when a test asked for it, read by the kernel
+  bool claimed;         // false: the workspace belongs to another layout (read nothing)
 };
-
-// Set-up before every look-back launch (one block): the next epoch (never 0)
-// and every group's ticket counter back to 0.
-__global__ __launch_bounds__(256) void wkv_lb_prepare(uint32_t* __restrict__ ctrl, int64_t groups) {
-  uint32_t* tickets = ctrl + kTicketStride;
-  for (int64_t g = threadIdx.x; g < groups; g += 256) tickets[g * kTicketStride] = 0u;
-  if (threadIdx.x == 0) {
-    const uint32_t e = ctrl[kCtrlEpoch] + 1u;
-    ctrl[kCtrlEpoch] = e == 0u ? 1u : e;
-  }
-}
 
 // Wait (bounded) until the n tagged words at p carry this launch's epoch and
 // return their values. Past the limit the error word is set and NaNs are
 // returned, so the kernel still finishes and what depends on them is NaN.
 template <int N>
 __device__ __forceinline__ void wait_words(const LbArgs& a, uint64_t* p, float (&x)[N]) {
+  if (!a.claimed) {  // another layout's words: none may be read (already flagged)
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = __builtin_nanf("");
+    return;
+  }
   for (uint32_t spin = 0;; ++spin) {
     bool ok = true;
 #pragma unroll
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   __shared__ Seg tot[W][CH];
   __shared__ Lane xs[CH];
   __shared__ Seg fetched[anchor_spacing<V, W>()][CH];
-  __shared__ uint32_t seg_s, epoch_s;
+  __shared__ uint32_t seg_s, epoch_s, test_s, ours_s;
 
   // Work assignment per channel group: block i = q G + o (row q, offset o)
   // serves group g(o), the same group in every row, and takes the group's
@@ -298,14 +299,21 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
                         ? o
                         : (o & ~int64_t{kNumXcd - 1}) | (((o & (kNumXcd - 1)) + (o / kNumXcd)) &
                                                          (kNumXcd - 1));
-  __shared__ uint32_t spin_s, flags_s;
+  // thread 0 issues its ticket, the layout claim and the test word together
+  // (one round trip); their values are needed only after the tile's prefetch
+  // is issued
+  uint64_t ticket = 0, claim = 0, words = 0;
+  const uint64_t layout = (static_cast<uint64_t>(a.groups) << 32) | static_cast<uint64_t>(a.segments);
   if (threadIdx.x == 0) {
-    uint32_t* tickets = a.ctrl + kTicketStride;
-    seg_s = __hip_atomic_fetch_add(tickets + g * kTicketStride, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    epoch_s = __hip_atomic_load(a.ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    flags_s = __hip_atomic_load(a.ctrl + kCtrlFlags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    spin_s = __hip_atomic_load(a.ctrl + kCtrlSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (the ticket last: the compiler waits for its value at once, and then
+    // the two loads are in flight already)
+    claim = __hip_atomic_load(reinterpret_cast<uint64_t*>(a.ctrl + kCtrlClaim), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    words = __hip_atomic_load(reinterpret_cast<uint64_t*>(a.ctrl + kCtrlErr), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(a.ctrl + kTicketStride) +
+                                        2 * g,
+                                    uint64_t{1}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // prefetch the likely segment's tile while the ticket is in flight: the
   // group's blocks are one per row, so this block is most likely its row-th
@@ -317,19 +325,28 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
     const int64_t off = lb_offset<V, W, L>(guess, g, a.gpr, T, C);
     chunk_load<IoT, V, L, false, G>(r, k + off, v + off, rat(off), C, L);
   }
+  const uint64_t S = static_cast<uint64_t>(a.segments);
+  if (threadIdx.x == 0) {
+    // an unclaimed (zero-filled) workspace holds no valid word, so every
+    // workgroup of its first launch may go ahead; the one with group 0's
+    // first ticket records the claim for the launches after it (a store by
+    // one workgroup, not an atomic update by all)
+    const bool ours = claim == 0 || claim == layout;
+    if (claim == 0 && ticket == 0 && g == 0)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(a.ctrl + kCtrlClaim), layout,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!ours)
+      __hip_atomic_fetch_or(a.ctrl + kCtrlErr, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seg_s = static_cast<uint32_t>(ticket % S);
+    epoch_s = static_cast<uint32_t>((ticket / S) % 0xffffffffull) + 1u;
+    test_s = static_cast<uint32_t>(words >> 32);
+    ours_s = ours ? 1u : 0u;
+  }
   __syncthreads();
   a.epoch = epoch_s;
-  a.spin_limit = spin_s != 0u ? spin_s : kSpinLimit;
-  a.publish = (flags_s & kFlagNoPublish) == 0u;
-  // the set-up kernel rewound the counters: exactly S workgroups per group
-  // take tickets 0 .. S-1, so the ticket is the segment. A ticket beyond that
-  // means another launch shares the workspace at the same time: flag it and
-  // leave (the waits that depended on this workgroup run out and flag too).
-  if (seg_s >= static_cast<uint64_t>(a.segments)) {
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_or(a.ctrl + kCtrlErr, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
+  a.spin_limit = (test_s >> 8) != 0u ? (test_s >> 8) : kSpinLimit;
+  a.claimed = ours_s != 0u;
+  a.publish = a.claimed && (test_s & kTestNoPublish) == 0u;
   const int64_t s = seg_s;
   const int64_t off = lb_offset<V, W, L>(s, g, a.gpr, T, C);
   if ((s + 1) * TL <= T) {
@@ -361,9 +378,9 @@ auto lb_dispatch(int64_t T, F&& f) {
   return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 32>{});
 }
 
-// Control words (16 bytes), then one ticket counter per channel group (16
-// bytes apart), rounded up to 256 bytes so the tagged words after them stay
-// aligned.
+// Control words (16 bytes), then one 64-bit ticket counter per channel group
+// (16 bytes apart), rounded up to 256 bytes so the tagged words after them
+// stay aligned.
 int64_t lookback_ctrl_bytes(int64_t groups) {
   return ((16 + 4 * kTicketStride * groups + 255) / 256) * 256;
 }
@@ -399,7 +416,7 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
   la.epoch = 0;          // these three are read from the control words by the kernel
   la.spin_limit = kSpinLimit;
   la.publish = true;
-  hipLaunchKernelGGL(wkv_lb_prepare, dim3(1), dim3(256), 0, st, ws.ctrl, groups);
+  la.claimed = true;
   const auto* kk = static_cast<const typename IoT::elem*>(a.k);
   const auto* vv = static_cast<const typename IoT::elem*>(a.v);
   const auto* rr = static_cast<const typename IoT::elem*>(a.r);
