@@ -149,9 +149,16 @@ def _summary_by_definition(w, k, v, n0, d0, m0):
 # ---------------------------------------------------------------------------
 
 def _share(x):
-    """1 / (1 + e^-x) for x in [-inf, inf], as exp(-log(1 + e^-x)) so that no
-    branch is needed and neither tail overflows."""
-    return np.exp(-np.logaddexp(0.0, -x))
+    """1 / (1 + e^-x) for x in [-inf, inf]: e^-x may overflow to inf for very
+    negative x, which gives the correct limit 0 (the warning is silenced)."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def _log_add(a, b):
+    """log(e^a + e^b) = max(a, b) + log(1 + e^-|a - b|), for a or b = -inf too
+    (not both)."""
+    return np.maximum(a, b) + np.log1p(np.exp(-np.abs(a - b)))
 
 
 def wkv_step_ref(w, u, k_t, v_t, state):
@@ -192,7 +199,7 @@ def wkv_step_ref(w, u, k_t, v_t, state):
     # the past decays by one step, the token joins without the bonus
     gap2 = (log_d - w) - k_t
     new_mean = _share(gap2) * mean + _share(-gap2) * v_t
-    new_log_d = np.logaddexp(log_d - w, k_t)
+    new_log_d = _log_add(log_d - w, k_t)
     return out_t, np.stack([new_mean, np.ones_like(new_mean), new_log_d])
 
 
