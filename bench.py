@@ -2,42 +2,35 @@
 """Benchmark of the WKV operator on one MI355X.
 
 Default run (one JSON line on stdout):
-  * prefill: 8 independent layers of wkv_forward at B=8, T=1024, C=768, fp32
-    (the MicroRWKV shape: 8 layers, width 768, 1024-token block), inputs
-    resident in HBM. One "step" = the 8 forward calls on one stream, captured
-    once into a HIP graph and replayed per step; value = G channel-tokens/s
-    over the timed replays. The same steps launched eagerly from Python are
-    reported beside it (eager_value).
-  * roofline: the prefill kernel's launch duration (HIP events around the
-    timed graph replays: step time over launches per step; the eager loop's
-    event pair around every launch is reported beside it) against its
-    algorithmic HBM bytes (read k, v; write out; write the final state; read
-    w, u).
-  * decode: 1024 consecutive wkv_step calls at B=256, C=768 after a T=512
-    prefill; steps/s for eager launches and for one HIP graph of all 1024.
-  * gated_forward: wkv_forward_gated (out = sigmoid(r) * wkv) on one layer of
-    the prefill shape.
-  * per_token_decay: wkv_forward_dd (a decay rate per token and channel) on
-    one layer of the prefill shape and on the decode workload's B=256 T=512
-    prefill shape.
-  * per_token_decay_backward: wkv_backward_dd (the gradients, a rate per
-    token) on the same two shapes, and the training pair with and without
-    the checkpoints wkv_forward_dd_ckpt saves.
-  * matrix_state: wkv_matrix_forward (a 64 x 64 state per head of 64
-    channels) on the same two shapes.
-  * backward: wkv_backward (the gradients) on one layer of the prefill shape
-    and on the decode workload's B=256 T=512 prefill shape, with the
-    roofline on its algorithmic bytes (read k, v, dL/dout; write dL/dk,
-    dL/dv).
-  * checkpointed_training: on the same two shapes, the plain prefill then
-    wkv_backward against wkv_forward_ckpt (the prefill that saves the
-    backward's checkpoints) then wkv_backward_ckpt (the backward that reads
-    them instead of re-running the recurrence).
-  * cpu_baseline: the float64 oracle on the host, on the same prefill workload.
+  * headline: wkv_forward_bf16 at B=64 T=4096 C=4096 (bf16 k, v, out; fp32
+    state and arithmetic), the largest single-GPU workload, inputs resident
+    in HBM. One "step" = one prefill call, captured once into a HIP graph and
+    replayed per step; value = G channel-tokens/s over the timed replays.
+  * roofline: the prefill kernel's launch duration (HIP events on the
+    launching stream around the timed graph replays: step time over launches
+    per step) against its algorithmic HBM bytes (read k, v; write out; write
+    the final state; read w, u), and the HBM traffic from rocprofv3 counter
+    summaries under profiles/ when they match the kernel's sources.
+  * workloads: the same measurement (value, roofline, traffic) for the other
+    prefill workloads: 8 layers of B=8 T=1024 C=768 fp32 (the MicroRWKV
+    shape), B=256 T=512 C=768 fp32 (the decode workload's prefill) and
+    B=4 T=16384 C=2048 fp32 (long context, through the look-back scan with
+    its workspace); the decode workload, 1024 consecutive wkv_step calls at
+    B=256 C=768 after a T=512 prefill (steps/s, eager and as one HIP graph);
+    and decode time per step after a T=16 prefill against after a T=16384
+    prefill (the state is the same size whatever came before).
+  * extended: the gated output, the backward pass and the checkpointed
+    training pair, per-token decay and its backward, the matrix-valued state,
+    the token shift, and the extended operators' decode steps, on the MicroRWKV
+    layer shape and the B=256 T=512 shape.
+  * cpu_baseline: the float64 oracle on the host's cores, one process per
+    core over disjoint lanes, for every workload above (the B=64 T=4096 one on
+    4 of its 64 batch rows, scaled to the whole); run before the GPU is
+    touched.
 
---config N measures another workload (0: B=1 T=64 C=768; 2: the decode
-workload's T=512 prefill; 3: B=4 T=16384 C=2048; 4: B=64 T=4096 C=4096 bf16)
-in the same format, without the decode part.
+--config N puts another workload in the headline (0: B=1 T=64 C=768; 1: the
+MicroRWKV layers; 2: B=256 T=512 C=768; 3: B=4 T=16384 C=2048).
+--prefill-only measures the prefill workloads alone (for counter runs).
 """
 
 from __future__ import annotations
@@ -70,34 +63,40 @@ def algorithmic_bytes(B, T, C, io_bytes, state_in=False):
     return b + (12 * B * C if state_in else 0)
 
 
-def build_layers(wl, n_layers, dev):
+def device_layer(wl, layer, dev):
+    """w, u, k, v of one layer of workload wl as device tensors (k, v bf16 for
+    bf16 workloads), drawn a few batch rows at a time so that host memory
+    stays bounded at any size."""
     import torch
     from wkv_recurrence_scan_amd import inputs as I
 
-    layers = []
-    for layer in range(n_layers):
-        w, u = I.params(wl, layer)
-        k, v = I.kv(wl, layer)
-        if wl.io == "bf16":
-            kd = torch.from_numpy(I.bf16_bits(k).view(np.int16)).to(dev).view(torch.bfloat16)
-            vd = torch.from_numpy(I.bf16_bits(v).view(np.int16)).to(dev).view(torch.bfloat16)
-        else:
-            kd = torch.from_numpy(k).to(dev)
-            vd = torch.from_numpy(v).to(dev)
-        layers.append(dict(
-            w=torch.from_numpy(w).to(dev), u=torch.from_numpy(u).to(dev), k=kd, v=vd,
-            out=torch.empty_like(kd),
-            st=torch.empty((3, wl.B, wl.C), dtype=torch.float32, device=dev),
-            host=(w, u, k, v)))
-        del k, v
-    return layers
+    w, u = I.params(wl, layer)
+    dt = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    k = torch.empty((wl.B, wl.T, wl.C), dtype=dt, device=dev)
+    v = torch.empty_like(k)
+    per = max(1, (1 << 25) // max(1, wl.T * wl.C))  # rows per batch: ~32M elements
+    for r0 in range(0, wl.B, per):
+        rows = list(range(r0, min(wl.B, r0 + per)))
+        kh, vh = I.kv(wl, layer, rows=rows)
+        for dst, h in ((k, kh), (v, vh)):
+            if wl.io == "bf16":
+                dst[r0:r0 + len(rows)] = torch.from_numpy(I.bf16_bits(h).view(np.int16)).to(
+                    dev).view(torch.bfloat16)
+            else:
+                dst[r0:r0 + len(rows)] = torch.from_numpy(h).to(dev)
+        del kh, vh
+    return dict(w=torch.from_numpy(w).to(dev), u=torch.from_numpy(u).to(dev), k=k, v=v,
+                out=torch.empty_like(k),
+                st=torch.empty((3, wl.B, wl.C), dtype=torch.float32, device=dev))
 
 
-def time_prefill(layers, steps, warmup, path):
+def time_prefill(layers, steps, warmup, path="auto"):
     """Times `steps` steps (all layers once each) after `warmup` steps, twice:
-    launched eagerly from Python with a HIP event pair around every kernel
-    (the per-kernel durations give the roofline figure), and replayed from one
-    HIP graph holding a whole step. Returns a dict of timings."""
+    launched eagerly from Python with a HIP event pair around every launch,
+    and replayed from one HIP graph holding a whole step (events on the
+    launching stream around the timed replays). Every call is a prepared
+    ForwardCall that owns the workspace its kernel may need. Returns the
+    timings and the calls."""
     import torch
     import wkv_recurrence_scan_amd as W
 
@@ -154,8 +153,40 @@ def time_prefill(layers, steps, warmup, path):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3 / steps
     graph_ms = t0.elapsed_time(t1) / steps
+    for c in calls:
+        c.check()  # a look-back launch that failed to chain its segments raises
     return {"graph_ms": graph_ms, "eager_ms": eager_ms, "kernel_ms": float(np.mean(kms)),
             "kernel_ms_median": float(np.median(kms)), "wall_ms": wall_ms}
+
+
+def prefill_kernel(path, wl):
+    """Name of the kernel function a prefill path launches for workload wl."""
+    if path == "seq":
+        return "wkv_seq_tile_kernel" if wl.io == "bf16" and wl.C % 512 == 0 else "wkv_seq_kernel"
+    return f"wkv_{path}_kernel"
+
+
+def prefill_record(wl, tm, path):
+    """Value and roofline of one timed prefill workload (see time_prefill)."""
+    io_bytes = 2 if wl.io == "bf16" else 4
+    kms = tm["graph_ms"] / wl.layers
+    ct_step = wl.B * wl.T * wl.C * wl.layers
+    abytes = algorithmic_bytes(wl.B, wl.T, wl.C, io_bytes)
+    achieved = abytes / (kms * 1e-3) / 1e9
+    kernel = prefill_kernel(path, wl)
+    return {
+        "workload": wl.name, "B": wl.B, "T": wl.T, "C": wl.C, "layers": wl.layers, "io": wl.io,
+        "path": path, "value": round(ct_step / (tm["graph_ms"] * 1e-3) / 1e9, 3),
+        "unit": "G channel-tokens/s", "ms_per_step": round(tm["graph_ms"], 5),
+        "eager_value": round(ct_step / (tm["eager_ms"] * 1e-3) / 1e9, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(wl.name, kernel),
+                     "kernel": kernel, "kernel_us": round(kms * 1e3, 3),
+                     "kernel_us_timing": "graph replay events: step time / launches per step",
+                     "kernel_us_event_pairs": round(tm["kernel_ms"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": abytes},
+    }
 
 
 def time_decode(wl, dev, n_steps, use_graph):
@@ -643,10 +674,10 @@ def time_matrix(wl, dev, reps=20):
                               "algorithmic_flops_per_call": aflops}}
 
 
-def measured_traffic(workload_key, path):
-    """HBM bytes per launch from the rocprofv3 counter summaries under
-    profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
-    None when there is none for this workload and kernel or when the kernel's
+def measured_traffic(workload_key, kernel):
+    """HBM bytes per launch of `kernel` on `workload_key` from the rocprofv3
+    counter summaries under profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated
+    against a plain copy), or None when there is none or when the kernel's
     sources have changed since the counters were taken."""
     import glob
     import hashlib
@@ -657,7 +688,7 @@ def measured_traffic(workload_key, path):
             if ":" in line and not line.startswith(("|", " ", "#")):
                 a, b = line.split(":", 1)
                 kv[a.strip()] = b.strip()
-        if kv.get("workload_key") != workload_key or kv.get("path") != path:
+        if kv.get("workload_key") != workload_key or kv.get("kernel") != kernel:
             continue
         h = hashlib.sha256()
         for src in kv.get("kernel_sources", "").split(","):
@@ -669,57 +700,210 @@ def measured_traffic(workload_key, path):
     return None
 
 
-def cpu_baseline(layers, wl, min_s=10.0, budget_s=30.0):
-    """The float64 oracle on the host over the benchmarked workload: whole batch
-    rows of each layer in turn, in full passes over the workload repeated until
-    at least min_s seconds of work are done, or a partial pass cut at about
-    budget_s seconds when one pass is longer than that."""
-    from oracle import wkv_recurrent
+def time_decode_after(dev, T, n_steps=1024, seed=5):
+    """Decode time per step after a T-token prefill at the decode workload's
+    B=256 C=768: the prefill's keys and values are drawn on the device
+    (seeded normal), then the decode workload's own 1024 steps run as one HIP
+    graph (median of five replays, each from the prefill's state)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
 
-    t0 = time.perf_counter()
-    rows_done = 0
-    passes = 0
-    total_rows = len(layers) * wl.B
-    rows_per_call = max(1, min(wl.B, 8192 // wl.C))  # the oracle vectorises over lanes
-    cut = False
-    while not cut:
-        for L in layers:
-            w, u, k, v = L["host"]
-            for r in range(0, wl.B, rows_per_call):
-                r1 = min(wl.B, r + rows_per_call)
-                wkv_recurrent(w, u, k[r:r1], v[r:r1])
-                rows_done += r1 - r
-                if time.perf_counter() - t0 > budget_s:
-                    cut = True
-                    break
-            if cut:
-                break
+    wl = I.WORKLOADS[2]
+    w, u = I.params(wl)
+    dw, du = torch.from_numpy(w).to(dev), torch.from_numpy(u).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    k = torch.randn((wl.B, T, wl.C), generator=g, device=dev)
+    v = torch.randn((wl.B, T, wl.C), generator=g, device=dev)
+    _, st0 = W.wkv_forward(dw, du, k, v)
+    del k, v
+    dk, dv = I.decode_kv(wl, steps=n_steps)
+    ks, vs = torch.from_numpy(dk).to(dev), torch.from_numpy(dv).to(dev)
+    del dk, dv
+    outs = torch.empty_like(ks)
+    state = st0.clone()
+    calls = [W.StepCall(dw, du, ks[s], vs[s], state, outs[s]) for s in range(n_steps)]
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(6):  # the first replay warms up
+        state.copy_(st0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    us = float(np.median(times[1:])) * 1e3 / n_steps
+    return {"prefill_T": T, "graph_us_per_step": round(us, 3),
+            "steps_per_s": round(1e6 / us, 1)}
+
+
+# ------------------------------------------------------------- CPU baseline
+#
+# The float64 oracle (its stabilised recurrence, numpy, vectorised over the
+# lanes it is given) on the host's cores: one process per core, each over a
+# disjoint piece of a workload's lanes, its inputs regenerated from the same
+# seeds. The processes are forked before the GPU is touched; each draws its
+# inputs (not timed), waits at a barrier with the others, then repeats its
+# piece until at least CPU_MIN_S seconds have passed; the rate of the whole is
+# the sum of the processes' rates.
+
+CPU_MIN_S = 1.0
+
+
+def _cpu_pieces(cfg, P):
+    """Workload cfg's lanes cut into P pieces: for each piece a list of
+    (layer, rows, c0, c1) blocks. Workload 4 keeps 4 of its 64 batch rows
+    (a sample: every lane costs the same, so the rate is the full one)."""
+    from wkv_recurrence_scan_amd import inputs as I
+
+    wl = I.WORKLOADS[2 if cfg == 22 else cfg]
+    units = []
+    if cfg in (1,):
+        units = [(layer, [r], 0, wl.C) for layer in range(wl.layers) for r in range(wl.B)]
+    elif cfg in (2, 22):
+        units = [(0, [r], 0, wl.C) for r in range(wl.B)]
+    else:
+        rows = list(range(4)) if cfg == 4 else list(range(wl.B))
+        per_row = max(1, -(-P // len(rows)))
+        cw = -(-wl.C // per_row)
+        units = [(0, [r], c0, min(wl.C, c0 + cw)) for r in rows for c0 in range(0, wl.C, cw)]
+    pieces = [[] for _ in range(P)]
+    for i, unit in enumerate(units):
+        pieces[i * P // len(units)].append(unit)
+    return pieces
+
+
+def _cpu_job(cfg, blocks):
+    """Inputs of the blocks (drawn here, not timed) and a function that runs
+    the oracle over them once and returns the channel-tokens it covered."""
+    from oracle import wkv_recurrent, wkv_step_ref
+    from wkv_recurrence_scan_amd import inputs as I
+
+    wl = I.WORKLOADS[2 if cfg == 22 else cfg]
+    work = []
+    for layer, rows, c0, c1 in blocks:
+        w, u = I.params(wl, layer)
+        k, v = I.kv(wl, layer, rows=rows)
+        k, v = np.ascontiguousarray(k[..., c0:c1]), np.ascontiguousarray(v[..., c0:c1])
+        if cfg == 22:
+            dk, dv = I.decode_kv(wl, rows=rows, steps=wl.decode_steps)
+            _, st = wkv_recurrent(w[c0:c1], u[c0:c1], k, v)
+            work.append(("decode", w[c0:c1], u[c0:c1], dk[..., c0:c1], dv[..., c0:c1], st))
         else:
-            passes += 1
-        if time.perf_counter() - t0 >= min_s:
-            break
-    dt = time.perf_counter() - t0
-    ct = rows_done * wl.T * wl.C
-    what = (f"{passes} full passes over" if rows_done == passes * total_rows
-            else f"{rows_done} sequences ({passes} full passes) of")
-    return {"value": round(ct / dt / 1e9, 6), "unit": "G channel-tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{what} the {total_rows} (layer, batch-row) sequences of T={wl.T} "
-                      f"C={wl.C}; float64 numpy recurrence in one process, {dt:.1f} s"}
+            work.append(("prefill", w[c0:c1], u[c0:c1], k, v, None))
+
+    def run():
+        done = 0
+        for kind, w, u, a, b, st in work:
+            if kind == "prefill":
+                wkv_recurrent(w, u, a, b)
+                done += a.size
+            else:
+                for t in range(a.shape[0]):
+                    _, st = wkv_step_ref(w, u, a[t], b[t], st)
+                done += a.size
+        return done
+
+    return run
+
+
+def _cpu_worker(idx, plan, barrier, queue):
+    try:
+        for name, cfg, blocks in plan:
+            run = _cpu_job(cfg, blocks)
+            barrier.wait(timeout=600)
+            t0 = time.perf_counter()
+            done = passes = 0
+            while True:
+                done += run()
+                passes += 1
+                if time.perf_counter() - t0 >= CPU_MIN_S:
+                    break
+            queue.put((name, idx, done, time.perf_counter() - t0, passes))
+    except Exception as e:  # reported by the parent
+        queue.put(("error", idx, repr(e), 0.0, 0))
+
+
+def cpu_baselines(cfgs):
+    """{name: cpu_baseline record} for the named workloads (cfg 22 is the
+    decode workload's 1024 steps), measured as described above."""
+    import multiprocessing as mp
+    import platform
+
+    try:
+        P = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        P = os.cpu_count() or 1
+    P = max(1, min(P, 16))
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(P)
+    queue = ctx.Queue()
+    plans = [[] for _ in range(P)]
+    for name, cfg in cfgs:
+        for i, blocks in enumerate(_cpu_pieces(cfg, P)):
+            plans[i].append((name, cfg, blocks))
+    procs = [ctx.Process(target=_cpu_worker, args=(i, plans[i], barrier, queue)) for i in range(P)]
+    for p in procs:
+        p.start()
+    results = {}
+    for _ in range(P * len(cfgs)):
+        name, idx, done, secs, passes = queue.get(timeout=900)
+        if name == "error":
+            raise RuntimeError(f"cpu baseline worker {idx}: {done}")
+        results.setdefault(name, []).append((done, secs, passes))
+    for p in procs:
+        p.join(timeout=60)
+    cpu_model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    out = {}
+    for name, cfg in cfgs:
+        rs = results[name]
+        rate = sum(d / s for d, s, _ in rs)
+        passes = min(p for _, _, p in rs)
+        sample = {4: "4 of the 64 batch rows (all channels, all 4096 tokens), scaled to the "
+                     "whole by the rate",
+                  22: "all 196608 lanes of 1024 decode steps after the T=512 prefill (the "
+                      "prefill itself not timed)"}.get(cfg, "every lane of the workload")
+        unit = "steps/s" if cfg == 22 else "G channel-tokens/s"
+        value = rate / (256 * 768) if cfg == 22 else rate / 1e9
+        out[name] = {"value": round(value, 6 if cfg != 22 else 2), "unit": unit, "cores": P,
+                     "kind": "oracle",
+                     "sample": f"{sample}; float64 numpy recurrence, one process per core over "
+                               f"disjoint lanes, each repeated >= {CPU_MIN_S:.0f} s "
+                               f"(>= {passes} passes)",
+                     "cpu": cpu_model}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk", "lookback"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the gated, per-token-decay, matrix-state and backward measurements")
+                    help="skip the extended measurements (gate, backward, per-token decay, "
+                         "matrix state, token shift)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill workloads (no decode, extended or CPU baseline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -729,10 +913,24 @@ def main():
               "lanes with no communication, so more GPUs are not part of this benchmark.",
               file=sys.stderr)
         sys.exit(2)
+    if args.prefill_only:
+        args.no_decode = args.no_backward = args.no_cpu_baseline = True
+
+    from wkv_recurrence_scan_amd import inputs as I
+
+    prefill_cfgs = [args.config] + [c for c in (1, 2, 3, 4) if c != args.config]
+    names = {c: I.WORKLOADS[c].name for c in (0, 1, 2, 3, 4)}
+    names[2] = "wkv_fwd_B256_T512_C768_f32"
+    cpu = {}
+    if not args.no_cpu_baseline:
+        # before anything touches the GPU: the workers are forked
+        _log("cpu baseline: float64 oracle on the host cores")
+        cfgs = [(names[c], c) for c in prefill_cfgs] + ([] if args.no_decode else
+                                                       [(I.WORKLOADS[2].name, 22)])
+        cpu = cpu_baselines(cfgs)
 
     import torch
     import wkv_recurrence_scan_amd as W
-    from wkv_recurrence_scan_amd import inputs as I
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -740,16 +938,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     W.load_library()
-
-    wl = I.WORKLOADS[args.config]
-    if args.config == 2:
-        wl = wl.scaled(decode_steps=0)
-    n_layers = wl.layers
-    _log(f"generating inputs for {wl.name}")
-    layers = build_layers(wl, n_layers, dev)
-    io_bytes = 2 if wl.io == "bf16" else 4
-    path_used = args.path if args.path != "auto" else W.wkv_select_path(
-        wl.B, wl.T, wl.C, W.WKV_IO_BF16 if wl.io == "bf16" else W.WKV_IO_F32)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -761,106 +949,119 @@ def main():
         _log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
         del a, b
 
-    _log(f"timing {args.steps} steps after {args.warmup} warm-up steps, path={path_used}")
-    tm = time_prefill(layers, args.steps, args.warmup, args.path)
-    ms_step = tm["graph_ms"]
-    # Launch duration of the kernel in steady state: HIP events around the
-    # timed graph replays, step time over the launches in a step (the gaps
-    # between back-to-back launches included). The eager loop's event pair
-    # around every single launch also counts the dispatch of each launch and
-    # reads a little higher; it is reported beside it.
-    kms = ms_step / n_layers
-    per_layer_ct = wl.B * wl.T * wl.C
-    ct_step = per_layer_ct * n_layers
-    value = ct_step / (ms_step * 1e-3) / 1e9
-    abytes = algorithmic_bytes(wl.B, wl.T, wl.C, io_bytes)
-    achieved = abytes / (kms * 1e-3) / 1e9
+    records = []
+    for c in prefill_cfgs:
+        wl = I.WORKLOADS[c]
+        if c == 2:
+            wl = wl.scaled(decode_steps=0, name=names[2])
+        path = W.wkv_select_path(wl.B, wl.T, wl.C, W.WKV_IO_BF16 if wl.io == "bf16" else W.WKV_IO_F32)
+        _log(f"prefill {wl.name}: generating inputs")
+        layers = [device_layer(wl, layer, dev) for layer in range(wl.layers)]
+        _log(f"prefill {wl.name}: {args.steps} steps after {args.warmup} warm-up steps, path={path}")
+        tm = time_prefill(layers, args.steps, args.warmup)
+        rec = prefill_record(wl, tm, path)
+        if names[c] in cpu:
+            rec["cpu_baseline"] = cpu[names[c]]
+        records.append(rec)
+        del layers
+        torch.cuda.empty_cache()
 
+    head = records[0]
     rec = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": head["value"],
         "unit": "G channel-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.io == "bf16" else "f32",
+        "dtype": "bf16" if head["io"] == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "C": wl.C, "layers": n_layers,
-                   "io": wl.io, "path": path_used, "launch": "hip_graph_per_step",
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(wl.name, path_used),
-                     "kernel": f"wkv_{path_used}_kernel", "kernel_us": round(kms * 1e3, 3),
-                     "kernel_us_timing": "graph replay events: step time / launches per step",
-                     "kernel_us_event_pairs": round(tm["kernel_ms"] * 1e3, 3),
-                     "algorithmic_bytes_per_launch": abytes},
-        "eager_ms_per_step": round(tm["eager_ms"], 5),
-        "eager_value": round(ct_step / (tm["eager_ms"] * 1e-3) / 1e9, 3),
-        "wall_ms_per_step": round(tm["wall_ms"], 5),
+        "config": {"workload": head["workload"], "B": head["B"], "T": head["T"], "C": head["C"],
+                   "layers": head["layers"], "io": head["io"], "path": head["path"],
+                   "launch": "hip_graph_per_step", "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "eager_value": head["eager_value"],
     }
+    if head["io"] == "bf16":
+        rec["dtype_note"] = "bf16 k, v, out; fp32 state and arithmetic"
+    if "cpu_baseline" in head:
+        rec["cpu_baseline"] = head["cpu_baseline"]
+    rec["workloads"] = records[1:]
 
-    if args.config == 1 and not args.no_decode:
+    if not args.no_decode:
         dwl = I.WORKLOADS[2]
         _log(f"decode: {args.decode_steps} steps at B={dwl.B} C={dwl.C} after T={dwl.T}")
         d = time_decode(dwl, dev, args.decode_steps, use_graph=True)
-        rec["decode"] = {
+        bstep = d["bytes_per_step"]
+        gus = d.get("graph_us_per_step", 0.0)
+        dec = {
             "workload": dwl.name, "B": dwl.B, "C": dwl.C, "prefill_T": dwl.T,
-            "steps": args.decode_steps,
-            "steps_per_s": round(d["steps_per_s"], 1),
-            "us_per_step": round(d["us_per_step"], 3),
-            "graph_steps_per_s": round(d.get("graph_steps_per_s", 0.0), 1),
-            "graph_us_per_step": round(d.get("graph_us_per_step", 0.0), 3),
-            "bytes_per_step": d["bytes_per_step"],
+            "steps": args.decode_steps, "value": round(d.get("graph_steps_per_s", 0.0), 1),
+            "unit": "steps/s", "launch": "one HIP graph of all steps",
+            "graph_us_per_step": round(gus, 3),
+            "eager_steps_per_s": round(d["steps_per_s"], 1),
+            "eager_us_per_step": round(d["us_per_step"], 3),
+            "roofline": {"bound": "hbm", "achieved": round(bstep / (gus * 1e-6) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(bstep / (gus * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "kernel": "wkv_step_kernel", "algorithmic_bytes_per_step": bstep,
+                         "note": "launch-bound: each step's own HBM time is under 1 us"},
         }
+        if dwl.name in cpu:
+            dec["cpu_baseline"] = cpu[dwl.name]
+        rec["decode"] = dec
+        torch.cuda.empty_cache()
+        _log("decode after a T=16 and a T=16384 prefill")
+        flat = [time_decode_after(dev, T) for T in (16, 16384)]
+        torch.cuda.empty_cache()
+        rec["decode_vs_prefill_length"] = {
+            "B": dwl.B, "C": dwl.C, "steps": args.decode_steps, "runs": flat,
+            "ratio_long_to_short": round(flat[1]["graph_us_per_step"]
+                                         / flat[0]["graph_us_per_step"], 4)}
 
-    if args.config == 1 and not args.no_backward:
+    if not args.no_backward:
+        wl1 = I.WORKLOADS[1]
+        path1 = W.wkv_select_path(wl1.B, wl1.T, wl1.C)
+        ext = {}
         _log("gated forward: one layer")
-        rec["gated_forward"] = time_gated(wl.scaled(layers=1), dev, path_used)
-        rec["backward"] = []
-        for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+        ext["gated_forward"] = time_gated(wl1.scaled(layers=1), dev, path1)
+        shapes = (wl1.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0))
+        ext["backward"] = []
+        for bwl in shapes:
             _log(f"backward: {bwl.name} (one layer)")
-            rec["backward"].append(time_backward(bwl, dev))
+            ext["backward"].append(time_backward(bwl, dev))
             torch.cuda.empty_cache()
-        rec["checkpointed_training"] = []
-        for bwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+        ext["checkpointed_training"] = []
+        for bwl in shapes:
             _log(f"checkpointed forward + backward: {bwl.name} (one layer)")
-            rec["checkpointed_training"].append(time_ckpt_pair(bwl, dev))
+            ext["checkpointed_training"].append(time_ckpt_pair(bwl, dev))
             torch.cuda.empty_cache()
-
-    if args.config == 1 and not args.no_backward:
-        rec["per_token_decay"] = []
-        for dwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
-            _log(f"per-token decay forward: {dwl.name} (one layer)")
-            rec["per_token_decay"].append(time_decay(dwl, dev))
+        ext["per_token_decay"] = []
+        for dwl_ in shapes:
+            _log(f"per-token decay forward: {dwl_.name} (one layer)")
+            ext["per_token_decay"].append(time_decay(dwl_, dev))
             torch.cuda.empty_cache()
-        rec["per_token_decay_backward"] = []
-        for dwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
-            _log(f"per-token decay backward: {dwl.name} (one layer)")
-            rec["per_token_decay_backward"].append(time_dd_backward(dwl, dev))
+        ext["per_token_decay_backward"] = []
+        for dwl_ in shapes:
+            _log(f"per-token decay backward: {dwl_.name} (one layer)")
+            ext["per_token_decay_backward"].append(time_dd_backward(dwl_, dev))
             torch.cuda.empty_cache()
-
-    if args.config == 1 and not args.no_backward:
-        rec["matrix_state"] = []
-        for mwl in (wl.scaled(layers=1), I.WORKLOADS[2].scaled(decode_steps=0)):
+        ext["matrix_state"] = []
+        for mwl in shapes:
             _log(f"matrix-valued state forward: {mwl.name} (one layer)")
-            rec["matrix_state"].append(time_matrix(mwl, dev))
+            ext["matrix_state"].append(time_matrix(mwl, dev))
             torch.cuda.empty_cache()
-
-    if args.config == 1 and not args.no_decode and not args.no_backward:
-        rec["decode_next"] = []
-        for kind in ("dd", "matrix"):
-            _log(f"decode steps: {kind} at B={I.WORKLOADS[2].B} C={I.WORKLOADS[2].C}")
-            rec["decode_next"].append(time_decode_steps(kind, I.WORKLOADS[2], dev))
-            torch.cuda.empty_cache()
-
-    if not args.no_cpu_baseline:
-        _log("cpu baseline: float64 oracle")
-        rec["cpu_baseline"] = cpu_baseline(layers, wl)
+        if not args.no_decode:
+            ext["decode_next"] = []
+            for kind in ("dd", "matrix"):
+                _log(f"decode steps: {kind} at B={I.WORKLOADS[2].B} C={I.WORKLOADS[2].C}")
+                ext["decode_next"].append(time_decode_steps(kind, I.WORKLOADS[2], dev))
+                torch.cuda.empty_cache()
+        rec["extended"] = ext
 
     print(json.dumps(rec), flush=True)
 
