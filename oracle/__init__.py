@@ -13,13 +13,17 @@ operator (wkv_decay) by tests/test_oracle_decay.py against its own mpmath
 recurrence, the constant-decay operator, a hand-worked case and invariants;
 the matrix-valued-state recurrence (wkv_matrix) by tests/test_oracle_matrix.py
 against its own mpmath attention form, causal linear attention by matmul,
-closed forms and invariants. None is "parity unpinned".
+closed forms and invariants; the token shift (wkv_shift) by
+tests/test_oracle_shift.py against the mixing fraction's end points and
+midpoint, affinity, split/resume, one-token steps, constant sequences, a
+hand-worked case and planted mistakes. None is "parity unpinned".
 """
 
 from .wkv_decay import wkv_dd_direct, wkv_dd_recurrent, wkv_dd_step_ref  # noqa: F401
 from .wkv_grad import (  # noqa: F401
     wkv_backward_direct, wkv_dd_backward_direct, wkv_gated_backward_direct)
 from .wkv_matrix import wkv6_direct, wkv6_recurrent, wkv6_step_ref  # noqa: F401
+from .wkv_shift import token_shift  # noqa: F401
 from .wkv_oracle import (  # noqa: F401
     EMPTY_MAX_EXP,
     canonical,
