@@ -537,6 +537,48 @@ def time_decay(wl, dev, reps=50):
                          "algorithmic_bytes_per_launch": abytes}}
 
 
+def time_shift(wl, dev, P=4, reps=50):
+    """wkv_token_shift (the P = 4 mixes of each token with the one before it)
+    on workload wl's first layer: microseconds per call from an event pair
+    around `reps` back-to-back calls, and the roofline on its algorithmic
+    bytes (read x once, write P mixes; read mu, x_prev; write x_last)."""
+    import torch
+    import wkv_recurrence_scan_amd as W
+    from wkv_recurrence_scan_amd import inputs as I
+
+    x, mu, xp = I.shift_inputs(wl, P=P)
+    dt = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    dx = torch.from_numpy(x).to(dev).to(dt)
+    dxp = torch.from_numpy(xp).to(dev).to(dt)
+    dmu = torch.from_numpy(mu).to(dev)
+    del x, xp
+    out = torch.empty((P,) + tuple(dx.shape), dtype=dt, device=dev)
+    last = torch.empty_like(dxp)
+    call = lambda: W.wkv_token_shift(dmu, dx, dxp, out=out, x_last=last)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    es = 2 if wl.io == "bf16" else 4
+    ct = wl.B * wl.T * wl.C
+    abytes = es * (1 + P) * ct + 4 * P * wl.C + 2 * es * wl.B * wl.C
+    achieved = abytes / (us * 1e-6) / 1e9
+    return {"workload": f"{wl.name}, one layer, token shift", "B": wl.B, "T": wl.T, "C": wl.C,
+            "io": wl.io, "projections": P,
+            "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
+            "us_per_call": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "kernel": "wkv_shift_kernel", "algorithmic_bytes_per_launch": abytes}}
+
+
 def time_decode_steps(kind, wl, dev, n_steps=256):
     """Decode steps of the per-token-decay operator (kind "dd": wkv_step_dd)
     or of the matrix-valued state (kind "matrix": wkv_matrix_step) at workload
@@ -1054,6 +1096,11 @@ def main():
         for mwl in shapes:
             _log(f"matrix-valued state forward: {mwl.name} (one layer)")
             ext["matrix_state"].append(time_matrix(mwl, dev))
+            torch.cuda.empty_cache()
+        ext["token_shift"] = []
+        for swl in (wl1.scaled(layers=1), I.WORKLOADS[4].scaled(layers=1)):
+            _log(f"token shift: {swl.name} (one layer, 4 projections)")
+            ext["token_shift"].append(time_shift(swl, dev))
             torch.cuda.empty_cache()
         if not args.no_decode:
             ext["decode_next"] = []

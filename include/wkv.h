@@ -436,6 +436,35 @@ int wkv_matrix_step(int64_t B, int64_t H, int64_t D, const float* w, const float
                     hipStream_t stream);
 
 /* Static, NUL-terminated name of a wkv_status code. */
+/* Token shift, the step in front of the projections whose outputs feed the
+ * WKV operator (page "RWKV-v6 Architecture: Attention-Free Linear
+ * Transformers", section "The Core Components of the RWKV-v6 Time-Mixing
+ * Block", item 1, Data-Dependent Token Shift; page "RWKV: Merging
+ * Transformer Training with RNN Speed", Time-Mixing block): for every
+ * projection p, the input is the current token vector moved towards the one
+ * before it by a per-channel fraction,
+ *
+ *     out[p][b][t][c] = x[b][t][c] + (x[b][t-1][c] - x[b][t][c]) * mu[p][c].
+ *
+ *   B, T, C    sizes (>= 0): batch rows, tokens, channels. B == 0 or C == 0:
+ *              nothing to do. T == 0: x_last receives x_prev (or zeros).
+ *   P          projections, 1 <= P <= 8 (WKV_ERR_DIM otherwise).
+ *   mu         [P][C] fp32 mixing fractions, one vector per projection.
+ *   x          [B][T][C] token vectors (fp32, or bf16 with io = WKV_IO_BF16).
+ *   x_prev     [B][C] the token before x[b][0] (the previous call's last), or
+ *              NULL for zeros (the start of a sequence).
+ *   out        [P][B][T][C] the P mixes, one [B][T][C] block per projection,
+ *              same element type as x (bf16: rounded to nearest even from the
+ *              fp32 result of one fused multiply-add).
+ *   x_last     [B][C] receives x[b][T-1], the next call's x_prev, or NULL to
+ *              skip it. May be the same pointer as x_prev (decode: T = 1, the
+ *              carried token updated in place); any other overlap of x_last or
+ *              out with an argument is WKV_ERR_ALIAS.
+ *   io         WKV_IO_F32 or WKV_IO_BF16 (WKV_ERR_ARG otherwise).
+ * Asynchronous on `stream` like every call here. */
+int wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t P, const float* mu, const void* x,
+                    const void* x_prev, void* out, void* x_last, int io, hipStream_t stream);
+
 const char* wkv_status_string(int status);
 
 /* hipError_t of the last WKV_ERR_LAUNCH / WKV_ERR_DEVICE returned on the

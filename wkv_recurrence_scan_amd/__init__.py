@@ -12,6 +12,7 @@ into that interface (see _lib). Build the library with
     out, state = wkv_forward_dd(w_t, u, k, v)     # per-token decay w_t (B, T, C)
     gw_t, gu, gk, gv, gs = wkv_backward_dd(w_t, u, k, v, gout)  # its gradients
     y, S = wkv_matrix_forward(w_t, k, v, r, H)     # matrix-valued state per head
+    xs, x_last = wkv_token_shift(mu, x, x_prev)     # token shift ahead of the projections
 """
 
 from ._lib import (  # noqa: F401
@@ -59,4 +60,5 @@ from ._lib import (  # noqa: F401
     wkv_step_gated,
     wkv_workspace_size,
     wkv_workspace_status,
+    wkv_token_shift,
 )

@@ -60,6 +60,7 @@ def load_library() -> ctypes.CDLL:
         "wkv_workspace_size": [i64, i64, i64, ci, ci],
         "wkv_workspace_status": [vp, i64, ci, vp],
         "wkv_forward_noalloc": [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp],
+        "wkv_token_shift": [i64, i64, i64, i64, vp, vp, vp, vp, vp, ci, vp],
         "wkv_select_path": [i64, i64, i64, ci],
         "wkv_step": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
         "wkv_step_bf16": [i64, i64, vp, vp, vp, vp, vp, vp, vp],
@@ -803,6 +804,43 @@ def wkv_matrix_step(w, k, v, r, H: int, state, out=None, *, stream=None):
                                  _ptr(state), _ptr(out), _stream_handle(dev, stream))
     _check(st, "wkv_matrix_step")
     return out
+
+
+def wkv_token_shift(mu: torch.Tensor, x: torch.Tensor, x_prev: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, x_last: Optional[torch.Tensor] = None, *,
+                    want_last: bool = True, stream=None):
+    """wkv_token_shift: mu (P, C) float32; x (B, T, C) float32 or bfloat16;
+    x_prev (B, C) like x or None (zeros). Returns (out (P, B, T, C), x_last
+    (B, C) or None); x_last may be x_prev itself (updated in place)."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError(f"x must be (B, T, C), got shape {tuple(x.shape)}")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    B, T, C = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    if mu.dim() != 2:
+        raise ValueError(f"mu must be (P, C), got shape {tuple(mu.shape)}")
+    P = mu.shape[0]
+    _need(mu, "mu", torch.float32, (P, C), dev)
+    _need(x, "x", x.dtype, (B, T, C), dev)
+    if x_prev is not None:
+        _need(x_prev, "x_prev", x.dtype, (B, C), dev)
+    if out is None:
+        out = torch.empty((P, B, T, C), dtype=x.dtype, device=dev)
+    _need(out, "out", x.dtype, (P, B, T, C), dev)
+    if x_last is None and want_last:
+        x_last = torch.empty((B, C), dtype=x.dtype, device=dev)
+    if x_last is not None:
+        _need(x_last, "x_last", x.dtype, (B, C), dev)
+    io = WKV_IO_BF16 if x.dtype == torch.bfloat16 else WKV_IO_F32
+    with torch.cuda.device(dev):
+        st = lib.wkv_token_shift(B, T, C, P, _ptr(mu), _ptr(x), _ptr(x_prev), _ptr(out),
+                                 _ptr(x_last), io, _stream_handle(dev, stream))
+    _check(st, "wkv_token_shift")
+    return out, x_last
 
 
 class ForwardCall:

@@ -25,10 +25,10 @@ LIB = os.path.join(PKG, "libwkv.so")
 
 ARCH = "gfx950"
 SOURCES = ["wkv_api.cpp", "wkv_seq.hip", "wkv_chunk.hip", "wkv_lookback.hip", "wkv_step.hip",
-           "wkv_backward.hip", "wkv_decay.hip", "wkv_decay_backward.hip", "wkv_matrix.hip"]
+           "wkv_backward.hip", "wkv_decay.hip", "wkv_decay_backward.hip", "wkv_matrix.hip", "wkv_shift.hip"]
 EXPORTS = [
     "wkv_forward", "wkv_forward_bf16", "wkv_forward_ex", "wkv_forward_ws", "wkv_workspace_size",
-    "wkv_workspace_status", "wkv_forward_noalloc",
+    "wkv_workspace_status", "wkv_forward_noalloc", "wkv_token_shift",
     "wkv_select_path",
     "wkv_step", "wkv_step_bf16", "wkv_status_string", "wkv_last_hip_error",
     "wkv_abi_version", "wkv_backward", "wkv_backward_workspace_size", "wkv_backward_ckpt",

@@ -219,6 +219,33 @@ void* scratch_on(int dev, hipError_t* e) {
   return p;
 }
 
+int shift_impl(int64_t B, int64_t T, int64_t C, int64_t P, const float* mu, const void* x,
+               const void* x_prev, void* out, void* x_last, int io, hipStream_t stream) {
+  if (io != WKV_IO_F32 && io != WKV_IO_BF16) return WKV_ERR_ARG;
+  if (B < 0 || T < 0 || C < 0 || P < 1 || P > wkv::kShiftMaxP) return WKV_ERR_DIM;
+  const int64_t es = io == WKV_IO_BF16 ? 2 : 4;
+  int64_t seq_bytes, out_bytes, row_bytes, mu_bytes;
+  if (!mul3(B, T, C, &seq_bytes) || __builtin_mul_overflow(seq_bytes, es, &seq_bytes) ||
+      __builtin_mul_overflow(seq_bytes, P, &out_bytes) || out_bytes > kMaxBytes)
+    return WKV_ERR_DIM;
+  if (!mul3(B, C, es, &row_bytes) || !mul3(P, C, 4, &mu_bytes)) return WKV_ERR_DIM;
+  if (B == 0 || C == 0) return WKV_OK;
+  if (T > 0 && (mu == nullptr || x == nullptr || out == nullptr)) return WKV_ERR_NULL;
+  if (misaligned(mu, 4) || misaligned(x, es) || misaligned(x_prev, es) || misaligned(out, es) ||
+      misaligned(x_last, es))
+    return WKV_ERR_ALIGN;
+  const int64_t sb = T > 0 ? seq_bytes : 0, ob = T > 0 ? out_bytes : 0;
+  if (overlaps(out, ob, x, sb) || overlaps(out, ob, x_prev, row_bytes) ||
+      overlaps(out, ob, mu, mu_bytes) || overlaps(out, ob, x_last, row_bytes))
+    return WKV_ERR_ALIAS;
+  if (overlaps(x_last, row_bytes, x, sb) || overlaps(x_last, row_bytes, mu, mu_bytes))
+    return WKV_ERR_ALIAS;
+  if (x_last != x_prev && overlaps(x_last, row_bytes, x_prev, row_bytes)) return WKV_ERR_ALIAS;
+  const wkv::ShiftArgs a{B, T, C, P, mu, x, x_prev, out, x_last};
+  const hipError_t e = wkv::launch_shift(a, io, stream);
+  return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
+}
+
 int step_impl(int64_t B, int64_t C, const float* w, const float* u, const void* k, const void* v,
               const void* r, bool gated, float* state, void* out, int io, hipStream_t stream) {
   if (B < 0 || C < 0) return WKV_ERR_DIM;
@@ -846,6 +873,11 @@ int wkv_workspace_status(void* workspace, int64_t workspace_bytes, int clear,
     if (e != hipSuccess) return fail(WKV_ERR_LAUNCH, e);
   }
   return err != 0 ? WKV_ERR_LOOKBACK : WKV_OK;
+}
+
+int wkv_token_shift(int64_t B, int64_t T, int64_t C, int64_t P, const float* mu, const void* x,
+                    const void* x_prev, void* out, void* x_last, int io, hipStream_t stream) {
+  return shift_impl(B, T, C, P, mu, x, x_prev, out, x_last, io, stream);
 }
 
 int wkv_last_hip_error(void) { return g_last_hip_error; }

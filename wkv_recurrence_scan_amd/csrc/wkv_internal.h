@@ -171,6 +171,19 @@ hipError_t launch_matrix_step(const MatrixStepArgs& m, hipStream_t s);
 hipError_t launch_matrix_state_copy(int64_t B, int64_t H, const float* src, float* dst,
                                     hipStream_t s);
 
+// Token shift: out[p][b][t][c] = x[b][t][c] + (x[b][t-1][c] - x[b][t][c]) * mu[p][c],
+// x[b][-1] = x_prev[b] (zeros when null); x_last[b] <- x[b][T-1] (may be x_prev).
+struct ShiftArgs {
+  int64_t B, T, C, P;
+  const float* mu;     // [P][C]
+  const void* x;       // [B][T][C]
+  const void* x_prev;  // [B][C] or nullptr
+  void* out;           // [P][B][T][C]
+  void* x_last;        // [B][C] or nullptr
+};
+constexpr int64_t kShiftMaxP = 8;
+hipError_t launch_shift(const ShiftArgs& a, int io, hipStream_t s);
+
 hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);

@@ -32,6 +32,7 @@ import numpy as np
 # tensor ids inside a seed
 _K, _V, _W, _U, _SPIKE_MASK, _SPIKE_SIGN, _DEC_K, _DEC_V, _GOUT, _R = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 _WT, _DEC_WT = 11, 12
+_SX, _SMU, _SXP = 13, 14, 15
 
 
 @dataclasses.dataclass(frozen=True)
@@ -269,3 +270,32 @@ def decode_decay_rates(wl: Workload, rows: Optional[Sequence[int]] = None,
 
     _map_rows(one, range(len(rows)))
     return out
+
+
+# Token shift (the step in front of the projections; page "RWKV-v6
+# Architecture: Attention-Free Linear Transformers", section "The Core
+# Components of the RWKV-v6 Time-Mixing Block", item 1): the block's input
+# vectors stand in as N(0, 1) activations of the workload's width, the
+# learned mixing fractions as U(0, 1) per projection and channel.
+SHIFT_PROJECTIONS = 4  # receptance, decay, key, value
+
+
+def shift_inputs(wl: Workload, layer: int = 0, P: int = SHIFT_PROJECTIONS,
+                 rows: Optional[Sequence[int]] = None, T: Optional[int] = None):
+    """(x (B_rows, T, C), mu (P, C), x_prev (B_rows, C)) float32; x and x_prev
+    rounded to bf16 for bf16 workloads; one independent stream per batch
+    row."""
+    rows = list(range(wl.B) if rows is None else rows)
+    T = wl.T if T is None else T
+    x = np.empty((len(rows), T, wl.C), np.float32)
+    xp = np.empty((len(rows), wl.C), np.float32)
+
+    def one(i):
+        xx = _values_row(wl, layer, rows[i], T, _SX)
+        pp = _values_row(wl, layer, rows[i], 1, _SXP)[0]
+        x[i] = round_to_bf16(xx) if wl.io == "bf16" else xx
+        xp[i] = round_to_bf16(pp) if wl.io == "bf16" else pp
+
+    _map_rows(one, range(len(rows)))
+    mu = _rng(wl, layer, _SMU).random((P, wl.C), dtype=np.float32)
+    return x, mu, xp
