@@ -191,6 +191,27 @@ def test_matrix_entry_points_validate_without_device():
     assert lib.wkv_matrix_step(1, 1, 64, w, k, v, r, P(a + 65536), w, nul) == 4
 
 
+def test_token_shift_validates_without_device():
+    lib = W.load_library()
+    P = ctypes.c_void_p
+    nul = None
+    a = 0x10000000
+    mu, x, xp, out, last = P(a), P(a + 4096), P(a + 8192), P(a + 16384), P(a + 65536)
+    f32 = W.WKV_IO_F32
+    # B, T, C, P, mu, x, x_prev, out, x_last, io, stream
+    assert lib.wkv_token_shift(1, 2, 8, 0, mu, x, xp, out, last, f32, nul) == 2
+    assert lib.wkv_token_shift(1, 2, 8, 9, mu, x, xp, out, last, f32, nul) == 2
+    assert lib.wkv_token_shift(-1, 2, 8, 4, mu, x, xp, out, last, f32, nul) == 2
+    assert lib.wkv_token_shift(1, 2, 8, 4, mu, x, xp, out, last, 5, nul) == 7
+    assert lib.wkv_token_shift(0, 2, 8, 4, nul, nul, nul, nul, nul, f32, nul) == 0
+    assert lib.wkv_token_shift(1, 2, 8, 4, mu, x, xp, nul, last, f32, nul) == 1
+    assert lib.wkv_token_shift(1, 2, 8, 4, mu, P(a + 4098), xp, out, last, f32, nul) == 3
+    # out over x; x_last inside x; x_last overlapping x_prev without being it
+    assert lib.wkv_token_shift(1, 2, 8, 4, mu, x, xp, P(a + 4096 + 32), last, f32, nul) == 4
+    assert lib.wkv_token_shift(1, 2, 8, 4, mu, x, xp, out, P(a + 4096 + 16), f32, nul) == 4
+    assert lib.wkv_token_shift(1, 2, 8, 4, mu, x, xp, out, P(a + 8192 + 8), f32, nul) == 4
+
+
 def test_checkpoint_entry_points_validate_without_device():
     lib = W.load_library()
     P = ctypes.c_void_p
