@@ -214,10 +214,15 @@ def test_extreme_keys(path, kmag, io):
 
 
 def test_auto_path_choice():
-    """Large B*C goes to the sequential scan; small B*C to the chunked scan up
-    to T = 2048 and to the look-back scan beyond (the chunked scan when no
-    workspace is given)."""
-    assert W.wkv_select_path(256, 512, 768) == "seq"
+    """Large B*C goes to the sequential scan (the chunked scan for fp32 rows
+    whose byte size is not a power of two, 512 <= T <= 2048); small B*C to the
+    chunked scan up to T = 2048 and to the look-back scan beyond (the chunked
+    scan when no workspace is given)."""
+    # fp32 rows of 1.5 MiB: the chunked scan; rows of a power-of-two size: the walk
+    assert W.wkv_select_path(256, 512, 768) == "chunk"
+    assert W.wkv_select_path(256, 512, 1024) == "seq"
+    assert W.wkv_select_path(512, 256, 768) == "seq"
+    assert W.wkv_select_path(256, 512, 768, W.WKV_IO_BF16) == "seq"
     assert W.wkv_select_path(64, 4096, 4096, W.WKV_IO_BF16) == "seq"
     assert W.wkv_select_path(8, 1024, 768) == "chunk"
     assert W.wkv_select_path(4, 16384, 2048) == "lookback"

@@ -65,6 +65,9 @@ def test_validation_codes_without_device():
                            P(a + 512), nul, nul) == 3
     assert lib.wkv_forward(1, 4, 4, P(a), P(a + 64), P(a + 128), P(a + 256), nul,
                            P(a + 128 + 32), nul, nul) == 4
+    assert lib.wkv_select_path(1 << 30, 1 << 30, 1 << 10, 0) == -2
+    assert lib.wkv_select_path(-1, 4, 4, 0) == -2
+    assert lib.wkv_select_path(1, 4, 4, 9) == -7
     for code in range(9):
         assert lib.wkv_status_string(code)
 

@@ -58,13 +58,29 @@ constexpr int64_t kMaxBytes = int64_t(1) << 60;
 // up to kChunkMaxT tokens the chunked scan (measured on MI355X: as fast as the
 // look-back scan there, and it needs no workspace), beyond it the look-back
 // scan when a workspace is available.
+//
+// One exception, measured on MI355X: the sequential scan walks every batch
+// row at the same token, and that access pattern streams at 0.71-0.75 of the
+// HBM peak when a row's bytes (T * C * 4 for fp32) are a power of two but at
+// only 0.64-0.66 otherwise (the same walk over rows padded from 1.5 to 2 MiB
+// went from 0.66 to 0.71). The chunked scan keeps a few rows' tiles in
+// flight instead and holds 0.66 there, so fp32 rows of another size with
+// 512 to kChunkMaxT tokens take it. bf16 keeps the sequential scan, whose
+// LDS-staged tiles stay ahead of the chunked scan at every measured size.
 constexpr int64_t kChunkMaxT = 2048;
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev, bool have_ws) {
   const int64_t per_thread = io == wkv::kBf16 ? 2 : 1;
   const int64_t waves = (B * C / per_thread + 63) / 64;
   if (T < 32) return WKV_PATH_SEQ;
-  if (waves >= 4LL * cu_count(dev)) return WKV_PATH_SEQ;
+  if (waves >= 4LL * cu_count(dev)) {
+    int64_t row_bytes = 0;
+    const bool uneven_rows =
+        io == wkv::kF32 && (__builtin_mul_overflow(T * C, 4, &row_bytes) || !pow2(row_bytes));
+    return uneven_rows && T >= 512 && T <= kChunkMaxT ? WKV_PATH_CHUNK : WKV_PATH_SEQ;
+  }
   return have_ws && T > kChunkMaxT ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
 }
 
@@ -815,6 +831,8 @@ int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path) {
 int wkv_select_path(int64_t B, int64_t T, int64_t C, int io) {
   if (io != WKV_IO_F32 && io != WKV_IO_BF16) return -WKV_ERR_ARG;
   if (B < 0 || T < 0 || C < 0) return -WKV_ERR_DIM;
+  int64_t n;
+  if (!mul3(B, T, C, &n) || n > kMaxBytes / 4) return -WKV_ERR_DIM;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
