@@ -145,6 +145,36 @@ def test_backward_large_batch_sampled_channels():
     say("  " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
 
 
+@pytest.mark.parametrize("wid,chans", [(1, (0, 31, 32, 300, 511, 767)), (2, (0, 385, 767))],
+                         ids=["B8_T1024_C768", "B256_T512_C768"])
+@pytest.mark.parametrize("ckpt", [False, True], ids=["plain", "from_checkpoints"])
+def test_backward_at_benchmark_shapes_on_sampled_channels(wid, chans, ckpt):
+    """The two benchmarked backward shapes (one layer of the 8-layer model:
+    B=8 T=1024 C=768, the segmented or one-pass chunked plan; B=256 T=512
+    C=768, one thread per lane) run at full size, through the plain backward
+    and the one from the forward's checkpoints; the oracle checks every batch
+    row of a few channels (group edges included), so dL/dw and dL/du, sums
+    over the batch, are checked too."""
+    wl = I.WORKLOADS[wid].scaled(decode_steps=0)
+    say(f"backward at B={wl.B} T={wl.T} C={wl.C} ckpt={ckpt}, channels {chans}")
+    w, u = I.params(wl)
+    k, v = I.kv(wl)
+    gout = I.grad_out(wl)
+    dw, du, dk, dv, dg = (dev_f32(a) for a in (w, u, k, v, gout))
+    ck = W.wkv_forward_ckpt(dw, du, dk, dv)[2] if ckpt else None
+    got = W.wkv_backward(dw, du, dk, dv, dg, ckpt=ck)
+    torch.cuda.synchronize()
+    cs = list(chans)
+    got = [host64(x) for x in got[:4]]
+    got = [got[0][cs], got[1][cs], got[2][:, :, cs], got[3][:, :, cs]]
+    ref = wkv_backward_direct(w[cs], u[cs], k[:, :, cs], v[:, :, cs], gout[:, :, cs])
+    companion = {0: 1, 1: 0, 2: 3, 3: 2}
+    errs = {}
+    for i, name in enumerate(("gw", "gu", "gk", "gv")):
+        errs[name] = assert_grad_close(got[i], ref[i], GRAD_TOL, name, rms(ref[companion[i]]))
+    say("  " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+
+
 def test_backward_abi_errors():
     say("backward abi errors")
     lib = W.load_library()
