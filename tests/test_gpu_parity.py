@@ -97,6 +97,23 @@ def test_bf16_tile_walk_from_state(gated):
     assert_state_close(host64(st), rst, F32_TOL * 10)
 
 
+@pytest.mark.parametrize("B,T,C", [(1, 257, 32), (3, 512, 33), (2, 768, 96), (1, 769, 64),
+                                   (2, 1023, 40), (1, 1024, 768), (2, 300, 7)])
+@pytest.mark.parametrize("with_state", [False, True], ids=["empty", "state"])
+def test_chunk_two_walkers(B, T, C, with_state):
+    """fp32 chunked scan over two to four 256-token tiles, where a workgroup
+    runs two walkers (the first half of the tiles from the initial state, the
+    second half from the first walker's final state): odd tile counts, a
+    ragged last tile, idle channel threads, several groups per row."""
+    say(f"chunk two walkers B={B} T={T} C={C} state={with_state}")
+    w, u, k, v = make_case(WL3, B, T, C)
+    s0 = random_state(B, C, 6) if with_state else None
+    got, gst = gpu_forward(w, u, k, v, "f32", state_in=s0, path="chunk")
+    ref, rst = wkv_recurrent(w, u, k, v, None if s0 is None else s0.astype(np.float64))
+    assert_out_close(got, ref, v, F32_TOL)
+    assert_state_close(gst, rst, F32_TOL)
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_state_in_place(path):
     B, T, C = 2, 200, 32

@@ -192,7 +192,7 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
   if (path == WKV_PATH_SEQ) {
     e = wkv::launch_seq(a, io, wkv::seq_vec_width(io, C, a), stream);
   } else if (path == WKV_PATH_CHUNK) {
-    e = wkv::launch_chunk(a, io, wkv::chunk_vec_width(io, C, a), stream);
+    e = wkv::launch_chunk(a, io, wkv::chunk_vec_width(io, C, a), cu_count(dev), stream);
   } else {
     const int vec = wkv::lookback_vec_width(io, C, a);
     if (!have_ws || workspace_bytes < wkv::lookback_workspace_bytes(vec, B, T, C))

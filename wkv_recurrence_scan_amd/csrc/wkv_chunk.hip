@@ -123,21 +123,6 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   float wd[V], ub[V];  // decay w and bonus u of the V channels
   IoF32::load<V, false>(w + cc, wd);
   IoF32::load<V, false>(u + cc, ub);
-  float cb[V];
-  bonus_ratios(wd, ub, cb);
-  const bool fast = wave_fast_ok(wd, ub);
-  Lane carry[V];
-  if (state_in != nullptr) {
-    float n[V], d[V], m[V];
-    IoF32::load<V, false>(state_in + lane0, n);
-    IoF32::load<V, false>(state_in + plane + lane0, d);
-    IoF32::load<V, false>(state_in + 2 * plane + lane0, m);
-#pragma unroll
-    for (int j = 0; j < V; ++j) carry[j] = lane_from_state(n[j], d[j], m[j]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < V; ++j) carry[j] = lane_empty();
-  }
 
   const int64_t base = b * T * C + cc + static_cast<int64_t>(sub) * L * C;
   const typename IoT::elem* kp = k + base;
@@ -162,12 +147,29 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   auto load = [&](ChunkRegs<V, L, G>& r, int64_t t) {
     chunk_load<IoT, V, L, false, G>(r, kp + t * step, vp + t * step, at(rp, t), C, L);
   };
+  if (full > 0) load(A, 0);
+  // what needs w, u and the initial state is worked out once the first
+  // tile's loads are in flight (each of these waits for its loads)
+  float cb[V];
+  bonus_ratios(wd, ub, cb);
+  const bool fast = wave_fast_ok(wd, ub);
+  Lane carry[V];
+  if (state_in != nullptr) {
+    float n[V], d[V], m[V];
+    IoF32::load<V, false>(state_in + lane0, n);
+    IoF32::load<V, false>(state_in + plane + lane0, d);
+    IoF32::load<V, false>(state_in + 2 * plane + lane0, m);
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = lane_from_state(n[j], d[j], m[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = lane_empty();
+  }
   auto tile_of = [&](const ChunkRegs<V, L, G>& r, int64_t t) {
     chunk_tile<IoT, V, LC, PS, W, L, false, G, CK>(r, L, carry, wd, ub, cb, fast, tot[t & 1],
                                                    op + t * step, C, cvalid, wave, sl, cl,
                                                    ck_at(t));
   };
-  if (full > 0) load(A, 0);
   int64_t tile = 0;
   for (; tile + 2 < full; tile += 2) {
     load(Bf, tile + 1);
@@ -212,6 +214,207 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
 // (fp32), so a load instruction reads whole lines from two rows.
 constexpr int kLC = 32, kPS = 2;
 
+// ------------------------------------------------ two walkers per workgroup
+//
+// The kernel above walks a workgroup's tiles one after another, so its time
+// is the sum of their latency chains (load wait, summary, scans, re-run).
+// With at most four tiles per sequence the workgroup is split into two
+// walkers of kSplitW waves, each loading its half of the tiles at once:
+// walker 0 walks the first half from the initial state as above; walker 1
+// summarises and scans the second half meanwhile. Walker 0 knows its final
+// state as soon as its last tile is scanned, hands it to walker 1 through LDS
+// and re-runs that tile while walker 1 re-runs its own tiles from it. Every
+// tile is still read from HBM once. Both walkers pass the same three
+// barriers. Measured on MI355X at B=8 T=1024 C=768 fp32 (traced per
+// workgroup): the two halves' tiles arrive about 3 and 6 us after the start
+// under the launch's load burst, and the re-runs then overlap.
+constexpr int kSplitW = 8, kSplitL = 16, kSplitMaxTiles = 4;
+constexpr int64_t kSplitTile = int64_t{kSplitW} * kPS * kSplitL;
+
+template <typename IoT, int V, int L, bool G, bool CK>
+__global__ __launch_bounds__(128 * kSplitW) void wkv_chunk_split_kernel(
+    int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
+    const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
+    const typename IoT::elem* __restrict__ rg, const float* __restrict__ state_in,
+    typename IoT::elem* __restrict__ out, float* __restrict__ state_out,
+    int64_t groups_per_row, float4* __restrict__ ckpt) {
+  constexpr int W = kSplitW, LC = kLC, PS = kPS;
+  constexpr int CH = LC * V;      // channels per workgroup
+  constexpr int TL = W * PS * L;  // tokens per tile
+  __shared__ Seg tot[2][2][W][CH];  // [walker][tile slot]
+  __shared__ Lane hand[CH];         // walker 0's final state, for walker 1
+
+  const int tid = threadIdx.x;
+  const int walker = tid / (64 * W);
+  const int wave = (tid >> 6) % W;  // inside the walker
+  const int lane = tid & 63;
+  const int cl = lane % LC;
+  const int sl = lane / LC;
+  const int sub = wave * PS + sl;
+
+  const int64_t g = xcd_swizzle(blockIdx.x, B * groups_per_row);
+  const int64_t b = g / groups_per_row;
+  const int64_t c0 = (g - b * groups_per_row) * CH + cl * V;
+  const bool cvalid = c0 < C;
+  const int64_t cc = cvalid ? c0 : C - V;  // idle tail threads mirror the last channels
+  const int64_t plane = B * C;
+  const int64_t lane0 = b * C + cc;
+
+  float wd[V], ub[V];
+  IoF32::load<V, false>(w + cc, wd);
+  IoF32::load<V, false>(u + cc, ub);
+
+  // tiles: walker 0 takes the first ceil(n / 2), walker 1 the rest (the
+  // launcher guarantees 1 <= n <= kSplitMaxTiles)
+  const int64_t n = (T + TL - 1) / TL;
+  const int64_t n0 = (n + 1) / 2;
+  const int64_t t0 = walker == 0 ? 0 : n0;
+  const int cnt = static_cast<int>(walker == 0 ? n0 : n - n0);
+
+  const int64_t base = b * T * C + cc + static_cast<int64_t>(sub) * L * C;
+  const typename IoT::elem* kp = k + base;
+  const typename IoT::elem* vp = v + base;
+  const typename IoT::elem* rp = G ? rg + base : nullptr;
+  typename IoT::elem* op = out + base;
+  const int64_t step = static_cast<int64_t>(TL) * C;
+  auto at = [&](const typename IoT::elem* p, int64_t t) { return G ? p + t * step : p; };
+  auto full = [&](int64_t t) { return (t + 1) * TL <= T; };
+  auto nvalid_of = [&](int64_t t) {
+    const int64_t left = T - (t * TL + static_cast<int64_t>(sub) * L);
+    return left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
+  };
+  auto ck_at = [&](int64_t t) {
+    return CkOut{ckpt, plane, lane0, t * TL + static_cast<int64_t>(sub) * L};
+  };
+
+  // both of the walker's tiles are loaded up front
+  ChunkRegs<V, L, G> R[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = t0 + i;
+    if (i < cnt) {
+      if (full(t)) {
+        chunk_load<IoT, V, L, false, G>(R[i], kp + t * step, vp + t * step, at(rp, t), C, L);
+      } else {
+        chunk_load<IoT, V, L, true, G>(R[i], kp + t * step, vp + t * step, at(rp, t), C,
+                                       nvalid_of(t));
+      }
+    }
+  }
+
+  // (what needs w, u and the initial state waits for their loads: after
+  // the tiles' loads are issued)
+  float cb[V];
+  bonus_ratios(wd, ub, cb);
+  const bool fast = wave_fast_ok(wd, ub);
+  Lane carry[V];
+  if (state_in != nullptr) {
+    float nn[V], d[V], m[V];
+    IoF32::load<V, false>(state_in + lane0, nn);
+    IoF32::load<V, false>(state_in + plane + lane0, d);
+    IoF32::load<V, false>(state_in + 2 * plane + lane0, m);
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = lane_from_state(nn[j], d[j], m[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = lane_empty();
+  }
+
+  // The state in front of this thread's sub-chunk of a scanned tile: the
+  // carry absorbs the tile's wave totals one by one (taken when its own wave
+  // comes up), then the sub-chunks before it in its wave; the carry moves past
+  // the tile. The same folds in the same order as the one-walker kernel, so
+  // both give the same bits.
+  auto enter = [&](Lane (&pre)[V], Seg (*totals)[CH], const Seg (&exc)[V]) {
+#pragma unroll
+    for (int jj = 0; jj < W; ++jj) {
+      if (jj == wave) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) pre[j] = carry[j];
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) lane_absorb(carry[j], totals[jj][cl * V + j], wd[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) lane_absorb(pre[j], exc[j], wd[j]);
+  };
+  auto rerun = [&](Lane (&pre)[V], const ChunkRegs<V, L, G>& r, int64_t t) {
+    if (full(t)) {
+      rescan_sel<IoT, V, L, false, G, CK>(fast, pre, r, wd, ub, cb, L, cvalid, op + t * step, C,
+                                          ck_at(t));
+    } else {
+      rescan_sel<IoT, V, L, true, G, CK>(fast, pre, r, wd, ub, cb, nvalid_of(t), cvalid,
+                                         op + t * step, C, ck_at(t));
+    }
+  };
+
+  // Walker 0 re-runs a tile that is not its last as soon as the tile's scan
+  // is complete; for its last tile it only works out the final state and
+  // hands it over before the third barrier, and re-runs that tile after it,
+  // side by side with walker 1's re-runs. Walker 1 folds its tiles' totals,
+  // which stay in LDS, once the state arrives.
+  Seg exc[2][V];
+  Lane pre_last[V];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = t0 + i;
+    if (i < cnt) {
+      if (full(t)) {
+        tile_scan_post<V, LC, PS, L, false, G>(R[i], wd, L, tot[walker][i], wave, exc[i]);
+      } else {
+        tile_scan_post<V, LC, PS, L, true, G>(R[i], wd, nvalid_of(t), tot[walker][i], wave,
+                                              exc[i]);
+      }
+    }
+    __syncthreads();
+    if (walker == 0 && i < cnt) {
+      if (i + 1 < cnt) {
+        Lane pre[V];
+        enter(pre, tot[0][i], exc[i]);
+        rerun(pre, R[i], t);
+      } else {
+        enter(pre_last, tot[0][i], exc[i]);
+        if (sub == 0) {
+#pragma unroll
+          for (int j = 0; j < V; ++j) hand[cl * V + j] = carry[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (walker == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i + 1 == cnt) rerun(pre_last, R[i], t0 + i);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) carry[j] = hand[cl * V + j];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i < cnt) {
+        Lane pre[V];
+        enter(pre, tot[1][i], exc[i]);
+        rerun(pre, R[i], t0 + i);
+      }
+    }
+    // walker 1 ends with the final state (walker 0's when it has no tile)
+    if (state_out != nullptr && sub == 0 && cvalid) {
+      float nn[V], d[V], m[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        nn[j] = carry[j].n;
+        d[j] = carry[j].d;
+        m[j] = lane_max_exp(carry[j], wd[j]);
+      }
+      IoF32::store<V, false>(state_out + lane0, nn);
+      IoF32::store<V, false>(state_out + plane + lane0, d);
+      IoF32::store<V, false>(state_out + 2 * plane + lane0, m);
+    }
+  }
+}
+
+
 // Workgroup shape by sequence length (measured on MI355X): short sequences
 // want the fewest serial tiles (B=8 T=1024 C=768: 8 waves of 16 tokens, 24.6
 // us, against 25.7-27.2 for 8 x 8, 4 x 16, 16 x 8 and 4 x 32); long ones
@@ -247,10 +450,41 @@ hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
                         : launch_chunk_g<IoT, V, W, L, false, false>(a, st);
 }
 
+template <typename IoT, int V, bool G, bool CK>
+hipError_t launch_chunk_split_g(const FwdArgs& a, hipStream_t st) {
+  constexpr int CH = kLC * V;
+  const int64_t gpr = (a.C + CH - 1) / CH;
+  const int64_t blocks = a.B * gpr;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((wkv_chunk_split_kernel<IoT, V, kSplitL, G, CK>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(128 * kSplitW), 0, st, a.B, a.T,
+                     a.C, a.w, a.u, static_cast<const typename IoT::elem*>(a.k),
+                     static_cast<const typename IoT::elem*>(a.v),
+                     static_cast<const typename IoT::elem*>(a.r), a.state_in,
+                     static_cast<typename IoT::elem*>(a.out), a.state_out, gpr,
+                     reinterpret_cast<float4*>(a.ckpt));
+  return hipGetLastError();
+}
+
 constexpr int64_t kShortT = 256, kLongT = 2048;
 
 template <typename IoT, int V>
-hipError_t launch_chunk_v(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_chunk_v(const FwdArgs& a, int cus, hipStream_t st) {
+  if constexpr (std::is_same<IoT, IoF32>::value && V == 1) {
+    // ungated fp32 sequences of two to four 256-token tiles whose workgroups
+    // each get a CU of their own: two walkers per workgroup (measured on
+    // MI355X: B=8 T=1024 C=768, 192 workgroups, 22.0 against 22.6 us; with
+    // more workgroups than CUs the one-walker kernel's two workgroups per CU
+    // win, B=256 T=512 C=768 223 against 265 us). The gated form would not
+    // fit its two tiles of k, v and r in the 128 registers a 1024-thread
+    // workgroup allows.
+    const int64_t blocks = a.B * ((a.C + kLC * V - 1) / (kLC * V));
+    if (a.T > kShortT && a.T <= kSplitMaxTiles * kSplitTile && a.r == nullptr &&
+        blocks <= cus) {
+      return a.ckpt != nullptr ? launch_chunk_split_g<IoT, V, false, true>(a, st)
+                               : launch_chunk_split_g<IoT, V, false, false>(a, st);
+    }
+  }
   if (a.T <= kShortT) return launch_chunk_t<IoT, V, 8, 4>(a, st);
   if (a.T <= kLongT) return launch_chunk_t<IoT, V, 8, 16>(a, st);
   return launch_chunk_t<IoT, V, 8, 8>(a, st);
@@ -270,10 +504,10 @@ int chunk_vec_width(int io, int64_t C, const FwdArgs& a) {
   return ok ? 2 : 1;
 }
 
-hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s) {
-  if (io == kF32) return launch_chunk_v<IoF32, 1>(a, s);
-  if (vec == 2) return launch_chunk_v<IoBf16, 2>(a, s);
-  return launch_chunk_v<IoBf16, 1>(a, s);
+hipError_t launch_chunk(const FwdArgs& a, int io, int vec, int cus, hipStream_t s) {
+  if (io == kF32) return launch_chunk_v<IoF32, 1>(a, cus, s);
+  if (vec == 2) return launch_chunk_v<IoBf16, 2>(a, cus, s);
+  return launch_chunk_v<IoBf16, 1>(a, cus, s);
 }
 
 }  // namespace wkv

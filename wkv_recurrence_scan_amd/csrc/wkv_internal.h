@@ -185,7 +185,9 @@ constexpr int64_t kShiftMaxP = 8;
 hipError_t launch_shift(const ShiftArgs& a, int io, hipStream_t s);
 
 hipError_t launch_seq(const FwdArgs& a, int io, int vec, hipStream_t s);
-hipError_t launch_chunk(const FwdArgs& a, int io, int vec, hipStream_t s);
+// cus: compute units of the device (the two-walker kernel serves grids that
+// give each workgroup a CU of its own)
+hipError_t launch_chunk(const FwdArgs& a, int io, int vec, int cus, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, int io, int vec, hipStream_t s);
 // T == 0: state_out <- state_in, or the empty state when state_in is null.
 hipError_t launch_state_copy(int64_t B, int64_t C, const float* state_in, float* state_out,

@@ -92,13 +92,14 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<V, L, G>& r,
 // (sl, cl) of wave `wave` holds sub-chunk wave*PS + sl of channel group cl.
 // Returns per thread the segments before its sub-chunk inside its wave (exc),
 // the totals of the waves before its own (before) and the whole tile
-// (whole). tot is LDS scratch of W x CH segments; the call synchronises the
-// workgroup once.
-template <int V, int LC, int PS, int W, int L, bool MASKED, bool G>
-__device__ __forceinline__ void tile_scan(const ChunkRegs<V, L, G>& r, const float (&wd)[V], int nvalid,
-                                          Seg (*tot)[LC * V], Seg (&exc)[V], Seg (&before)[V],
-                                          Seg (&whole)[V]) {
-  const int wave = threadIdx.x >> 6;
+// (whole). tot is LDS scratch of W x CH segments. In two halves around one
+// workgroup barrier, which the caller places (tile_scan does both): the first
+// summarises, scans inside the wave and posts the wave's total; the second
+// reads the totals of all W waves.
+template <int V, int LC, int PS, int L, bool MASKED, bool G>
+__device__ __forceinline__ void tile_scan_post(const ChunkRegs<V, L, G>& r, const float (&wd)[V],
+                                               int nvalid, Seg (*tot)[LC * V], int wave,
+                                               Seg (&exc)[V]) {
   const int lane = threadIdx.x & 63;
   const int cl = lane % LC;
   const int sl = lane / LC;
@@ -130,7 +131,12 @@ __device__ __forceinline__ void tile_scan(const ChunkRegs<V, L, G>& r, const flo
 #pragma unroll
     for (int j = 0; j < V; ++j) tot[wave][cl * V + j] = inc[j];
   }
-  __syncthreads();
+}
+
+template <int V, int LC, int W>
+__device__ __forceinline__ void tile_scan_totals(const float (&wd)[V], Seg (*tot)[LC * V], int wave,
+                                                 Seg (&before)[V], Seg (&whole)[V]) {
+  const int cl = (threadIdx.x & 63) % LC;
 #pragma unroll
   for (int j = 0; j < V; ++j) whole[j] = seg_identity();
 #pragma unroll
@@ -142,6 +148,16 @@ __device__ __forceinline__ void tile_scan(const ChunkRegs<V, L, G>& r, const flo
 #pragma unroll
     for (int j = 0; j < V; ++j) whole[j] = seg_combine(whole[j], tot[jj][cl * V + j], wd[j]);
   }
+}
+
+template <int V, int LC, int PS, int W, int L, bool MASKED, bool G>
+__device__ __forceinline__ void tile_scan(const ChunkRegs<V, L, G>& r, const float (&wd)[V], int nvalid,
+                                          Seg (*tot)[LC * V], Seg (&exc)[V], Seg (&before)[V],
+                                          Seg (&whole)[V]) {
+  const int wave = threadIdx.x >> 6;
+  tile_scan_post<V, LC, PS, L, MASKED, G>(r, wd, nvalid, tot, wave, exc);
+  __syncthreads();
+  tile_scan_totals<V, LC, W>(wd, tot, wave, before, whole);
 }
 
 // Where a prefill saves the backward pass's checkpoints (fp32, one channel
