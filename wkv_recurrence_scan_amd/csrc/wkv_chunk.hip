@@ -219,15 +219,18 @@ constexpr int kLC = 32, kPS = 2;
 // The kernel above walks a workgroup's tiles one after another, so its time
 // is the sum of their latency chains (load wait, summary, scans, re-run).
 // With at most four tiles per sequence the workgroup is split into two
-// walkers of kSplitW waves, each loading its half of the tiles at once:
-// walker 0 walks the first half from the initial state as above; walker 1
-// summarises and scans the second half meanwhile. Walker 0 knows its final
+// walkers of kSplitW waves, each loading both of its tiles at once: walker 0
+// walks the first half of the tiles from the initial state as above; walker
+// 1 summarises and scans the second half meanwhile. Walker 0 knows its final
 // state as soon as its last tile is scanned, hands it to walker 1 through LDS
-// and re-runs that tile while walker 1 re-runs its own tiles from it. Every
-// tile is still read from HBM once. Both walkers pass the same three
-// barriers. Measured on MI355X at B=8 T=1024 C=768 fp32 (traced per
-// workgroup): the two halves' tiles arrive about 3 and 6 us after the start
-// under the launch's load burst, and the re-runs then overlap.
+// and re-runs that tile while walker 1 re-runs its two tiles from it, side by
+// side. Every tile is still read from HBM once, and the folds are the
+// one-walker kernel's, in the same order, so both kernels give the same bits.
+// Measured on MI355X at B=8 T=1024 C=768 fp32: 21.7-22.1 us per launch
+// against 22.6; a per-workgroup trace shows the launch's loads arriving 3 to
+// 9 us after the start and the last stores leaving at about 15 us, so what
+// is left is the memory system's time for the loads and stores, not the
+// chain of tiles.
 constexpr int kSplitW = 8, kSplitL = 16, kSplitMaxTiles = 4;
 constexpr int64_t kSplitTile = int64_t{kSplitW} * kPS * kSplitL;
 
@@ -287,20 +290,25 @@ __global__ __launch_bounds__(128 * kSplitW) void wkv_chunk_split_kernel(
     return CkOut{ckpt, plane, lane0, t * TL + static_cast<int64_t>(sub) * L};
   };
 
-  // both of the walker's tiles are loaded up front
+  // A walker loads both of its tiles at once: walker 0 at the start, walker 1
+  // after the first barrier (see below), so that walker 0's tiles are not
+  // queued behind its.
   ChunkRegs<V, L, G> R[2];
+  auto load_tiles = [&]() {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t t = t0 + i;
-    if (i < cnt) {
-      if (full(t)) {
-        chunk_load<IoT, V, L, false, G>(R[i], kp + t * step, vp + t * step, at(rp, t), C, L);
-      } else {
-        chunk_load<IoT, V, L, true, G>(R[i], kp + t * step, vp + t * step, at(rp, t), C,
-                                       nvalid_of(t));
+    for (int i = 0; i < 2; ++i) {
+      const int64_t t = t0 + i;
+      if (i < cnt) {
+        if (full(t)) {
+          chunk_load<IoT, V, L, false, G>(R[i], kp + t * step, vp + t * step, at(rp, t), C, L);
+        } else {
+          chunk_load<IoT, V, L, true, G>(R[i], kp + t * step, vp + t * step, at(rp, t), C,
+                                         nvalid_of(t));
+        }
       }
     }
-  }
+  };
+  load_tiles();
 
   // (what needs w, u and the initial state waits for their loads: after
   // the tiles' loads are issued)
@@ -348,38 +356,55 @@ __global__ __launch_bounds__(128 * kSplitW) void wkv_chunk_split_kernel(
     }
   };
 
-  // Walker 0 re-runs a tile that is not its last as soon as the tile's scan
-  // is complete; for its last tile it only works out the final state and
-  // hands it over before the third barrier, and re-runs that tile after it,
-  // side by side with walker 1's re-runs. Walker 1 folds its tiles' totals,
-  // which stay in LDS, once the state arrives.
+  // Three barriers. Walker 1 runs one barrier behind walker 0, so that walker
+  // 0 never waits for walker 1's data:
+  //   barrier 1: walker 0's first tile scanned (walker 1 posts nothing);
+  //   barrier 2: walker 0's second tile (after re-running its first) and
+  //              walker 1's first tile scanned;
+  //   barrier 3: walker 1's second tile scanned; walker 0 has handed over its
+  //              final state, worked out from its last tile's scan.
+  // Then walker 0 re-runs its last tile and walker 1 its tiles, from the
+  // state handed over, side by side. A tile's wave totals stay in LDS
+  // (tot[walker][slot]) until the end.
   Seg exc[2][V];
   Lane pre_last[V];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  auto post = [&](int i) {
     const int64_t t = t0 + i;
-    if (i < cnt) {
-      if (full(t)) {
-        tile_scan_post<V, LC, PS, L, false, G>(R[i], wd, L, tot[walker][i], wave, exc[i]);
-      } else {
-        tile_scan_post<V, LC, PS, L, true, G>(R[i], wd, nvalid_of(t), tot[walker][i], wave,
-                                              exc[i]);
-      }
+    if (full(t)) {
+      tile_scan_post<V, LC, PS, L, false, G>(R[i], wd, L, tot[walker][i], wave, exc[i]);
+    } else {
+      tile_scan_post<V, LC, PS, L, true, G>(R[i], wd, nvalid_of(t), tot[walker][i], wave,
+                                            exc[i]);
     }
-    __syncthreads();
-    if (walker == 0 && i < cnt) {
-      if (i + 1 < cnt) {
-        Lane pre[V];
-        enter(pre, tot[0][i], exc[i]);
-        rerun(pre, R[i], t);
-      } else {
-        enter(pre_last, tot[0][i], exc[i]);
-        if (sub == 0) {
+  };
+  // walker 0's slot i is scanned: re-run it now unless it is its last, whose
+  // state goes to walker 1 first
+  auto w0_after = [&](int i) {
+    if (i + 1 < cnt) {
+      Lane pre[V];
+      enter(pre, tot[0][i], exc[i]);
+      rerun(pre, R[i], t0 + i);
+    } else {
+      enter(pre_last, tot[0][i], exc[i]);
+      if (sub == 0) {
 #pragma unroll
-          for (int j = 0; j < V; ++j) hand[cl * V + j] = carry[j];
-        }
+        for (int j = 0; j < V; ++j) hand[cl * V + j] = carry[j];
       }
     }
+  };
+  if (walker == 0) post(0);  // walker 0 always has a tile
+  __syncthreads();
+  if (walker == 0) {
+    w0_after(0);
+    if (cnt > 1) post(1);
+  } else if (cnt > 0) {
+    post(0);
+  }
+  __syncthreads();
+  if (walker == 0) {
+    if (cnt > 1) w0_after(1);
+  } else if (cnt > 1) {
+    post(1);
   }
   __syncthreads();
   if (walker == 0) {
@@ -390,13 +415,29 @@ __global__ __launch_bounds__(128 * kSplitW) void wkv_chunk_split_kernel(
   } else {
 #pragma unroll
     for (int j = 0; j < V; ++j) carry[j] = hand[cl * V + j];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (i < cnt) {
-        Lane pre[V];
-        enter(pre, tot[1][i], exc[i]);
-        rerun(pre, R[i], t0 + i);
+    if (cnt == 2) {
+      // both states first (each tile's carry-in comes from the scans), then
+      // the two re-runs side by side; only the second tile can be partial
+      Lane pa[V], pb[V];
+      enter(pa, tot[1][0], exc[0]);
+      enter(pb, tot[1][1], exc[1]);
+      const int64_t ta = t0, tb = t0 + 1;
+      auto both = [&](auto fast_c, auto masked_c) {
+        rescan2<IoT, V, L, decltype(masked_c)::value, decltype(fast_c)::value, G, CK>(
+            pa, R[0], op + ta * step, ck_at(ta), pb, R[1], nvalid_of(tb), op + tb * step,
+            ck_at(tb), wd, ub, cb, cvalid, C);
+      };
+      const std::true_type yes{};
+      const std::false_type no{};
+      if (full(tb)) {
+        if (fast) both(yes, no); else both(no, no);
+      } else {
+        if (fast) both(yes, yes); else both(no, yes);
       }
+    } else if (cnt == 1) {
+      Lane pre[V];
+      enter(pre, tot[1][0], exc[0]);
+      rerun(pre, R[0], t0);
     }
     // walker 1 ends with the final state (walker 0's when it has no tile)
     if (state_out != nullptr && sub == 0 && cvalid) {

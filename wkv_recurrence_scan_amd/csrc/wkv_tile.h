@@ -201,6 +201,46 @@ __device__ __forceinline__ void rescan(Lane (&pre)[V], const ChunkRegs<V, L, G>&
   }
 }
 
+// Two re-runs side by side, token i of tile a then token i of tile b: the
+// two recurrences are independent, so their latency chains overlap. Tile a
+// is complete; tile b has nvalid_b tokens when MASKED_B (its missing tokens
+// were loaded as zeros and are stepped over without being stored: the state
+// they leave is not used).
+template <typename IoT, int V, int L, bool MASKED_B, bool FAST, bool G, bool CK = false>
+__device__ __forceinline__ void rescan2(Lane (&pa)[V], const ChunkRegs<V, L, G>& ra,
+                                        typename IoT::elem* __restrict__ opa, const CkOut& cka,
+                                        Lane (&pb)[V], const ChunkRegs<V, L, G>& rb, int nvalid_b,
+                                        typename IoT::elem* __restrict__ opb, const CkOut& ckb,
+                                        const float (&wd)[V], const float (&ub)[V],
+                                        const float (&cb)[V], bool cvalid, int64_t C) {
+  static_assert(!CK || V == 1, "checkpoints are saved by one-channel threads");
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const bool bvalid = !MASKED_B || i < nvalid_b;
+    if constexpr (CK) {
+      const int64_t ta = cka.tok0 + i, tb = ckb.tok0 + i;
+      if (cvalid && (ta % kCkptTokens) == 0)
+        cka.p[(ta / kCkptTokens) * cka.lanes + cka.lane] =
+            make_float4(pa[0].n, pa[0].d, pa[0].base, pa[0].age);
+      if (cvalid && bvalid && (tb % kCkptTokens) == 0)
+        ckb.p[(tb / kCkptTokens) * ckb.lanes + ckb.lane] =
+            make_float4(pb[0].n, pb[0].d, pb[0].base, pb[0].age);
+    }
+    float oa[V], ob[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      oa[j] = step_sel<FAST>(pa[j], ra.k[i][j], ra.v[i][j], wd[j], ub[j], cb[j]);
+      ob[j] = step_sel<FAST>(pb[j], rb.k[i][j], rb.v[i][j], wd[j], ub[j], cb[j]);
+      if constexpr (G) {
+        oa[j] *= gate(ra.r[i][j]);
+        ob[j] *= gate(rb.r[i][j]);
+      }
+    }
+    if (cvalid) IoT::template store<V, true>(opa + i * C, oa);
+    if (cvalid && bvalid) IoT::template store<V, true>(opb + i * C, ob);
+  }
+}
+
 template <typename IoT, int V, int L, bool MASKED, bool G, bool CK = false>
 __device__ __forceinline__ void rescan_sel(bool fast, Lane (&pre)[V], const ChunkRegs<V, L, G>& r,
                                            const float (&wd)[V], const float (&ub)[V],
