@@ -160,9 +160,18 @@ def time_prefill(layers, steps, warmup, path="auto"):
 
 
 def prefill_kernel(path, wl):
-    """Name of the kernel function a prefill path launches for workload wl."""
+    """Name of the kernel function a prefill path launches for workload wl
+    (the library's launch rules: the bf16 walk stages whole 512-channel row
+    pieces through LDS; ungated fp32 chunked scans of two to four 256-token
+    tiles whose workgroups of 32 channels each get a CU run two walkers)."""
+    import torch
+
     if path == "seq":
         return "wkv_seq_tile_kernel" if wl.io == "bf16" and wl.C % 512 == 0 else "wkv_seq_kernel"
+    if path == "chunk" and wl.io == "f32" and 256 < wl.T <= 1024:
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        if wl.B * -(-wl.C // 32) <= cus:
+            return "wkv_chunk_split_kernel"
     return f"wkv_{path}_kernel"
 
 
@@ -527,9 +536,12 @@ def time_decay(wl, dev, reps=50):
     ct = wl.B * wl.T * wl.C
     abytes = 16 * ct + 12 * wl.B * wl.C + 4 * wl.C
     achieved = abytes / (us * 1e-6) / 1e9
-    path = W.wkv_select_path(wl.B, wl.T, wl.C, W.WKV_IO_F32)
+    # the per-token-decay forward's AUTO: the sequential scan wherever B*C
+    # lanes give every SIMD a wave (or T < 32), else the chunked scan
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    path = "seq" if wl.T < 32 or -(-wl.B * wl.C // 64) >= 4 * cus else "chunk"
     return {"workload": f"{wl.name}, one layer, per-token decay", "B": wl.B, "T": wl.T,
-            "C": wl.C, "path": "chunk" if path == "lookback" else path,
+            "C": wl.C, "path": path,
             "value": round(ct / (us * 1e-6) / 1e9, 3), "unit": "G channel-tokens/s",
             "us_per_call": round(us, 2),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,

@@ -201,7 +201,11 @@ int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path);
 /* The kernel WKV_PATH_AUTO uses for these sizes on the current device when a
  * workspace is available (WKV_PATH_SEQ, WKV_PATH_CHUNK or WKV_PATH_LOOKBACK;
  * without one, LOOKBACK becomes WKV_PATH_CHUNK), or a negative wkv_status on
- * error. */
+ * error. This is the plain forward's choice; the gated, checkpointing and
+ * per-token-decay forms differ in one case: where B*C alone fills the GPU they
+ * always take WKV_PATH_SEQ, while the plain fp32 forward takes WKV_PATH_CHUNK
+ * for 512 <= T <= 2048 when a batch row's T * C * 4 bytes are not a power of
+ * two. */
 int wkv_select_path(int64_t B, int64_t T, int64_t C, int io);
 
 /* One decode step for B sequences at once (page "Linear attention without

@@ -64,21 +64,26 @@ constexpr int64_t kMaxBytes = int64_t(1) << 60;
 // HBM peak when a row's bytes (T * C * 4 for fp32) are a power of two but at
 // only 0.64-0.66 otherwise (the same walk over rows padded from 1.5 to 2 MiB
 // went from 0.66 to 0.71). The chunked scan keeps a few rows' tiles in
-// flight instead and holds 0.66 there, so fp32 rows of another size with
-// 512 to kChunkMaxT tokens take it. bf16 keeps the sequential scan, whose
-// LDS-staged tiles stay ahead of the chunked scan at every measured size.
+// flight instead and holds 0.66 there, so plain (ungated, constant-decay,
+// no checkpoints) fp32 rows of another size with 512 to kChunkMaxT tokens
+// take it. The other forms keep the sequential scan: their chunked kernels
+// hold more registers (three waves per SIMD instead of four) and lose there
+// (B=256 T=512 C=768: the checkpointing prefill 273 against 246 us, the
+// per-token decay 341 against 313). bf16 keeps the sequential scan too,
+// whose LDS-staged tiles stay ahead of the chunked scan at every measured
+// size.
 constexpr int64_t kChunkMaxT = 2048;
 
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev, bool have_ws) {
+int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev, bool have_ws, bool plain) {
   const int64_t per_thread = io == wkv::kBf16 ? 2 : 1;
   const int64_t waves = (B * C / per_thread + 63) / 64;
   if (T < 32) return WKV_PATH_SEQ;
   if (waves >= 4LL * cu_count(dev)) {
     int64_t row_bytes = 0;
-    const bool uneven_rows =
-        io == wkv::kF32 && (__builtin_mul_overflow(T * C, 4, &row_bytes) || !pow2(row_bytes));
+    const bool uneven_rows = plain && io == wkv::kF32 &&
+                             (__builtin_mul_overflow(T * C, 4, &row_bytes) || !pow2(row_bytes));
     return uneven_rows && T >= 512 && T <= kChunkMaxT ? WKV_PATH_CHUNK : WKV_PATH_SEQ;
   }
   return have_ws && T > kChunkMaxT ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
@@ -188,7 +193,8 @@ int forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u
     return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
   }
 
-  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, have_ws);
+  if (path == WKV_PATH_AUTO)
+    path = choose_path(B, T, C, io, dev, have_ws, !gated && ckpt == nullptr);
   if (path == WKV_PATH_SEQ) {
     e = wkv::launch_seq(a, io, wkv::seq_vec_width(io, C, a), stream);
   } else if (path == WKV_PATH_CHUNK) {
@@ -349,7 +355,7 @@ int forward_dd_impl(int64_t B, int64_t T, int64_t C, const void* w, const float*
     return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
   }
   const wkv::DdArgs a{B, T, C, w, u, k, v, state_in, out, state_out, ckpt};
-  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, false);
+  if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, false, false);
   const int vec = wkv::dd_vec_width(io, C, a);
   e = path == WKV_PATH_SEQ ? wkv::launch_dd_seq(a, io, vec, stream)
                            : wkv::launch_dd_chunk(a, io, vec, stream);
@@ -747,7 +753,7 @@ int wkv_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w, const f
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(WKV_ERR_DEVICE, e);
   const bool fits = need <= kScratchBytes;
-  const int chosen = path == WKV_PATH_AUTO ? choose_path(B, T, C, io, dev, fits) : path;
+  const int chosen = path == WKV_PATH_AUTO ? choose_path(B, T, C, io, dev, fits, true) : path;
   if (chosen != WKV_PATH_LOOKBACK)
     return forward_impl(B, T, C, w, u, k, v, nullptr, false, state_in, out, state_out, io, chosen,
                         nullptr, 0, stream);
@@ -823,7 +829,7 @@ int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
-    path = choose_path(B, T, C, io, dev, true);
+    path = choose_path(B, T, C, io, dev, true, true);
   }
   return path == WKV_PATH_LOOKBACK ? lookback_bytes(io, B, T, C) : 0;
 }
@@ -836,7 +842,7 @@ int wkv_select_path(int64_t B, int64_t T, int64_t C, int io) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return -fail(WKV_ERR_DEVICE, e);
-  return choose_path(B, T, C, io, dev, true);
+  return choose_path(B, T, C, io, dev, true, true);
 }
 
 int wkv_step(int64_t B, int64_t C, const float* w, const float* u, const float* k, const float* v,
