@@ -317,9 +317,10 @@ def time_backward(wl, dev, reps=10):
             "workspace_bytes": int(ws.numel())}
 
 
-def time_ckpt_pair(wl, dev, reps=10):
+def time_ckpt_pair(wl, dev, reps=10, gated=False):
     """A training layer's two calls both ways on workload wl's first layer
-    (fp32, seeded inputs and upstream gradient): the plain prefill then
+    (fp32, seeded inputs and upstream gradient; with the receptance gate and
+    its gradient when `gated`): the plain prefill then
     wkv_backward, which re-runs the recurrence for its own checkpoints, against
     wkv_forward_ckpt, which saves them while it runs, then wkv_backward_ckpt,
     which reads them. Microseconds per call from event pairs around `reps`
@@ -336,6 +337,7 @@ def time_ckpt_pair(wl, dev, reps=10):
     g = I.grad_out(wl)
     t = lambda a: torch.from_numpy(a).to(dev)
     dw, du, dk, dv, dg = t(w), t(u), t(k), t(v), t(g)
+    dr = t(I.receptance(wl)) if gated else None
     del k, v, g
     out, st = torch.empty_like(dk), torch.empty((3, wl.B, wl.C), device=dev)
     ck = torch.empty(W.ckpt_shape(wl.B, wl.T, wl.C), device=dev)
@@ -343,14 +345,18 @@ def time_ckpt_pair(wl, dev, reps=10):
     gw, gu = torch.empty_like(dw), torch.empty_like(dw)
     ws = torch.empty(max(W.wkv_backward_workspace_size(wl.B, wl.T, wl.C), 1), dtype=torch.uint8,
                      device=dev)
-    grads = (gk, gv, gw, gu, None)
+    grads = (gk, gv, gw, gu, None) + ((torch.empty_like(dk),) if gated else ())
+    if gated:
+        fwd = lambda: W.wkv_forward_gated(dw, du, dk, dv, dr, out=out, state_out=st)
+    else:
+        fwd = lambda: W.wkv_forward_ex(dw, du, dk, dv, out=out, state_out=st)
     calls = {
-        "forward": lambda: W.wkv_forward_ex(dw, du, dk, dv, out=out, state_out=st),
-        "backward": lambda: W.wkv_backward(dw, du, dk, dv, dg, want_gstate_in=False,
+        "forward": fwd,
+        "backward": lambda: W.wkv_backward(dw, du, dk, dv, dg, r=dr, want_gstate_in=False,
                                            workspace=ws, out=grads),
-        "forward_ckpt": lambda: W.wkv_forward_ckpt(dw, du, dk, dv, out=out, state_out=st,
+        "forward_ckpt": lambda: W.wkv_forward_ckpt(dw, du, dk, dv, dr, out=out, state_out=st,
                                                    ckpt=ck),
-        "backward_ckpt": lambda: W.wkv_backward(dw, du, dk, dv, dg, want_gstate_in=False,
+        "backward_ckpt": lambda: W.wkv_backward(dw, du, dk, dv, dg, r=dr, want_gstate_in=False,
                                                 workspace=ws, out=grads, ckpt=ck),
     }
     stream = torch.cuda.current_stream()
@@ -368,8 +374,10 @@ def time_ckpt_pair(wl, dev, reps=10):
         us[name] = e0.elapsed_time(e1) * 1e3 / reps
     ct = wl.B * wl.T * wl.C
     ck_bytes = W.wkv_ckpt_bytes(wl.B, wl.T, wl.C)
-    fbytes = 12 * ct + 12 * wl.B * wl.C + 8 * wl.C + ck_bytes
-    bbytes = 20 * ct + 16 * wl.C + ck_bytes
+    # the gate adds r to the forward's reads, and r read plus dL/dr written
+    # to the backward's
+    fbytes = (16 if gated else 12) * ct + 12 * wl.B * wl.C + 8 * wl.C + ck_bytes
+    bbytes = (28 if gated else 20) * ct + 16 * wl.C + ck_bytes
 
     def roof(nbytes, t_us):
         a = nbytes / (t_us * 1e-6) / 1e9
@@ -378,8 +386,9 @@ def time_ckpt_pair(wl, dev, reps=10):
 
     plain = us["forward"] + us["backward"]
     saved = us["forward_ckpt"] + us["backward_ckpt"]
-    return {"workload": f"{wl.name}, one layer, forward then backward", "B": wl.B, "T": wl.T,
-            "C": wl.C, "io": "f32", "ckpt_bytes": ck_bytes,
+    gate = ", gated output" if gated else ""
+    return {"workload": f"{wl.name}, one layer{gate}, forward then backward", "B": wl.B,
+            "T": wl.T, "C": wl.C, "io": "f32", "gated": gated, "ckpt_bytes": ck_bytes,
             "us_per_call": {k_: round(x, 2) for k_, x in us.items()},
             "value": round(ct / (saved * 1e-6) / 1e9, 3),
             "plain_value": round(ct / (plain * 1e-6) / 1e9, 3),
@@ -1094,6 +1103,9 @@ def main():
             _log(f"checkpointed forward + backward: {bwl.name} (one layer)")
             ext["checkpointed_training"].append(time_ckpt_pair(bwl, dev))
             torch.cuda.empty_cache()
+        _log(f"checkpointed forward + backward, gated: {shapes[0].name} (one layer)")
+        ext["checkpointed_training"].append(time_ckpt_pair(shapes[0], dev, gated=True))
+        torch.cuda.empty_cache()
         ext["per_token_decay"] = []
         for dwl_ in shapes:
             _log(f"per-token decay forward: {dwl_.name} (one layer)")
