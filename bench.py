@@ -953,6 +953,37 @@ def cpu_baselines(cfgs):
     return out
 
 
+def headline_record(records, args):
+    """The bench line's headline fields from the first prefill record, with
+    the other prefill records as `workloads`."""
+    head = records[0]
+    rec = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "G channel-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if head["io"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "B": head["B"], "T": head["T"], "C": head["C"],
+                   "layers": head["layers"], "io": head["io"], "path": head["path"],
+                   "launch": "hip_graph_per_step", "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "eager_value": head["eager_value"],
+    }
+    if head["io"] == "bf16":
+        rec["dtype_note"] = "bf16 k, v, out; fp32 state and arithmetic"
+    if "cpu_baseline" in head:
+        rec["cpu_baseline"] = head["cpu_baseline"]
+    rec["workloads"] = records[1:]
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -967,6 +998,9 @@ def main():
                          "matrix state, token shift)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill workloads (no decode, extended or CPU baseline)")
+    ap.add_argument("--extended-only", action="store_true",
+                    help="only the extended measurements (for counter runs of their kernels; the "
+                         "line then carries no headline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -978,6 +1012,8 @@ def main():
         sys.exit(2)
     if args.prefill_only:
         args.no_decode = args.no_backward = args.no_cpu_baseline = True
+    if args.extended_only:
+        args.no_decode = args.no_cpu_baseline = True
 
     from wkv_recurrence_scan_amd import inputs as I
 
@@ -1013,7 +1049,7 @@ def main():
         del a, b
 
     records = []
-    for c in prefill_cfgs:
+    for c in ([] if args.extended_only else prefill_cfgs):
         wl = I.WORKLOADS[c]
         if c == 2:
             wl = wl.scaled(decode_steps=0, name=names[2])
@@ -1029,31 +1065,10 @@ def main():
         del layers
         torch.cuda.empty_cache()
 
-    head = records[0]
-    rec = {
-        "metric": METRIC,
-        "value": head["value"],
-        "unit": "G channel-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if head["io"] == "bf16" else "f32",
-        "data": "synthetic",
-        "config": {"workload": head["workload"], "B": head["B"], "T": head["T"], "C": head["C"],
-                   "layers": head["layers"], "io": head["io"], "path": head["path"],
-                   "launch": "hip_graph_per_step", "parallelism": "single GPU"},
-        "roofline": head["roofline"],
-        "eager_value": head["eager_value"],
-    }
-    if head["io"] == "bf16":
-        rec["dtype_note"] = "bf16 k, v, out; fp32 state and arithmetic"
-    if "cpu_baseline" in head:
-        rec["cpu_baseline"] = head["cpu_baseline"]
-    rec["workloads"] = records[1:]
+    if args.extended_only:
+        rec = {"metric": METRIC, "note": "extended measurements only (no headline)"}
+    else:
+        rec = headline_record(records, args)
 
     if not args.no_decode:
         dwl = I.WORKLOADS[2]
