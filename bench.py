@@ -988,7 +988,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps before each timed loop (the GPU reaches its steady clocks "
+                         "after a few tens of milliseconds of work)")
     ap.add_argument("--config", type=int, default=4, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
