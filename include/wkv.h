@@ -83,7 +83,9 @@ enum { WKV_IO_F32 = 0, WKV_IO_BF16 = 1 };
  * decoupled look-back through a device workspace (small B*C, most
  * parallelism). AUTO picks SEQ when B*C alone fills the GPU, otherwise CHUNK
  * up to T = 2048 and, for longer sequences, LOOKBACK when a workspace is
- * given (CHUNK when not). */
+ * given (CHUNK when not); the plain (ungated, no checkpoints) fp32 forward
+ * also takes CHUNK where B*C fills the GPU, 512 <= T <= 2048 and a batch
+ * row's T * C * 4 bytes are not a power of two (see wkv_select_path). */
 enum { WKV_PATH_AUTO = 0, WKV_PATH_SEQ = 1, WKV_PATH_CHUNK = 2, WKV_PATH_LOOKBACK = 3 };
 
 /* Prefill / training form over a whole sequence (page "Linear attention
