@@ -155,8 +155,12 @@ def time_prefill(layers, steps, warmup, path="auto"):
     graph_ms = t0.elapsed_time(t1) / steps
     for c in calls:
         c.check()  # a look-back launch that failed to chain its segments raises
+    # non-finite values among the last replay's outputs and final states
+    nonfinite = sum(int((~torch.isfinite(c.out)).sum()) + int((~torch.isfinite(c.state_out)).sum())
+                    for c in calls)
     return {"graph_ms": graph_ms, "eager_ms": eager_ms, "kernel_ms": float(np.mean(kms)),
-            "kernel_ms_median": float(np.median(kms)), "wall_ms": wall_ms}
+            "kernel_ms_median": float(np.median(kms)), "wall_ms": wall_ms,
+            "nonfinite": nonfinite}
 
 
 def prefill_kernel(path, wl):
@@ -188,6 +192,7 @@ def prefill_record(wl, tm, path):
         "path": path, "value": round(ct_step / (tm["graph_ms"] * 1e-3) / 1e9, 3),
         "unit": "G channel-tokens/s", "ms_per_step": round(tm["graph_ms"], 5),
         "eager_value": round(ct_step / (tm["eager_ms"] * 1e-3) / 1e9, 3),
+        "nonfinite_outputs": tm["nonfinite"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(wl.name, kernel),
@@ -975,6 +980,7 @@ def headline_record(records, args):
                    "launch": "hip_graph_per_step", "parallelism": "single GPU"},
         "roofline": head["roofline"],
         "eager_value": head["eager_value"],
+        "nonfinite_outputs": head["nonfinite_outputs"],
     }
     if head["io"] == "bf16":
         rec["dtype_note"] = "bf16 k, v, out; fp32 state and arithmetic"
