@@ -45,7 +45,11 @@
 // workgroup, double-buffered, with the next chunk's global loads in flight
 // while the current one is computed; the staging threads turn lam into the
 // factor e^-lam and r into its gate, and also store k, v and the factors
-// transposed (channel-major) for the column reads of the causal sum.
+// transposed (channel-major) for the column reads of the causal sum. Every
+// wave needs all of the key-value products; each forms the part of their
+// 64-deep sum over its own 16 channels and the four parts are added through
+// LDS (one barrier), 36 matrix instructions per wave and chunk instead of 48
+// (measured on MI355X at B=256 T=512, 12 heads: 643 against 667 us).
 //
 // Segments. With few (batch, head) pairs the sequence is cut into P segments
 // (of a whole number of chunks) so that there are enough workgroups: a first
@@ -185,8 +189,8 @@ __device__ __forceinline__ float sel4(int q, float x0, float x1, float x2, float
 // chunk's decay factors of row 16w + n.
 template <bool READ, bool FULL>
 __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[kMsCol],
-                                          const MsKernelArgs& a, int64_t orow, int64_t tb,
-                                          int64_t tend, f4 (&S)[4]) {
+                                          f4 (*gpart)[64], const MsKernelArgs& a, int64_t orow,
+                                          int64_t tb, int64_t tend, f4 (&S)[4]) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
   const int w = threadIdx.x >> 6;
@@ -206,28 +210,35 @@ __device__ __forceinline__ float ms_chunk(const MsStage<READ>& st, float (*gt)[k
   const f4 kh = tail * st.ld4(i, St::kKD, 4 * q);
 
   if constexpr (READ) {
-    // token-major operands: token ms_token(n) of the keys and token n of the
-    // values at channels 16m + 4q + e
-    f4 kA[4], vG[4];
+    // token-major operands: token ms_token(n) of the keys at channels
+    // 16m + 4q + e, and token n of the values at this wave's channels 16w +
+    // 4q + e
+    f4 kA[4], vG;
     const int tn = ms_token(n);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kA[m][e] = st.row[16 * m + 4 * q + e][St::kK + tn];
-        vG[m][e] = st.row[16 * m + 4 * q + e][St::kV + n];
-      }
+      for (int e = 0; e < 4; ++e) kA[m][e] = st.row[16 * m + 4 * q + e][St::kK + tn];
     }
-    // G[s][ms_token(n)] for s = 4q + e, and the readout X[ms_token(4q + e)][i]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vG[e] = st.row[16 * w + 4 * q + e][St::kV + n];
+    // G[s][ms_token(n)] for s = 4q + e is a 64-deep sum over the head's
+    // channels: each wave forms the part over its own 16 (4 instead of 16
+    // matrix instructions) and the four parts meet in LDS; the readout
+    // X[ms_token(4q + e)][i] runs while the parts are exchanged
     f4 g = {0.0f, 0.0f, 0.0f, 0.0f}, x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g = mfma4(vG[e], sel4(w, kA[0][e], kA[1][e], kA[2][e], kA[3][e]), g);
+    gpart[w][lane] = g;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        g = mfma4(vG[m][e], kA[m][e], g);
-        x = mfma4(kA[m][e], S[m][e], x);
-      }
+      for (int e = 0; e < 4; ++e) x = mfma4(kA[m][e], S[m][e], x);
     }
+    __syncthreads();
+    g = gpart[0][lane];
+#pragma unroll
+    for (int u = 1; u < kMsWaves; ++u) g += gpart[u][lane];
     // G to this wave's LDS tile, token-major: gt[t][s]
     *reinterpret_cast<f4*>(&gt[tn][4 * q]) = g;
     __builtin_amdgcn_wave_barrier();
@@ -289,6 +300,7 @@ __device__ __forceinline__ float ms_walk(const MsKernelArgs& a, int64_t row0, in
                                          int64_t tend, f4 (&S)[4]) {
   __shared__ MsStage<READ> stage[2];
   __shared__ float gtile[READ ? kMsWaves : 1][kMsL][kMsCol];
+  __shared__ f4 gparts[READ ? kMsWaves : 1][64];  // each wave's part of the key-value products
   float prod = 1.0f;
   const int64_t nch = (tend - t0 + kMsL - 1) / kMsL;
   if (nch <= 0) return prod;
@@ -301,9 +313,9 @@ __device__ __forceinline__ float ms_walk(const MsKernelArgs& a, int64_t row0, in
   for (int64_t c = 0; c < nch; ++c) {
     const int64_t tb = t0 + c * kMsL;
     if (tb + kMsL <= tend) {
-      prod *= ms_chunk<READ, true>(stage[c & 1], gt, a, row0, tb, tend, S);
+      prod *= ms_chunk<READ, true>(stage[c & 1], gt, gparts, a, row0, tb, tend, S);
     } else {
-      prod *= ms_chunk<READ, false>(stage[c & 1], gt, a, row0, tb, tend, S);
+      prod *= ms_chunk<READ, false>(stage[c & 1], gt, gparts, a, row0, tb, tend, S);
     }
     // the next chunk goes into the other stage buffer, whose readers (chunk
     // c - 1) all passed the previous barrier
