@@ -21,9 +21,9 @@ WL4 = I.WORKLOADS[4]   # bf16, k ~ U(-20, 20) with 1% +-60 spikes
 
 # T around the chunked kernel's tiles (64 tokens for T <= 256, 256 up to
 # T = 2048, 128 beyond; its workgroup shape changes at T = 256 and T = 2048) and the look-back kernel's
-# segments (32 tokens for T <= 512, else 128; anchors every 8 segments), and C
-# around both kernels' 32-channel groups (64 for bf16); every kernel runs every
-# shape.
+# segments (32 tokens for T <= 512, 256 beyond; anchors every 8 segments), and C
+# around both kernels' 32-channel groups (64 for bf16, and for the look-back's
+# fp32 layout past 2048 tokens); every kernel runs every shape.
 SHAPES = [
     (1, 1, 1), (2, 2, 7), (1, 3, 16), (3, 31, 33), (2, 32, 5), (2, 63, 48), (2, 64, 64),
     (2, 65, 17), (1, 255, 16), (1, 256, 32), (1, 257, 80), (2, 511, 24), (1, 1000, 40),
@@ -260,15 +260,16 @@ def test_lookback_workspace_claim_tickets_and_error_word():
     """The look-back workspace after n launches: it is claimed for its layout
     (G << 32 | S), every channel group's ticket counter has advanced by
     exactly S (segments per group) per launch, which is what gives each
-    launch its own epoch, and the error word stays zero. T = 3000 uses
-    256-token segments, so S = 12."""
+    launch its own epoch, and the error word stays zero. T = 3000 takes the
+    plain fp32 layout for sequences past 2048 tokens: 64-channel groups and
+    256-token segments, so G = 2 * 2 and S = 12."""
     wl = WL3.scaled(B=2, T=3000, C=96)
     w, u = I.params(wl)
     k, v = I.kv(wl)
     ws = W.new_workspace(W.wkv_workspace_size(2, 3000, 96, W.WKV_IO_F32, "lookback"), "cuda")
     say("look-back workspace counters")
     ref, _ = wkv_recurrent(w, u, k, v)
-    groups, S = 2 * ((96 + 31) // 32), (3000 + 255) // 256
+    groups, S = 2 * ((96 + 63) // 64), (3000 + 255) // 256
     for n in range(3):
         out, _ = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
                                   workspace=ws)

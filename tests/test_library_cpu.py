@@ -84,6 +84,13 @@ def test_workspace_size_and_requirement_without_device():
     # inclusive prefix (n, d, base, age); T = 1024 uses 256-token segments
     groups = 8 * 768 // 32
     assert n == ((16 + 16 * groups + 255) // 256) * 256 + 8 * 768 * (1024 // 256) * 7 * 8
+    # past 2048 tokens the plain fp32 form takes 64-channel groups and the
+    # gated one 32-channel groups (256-token segments both): the size covers
+    # the larger, here the 64-channel layout's 128 word columns per row of 96
+    ctrl = lambda g: ((16 + 16 * g + 255) // 256) * 256  # noqa: E731
+    S = (3000 + 255) // 256
+    assert lib.wkv_workspace_size(2, 3000, 96, 0, lookback) == max(
+        ctrl(2 * 3) + 2 * 96 * S * 7 * 8, ctrl(2 * 2) + 2 * 128 * S * 7 * 8)
     assert lib.wkv_workspace_size(8, 0, 768, 0, lookback) == 0
     assert lib.wkv_workspace_size(8, 1024, 768, 5, lookback) < 0
     assert lib.wkv_workspace_size(-1, 1024, 768, 0, lookback) < 0

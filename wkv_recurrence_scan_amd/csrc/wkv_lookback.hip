@@ -65,13 +65,15 @@
 namespace wkv {
 namespace {
 
-constexpr int kLbLC = 32, kLbPS = 2;
+// Lane layouts: LC lanes of adjacent channels by PS = 64 / LC sub-chunk rows
+// per wave (LC = 32: two 128-byte row pieces per load instruction; LC = 64:
+// one 256-byte piece).
 // Every K-th segment publishes its inclusive prefix, K = (threads per
 // workgroup) / (channels per workgroup). A segment needs its anchor's prefix
 // and the aggregates in between: one word group per (slot, channel), fetched
 // by one thread each, so a workgroup's threads cover all of them at once.
-template <int V, int W>
-constexpr int64_t anchor_spacing() { return (64 * W) / (kLbLC * V); }
+template <int V, int W, int LC>
+constexpr int64_t anchor_spacing() { return (64 * W) / (LC * V); }
 // Bound on every wait, in polls (~1 us each): far above any wait a correct
 // launch sees (microseconds), small enough that a broken one still ends fast.
 constexpr uint32_t kSpinLimit = 1u << 14;
@@ -136,30 +138,30 @@ __device__ __forceinline__ void wait_words(const LbArgs& a, uint64_t* p, float (
 }
 
 // Offset of thread (wave, lane)'s first token of segment s in k, v and out.
-template <int V, int W, int L>
+template <int V, int W, int L, int LC>
 __device__ __forceinline__ int64_t lb_offset(int64_t s, int64_t g, int64_t gpr, int64_t T,
                                              int64_t C) {
-  constexpr int CH = kLbLC * V, TL = W * kLbPS * L;
+  constexpr int PS = 64 / LC, CH = LC * V, TL = W * PS * L;
   const int lane = threadIdx.x & 63;
-  const int sub = (threadIdx.x >> 6) * kLbPS + lane / kLbLC;
+  const int sub = (threadIdx.x >> 6) * PS + lane / LC;
   const int64_t b = g / gpr;
-  const int64_t c0 = (g - b * gpr) * CH + (lane % kLbLC) * V;
+  const int64_t c0 = (g - b * gpr) * CH + (lane % LC) * V;
   const int64_t cc = c0 < C ? c0 : C - V;
   return b * T * C + cc + (s * TL + static_cast<int64_t>(sub) * L) * C;
 }
 
 // One segment of one channel group; r holds this thread's tokens of it
 // (loaded by the caller), the first nvalid of them valid.
-template <typename IoT, int V, int W, int L, bool MASKED, bool G>
+template <typename IoT, int V, int W, int L, int LC, bool MASKED, bool G>
 __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, int64_t B, int64_t T,
                                         int64_t C, const float* __restrict__ w,
                                         const float* __restrict__ u,
                                         const ChunkRegs<V, L, G>& r, int nvalid,
                                         const float* __restrict__ state_in,
                                         typename IoT::elem* __restrict__ out,
-                                        float* __restrict__ state_out, Seg (*tot)[kLbLC * V],
-                                        Lane* xs, Seg (*fetched)[kLbLC * V]) {
-  constexpr int LC = kLbLC, PS = kLbPS, CH = LC * V, TL = W * PS * L;
+                                        float* __restrict__ state_out, Seg (*tot)[LC * V],
+                                        Lane* xs, Seg (*fetched)[LC * V]) {
+  constexpr int PS = 64 / LC, CH = LC * V, TL = W * PS * L;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -172,7 +174,7 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   const int64_t cc = cvalid ? c0 : C - V;
   const int64_t plane = B * C;
   const int64_t lane0 = b * C + cc;
-  const int64_t base = lb_offset<V, W, L>(s, g, a.gpr, T, C);
+  const int64_t base = lb_offset<V, W, L, LC>(s, g, a.gpr, T, C);
 
   float wd[V], ub[V];
   IoF32::load<V, false>(w + cc, wd);
@@ -187,7 +189,7 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
   // segments in between; that fold order is fixed, so the kernel is
   // deterministic. Non-anchor segments publish their aggregate first (later
   // segments fold it in); anchors publish their inclusive prefix at the end.
-  constexpr int64_t K = anchor_spacing<V, W>();
+  constexpr int64_t K = anchor_spacing<V, W, LC>();
   const bool is_anchor = s % K == 0;
   const int64_t anchor = s == 0 ? 0 : ((s - 1) / K) * K;
   if (a.publish && s > 0 && !is_anchor && wave == 0 && sl == 0) {
@@ -263,7 +265,7 @@ __device__ __forceinline__ void lb_tile(const LbArgs& a, int64_t s, int64_t g, i
                                    out + base, C);
 }
 
-template <typename IoT, int V, int W, int L, bool G>
+template <typename IoT, int V, int W, int L, int LC, bool G>
 __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
@@ -272,10 +274,10 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   // (state_in is read by segment 0's workgroups before state_out is written
   // by the last segment's, which waited on segment 0 through the published
   // prefixes, so the two may be the same buffer)
-  constexpr int CH = kLbLC * V, TL = W * kLbPS * L;
+  constexpr int PS = 64 / LC, CH = LC * V, TL = W * PS * L;
   __shared__ Seg tot[W][CH];
   __shared__ Lane xs[CH];
-  __shared__ Seg fetched[anchor_spacing<V, W>()][CH];
+  __shared__ Seg fetched[anchor_spacing<V, W, LC>()][CH];
   __shared__ uint32_t seg_s, epoch_s, test_s, ours_s;
 
   // Work assignment per channel group: block i = q G + o (row q, offset o)
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   ChunkRegs<V, L, G> r;
   auto rat = [&](int64_t off) { return G ? rg + off : rg; };
   if (guess_full) {
-    const int64_t off = lb_offset<V, W, L>(guess, g, a.gpr, T, C);
+    const int64_t off = lb_offset<V, W, L, LC>(guess, g, a.gpr, T, C);
     chunk_load<IoT, V, L, false, G>(r, k + off, v + off, rat(off), C, L);
   }
   const uint64_t S = static_cast<uint64_t>(a.segments);
@@ -348,34 +350,45 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   a.claimed = ours_s != 0u;
   a.publish = a.claimed && (test_s & kTestNoPublish) == 0u;
   const int64_t s = seg_s;
-  const int64_t off = lb_offset<V, W, L>(s, g, a.gpr, T, C);
+  const int64_t off = lb_offset<V, W, L, LC>(s, g, a.gpr, T, C);
   if ((s + 1) * TL <= T) {
     if (!guess_full || s != guess) {
       chunk_load<IoT, V, L, false, G>(r, k + off, v + off, rat(off), C, L);
     }
-    lb_tile<IoT, V, W, L, false, G>(a, s, g, B, T, C, w, u, r, L, state_in, out, state_out, tot,
-                                    xs, fetched);
+    lb_tile<IoT, V, W, L, LC, false, G>(a, s, g, B, T, C, w, u, r, L, state_in, out, state_out,
+                                        tot, xs, fetched);
   } else {
-    const int sub = (threadIdx.x >> 6) * kLbPS + (threadIdx.x & 63) / kLbLC;
+    const int sub = (threadIdx.x >> 6) * PS + (threadIdx.x & 63) / LC;
     const int64_t left = T - (s * TL + static_cast<int64_t>(sub) * L);
     const int nvalid = left <= 0 ? 0 : (left >= L ? L : static_cast<int>(left));
     chunk_load<IoT, V, L, true, G>(r, k + off, v + off, rat(off), C, nvalid);
-    lb_tile<IoT, V, W, L, true, G>(a, s, g, B, T, C, w, u, r, nvalid, state_in, out, state_out,
-                                   tot, xs, fetched);
+    lb_tile<IoT, V, W, L, LC, true, G>(a, s, g, B, T, C, w, u, r, nvalid, state_in, out,
+                                       state_out, tot, xs, fetched);
   }
 }
 
-// Workgroup shape by sequence length (measured on MI355X): W waves of two
-// 32-channel sub-chunk rows, L tokens per sub-chunk, so a segment (one tile)
-// is 2*W*L tokens. One function decides; sizing and launching both go
+// Workgroup shape by sequence length and form (measured on MI355X): W waves
+// of PS = 64 / LC sub-chunk rows of LC channels, L tokens per sub-chunk, so
+// a segment (one tile) is W PS L tokens. Past 2048 tokens the ungated fp32
+// form takes one 64-channel row per wave (256-byte row pieces, 8 waves of 32
+// tokens: B=4 T=16384 C=2048 304-306 against 310-320 us for 32-channel
+// pairs, B=2 T=32768 C=1024 202 against 211; the same plain copy pattern,
+// 0.75 against 0.67 of the HBM peak); gated, its 147 registers would leave
+// one such workgroup per CU (414-424 against 354-366 us), so it keeps the
+// 32-channel pairs. One function decides; sizing and launching both go
 // through it, so they cannot disagree.
 constexpr int64_t kLbShortT = 512, kLbMidT = 2048;
 
 template <class F>
-auto lb_dispatch(int64_t T, F&& f) {
-  if (T <= kLbShortT) return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 4>{});
-  if (T <= kLbMidT) return f(std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{});
-  return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 32>{});
+auto lb_dispatch(bool plain_f32, int64_t T, F&& f) {
+  using std::integral_constant;
+  if (T <= kLbShortT)
+    return f(integral_constant<int, 4>{}, integral_constant<int, 4>{}, integral_constant<int, 32>{});
+  if (T <= kLbMidT)
+    return f(integral_constant<int, 8>{}, integral_constant<int, 16>{}, integral_constant<int, 32>{});
+  if (plain_f32)
+    return f(integral_constant<int, 8>{}, integral_constant<int, 32>{}, integral_constant<int, 64>{});
+  return f(integral_constant<int, 4>{}, integral_constant<int, 32>{}, integral_constant<int, 32>{});
 }
 
 // Control words (16 bytes), then one 64-bit ticket counter per channel group
@@ -385,20 +398,20 @@ int64_t lookback_ctrl_bytes(int64_t groups) {
   return ((16 + 4 * kTicketStride * groups + 255) / 256) * 256;
 }
 
-template <int V, int W, int L>
+template <int V, int W, int L, int LC>
 int64_t lb_bytes(int64_t B, int64_t T, int64_t C) {
-  constexpr int64_t CH = kLbLC * V, TL = W * kLbPS * L;
+  constexpr int64_t CH = LC * V, TL = W * (64 / LC) * L;
   const int64_t groups = B * ((C + CH - 1) / CH);
   const int64_t segments = (T + TL - 1) / TL;
   return lookback_ctrl_bytes(groups) +
          groups * segments * CH * 7 * static_cast<int64_t>(sizeof(uint64_t));
 }
 
-template <typename IoT, int V, int W, int L>
+template <typename IoT, int V, int W, int L, int LC>
 hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) {
-  constexpr int CH = kLbLC * V, TL = W * kLbPS * L;
+  constexpr int CH = LC * V, TL = W * (64 / LC) * L;
   // the slots this launch indexes must lie inside the workspace it was given
-  if (ws.bytes < lb_bytes<V, W, L>(a.B, a.T, a.C)) return hipErrorInvalidValue;
+  if (ws.bytes < lb_bytes<V, W, L, LC>(a.B, a.T, a.C)) return hipErrorInvalidValue;
   const int64_t gpr = (a.C + CH - 1) / CH;
   const int64_t groups = a.B * gpr;
   const int64_t segments = (a.T + TL - 1) / TL;
@@ -422,11 +435,11 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
   const auto* rr = static_cast<const typename IoT::elem*>(a.r);
   auto* oo = static_cast<typename IoT::elem*>(a.out);
   if (rr != nullptr) {
-    hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L, true>),
+    hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L, LC, true>),
                        dim3(static_cast<unsigned>(items)), dim3(64 * W), 0, st, a.B, a.T, a.C,
                        a.w, a.u, kk, vv, rr, a.state_in, oo, a.state_out, la);
   } else {
-    hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L, false>),
+    hipLaunchKernelGGL((wkv_lookback_kernel<IoT, V, W, L, LC, false>),
                        dim3(static_cast<unsigned>(items)), dim3(64 * W), 0, st, a.B, a.T, a.C,
                        a.w, a.u, kk, vv, rr, a.state_in, oo, a.state_out, la);
   }
@@ -435,8 +448,10 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
 
 template <typename IoT, int V>
 hipError_t launch_lb_v(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) {
-  return lb_dispatch(a.T, [&](auto w, auto l) {
-    return launch_lb_t<IoT, V, decltype(w)::value, decltype(l)::value>(a, ws, st);
+  const bool plain_f32 = std::is_same<IoT, IoF32>::value && a.r == nullptr;
+  return lb_dispatch(plain_f32, a.T, [&](auto w, auto l, auto lc) {
+    return launch_lb_t<IoT, V, decltype(w)::value, decltype(l)::value, decltype(lc)::value>(a, ws,
+                                                                                          st);
   });
 }
 
@@ -461,10 +476,18 @@ hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s) {
 int lookback_vec_width(int io, int64_t C, const FwdArgs& a) { return chunk_vec_width(io, C, a); }
 
 int64_t lookback_workspace_bytes(int vec, int64_t B, int64_t T, int64_t C) {
-  return lb_dispatch(T, [&](auto w, auto l) {
-    return vec == 2 ? lb_bytes<2, decltype(w)::value, decltype(l)::value>(B, T, C)
-                    : lb_bytes<1, decltype(w)::value, decltype(l)::value>(B, T, C);
-  });
+  // the larger of the plain fp32 layout and the others (one workspace serves
+  // a call whichever of them it takes)
+  int64_t most = 0;
+  for (bool plain_f32 : {false, true}) {
+    if (plain_f32 && vec == 2) continue;  // two channels per thread: bf16 only
+    const int64_t n = lb_dispatch(plain_f32, T, [&](auto w, auto l, auto lc) {
+      constexpr int W = decltype(w)::value, L = decltype(l)::value, LC = decltype(lc)::value;
+      return vec == 2 ? lb_bytes<2, W, L, LC>(B, T, C) : lb_bytes<1, W, L, LC>(B, T, C);
+    });
+    most = n > most ? n : most;
+  }
+  return most;
 }
 
 hipError_t launch_lookback(const FwdArgs& a, int io, int vec, const LbWorkspace& ws,
