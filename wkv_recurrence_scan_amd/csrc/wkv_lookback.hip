@@ -367,28 +367,35 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   }
 }
 
-// Workgroup shape by sequence length and form (measured on MI355X): W waves
-// of PS = 64 / LC sub-chunk rows of LC channels, L tokens per sub-chunk, so
-// a segment (one tile) is W PS L tokens. Past 2048 tokens the ungated fp32
-// form takes one 64-channel row per wave (256-byte row pieces, 8 waves of 32
-// tokens: B=4 T=16384 C=2048 304-306 against 310-320 us for 32-channel
-// pairs, B=2 T=32768 C=1024 202 against 211; the same plain copy pattern,
-// 0.75 against 0.67 of the HBM peak); gated, its 147 registers would leave
-// one such workgroup per CU (414-424 against 354-366 us), so it keeps the
-// 32-channel pairs. One function decides; sizing and launching both go
-// through it, so they cannot disagree.
+// Workgroup shape by sequence length and form (measured on MI355X): V
+// channels per thread (at most VMAX, what the pointers allow), W waves of
+// PS = 64 / LC sub-chunk rows of LC channel lanes, L tokens per sub-chunk,
+// so a segment (one tile) is W PS L tokens. Past 2048 tokens every form
+// takes one channel per thread: ungated in one 64-channel row per wave (8
+// waves of 32 tokens; the plain copy pattern of one 256-byte piece per load
+// instruction streams at 0.75 of the HBM peak against 0.67 for two 128-byte
+// pieces): B=4 T=16384 C=2048 fp32 304-306 against 310-320 us, bf16 209-215
+// against 226-249 (two channels per thread held 209 registers there);
+// gated, where 147 registers would leave one such 8-wave workgroup per CU,
+// in 32-channel pairs of 4 waves: fp32 354-366 against 414-424 us, bf16
+// 319-321 against 391 with two channels per thread. One function decides;
+// sizing and launching both go through it, so they cannot disagree.
 constexpr int64_t kLbShortT = 512, kLbMidT = 2048;
 
-template <class F>
-auto lb_dispatch(bool plain_f32, int64_t T, F&& f) {
+template <int VMAX, class F>
+auto lb_dispatch(bool gated, int64_t T, F&& f) {
   using std::integral_constant;
+  using V1 = integral_constant<int, 1>;
+  using VM = integral_constant<int, VMAX>;
   if (T <= kLbShortT)
-    return f(integral_constant<int, 4>{}, integral_constant<int, 4>{}, integral_constant<int, 32>{});
+    return f(VM{}, integral_constant<int, 4>{}, integral_constant<int, 4>{}, integral_constant<int, 32>{});
   if (T <= kLbMidT)
-    return f(integral_constant<int, 8>{}, integral_constant<int, 16>{}, integral_constant<int, 32>{});
-  if (plain_f32)
-    return f(integral_constant<int, 8>{}, integral_constant<int, 32>{}, integral_constant<int, 64>{});
-  return f(integral_constant<int, 4>{}, integral_constant<int, 32>{}, integral_constant<int, 32>{});
+    return f(VM{}, integral_constant<int, 8>{}, integral_constant<int, 16>{},
+             integral_constant<int, 32>{});
+  if (!gated)
+    return f(V1{}, integral_constant<int, 8>{}, integral_constant<int, 32>{},
+             integral_constant<int, 64>{});
+  return f(V1{}, integral_constant<int, 4>{}, integral_constant<int, 32>{}, integral_constant<int, 32>{});
 }
 
 // Control words (16 bytes), then one 64-bit ticket counter per channel group
@@ -446,13 +453,27 @@ hipError_t launch_lb_t(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) 
   return hipGetLastError();
 }
 
-template <typename IoT, int V>
-hipError_t launch_lb_v(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) {
-  const bool plain_f32 = std::is_same<IoT, IoF32>::value && a.r == nullptr;
-  return lb_dispatch(plain_f32, a.T, [&](auto w, auto l, auto lc) {
-    return launch_lb_t<IoT, V, decltype(w)::value, decltype(l)::value, decltype(lc)::value>(a, ws,
-                                                                                          st);
+template <typename IoT, int VMAX>
+hipError_t launch_lb_io(const FwdArgs& a, const LbWorkspace& ws, hipStream_t st) {
+  return lb_dispatch<VMAX>(a.r != nullptr, a.T, [&](auto v, auto w, auto l, auto lc) {
+    return launch_lb_t<IoT, decltype(v)::value, decltype(w)::value, decltype(l)::value,
+                       decltype(lc)::value>(a, ws, st);
   });
+}
+
+template <int VMAX>
+int64_t lb_bytes_any(int64_t B, int64_t T, int64_t C) {
+  // the larger of the gated and the plain layout: one workspace serves a
+  // call whichever it takes
+  int64_t most = 0;
+  for (bool gated : {false, true}) {
+    const int64_t n = lb_dispatch<VMAX>(gated, T, [&](auto v, auto w, auto l, auto lc) {
+      return lb_bytes<decltype(v)::value, decltype(w)::value, decltype(l)::value,
+                      decltype(lc)::value>(B, T, C);
+    });
+    most = n > most ? n : most;
+  }
+  return most;
 }
 
 }  // namespace
@@ -476,25 +497,14 @@ hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t s) {
 int lookback_vec_width(int io, int64_t C, const FwdArgs& a) { return chunk_vec_width(io, C, a); }
 
 int64_t lookback_workspace_bytes(int vec, int64_t B, int64_t T, int64_t C) {
-  // the larger of the plain fp32 layout and the others (one workspace serves
-  // a call whichever of them it takes)
-  int64_t most = 0;
-  for (bool plain_f32 : {false, true}) {
-    if (plain_f32 && vec == 2) continue;  // two channels per thread: bf16 only
-    const int64_t n = lb_dispatch(plain_f32, T, [&](auto w, auto l, auto lc) {
-      constexpr int W = decltype(w)::value, L = decltype(l)::value, LC = decltype(lc)::value;
-      return vec == 2 ? lb_bytes<2, W, L, LC>(B, T, C) : lb_bytes<1, W, L, LC>(B, T, C);
-    });
-    most = n > most ? n : most;
-  }
-  return most;
+  return vec == 2 ? lb_bytes_any<2>(B, T, C) : lb_bytes_any<1>(B, T, C);
 }
 
 hipError_t launch_lookback(const FwdArgs& a, int io, int vec, const LbWorkspace& ws,
                            hipStream_t s) {
-  if (io == kF32) return launch_lb_v<IoF32, 1>(a, ws, s);
-  if (vec == 2) return launch_lb_v<IoBf16, 2>(a, ws, s);
-  return launch_lb_v<IoBf16, 1>(a, ws, s);
+  if (io == kF32) return launch_lb_io<IoF32, 1>(a, ws, s);
+  if (vec == 2) return launch_lb_io<IoBf16, 2>(a, ws, s);
+  return launch_lb_io<IoBf16, 1>(a, ws, s);
 }
 
 }  // namespace wkv
