@@ -62,7 +62,8 @@ def test_dd_forward_f32(path, B, T, C, wl):
 
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("B,T,C", [(1, 1, 2), (2, 3, 6), (2, 65, 34), (1, 257, 64),
-                                   (3, 700, 32), (1, 2049, 66), (1, 130, 7), (1, 2500, 130)])
+                                   (3, 700, 32), (1, 2049, 66), (1, 130, 7), (1, 2500, 130),
+                                   (64, 300, 256)])
 def test_dd_forward_bf16(path, B, T, C):
     say(f"dd forward bf16 path={path} B={B} T={T} C={C}")
     wt, u, k, v = dd_case(WL4, B, T, C)

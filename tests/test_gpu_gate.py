@@ -25,7 +25,7 @@ def receptance(B, T, C, seed=0, scale=2.0):
 
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("B,T,C", [(1, 1, 8), (2, 37, 40), (1, 300, 32), (2, 1152, 33),
-                                   (1, 2500, 70)])
+                                   (1, 2500, 70), (64, 40, 256)])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_gated_forward(path, B, T, C, io):
     say(f"gated forward path={path} B={B} T={T} C={C} io={io}")

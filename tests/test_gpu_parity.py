@@ -47,7 +47,8 @@ def test_forward_f32(path, B, T, C, wl):
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("B,T,C", [(1, 1, 2), (2, 3, 6), (2, 65, 34), (1, 257, 64),
                                    (3, 700, 32), (1, 2049, 66), (1, 130, 7), (1, 2500, 130),
-                                   (1, 1, 512), (2, 9, 512), (1, 300, 1536), (2, 1029, 1024)])
+                                   (1, 1, 512), (2, 9, 512), (1, 300, 1536), (2, 1029, 1024),
+                                   (64, 300, 256)])
 def test_forward_bf16(path, B, T, C):
     say(f"forward bf16 path={path} B={B} T={T} C={C}")
     w, u, k, v = make_case(WL4, B, T, C)

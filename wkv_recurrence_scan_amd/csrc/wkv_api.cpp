@@ -358,7 +358,7 @@ int forward_dd_impl(int64_t B, int64_t T, int64_t C, const void* w, const float*
   if (path == WKV_PATH_AUTO) path = choose_path(B, T, C, io, dev, false, false);
   const int vec = wkv::dd_vec_width(io, C, a);
   e = path == WKV_PATH_SEQ ? wkv::launch_dd_seq(a, io, vec, stream)
-                           : wkv::launch_dd_chunk(a, io, vec, stream);
+                           : wkv::launch_dd_chunk(a, io, vec, cu_count(dev), stream);
   return e == hipSuccess ? WKV_OK : fail(WKV_ERR_LAUNCH, e);
 }
 

@@ -541,9 +541,14 @@ hipError_t launch_dd_seq(const DdArgs& a, int io, int vec, hipStream_t s) {
   return launch_dd_seq_t<IoBf16, 1>(a, s);
 }
 
-hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, hipStream_t s) {
+hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, int cus, hipStream_t s) {
   if (io == kF32) return launch_dd_chunk_v<IoF32, 1>(a, s);
-  if (vec == 2) return launch_dd_chunk_v<IoBf16, 2>(a, s);
+  // Two bf16 channels per thread halve the workgroups; while that leaves CUs
+  // idle, one channel per thread is faster (measured on MI355X, bf16: B=8
+  // T=1024 C=768 24.5 against 49.2 us, B=4 T=2048 C=2048 55.9 against 94.8;
+  // B=32 T=512 C=1024, 512 two-channel workgroups, 54.4 against 53.9).
+  const int64_t two_ch_blocks = a.B * ((a.C + 2 * kDdLC - 1) / (2 * kDdLC));
+  if (vec == 2 && two_ch_blocks >= cus) return launch_dd_chunk_v<IoBf16, 2>(a, s);
   return launch_dd_chunk_v<IoBf16, 1>(a, s);
 }
 

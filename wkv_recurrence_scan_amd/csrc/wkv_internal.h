@@ -136,7 +136,7 @@ struct DdStepArgs {
 int dd_vec_width(int io, int64_t C, const DdArgs& a);
 int dd_step_vec_width(int io, int64_t C, const DdStepArgs& a);
 hipError_t launch_dd_seq(const DdArgs& a, int io, int vec, hipStream_t s);
-hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, hipStream_t s);
+hipError_t launch_dd_chunk(const DdArgs& a, int io, int vec, int cus, hipStream_t s);
 hipError_t launch_dd_step(const DdStepArgs& a, int io, int vec, hipStream_t s);
 
 // Matrix-valued state (head size 64, fp32): r, k, v, lam, out [B][T][H*64];
