@@ -131,14 +131,21 @@ __device__ __forceinline__ void db_load(DbChunk<G>& c, const DdBwdKernelArgs& a,
                                         int n) {
 #pragma unroll
   for (int i = 0; i < kDbLc; ++i) {
-    if (!MASKED || i < n) {
-      c.k[i] = __builtin_nontemporal_load(a.k + o + i * a.C);
-      c.v[i] = __builtin_nontemporal_load(a.v + o + i * a.C);
-      c.w[i] = __builtin_nontemporal_load(a.w + o + i * a.C);
-      if constexpr (G) c.g[i] = __builtin_nontemporal_load(a.gout + o + i * a.C);
-    } else {
-      c.k[i] = c.v[i] = c.w[i] = 0.0f;
-      if constexpr (G) c.g[i] = 0.0f;
+    // MASKED (a sequence's partial last chunk, n >= 1 tokens): the tokens
+    // past the end re-read the last one and are replaced by zeros, so every
+    // load stays unconditional (conditional loads into the array put it in
+    // scratch memory)
+    const bool live = !MASKED || i < n;
+    const int64_t at = o + static_cast<int64_t>(live ? i : n - 1) * a.C;
+    const float k = __builtin_nontemporal_load(a.k + at);
+    const float v = __builtin_nontemporal_load(a.v + at);
+    const float w = __builtin_nontemporal_load(a.w + at);
+    c.k[i] = live ? k : 0.0f;
+    c.v[i] = live ? v : 0.0f;
+    c.w[i] = live ? w : 0.0f;
+    if constexpr (G) {
+      const float g = __builtin_nontemporal_load(a.gout + at);
+      c.g[i] = live ? g : 0.0f;
     }
   }
 }
