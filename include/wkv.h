@@ -127,8 +127,11 @@ int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float*
  *   workspace        device memory of at least wkv_workspace_size(...) bytes,
  *                    256-byte aligned, owned by the caller. It must be
  *                    zero-filled before its first use, and again before it
- *                    serves sizes with another look-back layout; every call
- *                    leaves it ready for the next call with the same sizes
+ *                    serves a call with another look-back layout (the layout
+ *                    follows from B, T and C, the element type, whether the
+ *                    bf16 pointers allow two channels per thread and, past
+ *                    2048 tokens, whether the call is gated); every call
+ *                    leaves it ready for the next call with the same layout
  *                    (no clearing in between, HIP graph replays included).
  *                    Calls that may run concurrently must not share a
  *                    workspace. It must not overlap any other argument.
@@ -137,7 +140,7 @@ int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float*
  *
  * Misuse is reported, never silent: the first LOOKBACK launch on a
  * zero-filled workspace claims it for its layout, and a later launch with
- * another layout (other sizes) on the same, uncleared workspace, or a wait
+ * another layout (see above) on the same, uncleared workspace, or a wait
  * for an earlier segment that runs out (as when overlapping calls share a
  * workspace), sets the workspace's error word and writes NaN where the
  * missing data would have gone, so the affected outputs are NaN rather than
@@ -196,8 +199,10 @@ int wkv_forward_gated(int64_t B, int64_t T, int64_t C, const float* w, const flo
                       void* out, float* state_out, int io, int path, void* workspace,
                       int64_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace wkv_forward_ws needs for these sizes and this path
- * (0 when the kernel uses none), or a negative wkv_status on error. */
+/* Bytes of workspace wkv_forward_ws (or wkv_forward_gated) needs for these
+ * sizes and this path (0 when the kernel uses none; enough for either form
+ * and either channel width the pointers may allow), or a negative
+ * wkv_status on error. */
 int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path);
 
 /* The kernel WKV_PATH_AUTO uses for these sizes on the current device when a

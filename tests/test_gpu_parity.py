@@ -314,6 +314,37 @@ def test_lookback_workspace_of_another_layout_is_reported():
             assert W.wkv_workspace_status(ws) == 0
 
 
+def test_lookback_gated_and_plain_layouts_on_one_workspace():
+    """Past 2048 tokens the gated and the plain forward chain their segments
+    in different look-back layouts (32-channel pairs of four waves against
+    64-channel rows of eight), so one workspace serves one of them at a time:
+    the gated call after a plain one on the same, uncleared workspace is
+    reported and its chained outputs are NaN; zero-filled again, it is right."""
+    B, T, C = 2, 3000, 96
+    w, u, k, v = make_case(WL3, B, T, C)
+    r = np.random.default_rng([62, B, T, C]).normal(0, 2.0, (B, T, C)).astype(np.float32)
+    ref, _ = wkv_recurrent(w, u, k, v)
+    gref = ref * sigmoid(r.astype(np.float64))
+    ws = W.new_workspace(W.wkv_workspace_size(B, T, C, W.WKV_IO_F32, "lookback"), "cuda")
+    say("look-back plain then gated on one workspace")
+    out, _ = W.wkv_forward_ws(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), path="lookback",
+                              workspace=ws)
+    torch.cuda.synchronize()
+    assert_out_close(host64(out), ref, v, F32_TOL)
+    assert W.wkv_workspace_status(ws) == 0
+    out, _ = W.wkv_forward_gated(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), dev_f32(r),
+                                 path="lookback", workspace=ws)
+    torch.cuda.synchronize()
+    assert W.wkv_workspace_status(ws, clear=True) == W.WKV_ERR_LOOKBACK
+    assert np.isnan(host64(out)[:, 256:]).all()
+    ws.zero_()
+    out, _ = W.wkv_forward_gated(dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v), dev_f32(r),
+                                 path="lookback", workspace=ws)
+    torch.cuda.synchronize()
+    assert_out_close(host64(out), gref, v, F32_TOL)
+    assert W.wkv_workspace_status(ws) == 0
+
+
 def test_lookback_wait_that_runs_out_is_reported_and_poisons_outputs():
     """Forced from the host through the workspace's test words: with nothing
     published and a bound of 64 polls, every wait for an earlier segment runs
