@@ -530,8 +530,8 @@ hipError_t launch_chunk_v(const FwdArgs& a, int cus, hipStream_t st) {
   if (a.T <= kLongT) {
     // gated fp32 holds r as well: 8 tokens per thread (105 VGPRs) beat 16
     // (155) on MI355X, B=8 T=1024 C=768 26.1 against 27.1 us per layer
-    if (std::is_same<IoT, IoF32>::value && a.r != nullptr) return launch_chunk_t<IoT, V, 8, 8>(a, st);
-    return launch_chunk_t<IoT, V, 8, 16>(a, st);
+    const bool gated_f32 = std::is_same<IoT, IoF32>::value && a.r != nullptr;
+    return gated_f32 ? launch_chunk_t<IoT, V, 8, 8>(a, st) : launch_chunk_t<IoT, V, 8, 16>(a, st);
   }
   return launch_chunk_t<IoT, V, 8, 8>(a, st);
 }

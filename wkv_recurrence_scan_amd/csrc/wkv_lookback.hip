@@ -80,10 +80,11 @@ constexpr uint32_t kSpinLimit = 1u << 14;
 
 // Control words at the start of the workspace (32-bit each): [0] the sticky
 // error word (bit 0: a wait ran out, as when overlapping launches share the
-// workspace; bit 2: the workspace is claimed by another layout), [1] a word only tests write (bit 0: publish
-// nothing, so that every wait runs out; bits 8-31: a replacement for
-// kSpinLimit, 0 for none), [2..3] the 64-bit claim (G << 32 | S, 0 while
-// unclaimed). Then per channel group a 64-bit ticket counter, 16 bytes apart.
+// workspace; bit 2: the workspace is claimed by another layout), [1] a word
+// only tests write (bit 0: publish nothing, so that every wait runs out;
+// bits 8-31: a replacement for kSpinLimit, 0 for none), [2..3] the 64-bit
+// claim (G << 32 | S, 0 while unclaimed). Then per channel group a 64-bit
+// ticket counter, 16 bytes apart.
 constexpr int kCtrlErr = 0, kCtrlTest = 1, kCtrlClaim = 2;
 constexpr uint32_t kTestNoPublish = 1u;
 constexpr int kTicketStride = 4;  // in 32-bit words
@@ -305,7 +306,8 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
   // (one round trip); their values are needed only after the tile's prefetch
   // is issued
   uint64_t ticket = 0, claim = 0, words = 0;
-  const uint64_t layout = (static_cast<uint64_t>(a.groups) << 32) | static_cast<uint64_t>(a.segments);
+  const uint64_t layout =
+      (static_cast<uint64_t>(a.groups) << 32) | static_cast<uint64_t>(a.segments);
   if (threadIdx.x == 0) {
     // (the ticket last: the compiler waits for its value at once, and then
     // the two loads are in flight already)
@@ -382,20 +384,16 @@ __global__ __launch_bounds__(64 * W) void wkv_lookback_kernel(
 // sizing and launching both go through it, so they cannot disagree.
 constexpr int64_t kLbShortT = 512, kLbMidT = 2048;
 
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+// f(V, W, L, LC) as integral constants
 template <int VMAX, class F>
 auto lb_dispatch(bool gated, int64_t T, F&& f) {
-  using std::integral_constant;
-  using V1 = integral_constant<int, 1>;
-  using VM = integral_constant<int, VMAX>;
-  if (T <= kLbShortT)
-    return f(VM{}, integral_constant<int, 4>{}, integral_constant<int, 4>{}, integral_constant<int, 32>{});
-  if (T <= kLbMidT)
-    return f(VM{}, integral_constant<int, 8>{}, integral_constant<int, 16>{},
-             integral_constant<int, 32>{});
-  if (!gated)
-    return f(V1{}, integral_constant<int, 8>{}, integral_constant<int, 32>{},
-             integral_constant<int, 64>{});
-  return f(V1{}, integral_constant<int, 4>{}, integral_constant<int, 32>{}, integral_constant<int, 32>{});
+  if (T <= kLbShortT) return f(Int<VMAX>{}, Int<4>{}, Int<4>{}, Int<32>{});
+  if (T <= kLbMidT) return f(Int<VMAX>{}, Int<8>{}, Int<16>{}, Int<32>{});
+  if (!gated) return f(Int<1>{}, Int<8>{}, Int<32>{}, Int<64>{});
+  return f(Int<1>{}, Int<4>{}, Int<32>{}, Int<32>{});
 }
 
 // Control words (16 bytes), then one 64-bit ticket counter per channel group
