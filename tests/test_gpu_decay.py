@@ -63,7 +63,7 @@ def test_dd_forward_f32(path, B, T, C, wl):
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("B,T,C", [(1, 1, 2), (2, 3, 6), (2, 65, 34), (1, 257, 64),
                                    (3, 700, 32), (1, 2049, 66), (1, 130, 7), (1, 2500, 130),
-                                   (64, 300, 256)])
+                                   (64, 300, 256), (1, 5, 512), (1, 16, 512), (3, 24, 1536)])
 def test_dd_forward_bf16(path, B, T, C):
     say(f"dd forward bf16 path={path} B={B} T={T} C={C}")
     wt, u, k, v = dd_case(WL4, B, T, C)
@@ -84,6 +84,33 @@ def test_dd_forward_from_initial_state(path, io):
     ref, rst = wkv_dd_recurrent(wt, u, k, v, s0.astype(np.float64))
     assert_out_close(got, ref, v, tol_for(io))
     assert_state_close(gst, rst, F32_TOL * (10 if io == "bf16" else 1))
+
+
+def test_dd_bf16_sequential_scan_both_widths_from_state():
+    """The bf16 sequential scan from an initial state at a wide row (C = 1024,
+    T = 333 ends in a partial block of the walk's 8-token unroll): first with
+    aligned buffers (two channels per thread), then with the same values one
+    element off 4-byte alignment (one channel per thread), to the same
+    result."""
+    B, T, C = 2, 333, 1024
+    say("dd bf16 sequential scan, both widths, from state")
+    wt, u, k, v = dd_case(WL4, B, T, C)
+    s0 = random_state(B, C, 5)
+    got, gst = gpu_dd(wt, u, k, v, "bf16", state_in=s0, path="seq")
+    ref, rst = wkv_dd_recurrent(wt, u, k, v, s0.astype(np.float64))
+    assert_out_close(got, ref, v, BF16_TOL)
+    assert_state_close(gst, rst, F32_TOL * 10)
+
+    def off(x):  # the same values at a 2-byte offset inside a larger buffer
+        flat = torch.empty(x.size + 1, dtype=torch.bfloat16, device="cuda")
+        flat[1:] = dev_io(x, "bf16").reshape(-1)
+        return flat[1:].view(x.shape)
+    out = torch.empty(B * T * C + 1, dtype=torch.bfloat16, device="cuda")[1:].view(B, T, C)
+    o2, st2 = W.wkv_forward_dd(off(wt), dev_f32(u), off(k), off(v), dev_f32(s0), out=out,
+                               path="seq")
+    torch.cuda.synchronize()
+    assert_out_close(host64(o2), ref, v, BF16_TOL)
+    assert_state_close(host64(st2), rst, F32_TOL * 10)
 
 
 @pytest.mark.parametrize("path", PATHS)

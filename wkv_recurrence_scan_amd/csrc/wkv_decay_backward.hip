@@ -86,15 +86,15 @@ struct DdBwdKernelArgs {
 // The state advance of laned_step alone.
 __device__ __forceinline__ void laned_advance(LaneD& s, float k, float v, float w) {
   const double kd = static_cast<double>(k);
-  const double wd = static_cast<double>(w);
-  const double s2 = (kd - s.m) + wd;  // k - (m - w)
+  const double mw = s.m - static_cast<double>(w);
+  const double s2 = kd - mw;  // k - (m - w)
   const float y = exp_neg_abs(s2);
   const bool tok_wins = s2 > 0.0;
   const float ga = tok_wins ? y : 1.0f;
   const float gb = tok_wins ? 1.0f : y;
   s.n = __builtin_fmaf(ga, s.n, gb * v);
   s.d = __builtin_fmaf(ga, s.d, gb);
-  s.m = tok_wins ? kd : s.m - wd;
+  s.m = __builtin_fmax(kd, mw);
 }
 
 // laned_step recording the output's denominator as e^M / rho and the current

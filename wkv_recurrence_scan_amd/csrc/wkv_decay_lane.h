@@ -44,15 +44,17 @@ __device__ __forceinline__ float laned_step(LaneD& s, float k, float v, float w,
   const float fa = cur_wins ? x : 1.0f;
   const float fb = cur_wins ? 1.0f : x;
   const float out = __builtin_fmaf(fa, s.n, fb * v) * fast_rcp(__builtin_fmaf(fa, s.d, fb));
-  const double wd = static_cast<double>(w);
-  const double s2 = dk + wd;    // k - (m - w)
+  // the decayed state's exponent against the token's; the new maximum is one
+  // v_max_f64 rather than a compare and a 64-bit select
+  const double mw = s.m - static_cast<double>(w);
+  const double s2 = kd - mw;
   const float y = exp_neg_abs(s2);
   const bool tok_wins = s2 > 0.0;
   const float ga = tok_wins ? y : 1.0f;
   const float gb = tok_wins ? 1.0f : y;
   s.n = __builtin_fmaf(ga, s.n, gb * v);
   s.d = __builtin_fmaf(ga, s.d, gb);
-  s.m = tok_wins ? kd : s.m - wd;
+  s.m = __builtin_fmax(kd, mw);
   return out;
 }
 
