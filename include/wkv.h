@@ -85,7 +85,10 @@ enum { WKV_IO_F32 = 0, WKV_IO_BF16 = 1 };
  * up to T = 2048 and, for longer sequences, LOOKBACK when a workspace is
  * given (CHUNK when not); the plain (ungated, no checkpoints) fp32 forward
  * also takes CHUNK where B*C fills the GPU, 512 <= T <= 2048 and a batch
- * row's T * C * 4 bytes are not a power of two (see wkv_select_path). */
+ * row's T * C * 4 bytes are not a power of two; with a workspace, fp32 takes
+ * LOOKBACK from T = 513 (gated: T = 1280) to 2048 where the 32-channel
+ * groups, B * ceil(C / 32), number more than the CUs and at most four times
+ * as many (see wkv_select_path). */
 enum { WKV_PATH_AUTO = 0, WKV_PATH_SEQ = 1, WKV_PATH_CHUNK = 2, WKV_PATH_LOOKBACK = 3 };
 
 /* Prefill / training form over a whole sequence (page "Linear attention
@@ -209,10 +212,14 @@ int64_t wkv_workspace_size(int64_t B, int64_t T, int64_t C, int io, int path);
  * workspace is available (WKV_PATH_SEQ, WKV_PATH_CHUNK or WKV_PATH_LOOKBACK;
  * without one, LOOKBACK becomes WKV_PATH_CHUNK), or a negative wkv_status on
  * error. This is the plain forward's choice; the gated, checkpointing and
- * per-token-decay forms differ in one case: where B*C alone fills the GPU they
+ * per-token-decay forms differ in two cases: where B*C alone fills the GPU they
  * always take WKV_PATH_SEQ, while the plain fp32 forward takes WKV_PATH_CHUNK
  * for 512 <= T <= 2048 when a batch row's T * C * 4 bytes are not a power of
- * two. */
+ * two; and where the plain fp32 forward with a workspace takes
+ * WKV_PATH_LOOKBACK below T = 2049 (513 <= T, more 32-channel groups than
+ * CUs, at most four per CU), the gated one does so from T = 1280 only, and
+ * the checkpointing and per-token-decay forms, which have no look-back
+ * kernel, take WKV_PATH_CHUNK. */
 int wkv_select_path(int64_t B, int64_t T, int64_t C, int io);
 
 /* One decode step for B sequences at once (page "Linear attention without

@@ -248,6 +248,48 @@ def test_auto_path_choice():
     assert W.wkv_select_path(4, 8, 64) == "seq"
 
 
+def test_auto_takes_lookback_for_mid_length_fp32_with_more_groups_than_cus():
+    """With a workspace, fp32 past 512 tokens (gated: from 1280) and up to
+    2048 takes the look-back scan where the chunked scan's 32-channel groups
+    outnumber the CUs by up to four to one: the choice itself at its edges,
+    and the AUTO result (bit for bit that of the explicit look-back call, and
+    against the oracle) on a plain and a gated shape just past one group per
+    CU."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    b2 = 2 * cus // 32  # B with 2 * cus groups of C = 1024
+    assert W.wkv_select_path(b2, 1024, 1024) == "lookback"
+    assert W.wkv_select_path(b2, 513, 1024) == "lookback"
+    assert W.wkv_select_path(b2, 512, 1024) == "chunk"
+    assert W.wkv_select_path(b2, 2048, 1024) == "lookback"
+    assert W.wkv_select_path(b2, 1024, 1024, W.WKV_IO_BF16) == "chunk"
+    assert W.wkv_select_path(cus // 32, 1024, 1024) == "chunk"  # one group per CU
+    assert W.wkv_select_path(4 * cus // 32, 1024, 1024) == "lookback"
+    assert W.wkv_select_path(4 * cus // 32 + 1, 1024, 1024) == "chunk"
+
+    B = cus // 24 + 1  # just past one group per CU at C = 768
+    for gated, T in ((False, 640), (True, 1280)):
+        say(f"auto look-back: B={B} T={T} C=768 gated={gated}")
+        w, u, k, v = make_case(WL3, B, T, 768)
+        ws = W.new_workspace(W.wkv_workspace_size(B, T, 768, W.WKV_IO_F32, "auto"), "cuda")
+        assert ws.numel() >= W.wkv_workspace_size(B, T, 768, W.WKV_IO_F32, "lookback") > 0
+        ref, rst = wkv_recurrent(w, u, k, v)
+        args = [dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v)]
+        if gated:
+            r = np.random.default_rng([63, T]).normal(0, 2, (B, T, 768)).astype(np.float32)
+            args.append(dev_f32(r))
+            ref = ref * sigmoid(r)
+            call = lambda path: W.wkv_forward_gated(*args, path=path, workspace=ws)
+        else:
+            call = lambda path: W.wkv_forward_ws(*args, path=path, workspace=ws)
+        auto_out, auto_st = call("auto")
+        lb_out, lb_st = call("lookback")
+        torch.cuda.synchronize()
+        assert W.wkv_workspace_status(ws) == 0
+        assert torch.equal(auto_out, lb_out) and torch.equal(auto_st, lb_st)
+        assert_out_close(host64(auto_out), ref, v, F32_TOL)
+        assert_state_close(host64(auto_st), rst, F32_TOL)
+
+
 def _lookback_words(ws, groups):
     """The look-back workspace's control words (error, test word, the 64-bit
     layout claim) and every channel group's 64-bit ticket counter."""

@@ -55,11 +55,11 @@ constexpr int64_t kMaxBytes = int64_t(1) << 60;
 // Kernel for AUTO. The sequential scan needs no cross-thread combine, so it
 // wins whenever B*C lanes alone give every SIMD at least one wave (4 SIMDs per
 // CU). Below that a time-parallel kernel creates the missing parallelism:
-// up to kChunkMaxT tokens the chunked scan (measured on MI355X: as fast as the
-// look-back scan there, and it needs no workspace), beyond it the look-back
-// scan when a workspace is available.
+// up to kChunkMaxT tokens the chunked scan (it needs no workspace; the
+// second exception below takes the look-back scan for some fp32 shapes),
+// beyond it the look-back scan when a workspace is available.
 //
-// One exception, measured on MI355X: the sequential scan walks every batch
+// First exception, measured on MI355X: the sequential scan walks every batch
 // row at the same token, and that access pattern streams at 0.71-0.75 of the
 // HBM peak when a row's bytes (T * C * 4 for fp32) are a power of two but at
 // only 0.64-0.66 otherwise (the same walk over rows padded from 1.5 to 2 MiB
@@ -72,7 +72,20 @@ constexpr int64_t kMaxBytes = int64_t(1) << 60;
 // per-token decay 341 against 313). bf16 keeps the sequential scan too,
 // whose LDS-staged tiles stay ahead of the chunked scan at every measured
 // size.
+//
+// Second exception, for fp32 with a workspace, measured on MI355X over
+// 8-layer graphs: once the chunked scan's 32-channel groups (B * ceil(C / 32),
+// one workgroup each) outnumber the CUs, but by at most four to one, the
+// chunked scan leaves CUs unevenly loaded, and the look-back scan's 256-token
+// segments win past 512 tokens (plain form, measured from T = 520: 3-38% on 19 shapes; B=16 T=2048
+// C=768 64 against 79 us) and from T = 1280 up when gated (14-29% on 5; at
+// T = 896-1152 the gated chunked scan still won by 7-10%). At up to one
+// group per CU the chunked scan's two walkers win (B=8 T=1024 C=768: 22
+// against 26 us); past four per CU neither wins everywhere (B=64 T=1536
+// C=768: the chunked scan by 7%), nor does the bf16 look-back scan anywhere
+// below T = 2048.
 constexpr int64_t kChunkMaxT = 2048;
+constexpr int64_t kLbMidMinT = 513, kLbMidMinTGated = 1280;
 
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -86,7 +99,12 @@ int choose_path(int64_t B, int64_t T, int64_t C, int io, int dev, bool have_ws, 
                              (__builtin_mul_overflow(T * C, 4, &row_bytes) || !pow2(row_bytes));
     return uneven_rows && T >= 512 && T <= kChunkMaxT ? WKV_PATH_CHUNK : WKV_PATH_SEQ;
   }
-  return have_ws && T > kChunkMaxT ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
+  if (!have_ws) return WKV_PATH_CHUNK;
+  if (T > kChunkMaxT) return WKV_PATH_LOOKBACK;
+  const int64_t groups = B * ((C + 31) / 32), cus = cu_count(dev);
+  const bool mid = io == wkv::kF32 && groups > cus && groups <= 4 * cus &&
+                   T >= (plain ? kLbMidMinT : kLbMidMinTGated);
+  return mid ? WKV_PATH_LOOKBACK : WKV_PATH_CHUNK;
 }
 
 // Workspace the look-back kernel needs, whichever channel width the pointers
