@@ -66,3 +66,23 @@ def test_noalloc_rejects_lookback_beyond_its_array():
     t = torch.zeros(4, device="cuda")
     assert lib.wkv_forward_noalloc(B, T, C, _p(t), _p(t), _p(t), _p(t), None, _p(t), None,
                                    W.WKV_IO_F32, W.WKV_PATH_LOOKBACK, _stream()) == 8
+
+
+def test_noalloc_auto_mid_length_lookback_between_other_layouts():
+    """Where AUTO takes the look-back scan below 2049 tokens (fp32 with more
+    32-channel groups than CUs, at most four per CU), the static array serves
+    it too: a call of that kind between two calls of other look-back layouts
+    (each call clears the part of the array it uses) matches wkv_forward_ws
+    bit for bit and the oracle."""
+    lib = W.load_library()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mid = (cus // 24 + 1, 640, 768)  # just past one 32-channel group per CU
+    assert W.wkv_select_path(*mid) == "lookback"
+    for i, (B, T, C) in enumerate([(1, 2305, 40), mid, (2, 4100, 96)]):
+        say(f"noalloc auto call {i}: B={B} T={T} C={C}")
+        (w, u, k, v), (oa, sa), (ob, sb) = _both(lib, B, T, C, W.WKV_PATH_AUTO, layer=i)
+        assert torch.equal(oa, ob), "outputs differ from wkv_forward_ws"
+        assert torch.equal(sa, sb), "final states differ from wkv_forward_ws"
+        ref, rst = wkv_recurrent(w, u, k, v)
+        assert_out_close(host64(ob), ref, v, F32_TOL)
+        assert_state_close(host64(sb), rst, F32_TOL)
