@@ -136,6 +136,11 @@ int wkv_forward_ex(int64_t B, int64_t T, int64_t C, const float* w, const float*
  *                    2048 tokens, whether the call is gated); every call
  *                    leaves it ready for the next call with the same layout
  *                    (no clearing in between, HIP graph replays included).
+ *                    Under AUTO this applies to every call that takes
+ *                    LOOKBACK (wkv_select_path), fp32 calls from 513 tokens
+ *                    included: a caller that varies B, T or C with one
+ *                    workspace zero-fills it when the layout changes, or
+ *                    keeps one workspace per shape.
  *                    Calls that may run concurrently must not share a
  *                    workspace. It must not overlap any other argument.
  *   workspace_bytes  its size in bytes.
