@@ -3,6 +3,8 @@ element by element, on seeded inputs small enough for the oracle: ragged
 sizes around every tile edge of both prefill kernels, initial states,
 in-place states, split/resume, decode, bf16 I/O and extreme keys."""
 
+import warnings
+
 import numpy as np
 import pytest
 import torch
@@ -288,6 +290,40 @@ def test_auto_takes_lookback_for_mid_length_fp32_with_more_groups_than_cus():
         assert torch.equal(auto_out, lb_out) and torch.equal(auto_st, lb_st)
         assert_out_close(host64(auto_out), ref, v, F32_TOL)
         assert_state_close(host64(auto_st), rst, F32_TOL)
+
+
+def test_one_shot_calls_under_graph_capture_take_no_cached_workspace():
+    """A one-shot AUTO call captured in a HIP graph takes no workspace from
+    the binding's cache (checking it afterwards would synchronise the
+    capturing stream), so AUTO picks a kernel that needs none: the replays
+    give exactly the chunked scan's eager result, at a mid length where AUTO
+    with a workspace takes the look-back scan and past 2048 tokens. An
+    explicit look-back call without a workspace is refused during capture."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, T, C in ((cus // 24 + 1, 640, 768), (2, 2300, 96)):
+        say(f"one-shot call under capture: B={B} T={T} C={C}")
+        w, u, k, v = make_case(WL3, B, T, C)
+        args = [dev_f32(w), dev_f32(u), dev_f32(k), dev_f32(v)]
+        ref_out, ref_st = W.wkv_forward_ex(*args, path="chunk")
+        out = torch.empty_like(ref_out)
+        st = torch.empty_like(ref_st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            W.wkv_forward_ex(*args, out=out, state_out=st)
+        for rep in range(3):
+            out.zero_()
+            st.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out) and torch.equal(st, ref_st), f"replay {rep}"
+    g2 = torch.cuda.CUDAGraph()
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", UserWarning)  # the refused call leaves the graph empty
+        with pytest.raises(ValueError, match="graph capture"):
+            with torch.cuda.graph(g2):
+                W.wkv_forward_ex(*args, out=out, state_out=st, path="lookback")
 
 
 def _lookback_words(ws, groups):

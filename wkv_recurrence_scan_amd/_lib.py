@@ -169,6 +169,24 @@ def check_workspace(workspace: Optional[torch.Tensor], stream=None) -> None:
         raise WKVError("wkv_forward_ws", WKV_ERR_LOOKBACK)
 
 
+def _one_shot_workspace(B, T, C, io, path, dev, strm) -> Optional[torch.Tensor]:
+    """The workspace a one-shot call takes from the per-(stream, sizes) cache.
+    Its status is checked after the call, which synchronises the stream; a
+    stream capturing a HIP graph cannot be synchronised, so there AUTO gets
+    no workspace (and picks among the kernels that need none) and an explicit
+    LOOKBACK must bring its own workspace."""
+    with torch.cuda.stream(strm):
+        capturing = torch.cuda.is_current_stream_capturing()
+    if capturing:
+        if path == "lookback":
+            raise ValueError("under HIP graph capture a LOOKBACK call needs a workspace of its "
+                             "own (or a ForwardCall), since checking the cached one would "
+                             "synchronise the capturing stream")
+        return None
+    return _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
+                             (B, T, C, io, path))
+
+
 def new_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     """A zero-filled device workspace of at least nbytes (None for 0 bytes).
     torch's allocator returns blocks aligned to at least 256 bytes."""
@@ -219,7 +237,9 @@ def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.T
     `workspace` or one cached for the stream. A cached workspace is checked
     after the call (check_workspace: the stream is synchronised and a failed
     look-back chain raises WKVError); a workspace passed in is the caller's to
-    check with wkv_workspace_status."""
+    check with wkv_workspace_status. Under HIP graph capture no cached
+    workspace is used: "auto" then picks a kernel that needs none, and
+    "lookback" needs `workspace`."""
     lib = load_library()
     if k.dim() != 3:
         raise ValueError(f"k must be (B, T, C), got shape {tuple(k.shape)}")
@@ -249,8 +269,7 @@ def wkv_forward_ex(w: torch.Tensor, u: torch.Tensor, k: torch.Tensor, v: torch.T
         strm = torch.cuda.current_stream(dev) if stream is None else stream
         owned = workspace is None
         if owned:
-            workspace = _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
-                                          (B, T, C, io, path))
+            workspace = _one_shot_workspace(B, T, C, io, path, dev, strm)
         elif workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the tensors' device")
         st = lib.wkv_forward_ws(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(state_in),
@@ -523,8 +542,7 @@ def wkv_forward_gated(w, u, k, v, r, state_in=None, out=None, state_out=None, *,
         strm = torch.cuda.current_stream(dev) if stream is None else stream
         owned = workspace is None
         if owned:
-            workspace = _cached_workspace(wkv_workspace_size(B, T, C, io, path), dev, strm,
-                                          (B, T, C, io, path))
+            workspace = _one_shot_workspace(B, T, C, io, path, dev, strm)
         st = lib.wkv_forward_gated(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(r),
                                    _ptr(state_in), _ptr(out), _ptr(state_out), io, _PATHS[path],
                                    _ptr(workspace), 0 if workspace is None else workspace.numel(),
