@@ -201,21 +201,17 @@ def test_deterministic(path, io):
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
 
 
-def ulp32(x: float) -> float:
-    """Spacing of float32 numbers at magnitude x."""
-    return float(np.spacing(np.float32(x)))
-
-
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("kmag", [60.0, 88.0, 1e4])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_extreme_keys(path, kmag, io):
     """No NaN/Inf and oracle agreement with keys far outside N(0, 1), at the
-    workload tolerance up to |k| = 88. Every kernel forms its exponent
-    differences from key differences plus whole numbers times w, so large
-    keys cost no accuracy beyond the data's own; at |k| = 1e4 an input key
-    itself sits on a grid of ulp(1e4) ~ 1e-3, and the bound allows that grid's
-    spacing: the larger of the workload tolerance and 4 ulp(|k|)."""
+    workload tolerance at every magnitude, |k| = 1e4 included. Every kernel
+    forms its exponent differences from key differences plus whole numbers
+    times w, and the time-parallel paths keep their sub-chunk sums exact
+    relative to each stored (rounded) maximum, so keys on the coarse grid of
+    ulp(1e4) ~ 1e-3 cost no accuracy beyond the data's own (measured on MI355X:
+    2.7e-7 on every fp32 path at |k| = 1e4)."""
     B, T, C = 2, 300, 32
     say(f"extreme keys path={path} k=+-{kmag} io={io}")
     g = np.random.default_rng([7, int(kmag)])
@@ -226,11 +222,11 @@ def test_extreme_keys(path, kmag, io):
         k = I.round_to_bf16(k)
     got, gst = gpu_forward(w, u, k, v, io, path=path)
     ref, rst = wkv_recurrent(w, u, k, v)
-    tol = tol_for(io) if kmag <= 88 else max(tol_for(io), 4 * ulp32(kmag))
+    tol = tol_for(io)
     e = assert_out_close(got, ref, v, tol)
     say(f"  max normalised output error {e:.3e} (bound {tol:.1e})")
     assert np.isfinite(gst).all()
-    assert_state_close(gst, rst, F32_TOL if kmag <= 88 else max(F32_TOL, 4 * ulp32(kmag)))
+    assert_state_close(gst, rst, F32_TOL)
 
 
 def test_auto_path_choice():

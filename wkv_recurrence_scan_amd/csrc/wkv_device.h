@@ -290,17 +290,24 @@ struct Seg {
 __device__ __forceinline__ Seg seg_identity() { return Seg{0.0f, 0.0f, kEmpty, 0.0f}; }
 
 // a then b: a is decayed by b.len steps while b passes, then the two add,
-// relative to the larger exponent.
+// relative to the larger exponent. When a's decayed maximum a.m - b.len w wins
+// it is stored rounded to fp32 (by up to ulp(|m|)/2, 5e-4 at |m| = 1e4); the
+// sums are scaled by e^delta, delta the rounding (formed exactly: the product
+// inside the fma is exact and a.m minus its rounded decay is exact for nearby
+// values), so they stay exact relative to the stored maximum.
 __device__ __forceinline__ Seg seg_combine(const Seg& a, const Seg& b, float w) {
   const float t = __builtin_fmaf(-b.len, w, a.m - b.m);  // (a.m - b.len w) - b.m
   const float e = fast_exp2(__builtin_fabsf(t) * -kLog2e);
   const bool a_wins = t >= 0.0f;
-  const float fa = a_wins ? 1.0f : e;
-  const float fb = a_wins ? e : 1.0f;
+  const float ma = __builtin_fmaf(-b.len, w, a.m);
+  const float delta = __builtin_fmaf(-b.len, w, a.m - ma);  // (a.m - b.len w) - ma
+  const float corr = a_wins ? fast_exp2(delta * kLog2e) : 1.0f;
+  const float fa = a_wins ? corr : e;
+  const float fb = a_wins ? e * corr : 1.0f;
   Seg r;
   r.n = __builtin_fmaf(fa, a.n, fb * b.n);
   r.d = __builtin_fmaf(fa, a.d, fb * b.d);
-  r.m = a_wins ? __builtin_fmaf(-b.len, w, a.m) : b.m;
+  r.m = a_wins ? ma : b.m;
   r.len = a.len + b.len;
   return r;
 }

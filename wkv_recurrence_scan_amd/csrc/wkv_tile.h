@@ -30,22 +30,25 @@ __device__ __forceinline__ Seg shfl_up_seg(const Seg& x, int delta) {
 
 // Summary of one sub-chunk: its own state from empty, maximum taken at the
 // end of the sub-chunk. MASKED: only the first nvalid tokens exist.
+// The maximum `top` is found on the rounded exponents k_i - (last - i) w, but
+// each weight's exponent is then formed against it as (k_i - top) - (last - i) w:
+// the key difference is exact for keys near the maximum, so the sums are exact
+// relative to the stored `top`, however coarse the keys' own grid (at |k| = 1e4
+// rounding k_i - (last - i) w first would move every weight by up to ulp(1e4)).
 template <int L, bool MASKED>
 __device__ __forceinline__ Seg summarize(const float (&kk)[L], const float (&vv)[L], float wd,
                                          int nvalid) {
-  float z[L];
   float top = kEmpty;
   const float last = MASKED ? static_cast<float>(nvalid - 1) : static_cast<float>(L - 1);
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    // exponent of token i once the sub-chunk has ended: k_i - (last - i) w
-    z[i] = __builtin_fmaf(static_cast<float>(i) - last, wd, kk[i]);
-    if (!MASKED || i < nvalid) top = __builtin_fmaxf(top, z[i]);
+    if (!MASKED || i < nvalid)
+      top = __builtin_fmaxf(top, __builtin_fmaf(static_cast<float>(i) - last, wd, kk[i]));
   }
   float n = 0.0f, d = 0.0f;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    float e = fast_exp2((z[i] - top) * kLog2e);
+    float e = fast_exp2(__builtin_fmaf(static_cast<float>(i) - last, wd, kk[i] - top) * kLog2e);
     if (MASKED && i >= nvalid) e = 0.0f;
     d += e;
     n = __builtin_fmaf(e, vv[i], n);
