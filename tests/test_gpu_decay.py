@@ -7,7 +7,7 @@ the constant-decay kernels, the error paths and a sampled check at the
 8-layer model's layer shape.
 
 Tolerances are those of the constant-decay kernels (wkvtest): 1e-5 for fp32,
-2e-2 for bf16 I/O, widened at extreme keys by the exponent's own ulp."""
+2e-2 for bf16 I/O, extreme keys included."""
 
 import ctypes
 
@@ -178,10 +178,6 @@ def test_dd_step_matches_oracle_and_forward(io):
     assert_state_close(host64(ds), rs, F32_TOL)
 
 
-def ulp32(x):
-    return float(np.spacing(np.float32(x)))
-
-
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("kmag", [60.0, 88.0, 1e4])
 def test_dd_extreme_keys(path, kmag):
@@ -192,10 +188,12 @@ def test_dd_extreme_keys(path, kmag):
     k = g.choice(np.array([-kmag, kmag, 0.0, 1.0, -3.0], dtype=np.float32), size=(B, T, C))
     got, gst = gpu_dd(wt, u, k, v, "f32", path=path)
     ref, rst = wkv_dd_recurrent(wt, u, k, v)
-    tol = max(F32_TOL, 4 * ulp32(kmag))
-    e = assert_out_close(got, ref, v, tol)
-    say(f"  max normalised output error {e:.3e} (bound {tol:.1e})")
-    assert_state_close(gst, rst, max(F32_TOL, 4 * ulp32(kmag)))
+    # every exponent difference is formed in fp64 and rounded once, so keys on
+    # the coarse fp32 grid of |k| = 1e4 are held to the flat bound (measured on
+    # MI355X: 1.2e-7 on both paths)
+    e = assert_out_close(got, ref, v, F32_TOL)
+    say(f"  max normalised output error {e:.3e} (bound {F32_TOL:.1e})")
+    assert_state_close(gst, rst, F32_TOL)
 
 
 @pytest.mark.parametrize("path", PATHS)

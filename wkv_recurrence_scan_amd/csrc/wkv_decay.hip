@@ -43,32 +43,34 @@ __device__ __forceinline__ SegD shfl_up_segd(const SegD& x, int delta) {
 
 // Summary of one thread's sub-chunk. Token i has decayed by the rates of the
 // sub-chunk's later steps (accumulated in fp64, newest first); its exponent
-// k_i minus that is rounded once to fp32, as the constant-decay kernels round
-// theirs. MASKED: only the first nvalid tokens exist.
+// k_i minus that stays fp64, and so does the maximum, so each weight's
+// exponent difference is rounded to fp32 only once, right before v_exp_f32
+// (rounding k_i minus the decay to fp32 first would move every weight by up
+// to ulp(|k|): 5e-4 at |k| = 1e4). MASKED: only the first nvalid tokens exist.
 template <int L, bool MASKED>
 __device__ __forceinline__ SegD summarize_d(const float (&kk)[L], const float (&vv)[L],
                                             const float (&ww)[L], int nvalid) {
-  float z[L];
+  double z[L];
   double suf = 0.0;
-  float top = kEmpty;
+  double top = kEmptyD;
 #pragma unroll
   for (int i = L - 1; i >= 0; --i) {
-    z[i] = kEmpty;
+    z[i] = kEmptyD;
     if (!MASKED || i < nvalid) {
-      z[i] = static_cast<float>(static_cast<double>(kk[i]) - suf);
+      z[i] = static_cast<double>(kk[i]) - suf;
       suf += static_cast<double>(ww[i]);
-      top = __builtin_fmaxf(top, z[i]);
+      top = __builtin_fmax(top, z[i]);
     }
   }
   float n = 0.0f, d = 0.0f;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    float e = fast_exp2((z[i] - top) * kLog2e);
+    float e = fast_exp2(static_cast<float>(z[i] - top) * kLog2e);
     if (MASKED && i >= nvalid) e = 0.0f;
     d += e;
     n = __builtin_fmaf(e, vv[i], n);
   }
-  return SegD{n, d, static_cast<double>(top), suf};
+  return SegD{n, d, top, suf};
 }
 
 template <int V>
