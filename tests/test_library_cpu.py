@@ -354,3 +354,15 @@ def test_stress_workload_distribution():
     assert 0.007 < spikes.mean() < 0.013
     assert np.abs(k[~spikes]).max() <= 20.0
     assert np.array_equal(I.round_to_bf16(k), k)
+
+
+def test_autograd_entry_rejects_host_tensors():
+    """The autograd entry point validates like the prefill it wraps: host
+    tensors are refused before any GPU call."""
+    import torch
+
+    import wkv_recurrence_scan_amd as W
+
+    z = torch.zeros((1, 4, 8))
+    with pytest.raises(ValueError, match="GPU"):
+        W.wkv(torch.zeros(8), torch.zeros(8), z, z)

@@ -13,6 +13,7 @@ into that interface (see _lib). Build the library with
     gw_t, gu, gk, gv, gs = wkv_backward_dd(w_t, u, k, v, gout)  # its gradients
     y, S = wkv_matrix_forward(w_t, k, v, r, H)     # matrix-valued state per head
     xs, x_last = wkv_token_shift(mu, x, x_prev)     # token shift ahead of the projections
+    out, state = wkv(w, u, k, v, r=None, state_in=None)  # autograd (checkpointed pair)
 """
 
 from ._lib import (  # noqa: F401
@@ -62,3 +63,4 @@ from ._lib import (  # noqa: F401
     wkv_workspace_status,
     wkv_token_shift,
 )
+from .autograd import WKVFunction, wkv  # noqa: F401,E402
