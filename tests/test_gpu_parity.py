@@ -30,7 +30,7 @@ SHAPES = [
     (1, 1, 1), (2, 2, 7), (1, 3, 16), (3, 31, 33), (2, 32, 5), (2, 63, 48), (2, 64, 64),
     (2, 65, 17), (1, 255, 16), (1, 256, 32), (1, 257, 80), (2, 511, 24), (1, 1000, 40),
     (1, 2048, 31), (1, 2049, 96), (2, 3000, 100), (1, 4097, 16), (1, 513, 40), (2, 1152, 33),
-    (1, 1153, 64),
+    (1, 1153, 64), (2, 2304, 33), (1, 2400, 40),
 ]
 
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ void chunk_tile(const ChunkRegs<V, L, G>& r, int nval
   rescan_sel<IoT, V, L, MASKED, G, CK>(fast, pre, r, wd, ub, cb, nvalid, cvalid, op, C, ck);
 }
 
-template <typename IoT, int V, int LC, int PS, int W, int L, bool G, bool CK>
+template <typename IoT, int V, int LC, int PS, int W, int L, bool G, bool CK, int PD>
 __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
     int64_t B, int64_t T, int64_t C, const float* __restrict__ w, const float* __restrict__ u,
     const typename IoT::elem* __restrict__ k, const typename IoT::elem* __restrict__ v,
@@ -136,18 +136,22 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
   };
 
   const int64_t full = T / TL;  // tiles with every token present
-  // Software pipeline over two register buffers: the loads of the next tile
-  // are issued before the current one is processed. Inside the loop every
-  // load is a real one and unconditional, so the compiler's counter-based
-  // waits stop at the current tile's loads instead of draining the prefetch;
-  // the last one or two tiles are processed after it (two: both loaded up
-  // front), so no tile is read twice.
-  ChunkRegs<V, L, G> A, Bf;
+  // Software pipeline over PD + 1 register buffers: the loads of the next PD
+  // tiles are issued before the current one is processed. Inside the loop
+  // every load is a real one and unconditional, so the compiler's
+  // counter-based waits stop at the current tile's loads instead of draining
+  // the prefetch; the last tiles are processed after it, so no tile is read
+  // twice.
+  static_assert(PD == 1 || PD == 2, "prefetch distance one or two tiles");
+  ChunkRegs<V, L, G> A, Bf, Cr;  // Cr: the third buffer (PD == 2)
   auto at = [&](const typename IoT::elem* p, int64_t t) { return G ? p + t * step : p; };
   auto load = [&](ChunkRegs<V, L, G>& r, int64_t t) {
     chunk_load<IoT, V, L, false, G>(r, kp + t * step, vp + t * step, at(rp, t), C, L);
   };
   if (full > 0) load(A, 0);
+  if constexpr (PD == 2) {
+    if (full > 1) load(Bf, 1);
+  }
   // what needs w, u and the initial state is worked out once the first
   // tile's loads are in flight (each of these waits for its loads)
   float cb[V];
@@ -171,18 +175,37 @@ __global__ __launch_bounds__(64 * W) void wkv_chunk_kernel(
                                                    ck_at(t));
   };
   int64_t tile = 0;
-  for (; tile + 2 < full; tile += 2) {
-    load(Bf, tile + 1);
-    tile_of(A, tile);
-    load(A, tile + 2);
-    tile_of(Bf, tile + 1);
-  }
-  if (tile + 1 < full) {  // two left
-    load(Bf, tile + 1);
-    tile_of(A, tile);
-    tile_of(Bf, tile + 1);
-  } else if (tile < full) {  // one left
-    tile_of(A, tile);
+  if constexpr (PD == 1) {
+    for (; tile + 2 < full; tile += 2) {
+      load(Bf, tile + 1);
+      tile_of(A, tile);
+      load(A, tile + 2);
+      tile_of(Bf, tile + 1);
+    }
+    if (tile + 1 < full) {  // two left
+      load(Bf, tile + 1);
+      tile_of(A, tile);
+      tile_of(Bf, tile + 1);
+    } else if (tile < full) {  // one left
+      tile_of(A, tile);
+    }
+  } else {
+    // A holds tile `tile` and Bf tile + 1 (both in flight) at the top
+    for (; tile + 4 < full; tile += 3) {
+      load(Cr, tile + 2);
+      tile_of(A, tile);
+      load(A, tile + 3);
+      tile_of(Bf, tile + 1);
+      load(Bf, tile + 4);
+      tile_of(Cr, tile + 2);
+    }
+    const int64_t left = full - tile;  // at most four, the first two loaded
+    if (left >= 3) load(Cr, tile + 2);
+    if (left >= 1) tile_of(A, tile);
+    if (left == 4) load(A, tile + 3);
+    if (left >= 2) tile_of(Bf, tile + 1);
+    if (left >= 3) tile_of(Cr, tile + 2);
+    if (left == 4) tile_of(A, tile + 3);
   }
   if (full * TL < T) {  // last, partial tile
     const int64_t first = full * TL + static_cast<int64_t>(sub) * L;
@@ -461,13 +484,13 @@ __global__ __launch_bounds__(128 * kSplitW) void wkv_chunk_split_kernel(
 // us, against 25.7-27.2 for 8 x 8, 4 x 16, 16 x 8 and 4 x 32); long ones
 // smaller tiles (B=4 T=16384 C=2048: 8 x 8, 346 us, against 370-402 for
 // 16 x 8, 8 x 16, 4 x 16 and 4 x 32).
-template <typename IoT, int V, int W, int L, bool G, bool CK>
+template <typename IoT, int V, int W, int L, bool G, bool CK, int PD>
 hipError_t launch_chunk_g(const FwdArgs& a, hipStream_t st) {
   constexpr int CH = kLC * V;
   const int64_t gpr = (a.C + CH - 1) / CH;
   const int64_t blocks = a.B * gpr;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L, G, CK>),
+  hipLaunchKernelGGL((wkv_chunk_kernel<IoT, V, kLC, kPS, W, L, G, CK, PD>),
                      dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0, st, a.B, a.T, a.C,
                      a.w, a.u, static_cast<const typename IoT::elem*>(a.k),
                      static_cast<const typename IoT::elem*>(a.v),
@@ -477,18 +500,20 @@ hipError_t launch_chunk_g(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename IoT, int V, int W, int L>
+// PD: prefetch distance of ungated calls (gated ones keep one tile: a third
+// buffer of k, v and r would cost a workgroup per CU)
+template <typename IoT, int V, int W, int L, int PD = 1>
 hipError_t launch_chunk_t(const FwdArgs& a, hipStream_t st) {
   if constexpr (std::is_same<IoT, IoF32>::value && V == 1) {
     if (a.ckpt != nullptr) {
-      return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true, true>(a, st)
-                            : launch_chunk_g<IoT, V, W, L, false, true>(a, st);
+      return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true, true, 1>(a, st)
+                            : launch_chunk_g<IoT, V, W, L, false, true, PD>(a, st);
     }
   } else {
     if (a.ckpt != nullptr) return hipErrorInvalidValue;  // checkpoints: fp32 only
   }
-  return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true, false>(a, st)
-                        : launch_chunk_g<IoT, V, W, L, false, false>(a, st);
+  return a.r != nullptr ? launch_chunk_g<IoT, V, W, L, true, false, 1>(a, st)
+                        : launch_chunk_g<IoT, V, W, L, false, false, PD>(a, st);
 }
 
 template <typename IoT, int V, bool G, bool CK>
@@ -533,7 +558,10 @@ hipError_t launch_chunk_v(const FwdArgs& a, int cus, hipStream_t st) {
     const bool gated_f32 = std::is_same<IoT, IoF32>::value && a.r != nullptr;
     return gated_f32 ? launch_chunk_t<IoT, V, 8, 8>(a, st) : launch_chunk_t<IoT, V, 8, 16>(a, st);
   }
-  return launch_chunk_t<IoT, V, 8, 8>(a, st);
+  // long sequences walk many tiles, one after another: with one channel per
+  // thread the loads run two tiles ahead (84 -> 103 VGPRs, still two 8-wave
+  // workgroups per CU; two channels per thread would drop to one)
+  return launch_chunk_t<IoT, V, 8, 8, V == 1 ? 2 : 1>(a, st);
 }
 
 bool aligned(const void* p, int bytes) {
